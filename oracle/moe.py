@@ -1,0 +1,453 @@
+"""Plain fp64 reference of the token-choice MoE layer (test infrastructure only).
+
+Notation: T tokens, d model width, E routed experts, k experts per token,
+f expert FFN width, A = T*k (token, expert) assignments.
+
+Where the pages leave a step open, the reading taken is stated at the function.
+Everything is computed in float64.  For layers whose storage type is bf16 the
+oracle rounds to bf16 exactly where such a layer stores a bf16 tensor
+(``bf16_points=True``): the saved gate/up pre-activations G and U, the SwiGLU
+output H, the gate-scaled output gradient dY_perm and the SwiGLU input
+gradients dG, dU.  Expert outputs, the combined output and every gradient that
+leaves the layer stay in high precision.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+SCORE_FNS = ("softmax", "sigmoid", "sqrt_softplus")
+
+
+# ----------------------------------------------------------------------------
+# bf16 storage (the oracle's own conversion; checked against torch in the tests)
+
+def bf16_from_bits(bits: np.ndarray) -> np.ndarray:
+    """Value of uint16 bf16 bit patterns, as float64 (exact)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def bf16_round(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value (8 significant bits,
+    ties to even), returned as float64.  Finite normal range only."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)                 # v = m * 2**e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)   # np.rint rounds half to even
+
+
+def _f64(a: np.ndarray) -> np.ndarray:
+    """Inputs arrive as float32/float64 arrays or as uint16 bf16 bit patterns."""
+    a = np.asarray(a)
+    return bf16_from_bits(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# routing — lesson "专家组合 (MoE)", Concept and Build it step 1; router score
+# functions and fp32 rule from the AREX article's router-precision paragraph.
+
+def score(logits: np.ndarray, fn: str) -> np.ndarray:
+    """Router score of each logit.
+
+    softmax: the raw logit itself (the softmax is taken later, over the chosen
+    experts only, as the lesson's router does); sigmoid: 1/(1+e^-l);
+    sqrt_softplus: sqrt(ln(1+e^l)), with ln(1+e^l) = max(l,0) + ln(1+e^-|l|)
+    (the two pages only name the last two functions; these are their standard
+    definitions)."""
+    l = np.asarray(logits, dtype=np.float64)
+    if fn == "softmax":
+        return l.copy()
+    if fn == "sigmoid":
+        return 1.0 / (1.0 + np.exp(-l))
+    if fn == "sqrt_softplus":
+        return np.sqrt(np.maximum(l, 0.0) + np.log1p(np.exp(-np.abs(l))))
+    raise ValueError(fn)
+
+
+def route(x, w_router, k: int, score_fn: str, sel_bias=None, logit_offset=None) -> dict:
+    """Router, top-k and gates for every token.
+
+    * logits l = x . W_r^T (+ a per-expert logit offset, used by synthetic
+      skewed workloads; it is part of the raw logit);
+    * selection key = score + bias: the loss-free bias moves which experts are
+      chosen but never enters the gate (lesson, Load balancing, and the remark
+      after Build it step 1);
+    * the k largest keys are chosen by a stable sort on -key, so equal keys go
+      to the lower expert index; slot order is the sort order;
+    * gates: softmax over the chosen experts' raw logits (lesson, step 1) for
+      ``softmax``; otherwise each chosen score divided by the sum of the chosen
+      scores.
+
+    Returns idx [T,k] int64, gates [T,k], logits [T,E], scores [T,E],
+    keys [T,E], margin [T] = |key_(k) - key_(k+1)| / max(|key_(k)|, |key_(k+1)|)
+    (0 when both are 0, +inf when k == E).
+    """
+    x = _f64(x)
+    w = _f64(w_router)
+    T = x.shape[0]
+    E = w.shape[0]
+    assert 1 <= k <= E
+    logits = x @ w.T
+    if logit_offset is not None:
+        logits = logits + _f64(logit_offset)[None, :]
+    s = score(logits, score_fn)
+    b = np.zeros(E) if sel_bias is None else _f64(sel_bias)
+    keys = s + b[None, :]
+    idx = np.empty((T, k), np.int64)
+    gates = np.empty((T, k))
+    margin = np.full(T, np.inf)
+    for t in range(T):
+        order = np.argsort(-keys[t], kind="stable")
+        chosen = order[:k]
+        idx[t] = chosen
+        if k < E:
+            a, c = keys[t, order[k - 1]], keys[t, order[k]]
+            den = max(abs(a), abs(c))
+            margin[t] = abs(a - c) / den if den > 0 else 0.0
+        if score_fn == "softmax":
+            raw = logits[t, chosen]
+            ex = np.exp(raw - raw.max())
+            gates[t] = ex / ex.sum()
+        else:
+            sc = s[t, chosen]
+            gates[t] = sc / sc.sum()
+    return {"idx": idx, "gates": gates, "logits": logits, "scores": s,
+            "keys": keys, "margin": margin}
+
+
+def route_token_lesson(hidden, W_router, top_k, bias, score_fn="softmax", offset=None):
+    """One token routed with plain Python lists and loops (lesson, Build it
+    step 1): E dot products, bias added for the ranking only, a stable sort,
+    then gates from the unbiased values of the chosen experts."""
+    E = len(W_router)
+    raw = []
+    for e in range(E):
+        acc = 0.0
+        for h, w in zip(hidden, W_router[e]):
+            acc += float(h) * float(w)
+        if offset is not None:
+            acc += float(offset[e])
+        raw.append(acc)
+    if score_fn == "softmax":
+        sc = raw[:]
+    elif score_fn == "sigmoid":
+        sc = [1.0 / (1.0 + math.exp(-v)) for v in raw]
+    else:
+        sc = [math.sqrt(max(v, 0.0) + math.log1p(math.exp(-abs(v)))) for v in raw]
+    biased = [sc[e] + float(bias[e]) for e in range(E)]
+    top = sorted(range(E), key=lambda e: -biased[e])[:top_k]
+    if score_fn == "softmax":
+        chosen = [raw[e] for e in top]
+        m = max(chosen)
+        ex = [math.exp(c - m) for c in chosen]
+        tot = sum(ex)
+        return top, [v / tot for v in ex]
+    chosen = [sc[e] for e in top]
+    tot = sum(chosen)
+    return top, [v / tot for v in chosen]
+
+
+# ----------------------------------------------------------------------------
+# permute — grouping the (token, expert) pairs by expert ahead of the expert
+# GEMMs (the "permute" the AREX article's permute-fusion paragraph refers to).
+
+def permute(idx: np.ndarray, E: int):
+    """Stable counting sort of the T*k assignments by expert.
+
+    counts[e] = number of assignments to e; offsets = exclusive prefix sum
+    (length E+1).  Experts are walked in ascending order and, inside an expert,
+    tokens in ascending order (the pages do not fix this order; ascending token
+    order makes the permutation unique).  Assignment (t, j) takes row
+    row_of[t, j]; token_of[row] = t."""
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    counts = np.zeros(E, np.int64)
+    for e in range(E):
+        counts[e] = int(np.count_nonzero(idx == e))
+    offsets = np.zeros(E + 1, np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    row_of = np.full((T, k), -1, np.int64)
+    token_of = np.full(T * k, -1, np.int64)
+    for e in range(E):
+        ts, js = np.nonzero(idx == e)      # row-major: tokens ascending
+        rows = offsets[e] + np.arange(len(ts))
+        row_of[ts, js] = rows
+        token_of[rows] = ts
+    return counts, offsets, row_of, token_of
+
+
+# ----------------------------------------------------------------------------
+# experts — each expert is an independent SwiGLU FFN (lesson, Concept; Key
+# terms "Expert").  Weight layout: w_gate_up [2f, d] (gate rows, then up rows),
+# w_down [d, f].
+
+def _silu(z):
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(xr, w_gate_up, w_down, bf16_points: bool) -> dict:
+    """SwiGLU expert on rows xr [n, d]: G = xr Wg^T, U = xr Wu^T,
+    H = silu(G) * U (computed from the unrounded G and U), Y = H Wd^T.
+    Returns G, U (saved form: bf16-rounded when bf16_points), H, Y."""
+    xr = _f64(xr)
+    wgu = _f64(w_gate_up)
+    wd = _f64(w_down)
+    f = wd.shape[1]
+    G = xr @ wgu[:f].T
+    U = xr @ wgu[f:].T
+    H = _silu(G) * U
+    if bf16_points:
+        H = bf16_round(H)
+        Gs, Us = bf16_round(G), bf16_round(U)
+    else:
+        Gs, Us = G, U
+    Y = H @ wd.T
+    return {"G": Gs, "U": Us, "H": H, "Y": Y}
+
+
+def grouped_ffn(x_perm, offsets, w_gate_up, w_down, bf16_points: bool) -> dict:
+    """Expert e applied to rows offsets[e]:offsets[e+1] of x_perm."""
+    x_perm = _f64(x_perm)
+    G_ = len(offsets) - 1
+    A = x_perm.shape[0]
+    f = np.asarray(w_down).shape[2]
+    d = np.asarray(w_down).shape[1]
+    out = {"G": np.zeros((A, f)), "U": np.zeros((A, f)), "H": np.zeros((A, f)),
+           "Y": np.zeros((A, d))}
+    for e in range(G_):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b == a:
+            continue
+        r = expert_ffn(x_perm[a:b], w_gate_up[e], w_down[e], bf16_points)
+        for key in out:
+            out[key][a:b] = r[key]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# combine — out = sum over the chosen experts of gate * expert output, plus the
+# shared experts every token passes through (lesson, Concept and Shared
+# experts).  The residual add sits outside the layer.
+
+def combine(y_perm, row_of, gates, shared_y=None):
+    y_perm = np.asarray(y_perm, np.float64)
+    T, k = row_of.shape
+    out = np.zeros((T, y_perm.shape[1])) if shared_y is None else np.array(shared_y, np.float64)
+    for j in range(k):
+        out += np.asarray(gates, np.float64)[:, j:j + 1] * y_perm[row_of[:, j]]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# loss-free balancing bias controller (lesson, Load balancing item 3 and Build
+# it step 2)
+
+def bias_update(bias, counts, T: int, k: int, gamma: float) -> np.ndarray:
+    """After a step, an expert used more than the uniform target T*k/E moves its
+    bias down by gamma, one used less moves it up, one exactly on target keeps
+    it.  The target comparison is done in integers (E*count vs T*k); the update
+    is one float32 add, as the bias is stored in float32."""
+    b = np.array(bias, dtype=np.float32)
+    E = b.shape[0]
+    g = np.float32(gamma)
+    for e in range(E):
+        load = E * int(counts[e])
+        if load > T * k:
+            b[e] = np.float32(b[e] - g)
+        elif load < T * k:
+            b[e] = np.float32(b[e] + g)
+    return b
+
+
+# ----------------------------------------------------------------------------
+# whole forward
+
+def forward(x, w_router, w_gate_up, w_down, k: int, score_fn: str, bf16_points: bool,
+            sel_bias=None, logit_offset=None, w_gate_up_shared=None, w_down_shared=None,
+            idx=None) -> dict:
+    """Route, permute, run the experts, add the shared experts, combine.
+
+    ``idx`` forces the expert choice (stage-isolated checks feed the GPU's own
+    choice); gates are then recomputed for that choice."""
+    E = np.asarray(w_router).shape[0]
+    r = route(x, w_router, k, score_fn, sel_bias, logit_offset)
+    if idx is not None:
+        idx = np.asarray(idx, np.int64)
+        r["idx"] = idx
+        r["gates"] = _gates_for(r, idx, score_fn)
+    counts, offsets, row_of, token_of = permute(r["idx"], E)
+    x64 = _f64(x)
+    x_perm = x64[token_of]
+    ex = grouped_ffn(x_perm, offsets, w_gate_up, w_down, bf16_points)
+    shared_y = None
+    sh = []
+    if w_gate_up_shared is not None:
+        shared_y = np.zeros_like(x64)
+        for s in range(len(w_gate_up_shared)):
+            o = expert_ffn(x64, w_gate_up_shared[s], w_down_shared[s], bf16_points)
+            sh.append(o)
+            shared_y += o["Y"]
+    out = combine(ex["Y"], row_of, r["gates"], shared_y)
+    res = dict(r)
+    res.update(counts=counts, offsets=offsets, row_of=row_of, token_of=token_of,
+               x_perm=x_perm, G=ex["G"], U=ex["U"], H=ex["H"], y_perm=ex["Y"],
+               shared=sh, shared_y=shared_y, out=out)
+    return res
+
+
+def _gates_for(r: dict, idx: np.ndarray, score_fn: str) -> np.ndarray:
+    T, k = idx.shape
+    g = np.empty((T, k))
+    for t in range(T):
+        if score_fn == "softmax":
+            raw = r["logits"][t, idx[t]]
+            ex = np.exp(raw - raw.max())
+            g[t] = ex / ex.sum()
+        else:
+            sc = r["scores"][t, idx[t]]
+            g[t] = sc / sc.sum()
+    return g
+
+
+# ----------------------------------------------------------------------------
+# backward (chain rule through the forward above; the bias, the logit offset and
+# the discrete top-k choice get no gradient — lesson, Key terms: the loss-free
+# bias adds no gradient signal)
+
+def gate_backward(dg, gates, logits_chosen, scores_chosen, score_fn: str):
+    """d loss / d logit of each chosen expert, given d loss / d gate.
+
+    softmax over the chosen: dl_j = g_j (dg_j - D), D = sum_i g_i dg_i.
+    normalised scores g_j = s_j / S: ds_j = (dg_j - D) / S, then
+    dl_j = ds_j * s'(l_j) with s' = s(1-s) for the sigmoid and
+    sigmoid(l) / (2 s) for sqrt(softplus)."""
+    dg = np.asarray(dg, np.float64)
+    g = np.asarray(gates, np.float64)
+    D = np.sum(g * dg, axis=1, keepdims=True)
+    if score_fn == "softmax":
+        return g * (dg - D)
+    s = np.asarray(scores_chosen, np.float64)
+    S = np.sum(s, axis=1, keepdims=True)
+    ds = (dg - D) / S
+    l = np.asarray(logits_chosen, np.float64)
+    if score_fn == "sigmoid":
+        return ds * s * (1.0 - s)
+    if score_fn == "sqrt_softplus":
+        return ds * (1.0 / (1.0 + np.exp(-l))) / (2.0 * s)
+    raise ValueError(score_fn)
+
+
+def router_backward(dl, idx, x, w_router):
+    """logits = x W_r^T: dW_r = dL^T x and dx = dL W_r, with dL the [T,E]
+    logit gradient that is dl at the chosen experts and zero elsewhere."""
+    x = _f64(x)
+    w = _f64(w_router)
+    T, k = idx.shape
+    E = w.shape[0]
+    dL = np.zeros((T, E))
+    for j in range(k):
+        dL[np.arange(T), idx[:, j]] += dl[:, j]
+    return dL.T @ x, dL @ w
+
+
+def expert_backward_rows(dy_rows, xr, G, U, H, w_gate_up, w_down, bf16_points: bool) -> dict:
+    """Backward of one SwiGLU expert over rows xr, given d loss / d Y rows.
+
+    dH = dY Wd; dG = dH * U * silu'(G); dU = dH * silu(G) (G, U in their saved
+    form); dWd = dY^T H; dWg = dG^T xr; dWu = dU^T xr; dX = dG Wg + dU Wu.
+    silu'(z) = sigma(z) (1 + z (1 - sigma(z)))."""
+    xr = _f64(xr)
+    wgu = _f64(w_gate_up)
+    wd = _f64(w_down)
+    f = wd.shape[1]
+    dy = np.asarray(dy_rows, np.float64)
+    dH = dy @ wd
+    sg = 1.0 / (1.0 + np.exp(-G))
+    dG = dH * U * sg * (1.0 + G * (1.0 - sg))
+    dU = dH * (G * sg)
+    if bf16_points:
+        dG, dU = bf16_round(dG), bf16_round(dU)
+    dX = dG @ wgu[:f] + dU @ wgu[f:]
+    dWgu = np.concatenate([dG.T @ xr, dU.T @ xr], axis=0)
+    dWd = dy.T @ H
+    return {"dH": dH, "dG": dG, "dU": dU, "dX": dX, "dW_gate_up": dWgu, "dW_down": dWd}
+
+
+def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
+             bf16_points: bool, w_gate_up_shared=None, w_down_shared=None) -> dict:
+    """Gradients of sum(out * dy) with respect to x and every weight.
+
+    combine:   dg[t,j] = <dy[t], Y[row_of[t,j]]>, dY_perm[row_of[t,j]] = g[t,j] dy[t]
+    gates:     dl via gate_backward; router: dW_r, dx_r via router_backward
+    experts:   expert_backward_rows per expert segment
+    unpermute: dx[t] = sum_j dX_perm[row_of[t,j]] + dx_r[t] (+ shared experts' dX)
+    """
+    dy = _f64(dy)
+    idx, gates, row_of = fwd["idx"], fwd["gates"], fwd["row_of"]
+    T, k = idx.shape
+    E = np.asarray(w_router).shape[0]
+    A = T * k
+    d = dy.shape[1]
+    y = fwd["y_perm"]
+    dg = np.empty((T, k))
+    dy_perm = np.zeros((A, d))
+    for j in range(k):
+        dg[:, j] = np.sum(dy * y[row_of[:, j]], axis=1)
+        dy_perm[row_of[:, j]] = gates[:, j:j + 1] * dy
+    if bf16_points:
+        dy_perm = bf16_round(dy_perm)
+    tt = np.arange(T)[:, None]
+    lc = fwd["logits"][tt, idx]
+    sc = fwd["scores"][tt, idx]
+    dl = gate_backward(dg, gates, lc, sc, score_fn)
+    dW_r, dx = router_backward(dl, idx, x, w_router)
+    f = np.asarray(w_down).shape[2]
+    dW_gu = np.zeros((E, 2 * f, d))
+    dW_d = np.zeros((E, d, f))
+    dX_perm = np.zeros((A, d))
+    dGU = np.zeros((A, 2 * f))
+    offs = fwd["offsets"]
+    for e in range(E):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if a == b:
+            continue
+        r = expert_backward_rows(dy_perm[a:b], fwd["x_perm"][a:b], fwd["G"][a:b], fwd["U"][a:b],
+                                 fwd["H"][a:b], w_gate_up[e], w_down[e], bf16_points)
+        dW_gu[e], dW_d[e] = r["dW_gate_up"], r["dW_down"]
+        dX_perm[a:b] = r["dX"]
+        dGU[a:b, :f], dGU[a:b, f:] = r["dG"], r["dU"]
+    for j in range(k):
+        dx += dX_perm[row_of[:, j]]
+    out = {"dx": dx, "dw_router": dW_r, "dw_gate_up": dW_gu, "dw_down": dW_d,
+           "dg": dg, "dl": dl, "dy_perm": dy_perm, "dx_perm": dX_perm, "dgu": dGU}
+    if w_gate_up_shared is not None:
+        x64 = _f64(x)
+        out["dw_gate_up_shared"], out["dw_down_shared"] = [], []
+        for s, o in enumerate(fwd["shared"]):
+            r = expert_backward_rows(dy, x64, o["G"], o["U"], o["H"], w_gate_up_shared[s],
+                                     w_down_shared[s], bf16_points)
+            out["dx"] = out["dx"] + r["dX"]
+            out["dw_gate_up_shared"].append(r["dW_gate_up"])
+            out["dw_down_shared"].append(r["dW_down"])
+    return out
+
+
+# ----------------------------------------------------------------------------
+# parameter arithmetic (lesson, Fine-grained experts and Cost profile; AREX
+# article, the 64-expert top-8 teaching model)
+
+def moe_ffn_params(d: int, f: int, E: int, k: int, shared: int = 0, f_shared: int = 0):
+    """(stored, active-per-token) parameters of one SwiGLU MoE layer:
+    E experts of 3*d*f each, a d x E router, shared experts always active."""
+    per = 3 * d * f
+    sh = shared * 3 * d * f_shared
+    return E * per + d * E + sh, k * per + d * E + sh
+
+
+def dense_ffn_params(d: int, F: int) -> int:
+    """A dense SwiGLU FFN of width F (gate, up and down projections)."""
+    return 3 * d * F
