@@ -1,0 +1,248 @@
+/*
+ * moe.h — C ABI of the token-choice Mixture-of-Experts layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer (as the "专家组合 (MoE)" lesson of AI Engineering from Scratch
+ * states it in its Concept section): a linear router scores every token
+ * against E experts, each token picks its k best experts, each chosen expert
+ * is an independent SwiGLU FFN, and the layer output is the gate-weighted sum
+ * of the chosen experts' outputs, plus the output of shared experts that every
+ * token passes through (Shared experts section).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked HOST.  The caller owns and
+ *     allocates every buffer, including workspaces (size them with
+ *     moe_workspace_size); the library allocates nothing per call and keeps no
+ *     pointer after a call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work and return without synchronising; device-side
+ *     faults surface at the caller's next synchronisation.
+ *   - Matrices are row-major with the last index contiguous.  Weights use the
+ *     nn.Linear layout [out, in].  bf16 tensors are raw 16-bit bf16 values.
+ *   - Indices and counts are int32; sizes are int64 where they can pass 2^31.
+ *   - Arguments are checked before anything is enqueued: MOE_EINVAL for a
+ *     NULL required pointer, a non-positive size, k outside [1, E] or a
+ *     workspace smaller than moe_workspace_size asks for; MOE_ENOTSUP for
+ *     shapes outside the supported set (stated per call); MOE_EHIP when a
+ *     kernel launch fails.  Nothing is enqueued when a call fails.
+ *   - Values that must agree between calls (offsets[G] == rows, the expert
+ *     indices being in [0, E)) live on the device and are not checked.
+ *   - NaN or Inf inputs give undefined expert selection.
+ *   - Calls on different streams with disjoint buffers may run concurrently;
+ *     the library has no mutable global state.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int moe_status;
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,     /* bad argument */
+  MOE_ENOTSUP = 2,    /* shape or option outside what the library supports */
+  MOE_EWORKSPACE = 3, /* workspace missing or too small */
+  MOE_EHIP = 4        /* a HIP runtime call or kernel launch failed */
+};
+
+/* storage type of activations and expert weights */
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+
+/* Router score function and gate rule.  The AREX article on The Ultimate MoE
+ * Training Handbook (router-precision paragraph) names the three score
+ * functions; the lesson's Build-it step 1 fixes the softmax-over-chosen gate.
+ *   MOE_SOFTMAX_CHOSEN:     score = logit; gates = softmax of the chosen
+ *                           experts' raw logits.
+ *   MOE_SIGMOID_NORM:       score = 1/(1+e^-logit); gates = chosen scores
+ *                           divided by their sum.
+ *   MOE_SQRT_SOFTPLUS_NORM: score = sqrt(ln(1+e^logit)); gates as above. */
+enum moe_score { MOE_SOFTMAX_CHOSEN = 0, MOE_SIGMOID_NORM = 1, MOE_SQRT_SOFTPLUS_NORM = 2 };
+
+/* which call a workspace is sized for */
+enum moe_call { MOE_CALL_ROUTE = 0, MOE_CALL_PERMUTE = 1, MOE_CALL_GROUPED_FFN = 2, MOE_CALL_BACKWARD = 3 };
+
+/* Largest supported expert count and top-k (the handbook article's router
+ * table has a model choosing 16 of 896 experts, the largest on the pages). */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 16
+
+/*
+ * moe_route — router GEMM, scoring, top-k selection and gates.
+ * Lesson "专家组合 (MoE)", Concept (scores = router(x), top-k) and Build it
+ * step 1 (bias added for the ranking only; gates from the unbiased values);
+ * Load balancing item 3 (the DeepSeek-V3 auxiliary-loss-free bias).
+ *
+ *   x            [T, d]  activations, x_dtype (MOE_F32 or MOE_BF16)
+ *   w_router     [E, d]  f32 router weight
+ *   logit_offset [E]     f32 or NULL: added to every token's logit for expert
+ *                        e (a fixed router bias term; it is part of the raw
+ *                        logit, so it moves both selection and gates)
+ *   sel_bias     [E]     f32 or NULL: the loss-free balancing bias; added to
+ *                        the score for selection only, never to a gate
+ *   E, k, score_fn       experts, experts per token, enum moe_score
+ *   topk_idx     [T, k]  int32 out: chosen experts, best first (key
+ *                        descending, equal keys to the lower expert index)
+ *   topk_gate    [T, k]  f32 out: gate of each chosen expert
+ *   logits_out   [T, E]  f32 out: router logits (offset included), kept for
+ *                        the backward
+ * Logits are computed in fp32 from x (bf16 widened exactly) and W_r, with
+ * blocked accumulation (partial sums of at most 64 products).
+ * ENOTSUP: E > MOE_MAX_EXPERTS, k > MOE_MAX_TOPK, d not a multiple of 8.
+ */
+moe_status moe_route(const void* x, int x_dtype, int64_t T, int64_t d,
+                     const float* w_router, const float* logit_offset, const float* sel_bias,
+                     int E, int k, int score_fn,
+                     int32_t* topk_idx, float* topk_gate, float* logits_out, void* stream);
+
+/*
+ * moe_permute — group the T*k (token, expert) assignments by expert.
+ * The expert GEMMs need each expert's tokens contiguous: this is the
+ * "permute" step whose fusion the AREX article's paragraph on hiding
+ * all-to-all reports (permute/copy kernels 11.45% -> 7.14% of step time).
+ * Stable counting sort: experts ascending, and inside an expert the tokens
+ * ascending, so the result is unique and reproducible bit for bit.  No
+ * atomics are used.
+ *
+ *   topk_idx [T, k]     int32 expert per assignment (from moe_route)
+ *   x        [T, d]     rows to copy, x_dtype
+ *   counts   [E]        int32 out: assignments per expert
+ *   offsets  [E+1]      int32 out: exclusive prefix sum of counts
+ *   row_of   [T, k]     int32 out: row of assignment (t, j) in x_perm
+ *   token_of [T*k]      int32 out: token of each x_perm row
+ *   x_perm   [T*k, d]   out: x_perm[r] = x[token_of[r]] (bit copy)
+ *   workspace           moe_workspace_size(MOE_CALL_PERMUTE, T, k, E, d, 0)
+ * ENOTSUP: E > MOE_MAX_EXPERTS, k > MOE_MAX_TOPK, T*k >= 2^31, d*elem not a
+ * multiple of 16 bytes.
+ */
+moe_status moe_permute(const int32_t* topk_idx, int64_t T, int k, int E,
+                       const void* x, int x_dtype, int64_t d,
+                       int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* token_of,
+                       void* x_perm, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_grouped_ffn — G independent SwiGLU experts over row segments.
+ * Lesson, Concept: each expert is an independent FFN, usually SwiGLU.
+ * Expert g runs on rows offsets[g] .. offsets[g+1]-1 of x_rows:
+ *   G = X W_gate^T, U = X W_up^T, H = silu(G) * U, Y = H W_down^T,
+ *   silu(z) = z / (1 + e^-z).
+ * The shared expert of the lesson's Shared-experts section is the same call
+ * with G = 1 and offsets = {0, T} over the layer input.
+ *
+ *   x_rows     [rows, d]     dtype
+ *   offsets    [G+1]         int32, offsets[0] = 0, offsets[G] = rows
+ *   w_gate_up  [G, 2f, d]    dtype: f gate rows, then f up rows per expert
+ *   w_down     [G, d, f]     dtype
+ *   gu_saved   [rows, 2f]    dtype out or NULL: G (cols 0..f-1) and U
+ *                            (cols f..2f-1), kept for the backward
+ *   h          [rows, f]     dtype out: SwiGLU output (from the unrounded
+ *                            fp32 G and U)
+ *   y          [rows, d]     f32 out
+ *   workspace                moe_workspace_size(MOE_CALL_GROUPED_FFN, rows, 1, G, d, f)
+ * bf16 uses MFMA with fp32 accumulation; f32 uses fp32 FMA.
+ * ENOTSUP: G > MOE_MAX_EXPERTS, rows >= 2^31; bf16 needs d and f to be
+ * multiples of 64; f32 needs d a multiple of 4.
+ */
+moe_status moe_grouped_ffn(const void* x_rows, int64_t rows, int64_t d, int dtype,
+                           const int32_t* offsets, int G, int64_t f,
+                           const void* w_gate_up, const void* w_down,
+                           void* gu_saved, void* h, float* y,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_combine — gate-weighted sum of each token's expert outputs.
+ * Lesson, Concept: the layer adds, over the chosen experts, gate times the
+ * expert's output; shared experts add their output unweighted.  The residual
+ * add of the transformer block is outside this call.
+ *   out[t] = shared_y[t] + sum_j topk_gate[t,j] * y_perm[row_of[t,j]]
+ * summed in fp32, j ascending.
+ *   y_perm   [T*k, d] f32;  row_of [T, k] int32;  topk_gate [T, k] f32
+ *   shared_y [T, d]   f32 or NULL
+ *   out      [T, d]   out_dtype (MOE_F32, or MOE_BF16 rounded to nearest even)
+ * ENOTSUP: k > MOE_MAX_TOPK, d not a multiple of 4.
+ */
+moe_status moe_combine(const float* y_perm, const int32_t* row_of, const float* topk_gate,
+                       const float* shared_y, int64_t T, int k, int64_t d,
+                       void* out, int out_dtype, void* stream);
+
+/*
+ * moe_bias_update — the loss-free balancing controller.
+ * Lesson, Load balancing item 3 and Build it step 2: after each step an
+ * expert used more than the uniform target moves its bias down by gamma, one
+ * used less moves it up.  Here: E*counts[e] > T*k -> bias[e] -= gamma;
+ * E*counts[e] < T*k -> bias[e] += gamma; equal -> unchanged (integer
+ * comparison, one fp32 add).
+ *   sel_bias [E] f32 in/out;  counts [E] int32 (from moe_permute)
+ */
+moe_status moe_bias_update(float* sel_bias, const int32_t* counts, int E, int64_t T, int k,
+                           float gamma, void* stream);
+
+/*
+ * moe_backward — gradients of the routed layer (training).
+ * The pages give no backward formulas; this is the chain rule through the
+ * forward above.  The selection bias and the logit offset get no gradient
+ * (lesson, Key terms: the loss-free bias adds no gradient signal), and the
+ * discrete top-k choice is held fixed.
+ *   combine:  dg[t,j] = <dy[t], y_perm[row_of[t,j]]>,
+ *             dY_perm[row_of[t,j]] = bf16(gate[t,j] * dy[t])
+ *   gates:    softmax: dl_j = g_j (dg_j - D), D = sum_i g_i dg_i;
+ *             normalised scores: dl_j = (dg_j - D) / S * s'(l_j), S = sum s
+ *   router:   dW_r = dL^T x, dx_r = dL W_r (dL = dl at the chosen experts)
+ *   experts:  dH = dY_perm W_down; dG = bf16(dH U silu'(G));
+ *             dU = bf16(dH silu(G)) from the saved bf16 G, U;
+ *             dW_down = dY_perm^T H; dW_gate = dG^T X; dW_up = dU^T X;
+ *             dX_perm = dG W_gate + dU W_up
+ *   unpermute: dx[t] = sum_j dX_perm[row_of[t,j]] + dx_r[t]
+ * All pointers are device pointers held in a HOST struct.  bf16 layers only.
+ */
+typedef struct moe_bwd_args {
+  size_t struct_size;          /* sizeof(moe_bwd_args): the ABI version */
+  int64_t T, d, f;
+  int E, k, score_fn;
+  /* inputs */
+  const void* dy;              /* [T, d] bf16: gradient of the layer output */
+  const void* x;               /* [T, d] bf16 */
+  const float* w_router;       /* [E, d] */
+  const float* logits;         /* [T, E] from moe_route */
+  const int32_t* topk_idx;     /* [T, k] */
+  const float* topk_gate;      /* [T, k] */
+  const int32_t* row_of;       /* [T, k] */
+  const int32_t* token_of;     /* [T*k] */
+  const int32_t* offsets;      /* [E+1] */
+  const void* x_perm;          /* [T*k, d] bf16 */
+  const void* gu_saved;        /* [T*k, 2f] bf16 */
+  const void* h;               /* [T*k, f] bf16 */
+  const float* y_perm;         /* [T*k, d] f32 */
+  const void* w_gate_up;       /* [E, 2f, d] bf16 */
+  const void* w_down;          /* [E, d, f] bf16 */
+  /* outputs (f32) */
+  float* dx;                   /* [T, d] */
+  float* dw_router;            /* [E, d] */
+  float* dw_gate_up;           /* [E, 2f, d] */
+  float* dw_down;              /* [E, d, f] */
+  float* dgate;                /* [T, k] or NULL: dg, exposed for checking */
+  float* dlogit;               /* [T, k] or NULL: dl at the chosen experts */
+  void* workspace;
+  size_t workspace_bytes;      /* moe_workspace_size(MOE_CALL_BACKWARD, T, k, E, d, f) */
+} moe_bwd_args;
+
+/* ENOTSUP: non-bf16 use, d or f not a multiple of 64, E > MOE_MAX_EXPERTS,
+ * k > MOE_MAX_TOPK.  EINVAL also for struct_size != sizeof(moe_bwd_args). */
+moe_status moe_backward(const moe_bwd_args* args, void* stream);
+
+/* Workspace bytes a call needs (0 if it needs none).  `which` is enum
+ * moe_call; arguments a call does not use are ignored.  For
+ * MOE_CALL_GROUPED_FFN pass T = rows, k = 1, E = G. */
+size_t moe_workspace_size(int which, int64_t T, int k, int E, int64_t d, int64_t f);
+
+/* Static description of a status code. */
+const char* moe_status_str(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,214 @@
+"""ctypes binding of libmoe.so: the C ABI of include/moe.h, one Python function
+per entry point, same names.  Argument marshalling only — every step runs in
+the library's HIP kernels; torch supplies device memory and the stream.
+
+The library must have been built (``python -m mixture_experts_layer_free_amd.build``);
+loading fails loudly otherwise.  There is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+SCORE = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2}
+MOE_CALL_ROUTE, MOE_CALL_PERMUTE, MOE_CALL_GROUPED_FFN, MOE_CALL_BACKWARD = range(4)
+MAX_EXPERTS, MAX_TOPK = 1024, 16
+
+_vp, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+
+
+class BwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", _sz), ("T", _i64), ("d", _i64), ("f", _i64),
+        ("E", _int), ("k", _int), ("score_fn", _int),
+        ("dy", _vp), ("x", _vp), ("w_router", _vp), ("logits", _vp), ("topk_idx", _vp),
+        ("topk_gate", _vp), ("row_of", _vp), ("token_of", _vp), ("offsets", _vp), ("x_perm", _vp),
+        ("gu_saved", _vp), ("h", _vp), ("y_perm", _vp), ("w_gate_up", _vp), ("w_down", _vp),
+        ("dx", _vp), ("dw_router", _vp), ("dw_gate_up", _vp), ("dw_down", _vp),
+        ("dgate", _vp), ("dlogit", _vp),
+        ("workspace", _vp), ("workspace_bytes", _sz),
+    ]
+
+
+_SIGS = {
+    "moe_route": [_vp, _int, _i64, _i64, _vp, _vp, _vp, _int, _int, _int, _vp, _vp, _vp, _vp],
+    "moe_permute": [_vp, _i64, _int, _int, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_grouped_ffn": [_vp, _i64, _i64, _int, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_combine": [_vp, _vp, _vp, _vp, _i64, _int, _i64, _vp, _int, _vp],
+    "moe_bias_update": [_vp, _vp, _int, _i64, _int, ctypes.c_float, _vp],
+    "moe_backward": [ctypes.POINTER(BwdArgs), _vp],
+    "moe_workspace_size": [_int, _i64, _int, _int, _i64, _i64],
+    "moe_status_str": [_int],
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library (loaded on first use; raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mixture_experts_layer_free_amd.build` (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = _int
+        L.moe_workspace_size.restype = _sz
+        L.moe_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+class MoEError(RuntimeError):
+    def __init__(self, name, status):
+        super().__init__(f"{name} failed: {lib().moe_status_str(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(name, st):
+    if st != MOE_OK:
+        raise MoEError(name, st)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _req(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def workspace_size(which: int, T: int, k: int, E: int, d: int = 0, f: int = 0) -> int:
+    return int(lib().moe_workspace_size(which, T, k, E, d, f))
+
+
+def _workspace(which, T, k, E, d, f, device, workspace=None):
+    n = workspace_size(which, T, k, E, d, f)
+    if workspace is None:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    return workspace, n
+
+
+# ----------------------------------------------------------------------------
+# entry points
+
+def moe_route(x, w_router, k, score_fn, logit_offset=None, sel_bias=None,
+              topk_idx=None, topk_gate=None, logits_out=None, stream=None):
+    T, d = x.shape
+    E = w_router.shape[0]
+    _req(x, "x")
+    _req(w_router, "w_router", torch.float32, (E, d))
+    if logit_offset is not None:
+        _req(logit_offset, "logit_offset", torch.float32, (E,))
+    if sel_bias is not None:
+        _req(sel_bias, "sel_bias", torch.float32, (E,))
+    dev = x.device
+    topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
+    topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_gate is None else topk_gate
+    logits_out = torch.empty((T, E), dtype=torch.float32, device=dev) if logits_out is None else logits_out
+    sf = SCORE[score_fn] if isinstance(score_fn, str) else int(score_fn)
+    _check("moe_route", lib().moe_route(_p(x), _dtype_code(x), T, d, _p(w_router), _p(logit_offset),
+                                        _p(sel_bias), E, k, sf, _p(topk_idx), _p(topk_gate),
+                                        _p(logits_out), _stream(stream)))
+    return topk_idx, topk_gate, logits_out
+
+
+def moe_permute(topk_idx, x, E, counts=None, offsets=None, row_of=None, token_of=None, x_perm=None,
+                workspace=None, stream=None):
+    T, k = topk_idx.shape
+    d = x.shape[1]
+    _req(topk_idx, "topk_idx", torch.int32)
+    _req(x, "x")
+    dev = x.device
+    A = T * k
+    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    row_of = torch.empty((T, k), dtype=torch.int32, device=dev) if row_of is None else row_of
+    token_of = torch.empty(A, dtype=torch.int32, device=dev) if token_of is None else token_of
+    x_perm = torch.empty((A, d), dtype=x.dtype, device=dev) if x_perm is None else x_perm
+    ws, n = _workspace(MOE_CALL_PERMUTE, T, k, E, d, 0, dev, workspace)
+    _check("moe_permute", lib().moe_permute(_p(topk_idx), T, k, E, _p(x), _dtype_code(x), d, _p(counts),
+                                            _p(offsets), _p(row_of), _p(token_of), _p(x_perm), _p(ws),
+                                            ws.numel(), _stream(stream)))
+    return counts, offsets, row_of, token_of, x_perm
+
+
+def moe_grouped_ffn(x_rows, offsets, w_gate_up, w_down, gu_saved=None, h=None, y=None, save_gu=False,
+                    workspace=None, stream=None):
+    rows, d = x_rows.shape
+    G = offsets.shape[0] - 1
+    f = w_down.shape[2]
+    _req(x_rows, "x_rows")
+    _req(offsets, "offsets", torch.int32)
+    _req(w_gate_up, "w_gate_up", x_rows.dtype, (G, 2 * f, d))
+    _req(w_down, "w_down", x_rows.dtype, (G, d, f))
+    dev = x_rows.device
+    if save_gu and gu_saved is None:
+        gu_saved = torch.empty((rows, 2 * f), dtype=x_rows.dtype, device=dev)
+    h = torch.empty((rows, f), dtype=x_rows.dtype, device=dev) if h is None else h
+    y = torch.empty((rows, d), dtype=torch.float32, device=dev) if y is None else y
+    ws, n = _workspace(MOE_CALL_GROUPED_FFN, rows, 1, G, d, f, dev, workspace)
+    _check("moe_grouped_ffn", lib().moe_grouped_ffn(_p(x_rows), rows, d, _dtype_code(x_rows), _p(offsets), G, f,
+                                                    _p(w_gate_up), _p(w_down), _p(gu_saved), _p(h), _p(y),
+                                                    _p(ws), ws.numel(), _stream(stream)))
+    return gu_saved, h, y
+
+
+def moe_combine(y_perm, row_of, topk_gate, shared_y=None, out=None, out_dtype=torch.float32, stream=None):
+    T, k = row_of.shape
+    d = y_perm.shape[1]
+    _req(y_perm, "y_perm", torch.float32, (T * k, d))
+    _req(row_of, "row_of", torch.int32)
+    _req(topk_gate, "topk_gate", torch.float32, (T, k))
+    if shared_y is not None:
+        _req(shared_y, "shared_y", torch.float32, (T, d))
+    out = torch.empty((T, d), dtype=out_dtype, device=y_perm.device) if out is None else out
+    _check("moe_combine", lib().moe_combine(_p(y_perm), _p(row_of), _p(topk_gate), _p(shared_y), T, k, d,
+                                            _p(out), _dtype_code(out), _stream(stream)))
+    return out
+
+
+def moe_bias_update(sel_bias, counts, T, k, gamma, stream=None):
+    E = sel_bias.shape[0]
+    _req(sel_bias, "sel_bias", torch.float32)
+    _req(counts, "counts", torch.int32, (E,))
+    _check("moe_bias_update", lib().moe_bias_update(_p(sel_bias), _p(counts), E, T, k, float(gamma),
+                                                    _stream(stream)))
+    return sel_bias
+
+
+def moe_backward(args: BwdArgs, stream=None):
+    args.struct_size = ctypes.sizeof(BwdArgs)
+    _check("moe_backward", lib().moe_backward(ctypes.byref(args), _stream(stream)))

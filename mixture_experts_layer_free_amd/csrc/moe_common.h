@@ -1,0 +1,61 @@
+// Device-side helpers shared by the MoE kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+#define MOE_WAVE 64
+
+typedef uint16_t bf16_t;                                          // raw bf16 storage
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));        // MFMA operand
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 -> f32 is exact: the bf16 bits are the top half of the f32.
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// f32 -> bf16, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float v) {
+  uint32_t u = __float_as_uint(v);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+// Lane mask of lanes strictly below this one.
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = threadIdx.x & (MOE_WAVE - 1);
+  return l == 0 ? 0ull : (~0ull >> (MOE_WAVE - l));
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+  return v;
+}
+
+// Host-side launch check: returns MOE_EHIP from the enclosing function.
+#define MOE_LAUNCH_CHECK()                                   \
+  do {                                                       \
+    if (hipPeekAtLastError() != hipSuccess) {                \
+      (void)hipGetLastError();                               \
+      return MOE_EHIP;                                       \
+    }                                                        \
+  } while (0)
+
+static inline hipStream_t moe_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Number of compute units of the current device (cached per device id).
+int moe_num_cus();

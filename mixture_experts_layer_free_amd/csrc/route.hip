@@ -1,0 +1,241 @@
+// Router: fp32 logits on MFMA, then one wavefront per token for scoring,
+// loss-free-biased top-k and gates.
+//
+// Method: lesson "专家组合 (MoE)" (AI Engineering from Scratch), Concept and
+// Build it step 1; score functions and the fp32 rule from the AREX article on
+// The Ultimate MoE Training Handbook, router-precision paragraph (a bf16
+// router can round two close logits to one value and change the winner).
+#include "moe_common.h"
+
+#include <float.h>
+#include <limits.h>
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// logits[t, e] = sum_i x[t, i] * w[e, i] (+ off[e]), fp32.
+//
+// Workgroup tile: 32 tokens x 64 experts, 4 waves.  Each wave owns the whole
+// 32x64 tile but a quarter of every 64-wide K slab (k in [16w, 16w+16)), so
+// the four partial tiles are summed at the end.  Inside a wave the products
+// go through v_mfma_f32_16x16x4_f32 into a chunk accumulator that is folded
+// into the running total every 64 products: every fp32 partial sum covers at
+// most 64 products (blocked accumulation keeps the logit error near 1e-7
+// relative at d = 7168).
+constexpr int RT_M = 32, RT_N = 64, RT_K = 64, RT_LD = RT_K + 4;  // +4 floats: conflict-free b128 reads
+
+template <bool XBF16>
+__global__ __launch_bounds__(256) void router_logits_kernel(const void* __restrict__ xv, const float* __restrict__ w,
+                                                            const float* __restrict__ off, float* __restrict__ logits,
+                                                            int T, int d, int E) {
+  __shared__ __attribute__((aligned(16))) float sA[RT_M * RT_LD];
+  __shared__ __attribute__((aligned(16))) float sB[RT_N * RT_LD];
+  __shared__ __attribute__((aligned(16))) float sR[4][RT_M][RT_N + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * RT_M, e0 = blockIdx.y * RT_N;
+
+  // global -> register staging (prefetch of the next K slab)
+  f32x4 ra[2];   // A: 32 rows x 64 k = 512 float4, 2 per thread
+  f32x4 rb[4];   // B: 64 rows x 64 k = 1024 float4, 4 per thread
+
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i, row = c >> 4, kc = (c & 15) * 4;
+      const int t = t0 + row, k = k0 + kc;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (t < T && k < d) {
+        if (XBF16) {
+          const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(xv) + (int64_t)t * d + k);
+          v[0] = bf16_to_f32(u.x & 0xFFFFu);
+          v[1] = bf16_to_f32(u.x >> 16);
+          v[2] = bf16_to_f32(u.y & 0xFFFFu);
+          v[3] = bf16_to_f32(u.y >> 16);
+        } else {
+          v = *reinterpret_cast<const f32x4*>(static_cast<const float*>(xv) + (int64_t)t * d + k);
+        }
+      }
+      ra[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, row = c >> 4, kc = (c & 15) * 4;
+      const int e = e0 + row, k = k0 + kc;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (e < E && k < d) v = *reinterpret_cast<const f32x4*>(w + (int64_t)e * d + k);
+      rb[i] = v;
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<f32x4*>(&sA[(c >> 4) * RT_LD + (c & 15) * 4]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<f32x4*>(&sB[(c >> 4) * RT_LD + (c & 15) * 4]) = rb[i];
+    }
+  };
+
+  f32x4 tot[2][4], chk[2][4];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) tot[m][n] = chk[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (d + RT_K - 1) / RT_K;
+  gload(0);
+  for (int it = 0; it < nk; ++it) {
+    sstore();
+    __syncthreads();
+    if (it + 1 < nk) gload((it + 1) * RT_K);
+    // this wave's 16 k: lane group g = lane/16 holds k = 16*wave + 4g + s, s = 0..3
+    const int kb = 16 * wave + 4 * (lane >> 4);
+    f32x4 a[2], b[4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) a[m] = *reinterpret_cast<const f32x4*>(&sA[(16 * m + (lane & 15)) * RT_LD + kb]);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) b[n] = *reinterpret_cast<const f32x4*>(&sB[(16 * n + (lane & 15)) * RT_LD + kb]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          chk[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m][s], b[n][s], chk[m][n], 0, 0, 0);
+    if ((it & 3) == 3 || it + 1 == nk) {   // 4 slabs x 16 k = 64 products per chunk
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          tot[m][n] += chk[m][n];
+          chk[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    __syncthreads();
+  }
+
+  // D layout of a 16x16 MFMA tile: lane holds rows 4*(lane/16)+r, column lane%16
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sR[wave][16 * m + 4 * (lane >> 4) + r][16 * n + (lane & 15)] = tot[m][n][r];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < (RT_M * RT_N) / 256; ++i) {
+    const int c = tid + 256 * i, row = c / RT_N, col = c % RT_N;
+    const int t = t0 + row, e = e0 + col;
+    if (t < T && e < E) {
+      float v = (sR[0][row][col] + sR[1][row][col]) + (sR[2][row][col] + sR[3][row][col]);
+      if (off) v += off[e];
+      logits[(int64_t)t * E + e] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One wavefront per token.  Lane l holds experts l, l+64, ...; k rounds of a
+// cross-lane argmax on (key desc, expert asc) pick the experts; lanes 0..k-1
+// then hold one chosen expert each and form the gates with wave reductions.
+
+__device__ __forceinline__ float score_of(float l, int fn) {
+  if (fn == MOE_SIGMOID_NORM) return 1.0f / (1.0f + expf(-l));
+  if (fn == MOE_SQRT_SOFTPLUS_NORM) return sqrtf(fmaxf(l, 0.0f) + log1pf(expf(-fabsf(l))));
+  return l;
+}
+
+__device__ __forceinline__ bool better(float v, int e, float bv, int be) {
+  return v > bv || (v == bv && e < be);
+}
+
+constexpr int TOPK_MAXV = MOE_MAX_EXPERTS / MOE_WAVE;  // experts per lane
+
+__global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
+                                                        int T, int E, int k, int fn, int32_t* __restrict__ idx,
+                                                        float* __restrict__ gate) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* lrow = logits + (int64_t)t * E;
+  const int nv = (E + MOE_WAVE - 1) / MOE_WAVE;
+
+  float key[TOPK_MAXV];
+#pragma unroll
+  for (int i = 0; i < TOPK_MAXV; ++i) {
+    const int e = lane + MOE_WAVE * i;
+    key[i] = -FLT_MAX;
+    if (i < nv && e < E) key[i] = score_of(lrow[e], fn) + (bias ? bias[e] : 0.0f);
+  }
+  uint32_t taken = 0;
+  int mine = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < TOPK_MAXV; ++i) {
+      const int e = lane + MOE_WAVE * i;
+      if (i < nv && e < E && !((taken >> i) & 1u) && better(key[i], e, bv, be)) {
+        bv = key[i];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, MOE_WAVE);
+      const int oe = __shfl_xor(be, o, MOE_WAVE);
+      if (better(ov, oe, bv, be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == j) mine = be;
+  }
+  // gates over the chosen experts, from the unbiased values
+  const bool act = lane < k;
+  const float l = act ? lrow[mine] : 0.0f;
+  float g;
+  if (fn == MOE_SOFTMAX_CHOSEN) {
+    float m = act ? l : -INFINITY;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, MOE_WAVE));
+    const float ex = act ? expf(l - m) : 0.0f;
+    g = ex / wave_sum(ex);
+  } else {
+    const float s = act ? score_of(l, fn) : 0.0f;
+    g = s / wave_sum(s);
+  }
+  if (act) {
+    idx[(int64_t)t * k + lane] = mine;
+    gate[(int64_t)t * k + lane] = g;
+  }
+}
+
+}  // namespace
+
+extern "C" moe_status moe_route(const void* x, int x_dtype, int64_t T, int64_t d, const float* w_router,
+                                const float* logit_offset, const float* sel_bias, int E, int k, int score_fn,
+                                int32_t* topk_idx, float* topk_gate, float* logits_out, void* stream) {
+  if (!x || !w_router || !topk_idx || !topk_gate || !logits_out) return MOE_EINVAL;
+  if (T < 1 || d < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EINVAL;
+  if (score_fn < MOE_SOFTMAX_CHOSEN || score_fn > MOE_SQRT_SOFTPLUS_NORM) return MOE_EINVAL;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || d % 8 != 0 || T >= (1ll << 31) || d >= (1ll << 31))
+    return MOE_ENOTSUP;
+  hipStream_t s = moe_stream(stream);
+  dim3 g1((unsigned)ceil_div(T, RT_M), (unsigned)ceil_div(E, RT_N));
+  if (x_dtype == MOE_BF16)
+    router_logits_kernel<true><<<g1, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
+  else
+    router_logits_kernel<false><<<g1, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
+  MOE_LAUNCH_CHECK();
+  topk_gate_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(logits_out, sel_bias, (int)T, E, k, score_fn, topk_idx,
+                                                            topk_gate);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}

@@ -1,0 +1,163 @@
+"""A token-choice MoE layer driven through the C ABI.
+
+``MoELayer`` owns the device weights and preallocated buffers and chains the
+library calls of one forward (route -> permute -> routed experts -> shared
+experts -> combine -> bias update) and, for training, the backward.  It does
+no arithmetic of its own: every step is a call into libmoe.so.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+
+@dataclass
+class Shape:
+    T: int
+    d: int
+    E: int
+    k: int
+    f: int
+    dtype: torch.dtype = torch.bfloat16
+    score: str = "softmax"
+    shared: int = 0
+    f_shared: int = 0
+    bias_update: bool = False
+    gamma: float = 1e-3
+    train: bool = False
+
+
+class CallTimer:
+    """HIP events around library calls, on the stream the calls go to."""
+
+    def __init__(self):
+        self.pairs = {}
+
+    def span(self, name, stream=None):
+        timer = self
+
+        class _Span:
+            def __enter__(self_):
+                self_.a = torch.cuda.Event(enable_timing=True)
+                self_.b = torch.cuda.Event(enable_timing=True)
+                self_.a.record(stream)
+
+            def __exit__(self_, *exc):
+                self_.b.record(stream)
+                timer.pairs.setdefault(name, []).append((self_.a, self_.b))
+        return _Span()
+
+    def mean_ms(self, name):
+        p = self.pairs.get(name, [])
+        return sum(a.elapsed_time(b) for a, b in p) / len(p) if p else float("nan")
+
+    def reset(self):
+        self.pairs = {}
+
+
+class _Null:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        return False
+
+
+def _span(timer, name, stream):
+    return timer.span(name, stream) if timer is not None else _Null()
+
+
+class MoELayer:
+    def __init__(self, shape: Shape, w_router, w_gate_up, w_down, sel_bias=None, logit_offset=None,
+                 w_gate_up_shared=None, w_down_shared=None, device="cuda"):
+        s = shape
+        self.s = s
+        dev = torch.device(device)
+        self.dev = dev
+        self.w_router = w_router
+        self.w_gate_up = w_gate_up
+        self.w_down = w_down
+        self.sel_bias = sel_bias
+        self.logit_offset = logit_offset
+        self.w_gate_up_shared = w_gate_up_shared
+        self.w_down_shared = w_down_shared
+        T, d, E, k, f, A = s.T, s.d, s.E, s.k, s.f, s.T * s.k
+        dt = s.dtype
+        z = lambda *shp, dtype=torch.float32: torch.empty(shp, dtype=dtype, device=dev)
+        self.idx = z(T, k, dtype=torch.int32)
+        self.gate = z(T, k)
+        self.logits = z(T, E)
+        self.counts = z(E, dtype=torch.int32)
+        self.offsets = z(E + 1, dtype=torch.int32)
+        self.row_of = z(T, k, dtype=torch.int32)
+        self.token_of = z(A, dtype=torch.int32)
+        self.x_perm = z(A, d, dtype=dt)
+        self.gu = z(A, 2 * f, dtype=dt) if s.train else None
+        self.h = z(A, f, dtype=dt)
+        self.y_perm = z(A, d)
+        self.out = z(T, d)
+        self.ws_perm = z(max(1, L.workspace_size(L.MOE_CALL_PERMUTE, T, k, E, d, f)), dtype=torch.uint8)
+        self.ws_ffn = z(max(1, L.workspace_size(L.MOE_CALL_GROUPED_FFN, A, 1, E, d, f)), dtype=torch.uint8)
+        if s.shared:
+            # S shared SwiGLU experts of width fs sum to one expert of width
+            # S*fs (gate/up rows and down columns concatenated): pass that one.
+            if s.shared != 1:
+                raise ValueError("pass S shared experts as one shared expert of width S*f_shared")
+            fs = s.f_shared
+            self.sh_offsets = torch.tensor([0, T], dtype=torch.int32, device=dev)
+            self.sh_h = z(T, fs, dtype=dt)
+            self.sh_y = z(T, d)
+            self.ws_sh = z(max(1, L.workspace_size(L.MOE_CALL_GROUPED_FFN, T, 1, 1, d, fs)), dtype=torch.uint8)
+        if s.train:
+            self.dx = z(T, d)
+            self.dw_router = z(E, d)
+            self.dw_gate_up = z(E, 2 * f, d)
+            self.dw_down = z(E, d, f)
+            self.dgate = z(T, k)
+            self.dlogit = z(T, k)
+            self.ws_bwd = z(max(1, L.workspace_size(L.MOE_CALL_BACKWARD, T, k, E, d, f)), dtype=torch.uint8)
+
+    def forward(self, x, stream=None, timer=None):
+        s = self.s
+        with _span(timer, "route", stream):
+            L.moe_route(x, self.w_router, s.k, s.score, self.logit_offset, self.sel_bias,
+                        self.idx, self.gate, self.logits, stream=stream)
+        with _span(timer, "permute", stream):
+            L.moe_permute(self.idx, x, s.E, self.counts, self.offsets, self.row_of, self.token_of, self.x_perm,
+                          workspace=self.ws_perm, stream=stream)
+        with _span(timer, "grouped_ffn", stream):
+            L.moe_grouped_ffn(self.x_perm, self.offsets, self.w_gate_up, self.w_down, self.gu, self.h,
+                              self.y_perm, workspace=self.ws_ffn, stream=stream)
+        shared_y = None
+        if s.shared:
+            with _span(timer, "shared_ffn", stream):
+                L.moe_grouped_ffn(x, self.sh_offsets, self.w_gate_up_shared, self.w_down_shared, None, self.sh_h,
+                                  self.sh_y, workspace=self.ws_sh, stream=stream)
+            shared_y = self.sh_y
+        with _span(timer, "combine", stream):
+            L.moe_combine(self.y_perm, self.row_of, self.gate, shared_y, self.out, stream=stream)
+        if s.bias_update and self.sel_bias is not None:
+            with _span(timer, "bias_update", stream):
+                L.moe_bias_update(self.sel_bias, self.counts, s.T, s.k, s.gamma, stream=stream)
+        return self.out
+
+    def backward(self, x, dy, stream=None, timer=None):
+        s = self.s
+        a = L.BwdArgs()
+        a.T, a.d, a.f, a.E, a.k, a.score_fn = s.T, s.d, s.f, s.E, s.k, L.SCORE[s.score]
+        for name, t in (("dy", dy), ("x", x), ("w_router", self.w_router), ("logits", self.logits),
+                        ("topk_idx", self.idx), ("topk_gate", self.gate), ("row_of", self.row_of),
+                        ("token_of", self.token_of), ("offsets", self.offsets), ("x_perm", self.x_perm),
+                        ("gu_saved", self.gu), ("h", self.h), ("y_perm", self.y_perm),
+                        ("w_gate_up", self.w_gate_up), ("w_down", self.w_down), ("dx", self.dx),
+                        ("dw_router", self.dw_router), ("dw_gate_up", self.dw_gate_up), ("dw_down", self.dw_down),
+                        ("dgate", self.dgate), ("dlogit", self.dlogit), ("workspace", self.ws_bwd)):
+            setattr(a, name, t.data_ptr())
+        a.workspace_bytes = self.ws_bwd.numel()
+        with _span(timer, "backward", stream):
+            L.moe_backward(a, stream=stream)
+        return self.dx

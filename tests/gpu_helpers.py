@@ -1,0 +1,100 @@
+"""Shared helpers of the GPU parity tests: host<->device transfer of the seeded
+inputs and the comparison rules.
+
+Comparison rules:
+* expert indices, counts, offsets, row maps and permuted rows: bit-exact;
+  a token whose k-th and (k+1)-th biased keys (oracle, fp64) differ by less
+  than 1e-6 relative is excluded from the index comparison and counted;
+* fp32 layers: max-abs and relative-L2 error <= 1e-4;
+* bf16 layers: max-abs <= 2e-2 and relative-L2 <= 1e-2;
+* gates and logits (fp32 in every layer): max-abs <= 1e-4.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+NEAR_TIE = 1e-6
+TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 1e-2)}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a, device="cuda"):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def host(t):
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def as_f64(a):
+    a = np.asarray(a)
+    return oracle.bf16_from_bits(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def check_close(got, ref, kind, name):
+    got = as_f64(got)
+    ref = as_f64(ref)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    tol_abs, tol_rel = TOL[kind]
+    err = np.abs(got - ref)
+    mx = float(err.max()) if err.size else 0.0
+    den = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(got - ref) / den) if den > 0 else float(np.linalg.norm(got - ref))
+    say(f"  {name}: max-abs {mx:.3e} rel-L2 {rel:.3e} (tol {tol_abs:g}/{tol_rel:g})")
+    assert mx <= tol_abs and rel <= tol_rel, (name, mx, rel)
+    return mx, rel
+
+
+def check_route(idx, gate, logits, ref, k):
+    """Compare GPU routing with the oracle's.  Returns the excluded count."""
+    idx = np.asarray(idx)
+    gate = np.asarray(gate, np.float64)
+    excl = ref["margin"] < NEAR_TIE
+    o_g = np.argsort(idx, axis=1, kind="stable")
+    o_r = np.argsort(ref["idx"], axis=1, kind="stable")
+    gi = np.take_along_axis(idx, o_g, 1)
+    ri = np.take_along_axis(ref["idx"], o_r, 1)
+    bad = np.any(gi != ri, axis=1) & ~excl
+    assert not bad.any(), f"{int(bad.sum())} tokens choose different experts, first {np.nonzero(bad)[0][:5]}"
+    ok = ~excl
+    gg = np.take_along_axis(gate, o_g, 1)[ok]
+    rg = np.take_along_axis(ref["gates"], o_r, 1)[ok]
+    gerr = float(np.abs(gg - rg).max()) if gg.size else 0.0
+    lerr = float(np.abs(np.asarray(logits, np.float64) - ref["logits"]).max())
+    # slot order: keys descending, equal keys to the lower index (oracle keys)
+    keys = np.take_along_axis(ref["keys"], idx.astype(np.int64), 1)
+    for j in range(k - 1):
+        a, b = keys[:, j], keys[:, j + 1]
+        rel = np.abs(a - b) / np.maximum(np.maximum(np.abs(a), np.abs(b)), 1e-300)
+        wrong = ((a < b) | ((a == b) & (idx[:, j] > idx[:, j + 1]))) & (rel >= NEAR_TIE) & ok
+        assert not wrong.any(), "slot order differs"
+    say(f"  route: excluded near-ties {int(excl.sum())}, gate max-abs {gerr:.2e}, logit max-abs {lerr:.2e}")
+    assert gerr <= 1e-4 and lerr <= 1e-4 * max(1.0, float(np.abs(ref["logits"]).max()))
+    return int(excl.sum())
+
+
+def check_permute(idx, E, counts, offsets, row_of, token_of, x_perm, x):
+    """Stage-isolated: the oracle permute fed the GPU's own choice."""
+    c, o, r, t = oracle.permute(np.asarray(idx, np.int64), E)
+    assert np.array_equal(np.asarray(counts), c), "counts"
+    assert np.array_equal(np.asarray(offsets), o), "offsets"
+    assert np.array_equal(np.asarray(row_of), r), "row_of"
+    assert np.array_equal(np.asarray(token_of), t), "token_of"
+    assert np.array_equal(np.asarray(x_perm), np.asarray(x)[t]), "x_perm"

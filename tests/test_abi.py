@@ -1,0 +1,90 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/moe.h declares, and rejects bad arguments before
+anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from mixture_experts_layer_free_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from mixture_experts_layer_free_amd import build
+        build.build()
+    return _lib
+
+
+def test_exports_every_declared_entry_point(L):
+    hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
+    names = sorted(set(re.findall(r"^\s*(?:moe_status|size_t|const char\*)\s+(moe_\w+)\s*\(", hdr, re.M)))
+    assert {"moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_bias_update", "moe_backward",
+            "moe_workspace_size", "moe_status_str"} <= set(names)
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+P = ctypes.c_void_p(4096)   # a non-null stand-in pointer: validation fails before it is ever used
+
+
+def test_route_validation(L):
+    lib = L.lib()
+    args = lambda **kw: [kw.get("x", P), kw.get("dt", 1), kw.get("T", 64), kw.get("d", 64), P, None, None,
+                         kw.get("E", 8), kw.get("k", 2), kw.get("sf", 0), P, P, kw.get("lo", P), None]
+    assert lib.moe_route(*args(x=None)) == L.MOE_EINVAL
+    assert lib.moe_route(*args(lo=None)) == L.MOE_EINVAL
+    assert lib.moe_route(*args(k=9)) == L.MOE_EINVAL
+    assert lib.moe_route(*args(k=0)) == L.MOE_EINVAL
+    assert lib.moe_route(*args(T=0)) == L.MOE_EINVAL
+    assert lib.moe_route(*args(sf=3)) == L.MOE_EINVAL
+    assert lib.moe_route(*args(dt=7)) == L.MOE_EINVAL
+    assert lib.moe_route(*args(E=1025, k=2)) == L.MOE_ENOTSUP
+    assert lib.moe_route(*args(E=64, k=17)) == L.MOE_ENOTSUP
+    assert lib.moe_route(*args(d=60)) == L.MOE_ENOTSUP
+
+
+def test_permute_validation(L):
+    lib = L.lib()
+    need = L.workspace_size(L.MOE_CALL_PERMUTE, 1000, 8, 64)
+    assert need >= 64 * ((8000 + 255) // 256) * 4
+    a = lambda **kw: [P, kw.get("T", 1000), kw.get("k", 8), kw.get("E", 64), P, kw.get("dt", 1), kw.get("d", 64),
+                      P, P, P, P, P, kw.get("ws", P), kw.get("wsb", need), None]
+    assert lib.moe_permute(*a(ws=None)) == L.MOE_EWORKSPACE
+    assert lib.moe_permute(*a(wsb=need - 1)) == L.MOE_EWORKSPACE
+    assert lib.moe_permute(*a(k=65)) == L.MOE_EINVAL
+    assert lib.moe_permute(*a(d=4)) == L.MOE_ENOTSUP        # 8-byte bf16 rows
+    assert lib.moe_permute(*a(T=1 << 28, k=8, wsb=1 << 40)) == L.MOE_ENOTSUP   # T*k >= 2^31
+
+
+def test_grouped_ffn_validation(L):
+    lib = L.lib()
+    need = L.workspace_size(L.MOE_CALL_GROUPED_FFN, 1000, 1, 64, 256, 128)
+    a = lambda **kw: [P, 1000, kw.get("d", 256), kw.get("dt", 1), P, kw.get("G", 64), kw.get("f", 128), P, P,
+                      None, kw.get("h", P), P, kw.get("ws", P), kw.get("wsb", need), None]
+    assert lib.moe_grouped_ffn(*a(h=None)) == L.MOE_EINVAL
+    assert lib.moe_grouped_ffn(*a(d=96)) == L.MOE_ENOTSUP
+    assert lib.moe_grouped_ffn(*a(f=100)) == L.MOE_ENOTSUP
+    assert lib.moe_grouped_ffn(*a(G=2000)) == L.MOE_ENOTSUP
+    assert lib.moe_grouped_ffn(*a(wsb=0)) == L.MOE_EWORKSPACE
+
+
+def test_combine_and_bias_validation(L):
+    lib = L.lib()
+    assert lib.moe_combine(None, P, P, None, 10, 2, 64, P, 0, None) == L.MOE_EINVAL
+    assert lib.moe_combine(P, P, P, None, 10, 17, 64, P, 0, None) == L.MOE_ENOTSUP
+    assert lib.moe_combine(P, P, P, None, 10, 2, 66, P, 0, None) == L.MOE_ENOTSUP
+    assert lib.moe_combine(P, P, P, None, 10, 2, 64, P, 5, None) == L.MOE_EINVAL
+    assert lib.moe_bias_update(None, P, 8, 64, 2, 1e-3, None) == L.MOE_EINVAL
+    assert lib.moe_bias_update(P, P, 8, 64, 9, 1e-3, None) == L.MOE_EINVAL
+
+
+def test_status_strings(L):
+    lib = L.lib()
+    assert lib.moe_status_str(0) == b"ok"
+    assert b"workspace" in lib.moe_status_str(3)
+    assert lib.moe_status_str(99) == b"unknown status"

@@ -1,0 +1,313 @@
+"""GPU parity of the forward path (route, permute, grouped FFN, combine, bias
+update, whole layer) against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import as_f64, check_close, check_permute, check_route, dev, host, say
+from workloads import CONFIGS, make_inputs, scaled
+
+pytestmark = pytest.mark.gpu
+
+L = None
+
+
+def setup_module():
+    global L
+    from mixture_experts_layer_free_amd import _lib
+    L = _lib
+    L.lib()
+    assert torch.cuda.is_available()
+
+
+def _kind(cfg):
+    return "bf16" if cfg.dtype == "bf16" else "f32"
+
+
+def _route_case(cfg, inp, score=None, bias=True, offset=True):
+    score = score or cfg.score
+    b = inp["bias"] if bias else None
+    o = inp["logit_offset"] if offset else None
+    x = dev(inp["x"])
+    idx, gate, logits = L.moe_route(x, dev(inp["w_router"]), cfg.k, score, dev(o), dev(b))
+    torch.cuda.synchronize()
+    ref = oracle.route(inp["x"], inp["w_router"], cfg.k, score, b, o)
+    return check_route(host(idx), host(gate), host(logits), ref, cfg.k), idx, x
+
+
+# ---------------------------------------------------------------------------- route
+
+@pytest.mark.parametrize("score", oracle.SCORE_FNS)
+def test_route_tiny(score):
+    cfg = CONFIGS["tiny"]
+    say(f"[route tiny {score}]")
+    inp = make_inputs(cfg)
+    inp["logit_offset"] = np.random.default_rng(5).uniform(-0.3, 0.3, cfg.E).astype(np.float32)
+    for k in (1, 2, 5, 8):
+        excl, _, _ = _route_case(scaled(cfg, k=k), inp, score)
+        assert excl == 0
+
+
+@pytest.mark.parametrize("T,d,E,k", [(300, 256, 16, 4), (77, 64, 1, 1), (129, 128, 96, 16), (64, 2048, 1024, 16),
+                                     (33, 64, 16, 16)])
+def test_route_shapes(T, d, E, k):
+    say(f"[route shape T={T} d={d} E={E} k={k}]")
+    cfg = scaled(CONFIGS["fine"], T=T, d=d, E=E, k=k, f=64, bias="uniform")
+    inp = make_inputs(cfg, experts=False)
+    for score in oracle.SCORE_FNS:
+        _route_case(cfg, inp, score)
+
+
+def test_route_ties_go_to_lower_index():
+    say("[route ties]")
+    T, d, E = 64, 64, 12
+    r = np.random.default_rng(0)
+    x = r.standard_normal((T, d)).astype(np.float32)
+    w = (r.standard_normal((E, d)) * 0.1).astype(np.float32)
+    w[2] = w[7] = w[11] = 1.0          # three identical, strong router rows
+    bias = np.zeros(E, np.float32)
+    idx, gate, logits = L.moe_route(dev(x), dev(w), 2, "softmax", None, dev(bias))
+    idx = host(idx)
+    ref = oracle.route(x, w, 2, "softmax", bias)
+    assert np.array_equal(idx, ref["idx"])
+    strong = x.sum(axis=1) > 1.0
+    assert np.all(idx[strong] == np.array([2, 7]))
+
+
+def test_route_fp32_not_bf16_winner():
+    """fp32-distinct, bf16-equal router rows: the GPU router picks the true
+    winner, which a bf16 router would not."""
+    say("[route bf16 counterexample]")
+    d, E = 8, 4
+    x = np.zeros((4, d), np.float32)
+    x[:, 0] = 1.0
+    w = np.zeros((E, d), np.float32)
+    w[0, 0] = 1.0
+    w[1, 0] = np.float32(1.0 + 2.0 ** -9)
+    w[2, 0] = 0.5
+    w[3, 0] = -1.0
+    idx, _, logits = L.moe_route(dev(x), dev(w), 1, "softmax")
+    assert np.all(host(idx)[:, 0] == 1)
+    assert oracle.bf16_round(float(w[1, 0])) == oracle.bf16_round(float(w[0, 0]))
+
+
+@pytest.mark.parametrize("name", ["coarse", "fine", "dsv3", "train"])
+def test_route_full_size(name):
+    cfg = CONFIGS[name]
+    say(f"[route full {name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k}]")
+    inp = make_inputs(cfg, experts=False)
+    excl, idx, x = _route_case(cfg, inp)
+    assert excl <= 10
+
+
+# ---------------------------------------------------------------------------- permute
+
+def _permute_case(idx_np, x_np, E):
+    idx = dev(idx_np.astype(np.int32))
+    x = dev(x_np)
+    counts, offsets, row_of, token_of, x_perm = L.moe_permute(idx, x, E)
+    torch.cuda.synchronize()
+    check_permute(idx_np, E, host(counts), host(offsets), host(row_of), host(token_of), host(x_perm), x_np)
+
+
+@pytest.mark.parametrize("T,E,k,d", [(1, 4, 2, 8), (255, 8, 2, 64), (257, 64, 8, 128), (1000, 37, 3, 32),
+                                     (4096, 1024, 16, 16), (513, 1, 1, 24)])
+def test_permute_random(T, E, k, d):
+    say(f"[permute T={T} E={E} k={k} d={d}]")
+    rng = np.random.default_rng(T + E)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    _permute_case(idx, x, E)
+    xb = (rng.integers(0, 65535, (T, d * 2))).astype(np.uint16)  # bf16 bit patterns, even d for 16-byte rows
+    _permute_case(idx, xb, E)
+
+
+def test_permute_skew_extremes():
+    say("[permute skew]")
+    T, E, d = 3000, 16, 64
+    x = np.random.default_rng(1).standard_normal((T, d)).astype(np.float32)
+    _permute_case(np.full((T, 1), 5), x, E)                        # everything on expert 5
+    _permute_case(np.tile(np.array([[15, 0]]), (T, 1)), x, E)      # two experts, rest empty
+    _permute_case(np.tile(np.arange(E)[::-1], (T, 1)), x, E)       # k = E
+
+
+@pytest.mark.parametrize("name", ["coarse", "fine", "dsv3", "train"])
+def test_permute_full_size(name):
+    cfg = CONFIGS[name]
+    say(f"[permute full {name}]")
+    inp = make_inputs(cfg, experts=False)
+    x = dev(inp["x"])
+    idx, _, _ = L.moe_route(x, dev(inp["w_router"]), cfg.k, cfg.score, dev(inp["logit_offset"]), dev(inp["bias"]))
+    counts, offsets, row_of, token_of, x_perm = L.moe_permute(idx, x, cfg.E)
+    torch.cuda.synchronize()
+    check_permute(host(idx), cfg.E, host(counts), host(offsets), host(row_of), host(token_of), host(x_perm), inp["x"])
+    c = host(counts)
+    say(f"  load max/mean {c.max() / c.mean():.2f} min/mean {c.min() / c.mean():.2f}")
+
+
+# ---------------------------------------------------------------------------- grouped FFN
+
+def _ffn_case(cfg, offsets_np, x_rows_np, wgu_np, wd_np, rows_to_check=None, save_gu=True):
+    G = len(offsets_np) - 1
+    gu, h, y = L.moe_grouped_ffn(dev(x_rows_np), dev(offsets_np.astype(np.int32)), dev(wgu_np), dev(wd_np),
+                                 save_gu=save_gu)
+    torch.cuda.synchronize()
+    bf = cfg.dtype == "bf16"
+    kind = _kind(cfg)
+    f = wd_np.shape[2]
+    rows = np.arange(x_rows_np.shape[0]) if rows_to_check is None else np.asarray(rows_to_check)
+    grp = np.searchsorted(offsets_np, rows, side="right") - 1
+    ref = {"G": [], "U": [], "H": [], "Y": []}
+    for g in np.unique(grp):
+        sel = rows[grp == g]
+        o = oracle.expert_ffn(x_rows_np[sel], wgu_np[g], wd_np[g], bf)
+        for key in ref:
+            ref[key].append((sel, o[key]))
+    def gather(key):
+        out = np.zeros((len(rows), ref[key][0][1].shape[1]))
+        pos = {r: i for i, r in enumerate(rows)}
+        for sel, v in ref[key]:
+            out[[pos[r] for r in sel]] = v
+        return out
+    check_close(host(y)[rows], gather("Y"), kind, "Y")
+    check_close(host(h)[rows], gather("H"), kind, "H")
+    if save_gu:
+        g_ = host(gu)[rows]
+        check_close(g_[:, :f], gather("G"), kind, "G")
+        check_close(g_[:, f:], gather("U"), kind, "U")
+
+
+def test_ffn_tiny_f32():
+    cfg = CONFIGS["tiny"]
+    say("[ffn tiny f32]")
+    inp = make_inputs(cfg)
+    offsets = np.array([0, 10, 10, 30, 31, 64, 64, 100, 128])
+    x = np.random.default_rng(0).standard_normal((128, cfg.d)).astype(np.float32)
+    _ffn_case(cfg, offsets, x, inp["w_gate_up"], inp["w_down"])
+
+
+@pytest.mark.parametrize("d,f,seg", [(128, 64, [0, 1, 129, 129, 300, 557]), (256, 192, [0, 0, 0, 1000]),
+                                     (192, 128, [0, 128, 256, 384])])
+def test_ffn_bf16_tiles_and_tails(d, f, seg):
+    say(f"[ffn bf16 d={d} f={f} seg={seg}]")
+    G = len(seg) - 1
+    cfg = scaled(CONFIGS["fine"], T=seg[-1], d=d, E=G, f=f, k=1)
+    inp = make_inputs(cfg)
+    _ffn_case(cfg, np.array(seg), inp["x"], inp["w_gate_up"], inp["w_down"])
+
+
+def test_ffn_bf16_many_groups():
+    say("[ffn bf16 300 groups]")
+    rng = np.random.default_rng(3)
+    G, d, f = 300, 128, 64
+    n = rng.integers(0, 300, G)
+    n[::7] = 0
+    offsets = np.concatenate([[0], np.cumsum(n)])
+    cfg = scaled(CONFIGS["dsv3"], T=int(offsets[-1]), d=d, E=G, f=f, k=1, shared=0)
+    inp = make_inputs(cfg)
+    check = np.unique(np.concatenate([offsets[:-1][n > 0], offsets[1:][n > 0] - 1, rng.integers(0, offsets[-1], 200)]))
+    _ffn_case(cfg, offsets, inp["x"], inp["w_gate_up"], inp["w_down"], rows_to_check=check)
+
+
+# ---------------------------------------------------------------------------- combine / bias
+
+@pytest.mark.parametrize("k,shared,bf16", [(2, False, False), (8, True, False), (16, False, True), (1, True, True)])
+def test_combine(k, shared, bf16):
+    say(f"[combine k={k} shared={shared} bf16={bf16}]")
+    rng = np.random.default_rng(k)
+    T, d = 333, 96
+    A = T * k
+    y = rng.standard_normal((A, d)).astype(np.float32)
+    row_of = rng.permutation(A).reshape(T, k).astype(np.int32)
+    g = rng.uniform(0, 1, (T, k)).astype(np.float32)
+    sh = rng.standard_normal((T, d)).astype(np.float32) if shared else None
+    out = L.moe_combine(dev(y), dev(row_of), dev(g), dev(sh), out_dtype=torch.bfloat16 if bf16 else torch.float32)
+    ref = oracle.combine(y, row_of, g, sh)
+    got = host(out)
+    if bf16:
+        # a bf16 output carries at most half a bf16 ulp (<= 2^-8 |value|) of
+        # rounding on top of the fp32 sum's own error
+        err = np.abs(as_f64(got) - ref)
+        assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-5), float((err - 2.0 ** -8 * np.abs(ref)).max())
+    else:
+        check_close(got, ref, "f32", "out")
+
+
+def test_bias_update_bit_exact():
+    say("[bias update]")
+    rng = np.random.default_rng(0)
+    for E, T, k in ((8, 64, 2), (64, 8192, 8), (256, 4096, 8), (7, 5, 3), (1024, 333, 16)):
+        b = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+        counts = rng.multinomial(T * k, np.ones(E) / E).astype(np.int32)
+        counts[:3] = T * k // E          # some exactly on target when divisible
+        tb = dev(b.copy())
+        L.moe_bias_update(tb, dev(counts), T, k, 1e-3)
+        assert np.array_equal(host(tb), oracle.bias_update(b, counts, T, k, 1e-3))
+
+
+# ---------------------------------------------------------------------------- whole layer
+
+def _layer(cfg, inp, train=False):
+    from mixture_experts_layer_free_amd.layer import MoELayer, Shape
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    s = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, dt, cfg.score, cfg.shared, cfg.f_shared, cfg.bias_update, cfg.gamma,
+              train)
+    return MoELayer(s, dev(inp["w_router"]), dev(inp["w_gate_up"]), dev(inp["w_down"]), dev(inp["bias"].copy()),
+                    dev(inp["logit_offset"]), dev(inp.get("w_gate_up_shared")), dev(inp.get("w_down_shared")))
+
+
+def _forward_check(cfg, inp, sample=None):
+    layer = _layer(cfg, inp)
+    x = dev(inp["x"])
+    out = host(layer.forward(x))
+    torch.cuda.synchronize()
+    T = cfg.T
+    tok = np.arange(T) if sample is None else np.asarray(sample)
+    ref = oracle.forward(np.asarray(inp["x"])[tok], inp["w_router"], inp["w_gate_up"], inp["w_down"], cfg.k, cfg.score,
+                         cfg.dtype == "bf16", sel_bias=inp["bias"], logit_offset=inp["logit_offset"],
+                         w_gate_up_shared=inp.get("w_gate_up_shared"), w_down_shared=inp.get("w_down_shared"))
+    keep = ref["margin"] >= 1e-6
+    say(f"  tokens compared {int(keep.sum())} of {len(tok)}")
+    check_close(out[tok][keep], ref["out"][keep], _kind(cfg), "out")
+    if cfg.bias_update:
+        b = oracle.bias_update(inp["bias"], host(layer.counts), T, cfg.k, cfg.gamma)
+        assert np.array_equal(host(layer.sel_bias), b)
+    return layer
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_dense"])
+@pytest.mark.parametrize("score", oracle.SCORE_FNS)
+def test_forward_tiny(name, score):
+    say(f"[forward {name} {score}]")
+    cfg = scaled(CONFIGS[name], score=score)
+    _forward_check(cfg, make_inputs(cfg))
+
+
+@pytest.mark.parametrize("score", oracle.SCORE_FNS)
+def test_forward_bf16_small(score):
+    say(f"[forward bf16 small {score}]")
+    cfg = scaled(CONFIGS["dsv3"], T=700, d=256, E=24, k=3, f=128, f_shared=192, score=score, bias_update=True)
+    _forward_check(cfg, make_inputs(cfg))
+
+
+@pytest.mark.parametrize("name", ["coarse", "fine"])
+def test_forward_full_size(name):
+    cfg = CONFIGS[name]
+    say(f"[forward full {name}]")
+    inp = make_inputs(cfg)
+    rng = np.random.default_rng(0)
+    _forward_check(cfg, inp, sample=np.sort(rng.choice(cfg.T, 48, replace=False)))
+
+
+def test_forward_deterministic():
+    say("[forward determinism]")
+    cfg = scaled(CONFIGS["fine"], T=1000, d=256, E=32, k=4, f=128)
+    inp = make_inputs(cfg)
+    a = _layer(cfg, inp)
+    b = _layer(cfg, inp)
+    x = dev(inp["x"])
+    oa = host(a.forward(x)).copy()
+    ob = host(b.forward(x))
+    assert np.array_equal(oa, ob)
+    assert np.array_equal(host(a.x_perm), host(b.x_perm))
