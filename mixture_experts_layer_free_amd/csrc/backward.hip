@@ -1,6 +1,317 @@
-// Backward of the routed MoE layer (placeholder until the kernels land).
-#include "moe_common.h"
+// Backward of the routed MoE layer.
+//
+// The pages give no backward; this is the chain rule through the forward of
+// the lesson "专家组合 (MoE)" (AI Engineering from Scratch: Concept, Build it
+// step 1).  The selection bias and the logit offset get no gradient (Key
+// terms: the loss-free bias adds no gradient signal) and the top-k choice is
+// held fixed.  Kernels, in stream order:
+//   1. combine_bwd   one wave per token: dg = <dy, y_perm[row]>, dY_perm =
+//                    bf16(g*dy), then the gate backward (dl on the chosen
+//                    experts) in the same wave
+//   2. router wgrad  dW_r[e] = sum over e's rows of dl * x_perm (row-chunk
+//                    partials, then an ordered reduction: deterministic)
+//   3. dgrad down    dH = dY_perm W_down, epilogue SwiGLU backward -> dG|dU
+//   4. wgrad down    dW_down[e] = dY_perm^T H over e's rows
+//   5. wgrad up      dW_gate_up[e] = [dG|dU]^T X_perm over e's rows
+//   6. dgrad up      dX_perm = [dG|dU] W_gate_up (fp32)
+//   7. unpermute_bwd one wave per token: dx = sum_j dX_perm[row] + sum_j dl*W_r[e]
+#include "gemm.h"
 
-size_t moe_backward_workspace(int64_t T, int k, int E, int64_t d, int64_t f) { return 0; }
+moe_status moe_tile_schedule_launch(const int32_t* offsets, int G, int bm, int32_t* mt_prefix, hipStream_t s);
 
-extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) { return MOE_ENOTSUP; }
+namespace {
+
+constexpr int RCH = 256;  // rows per router-wgrad partial
+
+__device__ __forceinline__ float score_of(float l, int fn) {
+  if (fn == MOE_SIGMOID_NORM) return 1.0f / (1.0f + expf(-l));
+  if (fn == MOE_SQRT_SOFTPLUS_NORM) return sqrtf(fmaxf(l, 0.0f) + log1pf(expf(-fabsf(l))));
+  return l;
+}
+
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restrict__ dy, const float* __restrict__ y,
+                                                          const int32_t* __restrict__ row_of,
+                                                          const float* __restrict__ gate, const int32_t* __restrict__ idx,
+                                                          const float* __restrict__ logits, int T, int k, int E,
+                                                          int64_t d, int fn, bf16_t* __restrict__ dy_perm,
+                                                          float* __restrict__ dg_out, float* __restrict__ dl_out,
+                                                          float* __restrict__ dl_perm) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const bool act = lane < k;
+  const int myr = act ? row_of[t * k + lane] : 0;
+  const float myg = act ? gate[t * k + lane] : 0.f;
+  const int mye = act ? idx[t * k + lane] : 0;
+  int rows[MOE_MAX_TOPK];
+  float g[MOE_MAX_TOPK], part[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    rows[j] = __shfl(myr, j, MOE_WAVE);
+    g[j] = __shfl(myg, j, MOE_WAVE);
+    part[j] = 0.f;
+  }
+  const int64_t nv = d / 8;  // 8 values per 16-byte bf16 vector
+  const u32x4* dyv = reinterpret_cast<const u32x4*>(dy + t * d);
+  for (int64_t v = lane; v < nv; v += MOE_WAVE) {
+    const u32x4 raw = dyv[v];
+    float a[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a[2 * q] = bf16_to_f32(raw[q] & 0xFFFFu);
+      a[2 * q + 1] = bf16_to_f32(raw[q] >> 16);
+    }
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j >= k) break;
+      const f32x4* yr = reinterpret_cast<const f32x4*>(y + (int64_t)rows[j] * d) + 2 * v;
+      const f32x4 y0 = yr[0], y1 = yr[1];
+      float s = part[j];
+      s = fmaf(a[0], y0[0], s); s = fmaf(a[1], y0[1], s); s = fmaf(a[2], y0[2], s); s = fmaf(a[3], y0[3], s);
+      s = fmaf(a[4], y1[0], s); s = fmaf(a[5], y1[1], s); s = fmaf(a[6], y1[2], s); s = fmaf(a[7], y1[3], s);
+      part[j] = s;
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(g[j] * a[2 * q], g[j] * a[2 * q + 1]);
+      reinterpret_cast<u32x4*>(dy_perm + (int64_t)rows[j] * d)[v] = o;
+    }
+  }
+  float dg = 0.f;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (j >= k) break;
+    const float s = wave_sum(part[j]);
+    if (lane == j) dg = s;
+  }
+  // gate backward (chosen experts only)
+  const float D = wave_sum(act ? myg * dg : 0.f);
+  float dl;
+  if (fn == MOE_SOFTMAX_CHOSEN) {
+    dl = myg * (dg - D);
+  } else {
+    const float l = act ? logits[t * E + mye] : 0.f;
+    const float s = act ? score_of(l, fn) : 0.f;
+    const float S = wave_sum(s);
+    const float ds = (dg - D) / S;
+    if (fn == MOE_SIGMOID_NORM) dl = ds * s * (1.0f - s);
+    else dl = ds * (1.0f / (1.0f + expf(-l))) / (2.0f * s);
+  }
+  if (act) {
+    dg_out[t * k + lane] = dg;
+    dl_out[t * k + lane] = dl;
+    dl_perm[myr] = dl;
+  }
+}
+
+// Partial router weight gradient over one chunk of at most RCH rows of one
+// expert: part[p][c] = sum over the chunk's rows of dl_perm[r] * x_perm[r][c].
+// Two columns per thread, 512 columns per workgroup.
+__global__ __launch_bounds__(256) void router_wgrad_part_kernel(const bf16_t* __restrict__ x_perm,
+                                                                const float* __restrict__ dl_perm,
+                                                                const int32_t* __restrict__ offsets,
+                                                                const int32_t* __restrict__ rc_prefix, int E, int64_t d,
+                                                                float* __restrict__ part) {
+  const int p = blockIdx.x;
+  if (p >= rc_prefix[E]) return;
+  int lo = 0, hi = E;  // expert of chunk p: largest e with rc_prefix[e] <= p
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (rc_prefix[mid] <= p) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int64_t r0 = offsets[e] + (int64_t)(p - rc_prefix[e]) * RCH;
+  const int64_t r1 = min((int64_t)offsets[e + 1], r0 + RCH);
+  const int64_t c = (int64_t)blockIdx.y * 512 + 2 * threadIdx.x;
+  if (c >= d) return;
+  float a0 = 0.f, a1 = 0.f;
+  for (int64_t r = r0; r < r1; ++r) {
+    const float w = dl_perm[r];
+    const uint32_t xv = *reinterpret_cast<const uint32_t*>(x_perm + r * d + c);
+    a0 = fmaf(w, bf16_to_f32(xv & 0xFFFFu), a0);
+    a1 = fmaf(w, bf16_to_f32(xv >> 16), a1);
+  }
+  part[(int64_t)p * d + c] = a0;
+  part[(int64_t)p * d + c + 1] = a1;
+}
+
+__global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* __restrict__ part,
+                                                                  const int32_t* __restrict__ rc_prefix, int64_t d,
+                                                                  float* __restrict__ dw) {
+  const int e = blockIdx.x;
+  const int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x;
+  if (c >= d) return;
+  float s = 0.f;
+  for (int p = rc_prefix[e]; p < rc_prefix[e + 1]; ++p) s += part[(int64_t)p * d + c];
+  dw[(int64_t)e * d + c] = s;
+}
+
+// dx[t] = sum_j dx_perm[row_of[t,j]] + sum_j dl[t,j] * w_router[idx[t,j]]
+__global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restrict__ dx_perm,
+                                                            const int32_t* __restrict__ row_of,
+                                                            const int32_t* __restrict__ idx, const float* __restrict__ dl,
+                                                            const f32x4* __restrict__ w_router, int T, int k,
+                                                            int64_t nv, f32x4* __restrict__ dx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int myr = lane < k ? row_of[t * k + lane] : 0;
+  const int mye = lane < k ? idx[t * k + lane] : 0;
+  const float myl = lane < k ? dl[t * k + lane] : 0.f;
+  int rows[MOE_MAX_TOPK], ex[MOE_MAX_TOPK];
+  float w[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    rows[j] = __shfl(myr, j, MOE_WAVE);
+    ex[j] = __shfl(mye, j, MOE_WAVE);
+    w[j] = __shfl(myl, j, MOE_WAVE);
+  }
+  for (int64_t v = lane; v < nv; v += MOE_WAVE) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j >= k) break;
+      acc += dx_perm[(int64_t)rows[j] * nv + v];
+    }
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j >= k) break;
+      const f32x4 wr = w_router[(int64_t)ex[j] * nv + v];
+      acc[0] = fmaf(w[j], wr[0], acc[0]);
+      acc[1] = fmaf(w[j], wr[1], acc[1]);
+      acc[2] = fmaf(w[j], wr[2], acc[2]);
+      acc[3] = fmaf(w[j], wr[3], acc[3]);
+    }
+    dx[t * nv + v] = acc;
+  }
+}
+
+struct BwdLayout {
+  size_t dy_perm, dgu, dx_perm, dg, dl, dl_perm, mt_prefix, rc_prefix, rpart, total;
+};
+
+BwdLayout layout(int64_t T, int k, int E, int64_t d, int64_t f) {
+  const int64_t A = T * k;
+  BwdLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
+  L.dy_perm = take((size_t)A * d * 2);
+  L.dgu = take((size_t)A * 2 * f * 2);
+  L.dx_perm = take((size_t)A * d * 4);
+  L.dg = take((size_t)T * k * 4);
+  L.dl = take((size_t)T * k * 4);
+  L.dl_perm = take((size_t)A * 4);
+  L.mt_prefix = take((size_t)(E + 1) * 4);
+  L.rc_prefix = take((size_t)(E + 1) * 4);
+  L.rpart = take((size_t)(ceil_div(A, RCH) + E) * d * 4);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+size_t moe_backward_workspace(int64_t T, int k, int E, int64_t d, int64_t f) {
+  if (d < 1 || f < 1) return 0;
+  return layout(T, k, E, d, f).total;
+}
+
+extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
+  if (!a || a->struct_size != sizeof(moe_bwd_args)) return MOE_EINVAL;
+  const int64_t T = a->T, d = a->d, f = a->f;
+  const int E = a->E, k = a->k;
+  if (T < 1 || d < 1 || f < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
+  if (a->score_fn < MOE_SOFTMAX_CHOSEN || a->score_fn > MOE_SQRT_SOFTPLUS_NORM) return MOE_EINVAL;
+  if (!a->dy || !a->x || !a->w_router || !a->logits || !a->topk_idx || !a->topk_gate || !a->row_of ||
+      !a->token_of || !a->offsets || !a->x_perm || !a->gu_saved || !a->h || !a->y_perm || !a->w_gate_up ||
+      !a->w_down || !a->dx || !a->dw_router || !a->dw_gate_up || !a->dw_down)
+    return MOE_EINVAL;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || d % 64 != 0 || f % 64 != 0 || T * k >= (1ll << 31) || T >= (1ll << 31))
+    return MOE_ENOTSUP;
+  const BwdLayout Lo = layout(T, k, E, d, f);
+  if (!a->workspace || a->workspace_bytes < Lo.total) return MOE_EWORKSPACE;
+  hipStream_t s = moe_stream(stream);
+  char* ws = static_cast<char*>(a->workspace);
+  bf16_t* dy_perm = reinterpret_cast<bf16_t*>(ws + Lo.dy_perm);
+  bf16_t* dgu = reinterpret_cast<bf16_t*>(ws + Lo.dgu);
+  float* dx_perm = reinterpret_cast<float*>(ws + Lo.dx_perm);
+  float* dg = a->dgate ? a->dgate : reinterpret_cast<float*>(ws + Lo.dg);
+  float* dl = a->dlogit ? a->dlogit : reinterpret_cast<float*>(ws + Lo.dl);
+  float* dl_perm = reinterpret_cast<float*>(ws + Lo.dl_perm);
+  int32_t* mt_prefix = reinterpret_cast<int32_t*>(ws + Lo.mt_prefix);
+  int32_t* rc_prefix = reinterpret_cast<int32_t*>(ws + Lo.rc_prefix);
+  float* rpart = reinterpret_cast<float*>(ws + Lo.rpart);
+  const int64_t A = T * k;
+  const bf16_t* x_perm = static_cast<const bf16_t*>(a->x_perm);
+  const bf16_t* wgu = static_cast<const bf16_t*>(a->w_gate_up);
+  const bf16_t* wd = static_cast<const bf16_t*>(a->w_down);
+
+  // 1. combine + gate backward
+  combine_bwd_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(
+      static_cast<const bf16_t*>(a->dy), a->y_perm, a->row_of, a->topk_gate, a->topk_idx, a->logits, (int)T, k, E, d,
+      a->score_fn, dy_perm, dg, dl, dl_perm);
+  MOE_LAUNCH_CHECK();
+  // 2. router weight gradient
+  moe_status st = moe_tile_schedule_launch(a->offsets, E, RCH, rc_prefix, s);
+  if (st != MOE_OK) return st;
+  router_wgrad_part_kernel<<<dim3((unsigned)(ceil_div(A, RCH) + E), (unsigned)ceil_div(d, 512)), 256, 0, s>>>(
+      x_perm, dl_perm, a->offsets, rc_prefix, E, d, rpart);
+  MOE_LAUNCH_CHECK();
+  router_wgrad_reduce_kernel<<<dim3((unsigned)E, (unsigned)ceil_div(d, 256)), 256, 0, s>>>(rpart, rc_prefix, d,
+                                                                                            a->dw_router);
+  MOE_LAUNCH_CHECK();
+  // expert GEMMs
+  using namespace moe_gemm;
+  st = moe_tile_schedule_launch(a->offsets, E, BM, mt_prefix, s);
+  if (st != MOE_OK) return st;
+  const int64_t mtiles = ceil_div(A, BM) + E;
+  {  // 3. dH = dY_perm W_down -> dG|dU
+    Args g{};
+    g.A = dy_perm; g.lda = d;
+    g.B = wd; g.ldb = f; g.b_group = d * f;
+    g.K = d; g.N = f;
+    g.offsets = a->offsets; g.mt_prefix = mt_prefix; g.G = E;
+    g.NB = (int)ceil_div(f, BN);
+    g.gu_in = static_cast<const bf16_t*>(a->gu_saved);
+    g.gu_out = dgu;
+    gemm_kernel<true, false, false, EPI_SWIGLU_BWD><<<grid_for(mtiles * g.NB), 256, 0, s>>>(g);
+    MOE_LAUNCH_CHECK();
+  }
+  {  // 4. dW_down[e] = dY_perm^T H
+    Args g{};
+    g.A = dy_perm; g.lda = d;
+    g.B = static_cast<const bf16_t*>(a->h); g.ldb = f;
+    g.M = d; g.N = f;
+    g.offsets = a->offsets; g.G = E;
+    g.MT = (int)ceil_div(d, BM); g.NB = (int)ceil_div(f, BN);
+    g.out = a->dw_down; g.ldo = f; g.out_group = d * f;
+    gemm_kernel<false, false, true, EPI_F32><<<grid_for((int64_t)E * g.MT * g.NB), 256, 0, s>>>(g);
+    MOE_LAUNCH_CHECK();
+  }
+  {  // 5. dW_gate_up[e] = [dG|dU]^T X_perm
+    Args g{};
+    g.A = dgu; g.lda = 2 * f;
+    g.B = x_perm; g.ldb = d;
+    g.M = 2 * f; g.N = d;
+    g.offsets = a->offsets; g.G = E;
+    g.MT = (int)ceil_div(2 * f, BM); g.NB = (int)ceil_div(d, BN);
+    g.out = a->dw_gate_up; g.ldo = d; g.out_group = 2 * f * d;
+    gemm_kernel<false, false, true, EPI_F32><<<grid_for((int64_t)E * g.MT * g.NB), 256, 0, s>>>(g);
+    MOE_LAUNCH_CHECK();
+  }
+  {  // 6. dX_perm = [dG|dU] W_gate_up
+    Args g{};
+    g.A = dgu; g.lda = 2 * f;
+    g.B = wgu; g.ldb = d; g.b_group = 2 * f * d;
+    g.K = 2 * f; g.N = d;
+    g.offsets = a->offsets; g.mt_prefix = mt_prefix; g.G = E;
+    g.NB = (int)ceil_div(d, BN);
+    g.out = dx_perm; g.ldo = d;
+    gemm_kernel<true, false, false, EPI_F32><<<grid_for(mtiles * g.NB), 256, 0, s>>>(g);
+    MOE_LAUNCH_CHECK();
+  }
+  // 7. unpermute + router input gradient
+  unpermute_bwd_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(
+      reinterpret_cast<const f32x4*>(dx_perm), a->row_of, a->topk_idx, dl, reinterpret_cast<const f32x4*>(a->w_router),
+      (int)T, k, d / 4, reinterpret_cast<f32x4*>(a->dx));
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}

@@ -20,163 +20,9 @@
 // persistent: workgroup i sits on XCD i%8 and takes, in each round, a tile
 // from that XCD's contiguous share of the round, so tiles that reuse a weight
 // panel run on one XCD and hit its L2.
-#include "moe_common.h"
+#include "gemm.h"
 
 namespace {
-
-constexpr int GBM = 128, GBN = 128, GBK = 64, GLD = GBK + 8;  // +8 bf16: conflict-free 16-byte reads
-
-struct GemmArgs {
-  const bf16_t* A;           // [rows, K]
-  const bf16_t* B;           // group g: B + g*b_group, rows of K
-  int64_t b_group;
-  int64_t K;
-  int64_t N;                 // output columns
-  const int32_t* offsets;    // [G+1]
-  const int32_t* mt_prefix;  // [G+1] row tiles before group g
-  int G;
-  int NB;                    // column blocks
-  void* out;                 // bf16 H [rows, N] (SwiGLU) or f32 Y [rows, N]
-  bf16_t* gu;                // [rows, 2N] or null (SwiGLU only)
-};
-
-enum { EPI_SWIGLU = 0, EPI_F32 = 1 };
-
-template <int EPI>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2][(GBM + GBN) * GLD];
-  __shared__ int32_t s_pref[MOE_MAX_EXPERTS + 1];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  for (int i = tid; i <= p.G; i += 256) s_pref[i] = p.mt_prefix[i];
-  __syncthreads();
-  const int NB = p.NB;
-  const int total = s_pref[p.G] * NB;
-  const int per = gridDim.x >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int64_t K = p.K;
-  const int nk = (int)(K / GBK);
-
-  for (int base = 0;; base += gridDim.x) {
-    const int L = base + xcd * per + slot;
-    if (L >= total) break;
-    int lo = 0, hi = p.G;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_pref[mid] * NB <= L) lo = mid; else hi = mid;
-    }
-    const int e = lo;
-    const int mte = s_pref[e + 1] - s_pref[e];
-    const int local = L - s_pref[e] * NB;
-    const int nb = local / mte, mt = local % mte;
-    const int row0 = p.offsets[e] + mt * GBM;
-    const int row_end = p.offsets[e + 1];
-    const bf16_t* Bg = p.B + (int64_t)e * p.b_group;
-
-    // per-thread source rows of the A and B tiles (4 x 16-byte chunks each)
-    const bf16_t* asrc[4];
-    const bf16_t* bsrc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, r = c >> 3, kc = (c & 7) * 8;
-      int ar = row0 + r;
-      if (ar >= row_end) ar = row_end - 1;   // ragged tail: valid row, result discarded
-      asrc[i] = p.A + (int64_t)ar * K + kc;
-      int64_t wr;
-      if (EPI == EPI_SWIGLU) {
-        const int jb = r >> 5;                 // 32-row blocks: gate, up, gate, up
-        wr = ((jb & 1) ? p.N : 0) + (int64_t)nb * 64 + (jb >> 1) * 32 + (r & 31);
-      } else {
-        wr = (int64_t)nb * GBN + r;
-        if (wr >= p.N) wr = p.N - 1;
-      }
-      bsrc[i] = Bg + wr * K + kc;
-    }
-    u32x4 ra[4], rb[4];
-    auto gload = [&](int64_t k0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = *reinterpret_cast<const u32x4*>(asrc[i] + k0);
-        rb[i] = *reinterpret_cast<const u32x4*>(bsrc[i] + k0);
-      }
-    };
-    auto sstore = [&](int buf) {
-      bf16_t* sa = smem[buf];
-      bf16_t* sb = smem[buf] + GBM * GLD;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i, r = c >> 3, kc = (c & 7) * 8;
-        *reinterpret_cast<u32x4*>(sa + r * GLD + kc) = ra[i];
-        *reinterpret_cast<u32x4*>(sb + r * GLD + kc) = rb[i];
-      }
-    };
-
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x16{};
-
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int it = 0; it < nk; ++it) {
-      const int cur = it & 1;
-      if (it + 1 < nk) gload((int64_t)(it + 1) * GBK);
-      const bf16_t* sa = smem[cur] + (wm * 64 + (lane & 31)) * GLD + 8 * (lane >> 5);
-      const bf16_t* sb = smem[cur] + GBM * GLD + (wn * 64 + (lane & 31)) * GLD + 8 * (lane >> 5);
-#pragma unroll
-      for (int kk = 0; kk < GBK; kk += 16) {
-        bf16x8 a[2], b[2];
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) a[mi] = *reinterpret_cast<const bf16x8*>(sa + mi * 32 * GLD + kk);
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) b[ni] = *reinterpret_cast<const bf16x8*>(sb + ni * 32 * GLD + kk);
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < 2; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
-      }
-      if (it + 1 < nk) sstore(cur ^ 1);
-      __syncthreads();
-    }
-
-    // 32x32 MFMA result: register r of lane holds row 8*(r/4) + 4*(lane/32) + r%4, column lane%32
-    if (EPI == EPI_SWIGLU) {
-      bf16_t* H = static_cast<bf16_t*>(p.out);
-      const int64_t col = (int64_t)nb * 64 + wn * 32 + (lane & 31);
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (row < row_end) {
-            const float g = acc[mi][0][r], u = acc[mi][1][r];
-            H[(int64_t)row * p.N + col] = (bf16_t)f32_to_bf16(silu_f32(g) * u);
-            if (p.gu) {
-              p.gu[(int64_t)row * 2 * p.N + col] = (bf16_t)f32_to_bf16(g);
-              p.gu[(int64_t)row * 2 * p.N + p.N + col] = (bf16_t)f32_to_bf16(u);
-            }
-          }
-        }
-    } else {
-      float* Y = static_cast<float*>(p.out);
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int64_t col = (int64_t)nb * GBN + wn * 64 + ni * 32 + (lane & 31);
-        if (col >= p.N) continue;
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = row0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (row < row_end) Y[(int64_t)row * p.N + col] = acc[mi][ni][r];
-          }
-      }
-    }
-  }
-}
 
 // mt_prefix[g] = sum over g' < g of ceil(n_g' / bm); one workgroup.
 __global__ __launch_bounds__(1024) void tile_schedule_kernel(const int32_t* __restrict__ offsets, int G, int bm,
@@ -252,48 +98,59 @@ __global__ __launch_bounds__(256) void ffn_down_f32_kernel(const float* __restri
 
 size_t moe_ffn_workspace(int G) { return align256((size_t)(G + 1) * sizeof(int32_t)); }
 
-// Launches the two bf16 grouped GEMMs (also used by the backward for the
-// shared forward pieces); mt_prefix must already hold the tile schedule.
+namespace moe_gemm {
+int grid_for(int64_t tiles_upper) {
+  const int max_wg = (2 * moe_num_cus()) & ~7;
+  const int64_t t = (tiles_upper + 7) & ~int64_t(7);
+  return (int)std::max<int64_t>(8, std::min<int64_t>(max_wg, t));
+}
+}  // namespace moe_gemm
+
+moe_status moe_tile_schedule_launch(const int32_t* offsets, int G, int bm, int32_t* mt_prefix, hipStream_t s) {
+  tile_schedule_kernel<<<1, 1024, 0, s>>>(offsets, G, bm, mt_prefix);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+// The two bf16 expert GEMMs of a grouped SwiGLU FFN; mt_prefix must already
+// hold the row-tile schedule of `offsets`.
 moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, const int32_t* offsets,
                                const int32_t* mt_prefix, int G, int64_t f, const bf16_t* wgu, const bf16_t* wd,
                                bf16_t* gu, bf16_t* h, float* y, hipStream_t s) {
-  const int max_wg = (2 * moe_num_cus()) & ~7;
-  const int64_t mtiles = ceil_div(rows, GBM) + G;
-  GemmArgs a{};
+  using namespace moe_gemm;
+  const int64_t mtiles = ceil_div(rows, BM) + G;
+  Args a{};
   a.A = x_rows;
+  a.lda = d;
   a.B = wgu;
+  a.ldb = d;
   a.b_group = 2 * f * d;
   a.K = d;
   a.N = f;
   a.offsets = offsets;
   a.mt_prefix = mt_prefix;
   a.G = G;
-  a.NB = (int)(f / 64);
+  a.NB = (int)(f / (BN / 2));
   a.out = h;
-  a.gu = gu;
-  int64_t grid = std::min<int64_t>(max_wg, (mtiles * a.NB + 7) & ~7ll);
-  grouped_gemm_kernel<EPI_SWIGLU><<<(unsigned)grid, 256, 0, s>>>(a);
+  a.ldo = f;
+  a.gu_out = gu;
+  gemm_kernel<true, true, false, EPI_SWIGLU><<<grid_for(mtiles * a.NB), 256, 0, s>>>(a);
   MOE_LAUNCH_CHECK();
-  GemmArgs b{};
+  Args b{};
   b.A = h;
+  b.lda = f;
   b.B = wd;
+  b.ldb = f;
   b.b_group = d * f;
   b.K = f;
   b.N = d;
   b.offsets = offsets;
   b.mt_prefix = mt_prefix;
   b.G = G;
-  b.NB = (int)ceil_div(d, GBN);
+  b.NB = (int)ceil_div(d, BN);
   b.out = y;
-  b.gu = nullptr;
-  grid = std::min<int64_t>(max_wg, (mtiles * b.NB + 7) & ~7ll);
-  grouped_gemm_kernel<EPI_F32><<<(unsigned)grid, 256, 0, s>>>(b);
-  MOE_LAUNCH_CHECK();
-  return MOE_OK;
-}
-
-moe_status moe_tile_schedule_launch(const int32_t* offsets, int G, int32_t* mt_prefix, hipStream_t s) {
-  tile_schedule_kernel<<<1, 1024, 0, s>>>(offsets, G, GBM, mt_prefix);
+  b.ldo = d;
+  gemm_kernel<true, true, false, EPI_F32><<<grid_for(mtiles * b.NB), 256, 0, s>>>(b);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
@@ -310,7 +167,7 @@ extern "C" moe_status moe_grouped_ffn(const void* x_rows, int64_t rows, int64_t 
     if (d % 64 != 0 || f % 64 != 0) return MOE_ENOTSUP;
     if (!workspace || workspace_bytes < moe_ffn_workspace(G)) return MOE_EWORKSPACE;
     int32_t* mt_prefix = static_cast<int32_t*>(workspace);
-    moe_status st = moe_tile_schedule_launch(offsets, G, mt_prefix, s);
+    moe_status st = moe_tile_schedule_launch(offsets, G, moe_gemm::BM, mt_prefix, s);
     if (st != MOE_OK) return st;
     return moe_ffn_bf16_launch(static_cast<const bf16_t*>(x_rows), rows, d, offsets, mt_prefix, G, f,
                                static_cast<const bf16_t*>(w_gate_up), static_cast<const bf16_t*>(w_down),

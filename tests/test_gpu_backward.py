@@ -1,0 +1,118 @@
+"""GPU parity of moe_backward against the oracle's chain rule.
+
+Weight gradients depend on every token of an expert, so they are compared
+stage-isolated: the oracle is fed the GPU's expert choice (index parity of
+that choice is covered by the routing tests).  The router weight gradient at
+full size is compared with the oracle's router backward fed the GPU's logit
+gradient, which is itself compared on sampled tokens."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import as_f64, check_close, dev, host, say
+from workloads import CONFIGS, make_inputs, scaled
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(cfg, inp):
+    from mixture_experts_layer_free_amd.layer import MoELayer, Shape
+    s = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, torch.bfloat16, cfg.score, 0, 0, False, cfg.gamma, True)
+    return MoELayer(s, dev(inp["w_router"]), dev(inp["w_gate_up"]), dev(inp["w_down"]), dev(inp["bias"].copy()),
+                    dev(inp["logit_offset"]))
+
+
+def _run(cfg, inp):
+    layer = _layer(cfg, inp)
+    x = dev(inp["x"])
+    layer.forward(x)
+    layer.backward(x, dev(inp["dy"]))
+    torch.cuda.synchronize()
+    return layer
+
+
+@pytest.mark.parametrize("score", oracle.SCORE_FNS)
+@pytest.mark.parametrize("T,d,E,k,f", [(700, 256, 24, 3, 128), (257, 128, 8, 8, 64), (96, 192, 40, 2, 192)])
+def test_backward_small(score, T, d, E, k, f):
+    say(f"[backward small {score} T={T} d={d} E={E} k={k} f={f}]")
+    cfg = scaled(CONFIGS["train"], T=T, d=d, E=E, k=k, f=f, score=score, bias="uniform")
+    inp = make_inputs(cfg)
+    layer = _run(cfg, inp)
+    idx = host(layer.idx).astype(np.int64)
+    fwd = oracle.forward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], k, score, True,
+                         sel_bias=inp["bias"], logit_offset=inp["logit_offset"], idx=idx)
+    g = oracle.backward(fwd, inp["dy"], inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], score, True)
+    check_close(host(layer.dgate), g["dg"], "bf16", "dg")
+    check_close(host(layer.dlogit), g["dl"], "bf16", "dl")
+    check_close(host(layer.dx), g["dx"], "bf16", "dx")
+    check_close(host(layer.dw_router), g["dw_router"], "bf16", "dW_router")
+    check_close(host(layer.dw_down), g["dw_down"], "bf16", "dW_down")
+    check_close(host(layer.dw_gate_up), g["dw_gate_up"], "bf16", "dW_gate_up")
+
+
+def test_backward_empty_and_skewed_experts():
+    """Experts that receive no token get exactly zero weight gradients; one
+    expert holding most rows spans many K tiles."""
+    say("[backward skew]")
+    cfg = scaled(CONFIGS["train"], T=600, d=128, E=16, k=2, f=64, score="sigmoid")
+    inp = make_inputs(cfg)
+    off = np.zeros(cfg.E, np.float32)
+    off[3], off[7] = 6.0, 5.0          # nearly every token picks experts 3 and 7
+    off[10:] = -30.0                   # experts 10.. never picked
+    inp["logit_offset"] = off
+    layer = _run(cfg, inp)
+    counts = host(layer.counts)
+    assert counts[10:].sum() == 0 and counts[3] > 500
+    idx = host(layer.idx).astype(np.int64)
+    fwd = oracle.forward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], cfg.k, cfg.score, True,
+                         logit_offset=off, idx=idx)
+    g = oracle.backward(fwd, inp["dy"], inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], cfg.score, True)
+    dwd = host(layer.dw_down)
+    assert np.all(dwd[10:] == 0) and np.all(host(layer.dw_gate_up)[10:] == 0) and np.all(host(layer.dw_router)[10:] == 0)
+    check_close(dwd, g["dw_down"], "bf16", "dW_down")
+    check_close(host(layer.dw_gate_up), g["dw_gate_up"], "bf16", "dW_gate_up")
+    check_close(host(layer.dx), g["dx"], "bf16", "dx")
+    check_close(host(layer.dw_router), g["dw_router"], "bf16", "dW_router")
+
+
+def test_backward_full_training_shape():
+    cfg = CONFIGS["train"]
+    say(f"[backward full train T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} f={cfg.f}]")
+    inp = make_inputs(cfg)
+    layer = _run(cfg, inp)
+    k = cfg.k
+    idx = host(layer.idx).astype(np.int64)
+    gates = host(layer.gate)
+    offsets = host(layer.offsets)
+    token_of = host(layer.token_of)
+    row_of = host(layer.row_of)
+    x64 = as_f64(inp["x"])
+    dy64 = as_f64(inp["dy"])
+    rng = np.random.default_rng(0)
+    # --- sampled tokens: dg, dl, dx
+    toks = np.sort(rng.choice(cfg.T, 24, replace=False))
+    fw = oracle.forward(inp["x"][toks], inp["w_router"], inp["w_gate_up"], inp["w_down"], k, cfg.score, True,
+                        idx=idx[toks])
+    gb = oracle.backward(fw, inp["dy"][toks], inp["x"][toks], inp["w_router"], inp["w_gate_up"], inp["w_down"],
+                         cfg.score, True)
+    check_close(host(layer.dgate)[toks], gb["dg"], "bf16", "dg (sampled tokens)")
+    check_close(host(layer.dlogit)[toks], gb["dl"], "bf16", "dl (sampled tokens)")
+    check_close(host(layer.dx)[toks], gb["dx"], "bf16", "dx (sampled tokens)")
+    # --- router weight gradient: the oracle's router backward fed the GPU's dl
+    dwr, _ = oracle.router_backward(host(layer.dlogit).astype(np.float64), idx, inp["x"], inp["w_router"])
+    check_close(host(layer.dw_router), dwr, "bf16", "dW_router (GPU dl)")
+    # --- expert weight gradients of sampled experts, over all of their rows
+    counts = np.diff(offsets)
+    for e in sorted({int(counts.argmin()), int(counts.argmax()), int(rng.integers(0, cfg.E))}):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        rows = np.arange(a, b)
+        tk = token_of[rows]
+        slot = np.array([np.nonzero(row_of[t] == r)[0][0] for t, r in zip(tk, rows)])
+        ex = oracle.expert_ffn(x64[tk], inp["w_gate_up"][e], inp["w_down"][e], True)
+        dyp = oracle.bf16_round(gates[tk, slot][:, None].astype(np.float64) * dy64[tk])
+        r = oracle.expert_backward_rows(dyp, x64[tk], ex["G"], ex["U"], ex["H"], inp["w_gate_up"][e],
+                                        inp["w_down"][e], True)
+        say(f"  expert {e}: {b - a} rows")
+        check_close(host(layer.dw_down[e]), r["dW_down"], "bf16", f"dW_down[{e}]")
+        check_close(host(layer.dw_gate_up[e]), r["dW_gate_up"], "bf16", f"dW_gate_up[{e}]")
