@@ -98,6 +98,7 @@ def main():
     ap.add_argument("--workload", default="train", choices=["train", "fine", "coarse", "dsv3"])
     ap.add_argument("--cpu-tokens", type=int, default=None, help="oracle sample size (tokens)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU: this layer's hot path runs on a single MI355X and has no multi-GPU "
@@ -133,18 +134,33 @@ def main():
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
+    # timed region 1: eager launches with HIP events around every library call
     timer = CallTimer()
-    log(f"[bench] timing {a.steps} steps")
+    log(f"[bench] timing {a.steps} eager steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(a.steps):
         step(timer)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms = elapsed / a.steps * 1e3
-    value = cfg.T * a.steps / elapsed
+    eager_ms = (time.perf_counter() - t0) / a.steps * 1e3
     calls = {n: round(timer.mean_ms(n), 4) for n in timer.pairs}
-    log(f"[bench] {ms:.3f} ms/step, per call ms: {calls}")
+    log(f"[bench] eager {eager_ms:.3f} ms/step, per call ms: {calls}")
+    # timed region 2: the same step captured once in a HIP graph and replayed
+    if a.no_graph:
+        ms = eager_ms
+    else:
+        graph = layer.capture(x, dy)
+        for _ in range(a.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        log(f"[bench] timing {a.steps} graph replays")
+        t0 = time.perf_counter()
+        for _ in range(a.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / a.steps * 1e3
+        log(f"[bench] graph {ms:.3f} ms/step")
+    value = cfg.T / (ms * 1e-3)
 
     # dominant call: the routed grouped FFN (forward) or the backward
     A = cfg.T * cfg.k
@@ -164,6 +180,7 @@ def main():
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": describe(cfg, train), "global_batch": cfg.T, "seq_len": None,
                       "parallelism": "none (1 GPU)"},
+           "eager_ms_per_step": round(eager_ms, 4), "step_mode": "eager" if a.no_graph else "hip_graph_replay",
            "calls_ms": calls, "expert_tflops": round(expert_flops(cfg, train) / (ms * 1e-3) / 1e12, 1),
            "roofline": roof}
     if not a.no_cpu_baseline:

@@ -260,20 +260,19 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   MOE_LAUNCH_CHECK();
   // expert GEMMs
   using namespace moe_gemm;
-  st = moe_tile_schedule_launch(a->offsets, E, BM, mt_prefix, s);
+  const bool large = use_large_rows(A, E, f);
+  st = moe_tile_schedule_launch(a->offsets, E, large ? BM_LARGE : BM, mt_prefix, s);
   if (st != MOE_OK) return st;
-  const int64_t mtiles = ceil_div(A, BM) + E;
   {  // 3. dH = dY_perm W_down -> dG|dU
     Args g{};
     g.A = dy_perm; g.lda = d;
     g.B = wd; g.ldb = f; g.b_group = d * f;
     g.K = d; g.N = f;
     g.offsets = a->offsets; g.mt_prefix = mt_prefix; g.G = E;
-    g.NB = (int)ceil_div(f, BN);
     g.gu_in = static_cast<const bf16_t*>(a->gu_saved);
     g.gu_out = dgu;
-    gemm_kernel<true, false, false, EPI_SWIGLU_BWD><<<grid_for(mtiles * g.NB), 256, 0, s>>>(g);
-    MOE_LAUNCH_CHECK();
+    st = launch_gemm<true, false, false, EPI_SWIGLU_BWD>(g, large, A, s);
+    if (st != MOE_OK) return st;
   }
   {  // 4. dW_down[e] = dY_perm^T H
     Args g{};
@@ -281,10 +280,9 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
     g.B = static_cast<const bf16_t*>(a->h); g.ldb = f;
     g.M = d; g.N = f;
     g.offsets = a->offsets; g.G = E;
-    g.MT = (int)ceil_div(d, BM); g.NB = (int)ceil_div(f, BN);
     g.out = a->dw_down; g.ldo = f; g.out_group = d * f;
-    gemm_kernel<false, false, true, EPI_F32><<<grid_for((int64_t)E * g.MT * g.NB), 256, 0, s>>>(g);
-    MOE_LAUNCH_CHECK();
+    st = launch_gemm<false, false, true, EPI_F32>(g, d >= BM_LARGE && f >= BN_LARGE, 0, s);
+    if (st != MOE_OK) return st;
   }
   {  // 5. dW_gate_up[e] = [dG|dU]^T X_perm
     Args g{};
@@ -292,10 +290,9 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
     g.B = x_perm; g.ldb = d;
     g.M = 2 * f; g.N = d;
     g.offsets = a->offsets; g.G = E;
-    g.MT = (int)ceil_div(2 * f, BM); g.NB = (int)ceil_div(d, BN);
     g.out = a->dw_gate_up; g.ldo = d; g.out_group = 2 * f * d;
-    gemm_kernel<false, false, true, EPI_F32><<<grid_for((int64_t)E * g.MT * g.NB), 256, 0, s>>>(g);
-    MOE_LAUNCH_CHECK();
+    st = launch_gemm<false, false, true, EPI_F32>(g, 2 * f >= BM_LARGE && d >= BN_LARGE, 0, s);
+    if (st != MOE_OK) return st;
   }
   {  // 6. dX_perm = [dG|dU] W_gate_up
     Args g{};
@@ -303,10 +300,9 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
     g.B = wgu; g.ldb = d; g.b_group = 2 * f * d;
     g.K = 2 * f; g.N = d;
     g.offsets = a->offsets; g.mt_prefix = mt_prefix; g.G = E;
-    g.NB = (int)ceil_div(d, BN);
     g.out = dx_perm; g.ldo = d;
-    gemm_kernel<true, false, false, EPI_F32><<<grid_for(mtiles * g.NB), 256, 0, s>>>(g);
-    MOE_LAUNCH_CHECK();
+    st = launch_gemm<true, false, false, EPI_F32>(g, large, A, s);
+    if (st != MOE_OK) return st;
   }
   // 7. unpermute + router input gradient
   unpermute_bwd_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(

@@ -99,8 +99,8 @@ __global__ __launch_bounds__(256) void ffn_down_f32_kernel(const float* __restri
 size_t moe_ffn_workspace(int G) { return align256((size_t)(G + 1) * sizeof(int32_t)); }
 
 namespace moe_gemm {
-int grid_for(int64_t tiles_upper) {
-  const int max_wg = (2 * moe_num_cus()) & ~7;
+int grid_for(int64_t tiles_upper, int per_cu) {
+  const int max_wg = (per_cu * moe_num_cus()) & ~7;
   const int64_t t = (tiles_upper + 7) & ~int64_t(7);
   return (int)std::max<int64_t>(8, std::min<int64_t>(max_wg, t));
 }
@@ -112,13 +112,14 @@ moe_status moe_tile_schedule_launch(const int32_t* offsets, int G, int bm, int32
   return MOE_OK;
 }
 
-// The two bf16 expert GEMMs of a grouped SwiGLU FFN; mt_prefix must already
-// hold the row-tile schedule of `offsets`.
-moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, const int32_t* offsets,
-                               const int32_t* mt_prefix, int G, int64_t f, const bf16_t* wgu, const bf16_t* wd,
-                               bf16_t* gu, bf16_t* h, float* y, hipStream_t s) {
+// Tile schedule plus the two bf16 expert GEMMs of a grouped SwiGLU FFN.
+moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, const int32_t* offsets, int32_t* mt_prefix,
+                               int G, int64_t f, const bf16_t* wgu, const bf16_t* wd, bf16_t* gu, bf16_t* h, float* y,
+                               hipStream_t s) {
   using namespace moe_gemm;
-  const int64_t mtiles = ceil_div(rows, BM) + G;
+  const bool large = use_large_rows(rows, G, f);
+  moe_status st = moe_tile_schedule_launch(offsets, G, large ? BM_LARGE : BM, mt_prefix, s);
+  if (st != MOE_OK) return st;
   Args a{};
   a.A = x_rows;
   a.lda = d;
@@ -130,12 +131,11 @@ moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, co
   a.offsets = offsets;
   a.mt_prefix = mt_prefix;
   a.G = G;
-  a.NB = (int)(f / (BN / 2));
   a.out = h;
   a.ldo = f;
   a.gu_out = gu;
-  gemm_kernel<true, true, false, EPI_SWIGLU><<<grid_for(mtiles * a.NB), 256, 0, s>>>(a);
-  MOE_LAUNCH_CHECK();
+  st = launch_gemm<true, true, false, EPI_SWIGLU>(a, large, rows, s);
+  if (st != MOE_OK) return st;
   Args b{};
   b.A = h;
   b.lda = f;
@@ -147,12 +147,9 @@ moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, co
   b.offsets = offsets;
   b.mt_prefix = mt_prefix;
   b.G = G;
-  b.NB = (int)ceil_div(d, BN);
   b.out = y;
   b.ldo = d;
-  gemm_kernel<true, true, false, EPI_F32><<<grid_for(mtiles * b.NB), 256, 0, s>>>(b);
-  MOE_LAUNCH_CHECK();
-  return MOE_OK;
+  return launch_gemm<true, true, false, EPI_F32>(b, large, rows, s);
 }
 
 extern "C" moe_status moe_grouped_ffn(const void* x_rows, int64_t rows, int64_t d, int dtype, const int32_t* offsets, int G,
@@ -167,8 +164,6 @@ extern "C" moe_status moe_grouped_ffn(const void* x_rows, int64_t rows, int64_t 
     if (d % 64 != 0 || f % 64 != 0) return MOE_ENOTSUP;
     if (!workspace || workspace_bytes < moe_ffn_workspace(G)) return MOE_EWORKSPACE;
     int32_t* mt_prefix = static_cast<int32_t*>(workspace);
-    moe_status st = moe_tile_schedule_launch(offsets, G, moe_gemm::BM, mt_prefix, s);
-    if (st != MOE_OK) return st;
     return moe_ffn_bf16_launch(static_cast<const bf16_t*>(x_rows), rows, d, offsets, mt_prefix, G, f,
                                static_cast<const bf16_t*>(w_gate_up), static_cast<const bf16_t*>(w_down),
                                static_cast<bf16_t*>(gu_saved), static_cast<bf16_t*>(h), y, s);

@@ -161,3 +161,24 @@ class MoELayer:
         with _span(timer, "backward", stream):
             L.moe_backward(a, stream=stream)
         return self.dx
+
+    def capture(self, x, dy=None):
+        """Record one step (forward, and the backward when dy is given) into a
+        HIP graph; replaying it runs the same library kernels on the same
+        buffers without per-call host work.  The library's calls allocate
+        nothing and clear nothing with memset, so they can be captured."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.forward(x)
+            if dy is not None:
+                self.backward(x, dy)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.forward(x)
+            if dy is not None:
+                self.backward(x, dy)
+        return g
+
