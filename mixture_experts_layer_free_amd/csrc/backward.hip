@@ -226,6 +226,10 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
     return MOE_EINVAL;
   if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || d % 64 != 0 || f % 64 != 0 || T * k >= (1ll << 31) || T >= (1ll << 31))
     return MOE_ENOTSUP;
+  // the weight-gradient GEMMs address one expert's rows of the permuted
+  // activations, and the data-gradient GEMMs one expert's weight, through
+  // 32-bit buffer resources
+  if (T * k * std::max(d, 2 * f) * 2 >= (1ll << 31) || 2 * f * d * 2 >= (1ll << 31)) return MOE_ENOTSUP;
   const BwdLayout Lo = layout(T, k, E, d, f);
   if (!a->workspace || a->workspace_bytes < Lo.total) return MOE_EWORKSPACE;
   hipStream_t s = moe_stream(stream);

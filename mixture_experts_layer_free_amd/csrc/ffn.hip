@@ -99,6 +99,10 @@ __global__ __launch_bounds__(256) void ffn_down_f32_kernel(const float* __restri
 size_t moe_ffn_workspace(int G) { return align256((size_t)(G + 1) * sizeof(int32_t)); }
 
 namespace moe_gemm {
+moe_status lds_attr(const void* fn, int bytes) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
 int grid_for(int64_t tiles_upper, int per_cu) {
   const int max_wg = (per_cu * moe_num_cus()) & ~7;
   const int64_t t = (tiles_upper + 7) & ~int64_t(7);
@@ -126,6 +130,7 @@ moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, co
   a.B = wgu;
   a.ldb = d;
   a.b_group = 2 * f * d;
+  a.b_rows = 2 * f;
   a.K = d;
   a.N = f;
   a.offsets = offsets;
@@ -142,6 +147,7 @@ moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, co
   b.B = wd;
   b.ldb = f;
   b.b_group = d * f;
+  b.b_rows = d;
   b.K = f;
   b.N = d;
   b.offsets = offsets;
@@ -162,6 +168,7 @@ extern "C" moe_status moe_grouped_ffn(const void* x_rows, int64_t rows, int64_t 
   hipStream_t s = moe_stream(stream);
   if (dtype == MOE_BF16) {
     if (d % 64 != 0 || f % 64 != 0) return MOE_ENOTSUP;
+    if (2 * f * d * 2 >= (1ll << 31)) return MOE_ENOTSUP;   // one expert's weight must fit a buffer resource
     if (!workspace || workspace_bytes < moe_ffn_workspace(G)) return MOE_EWORKSPACE;
     int32_t* mt_prefix = static_cast<int32_t*>(workspace);
     return moe_ffn_bf16_launch(static_cast<const bf16_t*>(x_rows), rows, d, offsets, mt_prefix, G, f,

@@ -3,11 +3,8 @@
 //
 //   C[m][n] = sum_k A(m,k) * B(n,k)
 //
-// Operand access: "K-contiguous" (A(m,k) = A[m*lda + k]) is loaded straight
-// into LDS with 16-byte vectors; "K-strided" (A(m,k) = A[k*lda + m]) is loaded
-// as 8x8 bf16 blocks (eight 16-byte rows along m) and transposed in registers
-// so that LDS always holds [m][k] with k contiguous, the layout the MFMA
-// operand reads want (one 16-byte read per lane per 16-deep step).
+// Operand access: "K-contiguous" (A(m,k) = A[m*lda + k]) or "K-strided"
+// (A(m,k) = A[k*lda + m]); the same for B with n in place of m.
 //
 // Grouping:
 //   row-grouped: group g owns rows offsets[g]..offsets[g+1]-1 of A and the
@@ -15,22 +12,40 @@
 //   K-grouped:   group g reduces over rows offsets[g]..offsets[g+1]-1 of
 //     both A and B and writes C_g = out + g*out_group (weight gradients).
 //
-// Tiles are 128x128x64 or 256x256x64 (chosen per call from the average rows
-// per group), 4 waves, LDS double-buffered with register prefetch.  The
-// kernel is persistent: grid = a multiple of 8 workgroups;
-// workgroup i runs on XCD i%8 and, in each round, takes the tile at position
-// i/8 of that XCD's contiguous share of the round, so neighbouring tiles
-// (which share a weight panel or an activation panel) meet in one XCD's L2.
+// Data movement.  Operand tiles go from HBM straight into LDS with
+// buffer_load_dwordx4 ... lds (no VGPR staging).  Each tile's buffer
+// resource is bounded to the rows that tile may use, so reads past a group's
+// last row (ragged row tiles, K tails of the weight gradients) return zeros.
+// The LDS holds an S-stage ring of BK-deep slabs; one barrier per slab, with
+// the loads for slab it+S-1 issued right after it, so S-1 slabs are in flight
+// while the waves multiply.  LDS rows carry no padding; 16-byte chunks are
+// XOR-swizzled by row so the MFMA operand reads are free of bank conflicts:
+//   K-contiguous slab [T rows][BK]: fragments by ds_read_b128 (8 k of one row);
+//   K-strided slab [BK rows][T]:    fragments by two ds_read_b64_tr_b16, which
+//     gather 4 consecutive k of one column per lane (the transpose happens in
+//     the LDS read, none in registers).
+//
+// Workgroup: 4 waves in 2x2, each wave (TM/2) x (TN/2) of 32x32 MFMA blocks.
+// Measured on MI355X, the loop is bound by the operand stream from L2 into
+// LDS (removing the in-loop loads alone lifts it from ~1.07 to ~1.75 PF/s),
+// so the tile order below is chosen for L2 reuse.
+// Two tile shapes: 256x256 (one workgroup per CU, accumulators in AGPRs,
+// half the LDS bytes per MFMA flop) for groups of >= 512 rows, 128x128 (two
+// workgroups per CU) otherwise.  The kernel is persistent: the grid is a
+// multiple of 8 workgroups; workgroup i runs on XCD i%8 and in each round
+// takes the tile at position i/8 of that XCD's contiguous share of the round,
+// so neighbouring tiles (sharing a weight or activation panel) meet in one
+// XCD's L2.
 #pragma once
 
 #include "moe_common.h"
 
 namespace moe_gemm {
 
-// Row tile of the small configuration: the tile schedule's unit for
-// row-grouped GEMMs is chosen per call (TILE_SMALL or TILE_LARGE rows).
-constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;  // +8 bf16 per LDS row: conflict-free b128 reads
-constexpr int BM_LARGE = 256, BN_LARGE = 256;
+constexpr int BM = 128, BN = 128;              // small tile
+constexpr int BM_LARGE = 256, BN_LARGE = 256;  // large tile
+constexpr int BK = 32;                         // slab depth
+constexpr int STAGES = 4;                      // LDS ring depth
 
 enum Epi {
   EPI_SWIGLU = 0,      // H = silu(G)*U from paired gate/up columns; optional bf16 G|U save
@@ -44,6 +59,7 @@ struct Args {
   const bf16_t* B;
   int64_t ldb;
   int64_t b_group;           // row-grouped: elements between groups' weights
+  int64_t b_rows;            // row-grouped: rows of one group's weight (its buffer bound)
   int64_t K;                 // row-grouped: reduction length (multiple of BK)
   int64_t M;                 // K-grouped: output rows per group
   int64_t N;                 // output columns
@@ -59,31 +75,66 @@ struct Args {
   bf16_t* gu_out;            // SwiGLU: G|U save (or null); SwiGLU-bwd: dG|dU out
 };
 
-// 8x8 bf16 transpose: in[r] holds row r (8 values along m), out[m] holds the
-// 8 values of column m (along k).
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = in[2 * j][c], hi = in[2 * j + 1][c];
-      out[2 * c][j] = (lo & 0xFFFFu) | (hi << 16);
-      out[2 * c + 1][j] = (lo >> 16) | (hi & 0xFFFF0000u);
-    }
+typedef __attribute__((address_space(3))) void lds_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0 : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
-// TM x TN workgroup tile, 4 waves in 2x2, each wave (TM/2) x (TN/2) made of
-// FM x FN blocks of 32x32.  128x128 tiles keep two workgroups per CU; 256x256
-// tiles (one workgroup per CU, accumulators in AGPRs) halve the LDS bytes
-// read per MFMA flop and give each 64-deep slab ~2k MFMA cycles per wave to
-// hide the next slab's global loads.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 16-byte chunk swizzles
+__device__ __forceinline__ int swz_kc(int row) { return ((row >> 2) ^ (row >> 1)) & 3; }  // slab [T][32]
+__device__ __forceinline__ int swz_ks(int k) { return (k & 3) << 2; }                     // slab [32][T]
+
+template <int TM, int TN>
+constexpr int lds_bytes() {
+  return STAGES * (TM + TN) * BK * 2 + 16 * ((MOE_MAX_EXPERTS + 1 + 3) / 4);
+}
+
+__device__ __forceinline__ bf16x8 join8(s16x4 lo, s16x4 hi) {
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Order of one group's mt x nb tiles: bands of BAND column blocks; inside a
+// band, row tiles in order with the column blocks fastest.  A persistent
+// round hands each XCD a run of consecutive tiles, so its concurrent tiles
+// form a compact (rows x BAND) block: every operand slab an XCD pulls into its
+// L2 feeds several workgroups (row panels are shared by BAND tiles, column
+// panels by all the block's row tiles).
+constexpr int BAND = 8;
+__device__ __forceinline__ void band_order(int t, int mts, int nbs, int& mt, int& nb) {
+  const int band = t / (mts * BAND);
+  const int r = t - band * mts * BAND;
+  const int w = nbs - band * BAND < BAND ? nbs - band * BAND : BAND;   // width of this band
+  mt = r / w;
+  nb = band * BAND + (r - mt * w);
+}
+
 template <int TM, int TN, bool AK, bool BKC, bool KG, int EPI>
-__global__ __launch_bounds__(256, (TM * TN > 128 * 128) ? 1 : 2) void gemm_kernel(Args p) {
+__global__ __launch_bounds__(256, (TM * TN > 128 * 128) ? 1 : 2)
+__attribute__((amdgpu_waves_per_eu((TM * TN > 128 * 128) ? 1 : 2, (TM * TN > 128 * 128) ? 1 : 2)))
+void gemm_kernel(Args p) {
   constexpr int WTM = TM / 2, WTN = TN / 2, FM = WTM / 32, FN = WTN / 32;
-  constexpr int CA = TM / 32, CB = TN / 32;      // 16-byte chunks per thread per slab (K-contiguous)
-  constexpr int UA = TM / 128, UB = TN / 128;    // 8x8 transpose units per thread-half per slab
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2][(TM + TN) * LDK];
-  __shared__ int32_t s_pref[MOE_MAX_EXPERTS + 1];
+  constexpr int SA = TM * BK * 2, SB = TN * BK * 2, STAGE = SA + SB;   // bytes
+  constexpr int LA = SA / 4096, LB = SB / 4096;                         // 1 KB loads per wave per slab
+  constexpr int LPS = LA + LB;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  int32_t* s_pref = reinterpret_cast<int32_t*>(smem + STAGES * STAGE);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -102,9 +153,7 @@ __global__ __launch_bounds__(256, (TM * TN > 128 * 128) ? 1 : 2) void gemm_kerne
     int64_t row0, row_end, kbeg, kend;
     if (KG) {
       e = L / (p.MT * NB);
-      const int r = L - e * p.MT * NB;
-      nb = r / p.MT;
-      mt = r - nb * p.MT;
+      band_order(L - e * p.MT * NB, p.MT, NB, mt, nb);
       row0 = (int64_t)mt * TM;
       row_end = p.M;
       kbeg = p.offsets[e];
@@ -116,125 +165,113 @@ __global__ __launch_bounds__(256, (TM * TN > 128 * 128) ? 1 : 2) void gemm_kerne
         if (s_pref[mid] * NB <= L) lo = mid; else hi = mid;
       }
       e = lo;
-      const int mte = s_pref[e + 1] - s_pref[e];
-      const int local = L - s_pref[e] * NB;
-      nb = local / mte;
-      mt = local - nb * mte;
+      band_order(L - s_pref[e] * NB, s_pref[e + 1] - s_pref[e], NB, mt, nb);
       row0 = p.offsets[e] + (int64_t)mt * TM;
       row_end = p.offsets[e + 1];
       kbeg = 0;
       kend = p.K;
     }
-    const int nk = (int)((kend - kbeg + BK - 1) / BK);
-    const bf16_t* Bg = KG ? p.B : p.B + (int64_t)e * p.b_group;
+    // slabs: K / BK for a row-grouped GEMM (even: K is a multiple of 64);
+    // rounded up to even for a K-grouped one (the extra slab reads zeros)
+    const int nk = KG ? (int)((kend - kbeg + 2 * BK - 1) / (2 * BK)) * 2 : (int)((kend - kbeg) / BK);
 
-    // ---- loader set-up
-    // K-contiguous operands: 16-byte chunks, chunk c -> tile row c/8, k (c%8)*8
-    const bf16_t* a_row[CA];
-    const bf16_t* b_row[CB];
+    // ---- buffer resources and per-lane byte offsets of this tile's loads.
+    // A K-contiguous: rows row0.. of A, bounded at the group's last row.
+    // A K-strided:    rows kbeg.. of A, bounded at kend; columns from row0.
+    const void* a_base;
+    const void* b_base;
+    int64_t a_bytes, b_bytes;
+    uint32_t a_voff[LA], b_voff[LB];
+    uint32_t a_step, b_step;   // bytes per slab
     if (AK) {
+      const int64_t a_rows = row_end - row0 < TM ? row_end - row0 : TM;
+      a_base = p.A + row0 * p.lda;
+      a_bytes = a_rows * p.lda * 2;
+      a_step = BK * 2;
 #pragma unroll
-      for (int i = 0; i < CA; ++i) {
-        const int c = tid + 256 * i;
-        int64_t r = row0 + (c >> 3);
-        if (r >= row_end) r = row_end - 1;   // ragged tail: a valid row, its result is discarded
-        a_row[i] = p.A + r * p.lda + (c & 7) * 8;
+      for (int q = 0; q < LA; ++q) {
+        const int r = (wave * LA + q) * 16 + (lane >> 2);      // tile row of this lane
+        const int c = (lane & 3) ^ swz_kc(r);                  // logical chunk it fetches
+        a_voff[q] = (uint32_t)((int64_t)r * p.lda * 2 + c * 16);
+      }
+    } else {
+      a_base = p.A + kbeg * p.lda;
+      a_bytes = (kend - kbeg) * p.lda * 2;
+      a_step = (uint32_t)(BK * p.lda * 2);
+      constexpr int CPR = TM / 8;                              // chunks per slab row
+#pragma unroll
+      for (int q = 0; q < LA; ++q) {
+        const int idx = (wave * LA + q) * 64 + lane;           // physical chunk index in the slab
+        const int k = idx / CPR, pc = idx % CPR;
+        const int c = pc ^ swz_ks(k);
+        a_voff[q] = (uint32_t)((int64_t)k * p.lda * 2 + (row0 + c * 8) * 2);
       }
     }
     if (BKC) {
+      b_base = p.B + (int64_t)e * p.b_group;
+      b_bytes = p.b_rows * p.ldb * 2;
+      b_step = BK * 2;
 #pragma unroll
-      for (int i = 0; i < CB; ++i) {
-        const int c = tid + 256 * i, r = c >> 3;
+      for (int q = 0; q < LB; ++q) {
+        const int r = (wave * LB + q) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swz_kc(r);
         int64_t n;
         if (EPI == EPI_SWIGLU) {
           const int jb = r >> 5;   // 32-row blocks of the tile: gate, up, gate, up, ...
           n = ((jb & 1) ? p.N : 0) + (int64_t)nb * (TN / 2) + (jb >> 1) * 32 + (r & 31);
         } else {
-          n = (int64_t)nb * TN + r;
-          if (n >= p.N) n = p.N - 1;
+          n = (int64_t)nb * TN + r;   // rows past the weight read as zeros
         }
-        b_row[i] = Bg + n * p.ldb + (c & 7) * 8;
+        b_voff[q] = (uint32_t)(n * p.ldb * 2 + c * 16);
       }
-    }
-    // K-strided operands: 8(k) x 8(m) units; unit u -> k block u/(T/8), m block
-    // u%(T/8).  Threads 0..127 serve A, threads 128..255 serve B.
-    const bool t_is_a = tid < 128;
-    constexpr int UMAX = UA > UB ? UA : UB;
-    const int nunits = t_is_a ? (AK ? 0 : UA) : (BKC ? 0 : UB);
-    const int tdim = t_is_a ? TM : TN;
-    const bf16_t* t_src[UMAX];
-    bool t_mvalid[UMAX];
-    int t_kb[UMAX], t_mb[UMAX];
-    const int64_t t_ld = t_is_a ? p.lda : p.ldb;
+    } else {
+      const bf16_t* Bk = KG ? p.B + kbeg * p.ldb : p.B + (int64_t)e * p.b_group;
+      b_base = Bk;
+      b_bytes = (KG ? (kend - kbeg) : p.K) * p.ldb * 2;
+      b_step = (uint32_t)(BK * p.ldb * 2);
+      constexpr int CPR = TN / 8;
 #pragma unroll
-    for (int q = 0; q < UMAX; ++q) {
-      const int u = (tid & 127) + 128 * q;
-      t_kb[q] = u / (tdim / 8);
-      t_mb[q] = u % (tdim / 8);
-      t_src[q] = nullptr;
-      t_mvalid[q] = false;
-      if (q < nunits) {
-        if (t_is_a) {
-          const int64_t m = row0 + 8 * t_mb[q];
-          t_mvalid[q] = m < row_end;
-          t_src[q] = p.A + (kbeg + 8 * t_kb[q]) * p.lda + m;
-        } else {
-          const int64_t n = (int64_t)nb * TN + 8 * t_mb[q];
-          t_mvalid[q] = n < p.N;
-          t_src[q] = Bg + (kbeg + 8 * t_kb[q]) * p.ldb + n;
-        }
+      for (int q = 0; q < LB; ++q) {
+        const int idx = (wave * LB + q) * 64 + lane;
+        const int k = idx / CPR, pc = idx % CPR;
+        const int c = pc ^ swz_ks(k);
+        b_voff[q] = (uint32_t)((int64_t)k * p.ldb * 2 + ((int64_t)nb * TN + c * 8) * 2);
       }
     }
 
-    u32x4 ra[AK ? CA : 1], rb[BKC ? CB : 1], rt[UMAX][8];
-    auto gload = [&](int it) {
-      const int64_t k0 = (int64_t)it * BK;
-      if (AK) {
-#pragma unroll
-        for (int i = 0; i < CA; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_row[i] + k0);
-      }
-      if (BKC) {
-#pragma unroll
-        for (int i = 0; i < CB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b_row[i] + k0);
-      }
-#pragma unroll
-      for (int q = 0; q < UMAX; ++q) {
-        if (q < nunits) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const bool ok = t_mvalid[q] && (kbeg + k0 + 8 * t_kb[q] + i < kend);
-            rt[q][i] = ok ? *reinterpret_cast<const u32x4*>(t_src[q] + (k0 + i) * t_ld) : u32x4{0u, 0u, 0u, 0u};
-          }
-        }
-      }
+    // Loads of one BK-deep slab into its ring stage: LA (LB) 1 KB
+    // buffer->LDS loads per wave for A (B), 16 bytes per lane placed
+    // lane-linearly.  The host compilation pass only needs this kernel's
+    // signature (for its launch stub) and cannot type the LDS-pointer cast,
+    // so the statement exists in the device pass only.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define MOE_ISSUE(slab_)                                                                             \
+  do {                                                                                               \
+    const int slab = (slab_);                                                                        \
+    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a_base, a_bytes);                                  \
+    const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(b_base, b_bytes);                                  \
+    char* st_ = smem + (slab % STAGES) * STAGE;                                                      \
+    _Pragma("unroll") for (int q = 0; q < LA; ++q)                                                   \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_t*)(st_ + (wave * LA + q) * 1024), 16, a_voff[q], \
+                                               (uint32_t)slab * a_step, 0, 0);                       \
+    _Pragma("unroll") for (int q = 0; q < LB; ++q)                                                   \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_t*)(st_ + SA + (wave * LB + q) * 1024), 16,      \
+                                               b_voff[q], (uint32_t)slab * b_step, 0, 0);            \
+  } while (0)
+#else
+#define MOE_ISSUE(slab_) ((void)(slab_))
+#endif
+
+    // fragment byte offsets inside a stage for the 16-deep step kk
+    auto frag_kc = [&](int region, int row, int kk) -> int {   // K-contiguous slab: ds_read_b128
+      const int c = (kk >> 3) + (lane >> 5);
+      return region + row * (BK * 2) + ((c ^ swz_kc(row)) << 4);
     };
-    auto sstore = [&](int buf) {
-      bf16_t* sa = smem[buf];
-      bf16_t* sb = smem[buf] + TM * LDK;
-      if (AK) {
-#pragma unroll
-        for (int i = 0; i < CA; ++i) {
-          const int c = tid + 256 * i;
-          *reinterpret_cast<u32x4*>(sa + (c >> 3) * LDK + (c & 7) * 8) = ra[i];
-        }
-      }
-      if (BKC) {
-#pragma unroll
-        for (int i = 0; i < CB; ++i) {
-          const int c = tid + 256 * i;
-          *reinterpret_cast<u32x4*>(sb + (c >> 3) * LDK + (c & 7) * 8) = rb[i];
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < UMAX; ++q) {
-        if (q < nunits) {
-          u32x4 tr[8];
-          transpose8x8(rt[q], tr);
-          bf16_t* s = (t_is_a ? sa : sb) + (8 * t_mb[q]) * LDK + 8 * t_kb[q];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(s + i * LDK) = tr[i];
-        }
-      }
+    auto frag_ks = [&](int region, int T, int col0, int kk, int t) -> int {   // K-strided slab: ds_read_b64_tr_b16
+      const int g = lane >> 4, a = lane & 15;
+      const int k = kk + 8 * (g >> 1) + 4 * t + (a >> 2);
+      const int m = col0 + 16 * (g & 1) + 4 * (a & 3);
+      return region + k * (T * 2) + (((m >> 3) ^ swz_ks(k)) << 4) + ((m & 7) << 1);
     };
 
     f32x16 acc[FM][FN];
@@ -243,85 +280,193 @@ __global__ __launch_bounds__(256, (TM * TN > 128 * 128) ? 1 : 2) void gemm_kerne
 #pragma unroll
       for (int ni = 0; ni < FN; ++ni) acc[mi][ni] = f32x16{};
 
-    if (nk > 0) {
-      gload(0);
-      sstore(0);
-      __syncthreads();
-      for (int it = 0; it < nk; ++it) {
-        const int cur = it & 1;
-        if (it + 1 < nk) gload(it + 1);
-        const bf16_t* sa = smem[cur] + (wm * WTM + (lane & 31)) * LDK + 8 * (lane >> 5);
-        const bf16_t* sb = smem[cur] + TM * LDK + (wn * WTN + (lane & 31)) * LDK + 8 * (lane >> 5);
+    // Fragment reads of one slab into a register set (both 16-deep steps).
+    auto read_frags = [&](const char* st, bf16x8 (&fa)[2][FM], bf16x8 (&fb)[2][FN]) {
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-          bf16x8 a[FM], b[FN];
+      for (int h = 0; h < 2; ++h) {
+        const int kk = 16 * h;
 #pragma unroll
-          for (int mi = 0; mi < FM; ++mi) a[mi] = *reinterpret_cast<const bf16x8*>(sa + mi * 32 * LDK + kk);
-#pragma unroll
-          for (int ni = 0; ni < FN; ++ni) b[ni] = *reinterpret_cast<const bf16x8*>(sb + ni * 32 * LDK + kk);
-#pragma unroll
-          for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < FN; ++ni)
-              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+        for (int mi = 0; mi < FM; ++mi) {
+          const int m0 = wm * WTM + mi * 32;
+          if (AK) {
+            fa[h][mi] = *reinterpret_cast<const bf16x8*>(st + frag_kc(0, m0 + (lane & 31), kk));
+          } else {
+            fa[h][mi] = join8(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + frag_ks(0, TM, m0, kk, 0))),
+                              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + frag_ks(0, TM, m0, kk, 1))));
+          }
         }
-        if (it + 1 < nk) sstore(cur ^ 1);
-        __syncthreads();
-      }
-    }
-
-    // ---- epilogue.  32x32 MFMA result: register r of a lane holds row
-    // 8*(r/4) + 4*(lane/32) + r%4 and column lane%32 of the 32x32 block.
-    if (EPI == EPI_SWIGLU) {
-      bf16_t* H = static_cast<bf16_t*>(p.out);
 #pragma unroll
-      for (int pi = 0; pi < FN / 2; ++pi) {   // wave column blocks come in (gate, up) pairs
-        const int64_t col = (int64_t)nb * (TN / 2) + (wn * (WTN / 64) + pi) * 32 + (lane & 31);
+        for (int ni = 0; ni < FN; ++ni) {
+          const int n0 = wn * WTN + ni * 32;
+          if (BKC) {
+            fb[h][ni] = *reinterpret_cast<const bf16x8*>(st + frag_kc(SA, n0 + (lane & 31), kk));
+          } else {
+            fb[h][ni] = join8(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + frag_ks(SA, TN, n0, kk, 0))),
+                              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + frag_ks(SA, TN, n0, kk, 1))));
+          }
+        }
+      }
+    };
+    auto mfmas = [&](const bf16x8 (&fa)[2][FM], const bf16x8 (&fb)[2][FN]) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t row = row0 + wm * WTM + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (row < row_end) {
-              const float g = acc[mi][2 * pi][r], u = acc[mi][2 * pi + 1][r];
-              H[row * p.ldo + col] = (bf16_t)f32_to_bf16(silu_f32(g) * u);
-              if (p.gu_out) {
-                p.gu_out[row * 2 * p.N + col] = (bf16_t)f32_to_bf16(g);
-                p.gu_out[row * 2 * p.N + p.N + col] = (bf16_t)f32_to_bf16(u);
+          for (int ni = 0; ni < FN; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[h][mi], fb[h][ni], acc[mi][ni], 0, 0, 0);
+    };
+    // LDS reads per slab (a transposing fragment takes two) and MFMAs per slab
+    constexpr int NREAD = 2 * (FM * (AK ? 1 : 2) + FN * (BKC ? 1 : 2));
+    constexpr int NMFMA = 2 * FM * FN;
+
+    // Slab step it: make slab it+1 visible, refill the ring three slabs
+    // ahead, and multiply slab it (registers `ca/cb`, read one step earlier)
+    // while the fragments of slab it+1 stream into `na/nb`, one LDS read per
+    // NMFMA/NREAD MFMAs.  Slab it+3 goes into the stage slab it-1 used; every
+    // wave consumed those fragments before this step's barrier.  Steps come
+    // in pairs that swap the two register sets, and no branch surrounds the
+    // MFMAs (a branch there makes the compiler copy the accumulators): the
+    // slab count is even (K of a row-grouped GEMM is a multiple of 64; a
+    // K-grouped tile rounds up and its extra slab reads zeros past the
+    // group's rows), and on the last step the wait and barrier are no-ops and
+    // the reads fetch a stage nobody writes any more.
+#define MOE_STEP(it_, ca, cb, na, nb_)                                                            \
+  do {                                                                                          \
+    const int it = (it_);                                                                       \
+    if (it + 2 < nk) wait_vmcnt<LPS>(); else wait_vmcnt<0>();                                   \
+    block_barrier();                                                                            \
+    if (it + STAGES - 1 < nk) MOE_ISSUE(it + STAGES - 1);                                       \
+    read_frags(smem + ((it + 1) % STAGES) * STAGE, na, nb_);                                    \
+    mfmas(ca, cb);                                                                              \
+    _Pragma("unroll") for (int g_ = 0; g_ < NREAD; ++g_) {                                      \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                        \
+      __builtin_amdgcn_sched_group_barrier(0x008, NMFMA / NREAD > 0 ? NMFMA / NREAD : 1, 0);    \
+    }                                                                                           \
+  } while (0)
+
+    wait_vmcnt<0>();   // previous tile's epilogue stores done: vmcnt now counts slab loads only
+    if (nk > 0) {
+#pragma unroll
+      for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk) MOE_ISSUE(s);
+      bf16x8 fa0[2][FM], fb0[2][FN], fa1[2][FM], fb1[2][FN];
+      if (nk >= 3) wait_vmcnt<2 * LPS>();
+      else if (nk == 2) wait_vmcnt<LPS>();
+      else wait_vmcnt<0>();
+      block_barrier();
+      read_frags(smem, fa0, fb0);
+      for (int it2 = 0; it2 < nk; it2 += 2) {
+        MOE_STEP(it2, fa0, fb0, fa1, fb1);
+        MOE_STEP(it2 + 1, fa1, fb1, fa0, fb0);
+      }
+      block_barrier();   // every wave is done with the ring before the epilogue stages in it
+    }
+#undef MOE_STEP
+#undef MOE_ISSUE
+
+    // ---- epilogue.  Each 32x32 result block goes through LDS (the ring is
+    // idle now): the MFMA layout (register r of a lane = row 8*(r/4) +
+    // 4*(lane/32) + r%4, column lane%32) is written out, then read back as
+    // 4-column chunks so every global store is a row-contiguous vector
+    // (16 bytes of fp32 or 8 bytes of bf16) and the SwiGLU math runs on them.
+    {
+      constexpr int SLD = 36;   // floats per staged row (16-byte aligned rows, spread banks)
+      float* stg0 = reinterpret_cast<float*>(smem) + wave * (2 * 32 * SLD);
+      float* stg1 = stg0 + 32 * SLD;
+      auto stage = [&](float* stg, const f32x16& v) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) stg[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * SLD + (lane & 31)] = v[r];
+      };
+      if (EPI == EPI_SWIGLU) {
+        bf16_t* H = static_cast<bf16_t*>(p.out);
+#pragma unroll
+        for (int pi = 0; pi < FN / 2; ++pi) {   // wave column blocks come in (gate, up) pairs
+          const int64_t col0 = (int64_t)nb * (TN / 2) + (wn * (WTN / 64) + pi) * 32;
+#pragma unroll
+          for (int mi = 0; mi < FM; ++mi) {
+            stage(stg0, acc[mi][2 * pi]);
+            stage(stg1, acc[mi][2 * pi + 1]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int idx = lane + 64 * j, rr = idx >> 3, c4 = (idx & 7) * 4;
+              const int64_t row = row0 + wm * WTM + mi * 32 + rr;
+              const f32x4 g = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c4);
+              const f32x4 u = *reinterpret_cast<const f32x4*>(stg1 + rr * SLD + c4);
+              if (row < row_end) {
+                const int64_t col = col0 + c4;
+                uint2 h;
+                h.x = pack_bf16x2(silu_f32(g[0]) * u[0], silu_f32(g[1]) * u[1]);
+                h.y = pack_bf16x2(silu_f32(g[2]) * u[2], silu_f32(g[3]) * u[3]);
+                *reinterpret_cast<uint2*>(H + row * p.ldo + col) = h;
+                if (p.gu_out) {
+                  uint2 gg, uu;
+                  gg.x = pack_bf16x2(g[0], g[1]);
+                  gg.y = pack_bf16x2(g[2], g[3]);
+                  uu.x = pack_bf16x2(u[0], u[1]);
+                  uu.y = pack_bf16x2(u[2], u[3]);
+                  *reinterpret_cast<uint2*>(p.gu_out + row * 2 * p.N + col) = gg;
+                  *reinterpret_cast<uint2*>(p.gu_out + row * 2 * p.N + p.N + col) = uu;
+                }
               }
             }
           }
-      }
-    } else {
+        }
+      } else {
 #pragma unroll
-      for (int ni = 0; ni < FN; ++ni) {
-        const int64_t col = (int64_t)nb * TN + wn * WTN + ni * 32 + (lane & 31);
-        if (col >= p.N) continue;
+        for (int ni = 0; ni < FN; ++ni) {
+          const int64_t col0 = (int64_t)nb * TN + wn * WTN + ni * 32;
+          if (col0 >= p.N) continue;
 #pragma unroll
-        for (int mi = 0; mi < FM; ++mi)
+          for (int mi = 0; mi < FM; ++mi) {
+            stage(stg0, acc[mi][ni]);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t row = row0 + wm * WTM + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (row >= row_end) continue;
-            const float v = acc[mi][ni][r];
-            if (EPI == EPI_F32) {
-              float* C = static_cast<float*>(p.out) + (KG ? (int64_t)e * p.out_group : 0);
-              C[row * p.ldo + col] = v;
-            } else {  // EPI_SWIGLU_BWD: v = dH[row][col]
-              const float g = bf16_to_f32(p.gu_in[row * 2 * p.N + col]);
-              const float u = bf16_to_f32(p.gu_in[row * 2 * p.N + p.N + col]);
-              const float sg = 1.0f / (1.0f + __expf(-g));
-              p.gu_out[row * 2 * p.N + col] = (bf16_t)f32_to_bf16(v * u * sg * (1.0f + g * (1.0f - sg)));
-              p.gu_out[row * 2 * p.N + p.N + col] = (bf16_t)f32_to_bf16(v * g * sg);
+            for (int j = 0; j < 4; ++j) {
+              const int idx = lane + 64 * j, rr = idx >> 3, c4 = (idx & 7) * 4;
+              const int64_t row = row0 + wm * WTM + mi * 32 + rr;
+              const f32x4 v = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c4);
+              const int64_t col = col0 + c4;
+              if (row < row_end && col < p.N) {
+                if (EPI == EPI_F32) {
+                  float* C = static_cast<float*>(p.out) + (KG ? (int64_t)e * p.out_group : 0);
+                  *reinterpret_cast<f32x4*>(C + row * p.ldo + col) = v;
+                } else {  // EPI_SWIGLU_BWD: v = dH[row][col..col+3]
+                  const uint2 gb = *reinterpret_cast<const uint2*>(p.gu_in + row * 2 * p.N + col);
+                  const uint2 ub = *reinterpret_cast<const uint2*>(p.gu_in + row * 2 * p.N + p.N + col);
+                  const float g[4] = {bf16_to_f32(gb.x & 0xFFFFu), bf16_to_f32(gb.x >> 16), bf16_to_f32(gb.y & 0xFFFFu),
+                                      bf16_to_f32(gb.y >> 16)};
+                  const float u[4] = {bf16_to_f32(ub.x & 0xFFFFu), bf16_to_f32(ub.x >> 16), bf16_to_f32(ub.y & 0xFFFFu),
+                                      bf16_to_f32(ub.y >> 16)};
+                  float dg[4], du[4];
+#pragma unroll
+                  for (int q = 0; q < 4; ++q) {
+                    const float sg = 1.0f / (1.0f + __expf(-g[q]));
+                    dg[q] = v[q] * u[q] * sg * (1.0f + g[q] * (1.0f - sg));
+                    du[q] = v[q] * g[q] * sg;
+                  }
+                  uint2 o1, o2;
+                  o1.x = pack_bf16x2(dg[0], dg[1]);
+                  o1.y = pack_bf16x2(dg[2], dg[3]);
+                  o2.x = pack_bf16x2(du[0], du[1]);
+                  o2.y = pack_bf16x2(du[2], du[3]);
+                  *reinterpret_cast<uint2*>(p.gu_out + row * 2 * p.N + col) = o1;
+                  *reinterpret_cast<uint2*>(p.gu_out + row * 2 * p.N + p.N + col) = o2;
+                }
+              }
             }
           }
+        }
       }
     }
+    block_barrier();   // staging areas sit in the ring: free them before the next tile's loads
   }
 }
 
 // Persistent grid: at most `per_cu` workgroups per CU, a multiple of 8.
 int grid_for(int64_t tiles_upper, int per_cu);
+
+// Raises a kernel's dynamic-LDS limit (once per kernel, at its first launch).
+moe_status lds_attr(const void* fn, int bytes);
 
 // Fills in the tile counts of `a` for a TM x TN tile and launches.  `rows`
 // (row-grouped only) bounds the row tiles: sum over groups of
@@ -337,7 +482,11 @@ moe_status launch_cfg(Args a, int64_t rows, hipStream_t s) {
   } else {
     tiles = (ceil_div(rows, TM) + a.G) * a.NB;
   }
-  gemm_kernel<TM, TN, AK, BKC, KG, EPI><<<grid_for(tiles, TM * TN > 128 * 128 ? 1 : 2), 256, 0, s>>>(a);
+  constexpr int lds = lds_bytes<TM, TN>();
+  static const moe_status attr =
+      lds_attr(reinterpret_cast<const void*>(&gemm_kernel<TM, TN, AK, BKC, KG, EPI>), lds);
+  if (attr != MOE_OK) return attr;
+  gemm_kernel<TM, TN, AK, BKC, KG, EPI><<<grid_for(tiles, TM * TN > 128 * 128 ? 1 : 2), 256, lds, s>>>(a);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
