@@ -99,6 +99,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=None, help="oracle sample size (tokens)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="time a plain 2 GiB device-to-device copy (HBM reference and PMC byte calibration)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU: this layer's hot path runs on a single MI355X and has no multi-GPU "
@@ -106,6 +108,23 @@ def main():
         sys.exit(2)
 
     import torch
+    if a.copy_probe:
+        n = 1 << 31
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(a.steps):
+            dst.copy_(src)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / a.steps
+        print(json.dumps({"copy_bytes_per_launch": 2 * n, "ms": round(ms, 4),
+                          "gb_per_s": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+        return
     from mixture_experts_layer_free_amd import _lib
     from mixture_experts_layer_free_amd.layer import CallTimer, MoELayer, Shape
     from workloads import CONFIGS, make_inputs

@@ -5,9 +5,9 @@
 // step 1).  The selection bias and the logit offset get no gradient (Key
 // terms: the loss-free bias adds no gradient signal) and the top-k choice is
 // held fixed.  Kernels, in stream order:
-//   1. combine_bwd   one wave per token: dg = <dy, y_perm[row]>, dY_perm =
-//                    bf16(g*dy), then the gate backward (dl on the chosen
-//                    experts) in the same wave
+//   1. combine_bwd   one wave per expert row: dg = <dy, y_perm[row]>,
+//                    dY_perm = bf16(g*dy); then one wave per token for the
+//                    gate backward (dl on the chosen experts)
 //   2. router wgrad  dW_r[e] = sum over e's rows of dl * x_perm (row-chunk
 //                    partials, then an ordered reduction: deterministic)
 //   3. dgrad down    dH = dY_perm W_down, epilogue SwiGLU backward -> dG|dU
@@ -29,13 +29,59 @@ __device__ __forceinline__ float score_of(float l, int fn) {
   return l;
 }
 
-__global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restrict__ dy, const float* __restrict__ y,
-                                                          const int32_t* __restrict__ row_of,
-                                                          const float* __restrict__ gate, const int32_t* __restrict__ idx,
-                                                          const float* __restrict__ logits, int T, int k, int E,
-                                                          int64_t d, int fn, bf16_t* __restrict__ dy_perm,
-                                                          float* __restrict__ dg_out, float* __restrict__ dl_out,
-                                                          float* __restrict__ dl_perm) {
+// Combine backward in the permuted domain, one wave per expert row r (of
+// token t, slot j): dY_perm[r] = bf16(g[t,j] * dy[t]) and
+// dgp[r] = <dy[t], y_perm[r]>.  Rows are streamed in order (y_perm read and
+// dY_perm written sequentially); only dy rows are gathered, and those are
+// re-read k times from cache.
+__global__ __launch_bounds__(256) void combine_bwd_rows_kernel(const bf16_t* __restrict__ dy, const float* __restrict__ y,
+                                                               const int32_t* __restrict__ row_of,
+                                                               const int32_t* __restrict__ token_of,
+                                                               const float* __restrict__ gate, int64_t A, int k,
+                                                               int64_t d, bf16_t* __restrict__ dy_perm,
+                                                               float* __restrict__ dgp) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= A) return;
+  const int64_t t = token_of[r];
+  const uint64_t hit = __ballot(lane < k && row_of[t * k + lane] == (int32_t)r);
+  const int j = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
+  const float g = gate[t * k + j];
+  const int64_t nv = d / 8;   // 8 values per 16-byte bf16 vector
+  const u32x4* dyv = reinterpret_cast<const u32x4*>(dy + t * d);
+  const f32x4* yr = reinterpret_cast<const f32x4*>(y + r * d);
+  u32x4* out = reinterpret_cast<u32x4*>(dy_perm + r * d);
+  float part = 0.f;
+  for (int64_t v = lane; v < nv; v += MOE_WAVE) {
+    const u32x4 raw = dyv[v];
+    const f32x4 y0 = __builtin_nontemporal_load(yr + 2 * v);
+    const f32x4 y1 = __builtin_nontemporal_load(yr + 2 * v + 1);
+    float a[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      a[2 * q] = bf16_to_f32(raw[q] & 0xFFFFu);
+      a[2 * q + 1] = bf16_to_f32(raw[q] >> 16);
+    }
+    part = fmaf(a[0], y0[0], part); part = fmaf(a[1], y0[1], part);
+    part = fmaf(a[2], y0[2], part); part = fmaf(a[3], y0[3], part);
+    part = fmaf(a[4], y1[0], part); part = fmaf(a[5], y1[1], part);
+    part = fmaf(a[6], y1[2], part); part = fmaf(a[7], y1[3], part);
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(g * a[2 * q], g * a[2 * q + 1]);
+    out[v] = o;
+  }
+  part = wave_sum(part);
+  if (lane == 0) dgp[r] = part;
+}
+
+// Gate backward, one wave per token (lanes 0..k-1 hold the chosen experts):
+// dl on the chosen experts from dg = dgp[row_of[t,j]].
+__global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__ dgp, const int32_t* __restrict__ row_of,
+                                                       const float* __restrict__ gate, const int32_t* __restrict__ idx,
+                                                       const float* __restrict__ logits, int T, int k, int E, int fn,
+                                                       float* __restrict__ dg_out, float* __restrict__ dl_out,
+                                                       float* __restrict__ dl_perm) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -43,47 +89,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restri
   const int myr = act ? row_of[t * k + lane] : 0;
   const float myg = act ? gate[t * k + lane] : 0.f;
   const int mye = act ? idx[t * k + lane] : 0;
-  int rows[MOE_MAX_TOPK];
-  float g[MOE_MAX_TOPK], part[MOE_MAX_TOPK];
-#pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-    rows[j] = __shfl(myr, j, MOE_WAVE);
-    g[j] = __shfl(myg, j, MOE_WAVE);
-    part[j] = 0.f;
-  }
-  const int64_t nv = d / 8;  // 8 values per 16-byte bf16 vector
-  const u32x4* dyv = reinterpret_cast<const u32x4*>(dy + t * d);
-  for (int64_t v = lane; v < nv; v += MOE_WAVE) {
-    const u32x4 raw = dyv[v];
-    float a[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      a[2 * q] = bf16_to_f32(raw[q] & 0xFFFFu);
-      a[2 * q + 1] = bf16_to_f32(raw[q] >> 16);
-    }
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-      if (j >= k) break;
-      const f32x4* yr = reinterpret_cast<const f32x4*>(y + (int64_t)rows[j] * d) + 2 * v;
-      const f32x4 y0 = yr[0], y1 = yr[1];
-      float s = part[j];
-      s = fmaf(a[0], y0[0], s); s = fmaf(a[1], y0[1], s); s = fmaf(a[2], y0[2], s); s = fmaf(a[3], y0[3], s);
-      s = fmaf(a[4], y1[0], s); s = fmaf(a[5], y1[1], s); s = fmaf(a[6], y1[2], s); s = fmaf(a[7], y1[3], s);
-      part[j] = s;
-      u32x4 o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(g[j] * a[2 * q], g[j] * a[2 * q + 1]);
-      reinterpret_cast<u32x4*>(dy_perm + (int64_t)rows[j] * d)[v] = o;
-    }
-  }
-  float dg = 0.f;
-#pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-    if (j >= k) break;
-    const float s = wave_sum(part[j]);
-    if (lane == j) dg = s;
-  }
-  // gate backward (chosen experts only)
+  const float dg = act ? dgp[myr] : 0.f;
   const float D = wave_sum(act ? myg * dg : 0.f);
   float dl;
   if (fn == MOE_SOFTMAX_CHOSEN) {
@@ -105,7 +111,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16_t* __restri
 
 // Partial router weight gradient over one chunk of at most RCH rows of one
 // expert: part[p][c] = sum over the chunk's rows of dl_perm[r] * x_perm[r][c].
-// Two columns per thread, 512 columns per workgroup.
+// Eight columns (one 16-byte vector) per thread, 2048 columns per workgroup,
+// four rows in flight per thread.
 __global__ __launch_bounds__(256) void router_wgrad_part_kernel(const bf16_t* __restrict__ x_perm,
                                                                 const float* __restrict__ dl_perm,
                                                                 const int32_t* __restrict__ offsets,
@@ -121,17 +128,38 @@ __global__ __launch_bounds__(256) void router_wgrad_part_kernel(const bf16_t* __
   const int e = lo;
   const int64_t r0 = offsets[e] + (int64_t)(p - rc_prefix[e]) * RCH;
   const int64_t r1 = min((int64_t)offsets[e + 1], r0 + RCH);
-  const int64_t c = (int64_t)blockIdx.y * 512 + 2 * threadIdx.x;
+  const int64_t c = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 8;
   if (c >= d) return;
-  float a0 = 0.f, a1 = 0.f;
-  for (int64_t r = r0; r < r1; ++r) {
-    const float w = dl_perm[r];
-    const uint32_t xv = *reinterpret_cast<const uint32_t*>(x_perm + r * d + c);
-    a0 = fmaf(w, bf16_to_f32(xv & 0xFFFFu), a0);
-    a1 = fmaf(w, bf16_to_f32(xv >> 16), a1);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int64_t r = r0;
+  for (; r + 4 <= r1; r += 4) {
+    u32x4 xv[4];
+    float w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      xv[u] = *reinterpret_cast<const u32x4*>(x_perm + (r + u) * d + c);
+      w[u] = dl_perm[r + u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(w[u], bf16_to_f32(xv[u][q] & 0xFFFFu), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(w[u], bf16_to_f32(xv[u][q] >> 16), acc[2 * q + 1]);
+      }
   }
-  part[(int64_t)p * d + c] = a0;
-  part[(int64_t)p * d + c + 1] = a1;
+  for (; r < r1; ++r) {
+    const u32x4 xv = *reinterpret_cast<const u32x4*>(x_perm + r * d + c);
+    const float w = dl_perm[r];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] = fmaf(w, bf16_to_f32(xv[q] & 0xFFFFu), acc[2 * q]);
+      acc[2 * q + 1] = fmaf(w, bf16_to_f32(xv[q] >> 16), acc[2 * q + 1]);
+    }
+  }
+  f32x4* o = reinterpret_cast<f32x4*>(part + (int64_t)p * d + c);
+  o[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  o[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
 }
 
 __global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* __restrict__ part,
@@ -146,47 +174,50 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* _
 }
 
 // dx[t] = sum_j dx_perm[row_of[t,j]] + sum_j dl[t,j] * w_router[idx[t,j]]
+template <int K>
 __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restrict__ dx_perm,
                                                             const int32_t* __restrict__ row_of,
                                                             const int32_t* __restrict__ idx, const float* __restrict__ dl,
-                                                            const f32x4* __restrict__ w_router, int T, int k,
-                                                            int64_t nv, f32x4* __restrict__ dx) {
+                                                            const f32x4* __restrict__ w_router, int T, int64_t nv,
+                                                            f32x4* __restrict__ dx) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int myr = lane < k ? row_of[t * k + lane] : 0;
-  const int mye = lane < k ? idx[t * k + lane] : 0;
-  const float myl = lane < k ? dl[t * k + lane] : 0.f;
-  int rows[MOE_MAX_TOPK], ex[MOE_MAX_TOPK];
-  float w[MOE_MAX_TOPK];
+  const int myr = lane < K ? row_of[t * K + lane] : 0;
+  const int mye = lane < K ? idx[t * K + lane] : 0;
+  const float myl = lane < K ? dl[t * K + lane] : 0.f;
+  const f32x4* xr[K];
+  const f32x4* wr[K];
+  float w[K];
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-    rows[j] = __shfl(myr, j, MOE_WAVE);
-    ex[j] = __shfl(mye, j, MOE_WAVE);
+  for (int j = 0; j < K; ++j) {
+    xr[j] = dx_perm + (int64_t)__shfl(myr, j, MOE_WAVE) * nv;
+    wr[j] = w_router + (int64_t)__shfl(mye, j, MOE_WAVE) * nv;
     w[j] = __shfl(myl, j, MOE_WAVE);
   }
   for (int64_t v = lane; v < nv; v += MOE_WAVE) {
+    f32x4 xs[K], ws[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      xs[j] = __builtin_nontemporal_load(xr[j] + v);
+      ws[j] = wr[j][v];
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-      if (j >= k) break;
-      acc += dx_perm[(int64_t)rows[j] * nv + v];
-    }
+    for (int j = 0; j < K; ++j) acc += xs[j];
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-      if (j >= k) break;
-      const f32x4 wr = w_router[(int64_t)ex[j] * nv + v];
-      acc[0] = fmaf(w[j], wr[0], acc[0]);
-      acc[1] = fmaf(w[j], wr[1], acc[1]);
-      acc[2] = fmaf(w[j], wr[2], acc[2]);
-      acc[3] = fmaf(w[j], wr[3], acc[3]);
+    for (int j = 0; j < K; ++j) {
+      acc[0] = fmaf(w[j], ws[j][0], acc[0]);
+      acc[1] = fmaf(w[j], ws[j][1], acc[1]);
+      acc[2] = fmaf(w[j], ws[j][2], acc[2]);
+      acc[3] = fmaf(w[j], ws[j][3], acc[3]);
     }
     dx[t * nv + v] = acc;
   }
 }
 
 struct BwdLayout {
-  size_t dy_perm, dgu, dx_perm, dg, dl, dl_perm, mt_prefix, rc_prefix, rpart, total;
+  size_t dy_perm, dgu, dx_perm, dg, dl, dl_perm, dgp, mt_prefix, rc_prefix, rpart, total;
 };
 
 BwdLayout layout(int64_t T, int k, int E, int64_t d, int64_t f) {
@@ -200,6 +231,7 @@ BwdLayout layout(int64_t T, int k, int E, int64_t d, int64_t f) {
   L.dg = take((size_t)T * k * 4);
   L.dl = take((size_t)T * k * 4);
   L.dl_perm = take((size_t)A * 4);
+  L.dgp = take((size_t)A * 4);
   L.mt_prefix = take((size_t)(E + 1) * 4);
   L.rc_prefix = take((size_t)(E + 1) * 4);
   L.rpart = take((size_t)(ceil_div(A, RCH) + E) * d * 4);
@@ -233,6 +265,7 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   const BwdLayout Lo = layout(T, k, E, d, f);
   if (!a->workspace || a->workspace_bytes < Lo.total) return MOE_EWORKSPACE;
   hipStream_t s = moe_stream(stream);
+  const int64_t A = T * k;
   char* ws = static_cast<char*>(a->workspace);
   bf16_t* dy_perm = reinterpret_cast<bf16_t*>(ws + Lo.dy_perm);
   bf16_t* dgu = reinterpret_cast<bf16_t*>(ws + Lo.dgu);
@@ -240,23 +273,26 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   float* dg = a->dgate ? a->dgate : reinterpret_cast<float*>(ws + Lo.dg);
   float* dl = a->dlogit ? a->dlogit : reinterpret_cast<float*>(ws + Lo.dl);
   float* dl_perm = reinterpret_cast<float*>(ws + Lo.dl_perm);
+  float* dgp = reinterpret_cast<float*>(ws + Lo.dgp);
   int32_t* mt_prefix = reinterpret_cast<int32_t*>(ws + Lo.mt_prefix);
   int32_t* rc_prefix = reinterpret_cast<int32_t*>(ws + Lo.rc_prefix);
   float* rpart = reinterpret_cast<float*>(ws + Lo.rpart);
-  const int64_t A = T * k;
   const bf16_t* x_perm = static_cast<const bf16_t*>(a->x_perm);
   const bf16_t* wgu = static_cast<const bf16_t*>(a->w_gate_up);
   const bf16_t* wd = static_cast<const bf16_t*>(a->w_down);
 
-  // 1. combine + gate backward
-  combine_bwd_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(
-      static_cast<const bf16_t*>(a->dy), a->y_perm, a->row_of, a->topk_gate, a->topk_idx, a->logits, (int)T, k, E, d,
-      a->score_fn, dy_perm, dg, dl, dl_perm);
+  // 1. combine backward (permuted domain) + gate backward
+  combine_bwd_rows_kernel<<<(unsigned)ceil_div(A, 4), 256, 0, s>>>(static_cast<const bf16_t*>(a->dy), a->y_perm,
+                                                                     a->row_of, a->token_of, a->topk_gate, A, k, d,
+                                                                     dy_perm, dgp);
+  MOE_LAUNCH_CHECK();
+  gate_bwd_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(dgp, a->row_of, a->topk_gate, a->topk_idx, a->logits, (int)T,
+                                                           k, E, a->score_fn, dg, dl, dl_perm);
   MOE_LAUNCH_CHECK();
   // 2. router weight gradient
   moe_status st = moe_tile_schedule_launch(a->offsets, E, RCH, rc_prefix, s);
   if (st != MOE_OK) return st;
-  router_wgrad_part_kernel<<<dim3((unsigned)(ceil_div(A, RCH) + E), (unsigned)ceil_div(d, 512)), 256, 0, s>>>(
+  router_wgrad_part_kernel<<<dim3((unsigned)(ceil_div(A, RCH) + E), (unsigned)ceil_div(d, 2048)), 256, 0, s>>>(
       x_perm, dl_perm, a->offsets, rc_prefix, E, d, rpart);
   MOE_LAUNCH_CHECK();
   router_wgrad_reduce_kernel<<<dim3((unsigned)E, (unsigned)ceil_div(d, 256)), 256, 0, s>>>(rpart, rc_prefix, d,
@@ -309,9 +345,12 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
     if (st != MOE_OK) return st;
   }
   // 7. unpermute + router input gradient
-  unpermute_bwd_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(
-      reinterpret_cast<const f32x4*>(dx_perm), a->row_of, a->topk_idx, dl, reinterpret_cast<const f32x4*>(a->w_router),
-      (int)T, k, d / 4, reinterpret_cast<f32x4*>(a->dx));
+#define MOE_UBWD(K)                                                                                             \
+  unpermute_bwd_kernel<K><<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(                                             \
+      reinterpret_cast<const f32x4*>(dx_perm), a->row_of, a->topk_idx, dl, reinterpret_cast<const f32x4*>(a->w_router), \
+      (int)T, d / 4, reinterpret_cast<f32x4*>(a->dx))
+  MOE_DISPATCH_K(k, MOE_UBWD);
+#undef MOE_UBWD
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -9,33 +9,36 @@
 namespace {
 
 // One wave per token: out[t] = shared[t] + sum_j gate[t,j] * y[row_of[t,j]],
-// fp32, j ascending, 16-byte vectors along the row.
+// fp32, j ascending, 16-byte vectors along the row; the K row loads of a
+// vector are issued together.
+template <int K>
 __global__ __launch_bounds__(256) void combine_kernel(const f32x4* __restrict__ y, const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ gate, const f32x4* __restrict__ shared,
-                                                      int64_t T, int k, int64_t nv, void* __restrict__ out, int out_bf16) {
+                                                      int64_t T, int64_t nv, void* __restrict__ out, int out_bf16) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int myr = lane < k ? row_of[t * k + lane] : 0;
-  const float myg = lane < k ? gate[t * k + lane] : 0.f;
-  int rows[MOE_MAX_TOPK];
-  float g[MOE_MAX_TOPK];
+  const int myr = lane < K ? row_of[t * K + lane] : 0;
+  const float myg = lane < K ? gate[t * K + lane] : 0.f;
+  const f32x4* yr[K];
+  float g[K];
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-    rows[j] = __shfl(myr, j, MOE_WAVE);
+  for (int j = 0; j < K; ++j) {
+    yr[j] = y + (int64_t)__shfl(myr, j, MOE_WAVE) * nv;
     g[j] = __shfl(myg, j, MOE_WAVE);
   }
   for (int64_t v = lane; v < nv; v += MOE_WAVE) {
+    f32x4 yv[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) yv[j] = __builtin_nontemporal_load(yr[j] + v);
     f32x4 acc = shared ? shared[t * nv + v] : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j)
-      if (j < k) {
-        const f32x4 yv = y[(int64_t)rows[j] * nv + v];
-        acc[0] = fmaf(g[j], yv[0], acc[0]);
-        acc[1] = fmaf(g[j], yv[1], acc[1]);
-        acc[2] = fmaf(g[j], yv[2], acc[2]);
-        acc[3] = fmaf(g[j], yv[3], acc[3]);
-      }
+    for (int j = 0; j < K; ++j) {
+      acc[0] = fmaf(g[j], yv[j][0], acc[0]);
+      acc[1] = fmaf(g[j], yv[j][1], acc[1]);
+      acc[2] = fmaf(g[j], yv[j][2], acc[2]);
+      acc[3] = fmaf(g[j], yv[j][3], acc[3]);
+    }
     if (out_bf16) {
       uint2 o;
       o.x = pack_bf16x2(acc[0], acc[1]);
@@ -64,9 +67,12 @@ extern "C" moe_status moe_combine(const float* y_perm, const int32_t* row_of, co
   if (T < 1 || d < 1 || k < 1) return MOE_EINVAL;
   if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_EINVAL;
   if (k > MOE_MAX_TOPK || d % 4 != 0) return MOE_ENOTSUP;
-  combine_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, moe_stream(stream)>>>(
-      reinterpret_cast<const f32x4*>(y_perm), row_of, topk_gate, reinterpret_cast<const f32x4*>(shared_y), T, k, d / 4,
-      out, out_dtype == MOE_BF16);
+#define MOE_COMBINE(K)                                                                                      \
+  combine_kernel<K><<<(unsigned)ceil_div(T, 4), 256, 0, moe_stream(stream)>>>(                              \
+      reinterpret_cast<const f32x4*>(y_perm), row_of, topk_gate, reinterpret_cast<const f32x4*>(shared_y), T, d / 4, \
+      out, out_dtype == MOE_BF16)
+  MOE_DISPATCH_K(k, MOE_COMBINE);
+#undef MOE_COMBINE
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -412,7 +412,7 @@ void gemm_kernel(Args p) {
             }
           }
         }
-      } else {
+      } else if (EPI == EPI_F32) {
 #pragma unroll
         for (int ni = 0; ni < FN; ++ni) {
           const int64_t col0 = (int64_t)nb * TN + wn * WTN + ni * 32;
@@ -427,32 +427,68 @@ void gemm_kernel(Args p) {
               const f32x4 v = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c4);
               const int64_t col = col0 + c4;
               if (row < row_end && col < p.N) {
-                if (EPI == EPI_F32) {
-                  float* C = static_cast<float*>(p.out) + (KG ? (int64_t)e * p.out_group : 0);
-                  *reinterpret_cast<f32x4*>(C + row * p.ldo + col) = v;
-                } else {  // EPI_SWIGLU_BWD: v = dH[row][col..col+3]
-                  const uint2 gb = *reinterpret_cast<const uint2*>(p.gu_in + row * 2 * p.N + col);
-                  const uint2 ub = *reinterpret_cast<const uint2*>(p.gu_in + row * 2 * p.N + p.N + col);
-                  const float g[4] = {bf16_to_f32(gb.x & 0xFFFFu), bf16_to_f32(gb.x >> 16), bf16_to_f32(gb.y & 0xFFFFu),
-                                      bf16_to_f32(gb.y >> 16)};
-                  const float u[4] = {bf16_to_f32(ub.x & 0xFFFFu), bf16_to_f32(ub.x >> 16), bf16_to_f32(ub.y & 0xFFFFu),
-                                      bf16_to_f32(ub.y >> 16)};
-                  float dg[4], du[4];
-#pragma unroll
-                  for (int q = 0; q < 4; ++q) {
-                    const float sg = 1.0f / (1.0f + __expf(-g[q]));
-                    dg[q] = v[q] * u[q] * sg * (1.0f + g[q] * (1.0f - sg));
-                    du[q] = v[q] * g[q] * sg;
-                  }
-                  uint2 o1, o2;
-                  o1.x = pack_bf16x2(dg[0], dg[1]);
-                  o1.y = pack_bf16x2(dg[2], dg[3]);
-                  o2.x = pack_bf16x2(du[0], du[1]);
-                  o2.y = pack_bf16x2(du[2], du[3]);
-                  *reinterpret_cast<uint2*>(p.gu_out + row * 2 * p.N + col) = o1;
-                  *reinterpret_cast<uint2*>(p.gu_out + row * 2 * p.N + p.N + col) = o2;
-                }
+                float* C = static_cast<float*>(p.out) + (KG ? (int64_t)e * p.out_group : 0);
+                *reinterpret_cast<f32x4*>(C + row * p.ldo + col) = v;
               }
+            }
+          }
+        }
+      } else {  // EPI_SWIGLU_BWD: dH block -> dG, dU from the saved G, U
+        // the saved G|U vectors of block b+1 are loaded while block b is
+        // computed, so only the first block waits for memory
+        uint2 gn[4], un[4];
+        auto load_gu = [&](int b, uint2 (&gb)[4], uint2 (&ub)[4]) {
+          const int mi = b / FN, ni = b % FN;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int idx = lane + 64 * j, rr = idx >> 3, c4 = (idx & 7) * 4;
+            const int64_t row = row0 + wm * WTM + mi * 32 + rr;
+            const int64_t col = (int64_t)nb * TN + wn * WTN + ni * 32 + c4;
+            gb[j] = ub[j] = uint2{0u, 0u};
+            if (row < row_end && col < p.N) {
+              gb[j] = *reinterpret_cast<const uint2*>(p.gu_in + row * 2 * p.N + col);
+              ub[j] = *reinterpret_cast<const uint2*>(p.gu_in + row * 2 * p.N + p.N + col);
+            }
+          }
+        };
+        load_gu(0, gn, un);
+#pragma unroll
+        for (int b = 0; b < FM * FN; ++b) {
+          const int mi = b / FN, ni = b % FN;
+          uint2 gc[4], uc[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            gc[j] = gn[j];
+            uc[j] = un[j];
+          }
+          if (b + 1 < FM * FN) load_gu(b + 1, gn, un);
+          const int64_t col0 = (int64_t)nb * TN + wn * WTN + ni * 32;
+          stage(stg0, acc[mi][ni]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int idx = lane + 64 * j, rr = idx >> 3, c4 = (idx & 7) * 4;
+            const int64_t row = row0 + wm * WTM + mi * 32 + rr;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c4);
+            const int64_t col = col0 + c4;
+            if (row < row_end && col < p.N) {
+              const float g[4] = {bf16_to_f32(gc[j].x & 0xFFFFu), bf16_to_f32(gc[j].x >> 16),
+                                  bf16_to_f32(gc[j].y & 0xFFFFu), bf16_to_f32(gc[j].y >> 16)};
+              const float u[4] = {bf16_to_f32(uc[j].x & 0xFFFFu), bf16_to_f32(uc[j].x >> 16),
+                                  bf16_to_f32(uc[j].y & 0xFFFFu), bf16_to_f32(uc[j].y >> 16)};
+              float dg[4], du[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float sg = 1.0f / (1.0f + __expf(-g[q]));
+                dg[q] = v[q] * u[q] * sg * (1.0f + g[q] * (1.0f - sg));
+                du[q] = v[q] * g[q] * sg;
+              }
+              uint2 o1, o2;
+              o1.x = pack_bf16x2(dg[0], dg[1]);
+              o1.y = pack_bf16x2(dg[2], dg[3]);
+              o2.x = pack_bf16x2(du[0], du[1]);
+              o2.y = pack_bf16x2(du[2], du[3]);
+              *reinterpret_cast<uint2*>(p.gu_out + row * 2 * p.N + col) = o1;
+              *reinterpret_cast<uint2*>(p.gu_out + row * 2 * p.N + p.N + col) = o2;
             }
           }
         }

@@ -57,5 +57,21 @@ static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 static inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
+// Runs MACRO(K) with K the compile-time value of runtime k in [1, MOE_MAX_TOPK]:
+// per-token kernels keep their k row addresses in registers and issue all k
+// row loads together, which a runtime-bounded loop would serialise.
+#define MOE_DISPATCH_K(k, MACRO)                                             \
+  switch (k) {                                                              \
+    case 1: MACRO(1); break;   case 2: MACRO(2); break;                     \
+    case 3: MACRO(3); break;   case 4: MACRO(4); break;                     \
+    case 5: MACRO(5); break;   case 6: MACRO(6); break;                     \
+    case 7: MACRO(7); break;   case 8: MACRO(8); break;                     \
+    case 9: MACRO(9); break;   case 10: MACRO(10); break;                   \
+    case 11: MACRO(11); break; case 12: MACRO(12); break;                   \
+    case 13: MACRO(13); break; case 14: MACRO(14); break;                   \
+    case 15: MACRO(15); break; case 16: MACRO(16); break;                   \
+    default: return MOE_ENOTSUP;                                            \
+  }
+
 // Number of compute units of the current device (cached per device id).
 int moe_num_cus();

@@ -132,22 +132,35 @@ __global__ __launch_bounds__(PCH) void perm_index_kernel(const int32_t* __restri
 }
 
 // Token-major row copy: one wave per token reads its row once (16-byte
-// vectors) and writes it to the token's k expert rows.
-__global__ __launch_bounds__(256) void perm_copy_kernel(const u32x4* __restrict__ src, int64_t T, int k, int64_t nvec,
+// vectors) and writes it to the token's K expert rows.
+template <int K>
+__global__ __launch_bounds__(256) void perm_copy_kernel(const u32x4* __restrict__ src, int64_t T, int64_t nvec,
                                                         const int32_t* __restrict__ row_of, u32x4* __restrict__ dst) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int my = lane < k ? row_of[t * k + lane] : 0;
-  int rows[MOE_MAX_TOPK];
+  const int my = lane < K ? row_of[t * K + lane] : 0;
+  int rows[K];
+  bool ok = true;
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) rows[j] = __shfl(my, j, MOE_WAVE);
+  for (int j = 0; j < K; ++j) {
+    rows[j] = __shfl(my, j, MOE_WAVE);
+    ok = ok && rows[j] >= 0;   // an out-of-range expert id left its row unset
+  }
   const u32x4* s = src + t * nvec;
-  for (int64_t v = lane; v < nvec; v += MOE_WAVE) {
-    const u32x4 val = s[v];
+  if (ok) {
+    for (int64_t v = lane; v < nvec; v += MOE_WAVE) {
+      const u32x4 val = s[v];
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j)
-      if (j < k && rows[j] >= 0) dst[(int64_t)rows[j] * nvec + v] = val;
+      for (int j = 0; j < K; ++j) dst[(int64_t)rows[j] * nvec + v] = val;
+    }
+  } else {
+    for (int64_t v = lane; v < nvec; v += MOE_WAVE) {
+      const u32x4 val = s[v];
+#pragma unroll
+      for (int j = 0; j < K; ++j)
+        if (rows[j] >= 0) dst[(int64_t)rows[j] * nvec + v] = val;
+    }
   }
 }
 
@@ -179,8 +192,11 @@ extern "C" moe_status moe_permute(const int32_t* topk_idx, int64_t T, int k, int
   perm_index_kernel<<<nchunks, PCH, 0, s>>>(topk_idx, A, k, E, nchunks, hist, offsets, row_of, token_of);
   MOE_LAUNCH_CHECK();
   const int64_t nvec = d * es / 16;
-  perm_copy_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(static_cast<const u32x4*>(x), T, k, nvec, row_of,
-                                                             static_cast<u32x4*>(x_perm));
+#define MOE_PCOPY(K)                                                                                       \
+  perm_copy_kernel<K><<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(static_cast<const u32x4*>(x), T, nvec, row_of, \
+                                                               static_cast<u32x4*>(x_perm))
+  MOE_DISPATCH_K(k, MOE_PCOPY);
+#undef MOE_PCOPY
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
