@@ -61,6 +61,118 @@ def expert_flops(cfg, train):
     return f
 
 
+CSRC = os.path.join(ROOT, "mixture_experts_layer_free_amd", "csrc")
+TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_hash():
+    """sha256 over the HIP sources: measured HBM traffic is only reported for
+    the kernels it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+# which library call launched a kernel (by kernel name), for per-call PMC sums
+CALL_OF = [
+    ("router_logits_kernel", "route"), ("topk_gate_kernel", "route"),
+    ("perm_", "permute"),
+    ("gemm_kernel<256, 256, true, true, false", "grouped_ffn"), ("gemm_kernel<128, 128, true, true, false", "grouped_ffn"),
+    ("ffn_up_f32", "grouped_ffn"), ("ffn_down_f32", "grouped_ffn"),
+    ("combine_kernel", "combine"), ("bias_update_kernel", "bias_update"),
+    ("combine_bwd", "backward"), ("gate_bwd", "backward"), ("router_wgrad", "backward"), ("unpermute_bwd", "backward"),
+    ("gemm_kernel", "backward"),
+]
+
+
+def call_of(name):
+    for pat, call in CALL_OF:
+        if pat in name:
+            return call
+    return None
+
+
+def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload, launches):
+    """Per-call HBM bytes per step from rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs (KiB per dispatch), each scaled by what the counter reads for the
+    plain 2 GiB copy of --copy-probe; merged into profiles/traffic.json."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        tot = {}
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                tot.setdefault((r["Dispatch_Id"], r["Kernel_Name"]), 0.0)
+                tot[(r["Dispatch_Id"], r["Kernel_Name"])] += float(r["Counter_Value"])
+        return tot
+
+    def copy_factor(d, counter, known):
+        vals = [v for (_, name), v in per_kernel(d, counter).items() if "copy" in name.lower()]
+        if not vals:
+            raise SystemExit(f"no copy kernel in the {counter} run under {d}")
+        return known / (sum(vals) / len(vals) * 1024.0)
+
+    n = 1 << 31
+    ff = copy_factor(copy_fetch_dir, "FETCH_SIZE", n)
+    fw = copy_factor(copy_write_dir, "WRITE_SIZE", n)
+    calls = {}
+    for d, counter, fac, key in ((fetch_dir, "FETCH_SIZE", ff, "read"), (write_dir, "WRITE_SIZE", fw, "write")):
+        for (_, name), kib in per_kernel(d, counter).items():
+            c = call_of(name)
+            if c:
+                calls.setdefault(c, {"read": 0.0, "write": 0.0})[key] += kib * 1024.0 * fac
+    out = json.load(open(TRAFFIC)) if os.path.exists(TRAFFIC) else {}
+    out["source_sha"] = source_hash()
+    out["calibration"] = {"fetch_factor": round(ff, 4), "write_factor": round(fw, 4),
+                          "note": "bytes = counter KiB x 1024 x factor; factor = 2 GiB / counter of a plain 2 GiB copy"}
+    out.setdefault("workloads", {})[workload] = {c: {k: int(v / launches) for k, v in rw.items()} for c, rw in calls.items()}
+    os.makedirs(os.path.dirname(TRAFFIC), exist_ok=True)
+    json.dump(out, open(TRAFFIC, "w"), indent=1)
+    print(json.dumps(out["workloads"][workload]))
+
+
+def short_name(name):
+    n = name.replace("void ", "").replace("(anonymous namespace)::", "").replace("moe_gemm::", "")
+    return n[:n.index("(")] if "(" in n else n
+
+
+def summarize_stats(stats_csv, steps, title):
+    """Markdown table of a rocprofv3 --stats kernel summary: per kernel the
+    launches, average duration and the library call it belongs to, then the
+    per-step time of each call (sum of its kernels), comparable to the
+    event-timed calls_ms of the bench line."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"### {title}", "", "| kernel | call | launches | avg us | min us | max us | % |",
+             "|---|---|---:|---:|---:|---:|---:|"]
+    per_call = {}
+    for r in rows:
+        c = call_of(r["Name"]) or "-"
+        lines.append(f"| `{short_name(r['Name'])}` | {c} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+        if c != "-":
+            per_call[c] = per_call.get(c, 0.0) + float(r["TotalDurationNs"]) / steps / 1e6
+    lines += ["", f"Per step ({steps} steps in the run), sum of each call's kernels, ms:", ""]
+    lines += [f"- {c}: {v:.4f}" for c, v in per_call.items()]
+    print("\n".join(lines))
+
+
+def measured_traffic(workload):
+    try:
+        t = json.load(open(TRAFFIC))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != source_hash():
+        return None
+    return t.get("workloads", {}).get(workload)
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -90,6 +202,36 @@ def cpu_baseline(cfg, inp, train, tokens):
                       f"{'forward+backward' if train else 'forward'} in fp64 numpy ({dt:.1f} s)"}
 
 
+def fwd_line(_lib, a, device):
+    """Forward-only tokens/s on the 64-expert top-8 shape (T=8192, sigmoid
+    router with the Zipf-skewed logit offset, bias update), graph replays."""
+    import torch
+    from mixture_experts_layer_free_amd.layer import MoELayer, Shape
+    from workloads import CONFIGS, make_inputs
+    cfg = CONFIGS["fine"]
+    log(f"[bench] forward line: generating inputs for {cfg.name}")
+    inp = make_inputs(cfg)
+    d = lambda k: _dev(inp.get(k), device)
+    layer = MoELayer(Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, torch.bfloat16, cfg.score, 0, 0, cfg.bias_update,
+                           cfg.gamma, False), d("w_router"), d("w_gate_up"), d("w_down"), d("bias"),
+                     d("logit_offset"), device=device)
+    x = d("x")
+    for _ in range(a.warmup):
+        layer.forward(x)
+    graph = layer.capture(x)
+    for _ in range(a.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / a.steps * 1e3
+    log(f"[bench] forward line: {ms:.3f} ms/step")
+    return {"workload": describe(cfg, False), "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+            "ms_per_step": round(ms, 4), "expert_tflops": round(expert_flops(cfg, False) / (ms * 1e-3) / 1e12, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,9 +241,21 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=None, help="oracle sample size (tokens)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--no-fwd", action="store_true", help="skip the forward-only line on the 64-expert shape")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs of this bench into profiles/traffic.json")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "STEPS"),
+                    help="print a rocprofv3 kernel_stats.csv of this bench as a markdown table")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 2 GiB device-to-device copy (HBM reference and PMC byte calibration)")
     a = ap.parse_args()
+    if a.summarize_stats:
+        summarize_stats(a.summarize_stats[0], int(a.summarize_stats[1]), a.workload)
+        return
+    if a.summarize_pmc:
+        # the profiled run is `bench.py --no-graph --no-fwd --no-cpu-baseline` with the same --steps/--warmup
+        summarize_pmc(*a.summarize_pmc, workload=a.workload, launches=a.steps + a.warmup)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU: this layer's hot path runs on a single MI355X and has no multi-GPU "
               f"mode (asked for --gpus {a.gpus}).", file=sys.stderr)
@@ -181,18 +335,34 @@ def main():
         log(f"[bench] graph {ms:.3f} ms/step")
     value = cfg.T / (ms * 1e-3)
 
-    # dominant call: the routed grouped FFN (forward) or the backward
+    # per-call rooflines: algorithmic work per call / the call's event time
     A = cfg.T * cfg.k
-    dom = "backward" if train else "grouped_ffn"
-    if dom == "grouped_ffn":
-        flops = 6 * A * cfg.d * cfg.f
-    else:
-        flops = 12 * A * cfg.d * cfg.f
-    dom_ms = calls.get(dom, float("nan"))
-    achieved = flops / (dom_ms * 1e-3) / 1e12
-    roof = {"bound": "mfma", "kernel": f"moe_{dom} ({'12' if train else '6'}*A*d*f flops per call)",
-            "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "call_ms": dom_ms}
+    work = {
+        "route": ("fp32", 2.0 * cfg.T * cfg.d * cfg.E),
+        "permute": ("hbm", cfg.T * cfg.d * 2.0 + A * cfg.d * 2.0),
+        "grouped_ffn": ("mfma", 6.0 * A * cfg.d * cfg.f),
+        "shared_ffn": ("mfma", 6.0 * cfg.T * cfg.d * cfg.f_shared),
+        "combine": ("hbm", A * cfg.d * 4.0 + cfg.T * cfg.d * 4.0 * (2 if cfg.shared else 1)),
+        "backward": ("mfma", 12.0 * A * cfg.d * cfg.f + 4.0 * A * cfg.d),
+    }
+    peaks = {"mfma": (PEAK_BF16_TFLOPS, "TFLOP/s", 1e12), "hbm": (PEAK_HBM_GBS, "GB/s", 1e9),
+             "fp32": (157.3, "TFLOP/s", 1e12)}
+    traffic = measured_traffic(cfg.name)
+    rooflines = {}
+    for call, (bound, w) in work.items():
+        if call not in calls or w == 0:
+            continue
+        peak, unit, scale = peaks[bound]
+        ach = w / (calls[call] * 1e-3) / scale
+        tr = traffic.get(call) if traffic else None
+        # the router runs on fp32 MFMA (16x16x4 f32): its peak is the fp32 matrix rate
+        rooflines[call] = {"bound": "mfma" if bound == "fp32" else bound, "achieved": round(ach, 1), "peak": peak,
+                           "unit": unit, "frac": round(ach / peak, 4), "call_ms": calls[call],
+                           "peak_dtype": {"mfma": "bf16", "fp32": "fp32", "hbm": None}[bound],
+                           "traffic": (tr["read"] + tr["write"]) if tr else None}
+    dom = max((c for c in rooflines), key=lambda c: calls[c])
+    roof = dict(rooflines[dom])
+    roof["kernel"] = f"moe_{dom} (library call, all of its kernels)"
 
     res = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
            "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
@@ -201,9 +371,12 @@ def main():
                       "parallelism": "none (1 GPU)"},
            "eager_ms_per_step": round(eager_ms, 4), "step_mode": "eager" if a.no_graph else "hip_graph_replay",
            "calls_ms": calls, "expert_tflops": round(expert_flops(cfg, train) / (ms * 1e-3) / 1e12, 1),
-           "roofline": roof}
+           "roofline": roof, "rooflines": rooflines}
+    if train and not a.no_fwd:
+        res["fwd"] = fwd_line(_lib, a, device)
     if not a.no_cpu_baseline:
-        tokens = a.cpu_tokens or (1024 if train else cfg.T)
+        # about 10-30 s of oracle work on the host's cores
+        tokens = a.cpu_tokens or {"train": 6144, "fine": 8192, "coarse": 4096, "dsv3": 1024}[cfg.name]
         log(f"[bench] cpu oracle on {tokens} tokens")
         res["cpu_baseline"] = cpu_baseline(cfg, inp, train, tokens)
     print(json.dumps(res), flush=True)
