@@ -173,6 +173,33 @@ def measured_traffic(workload):
     return t.get("workloads", {}).get(workload)
 
 
+def algorithmic(cfg):
+    """Per library call: (flops, bytes, peak TFLOP/s of its arithmetic) that
+    the method itself needs -- every tensor read or written once, weights
+    once, intermediates written once and read once."""
+    T, d, E, k, f, A = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.T * cfg.k
+    xb = 2 if cfg.dtype == "bf16" else 4
+    gu = A * 2 * f * 2 if cfg.train else 0                  # saved G|U (training)
+    out = {
+        "route": (2.0 * T * d * E, T * d * xb + E * d * 4 + T * E * 4 + T * k * 8, 157.3),
+        "permute": (0, T * d * xb + A * d * xb + T * k * 8 + A * 4, None),
+        "grouped_ffn": (6.0 * A * d * f, A * d * xb + 3 * E * d * f * xb + 2 * A * f * xb + A * d * 4 + gu,
+                        PEAK_BF16_TFLOPS),
+        "combine": (0, A * d * 4 + T * d * 4 * (2 if cfg.shared else 1) + T * k * 8, None),
+        "bias_update": (0, E * 12, None),
+    }
+    if cfg.shared:
+        fs = cfg.f_shared
+        out["shared_ffn"] = (6.0 * T * d * fs, T * d * xb + 3 * d * fs * xb + 2 * T * fs * xb + T * d * 4,
+                             PEAK_BF16_TFLOPS)
+    if cfg.train:
+        # inputs dY, Y, X_perm, G|U, H, weights; outputs dx, dW; dY_perm, dG|U, dX_perm written and read once
+        nbytes = (T * d * 2 + A * d * 4 + A * d * 2 + A * 2 * f * 2 + A * f * 2 + 3 * E * d * f * 2
+                  + T * d * 4 + 3 * E * d * f * 4 + 2 * (A * d * 2 + A * 2 * f * 2 + A * d * 4))
+        out["backward"] = (12.0 * A * d * f + 4.0 * A * d, nbytes, PEAK_BF16_TFLOPS)
+    return out
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -336,30 +363,21 @@ def main():
     value = cfg.T / (ms * 1e-3)
 
     # per-call rooflines: algorithmic work per call / the call's event time
-    A = cfg.T * cfg.k
-    work = {
-        "route": ("fp32", 2.0 * cfg.T * cfg.d * cfg.E),
-        "permute": ("hbm", cfg.T * cfg.d * 2.0 + A * cfg.d * 2.0),
-        "grouped_ffn": ("mfma", 6.0 * A * cfg.d * cfg.f),
-        "shared_ffn": ("mfma", 6.0 * cfg.T * cfg.d * cfg.f_shared),
-        "combine": ("hbm", A * cfg.d * 4.0 + cfg.T * cfg.d * 4.0 * (2 if cfg.shared else 1)),
-        "backward": ("mfma", 12.0 * A * cfg.d * cfg.f + 4.0 * A * cfg.d),
-    }
-    peaks = {"mfma": (PEAK_BF16_TFLOPS, "TFLOP/s", 1e12), "hbm": (PEAK_HBM_GBS, "GB/s", 1e9),
-             "fp32": (157.3, "TFLOP/s", 1e12)}
     traffic = measured_traffic(cfg.name)
     rooflines = {}
-    for call, (bound, w) in work.items():
-        if call not in calls or w == 0:
+    for call, (flops, nbytes, peak_flops) in algorithmic(cfg).items():
+        if call not in calls:
             continue
-        peak, unit, scale = peaks[bound]
-        ach = w / (calls[call] * 1e-3) / scale
+        t = calls[call] * 1e-3
         tr = traffic.get(call) if traffic else None
-        # the router runs on fp32 MFMA (16x16x4 f32): its peak is the fp32 matrix rate
-        rooflines[call] = {"bound": "mfma" if bound == "fp32" else bound, "achieved": round(ach, 1), "peak": peak,
-                           "unit": unit, "frac": round(ach / peak, 4), "call_ms": calls[call],
-                           "peak_dtype": {"mfma": "bf16", "fp32": "fp32", "hbm": None}[bound],
-                           "traffic": (tr["read"] + tr["write"]) if tr else None}
+        if flops and flops / nbytes >= peak_flops / PEAK_HBM_GBS * 1e3:   # at or above the ridge: compute-bound
+            ach, peak, unit = flops / t / 1e12, peak_flops, "TFLOP/s"
+            bound, dt = "mfma", ("fp32" if peak_flops < PEAK_BF16_TFLOPS else "bf16")
+        else:
+            ach, peak, unit, bound, dt = nbytes / t / 1e9, PEAK_HBM_GBS, "GB/s", "hbm", None
+        rooflines[call] = {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit,
+                           "frac": round(ach / peak, 4), "call_ms": calls[call], "peak_dtype": dt,
+                           "flops": flops, "bytes": nbytes, "traffic": (tr["read"] + tr["write"]) if tr else None}
     dom = max((c for c in rooflines), key=lambda c: calls[c])
     roof = dict(rooflines[dom])
     roof["kernel"] = f"moe_{dom} (library call, all of its kernels)"

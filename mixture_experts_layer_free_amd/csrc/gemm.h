@@ -27,8 +27,10 @@
 //
 // Workgroup: 4 waves in 2x2, each wave (TM/2) x (TN/2) of 32x32 MFMA blocks.
 // Measured on MI355X, the loop is bound by the operand stream from L2 into
-// LDS (removing the in-loop loads alone lifts it from ~1.07 to ~1.75 PF/s),
-// so the tile order below is chosen for L2 reuse.
+// LDS (removing the in-loop loads alone lifts it from ~1.07 to ~1.75 PF/s):
+// the slab loads of a step are spread between its MFMAs (issued together,
+// the 4 waves' 32 loads queue behind one texture unit for ~500 cycles while
+// the matrix cores idle), and the tile order below is chosen for L2 reuse.
 // Two tile shapes: 256x256 (one workgroup per CU, accumulators in AGPRs,
 // half the LDS bytes per MFMA flop) for groups of >= 512 rows, 128x128 (two
 // workgroups per CU) otherwise.  The kernel is persistent: the grid is a
@@ -123,6 +125,25 @@ __device__ __forceinline__ void band_order(int t, int mts, int nbs, int& mt, int
   const int w = nbs - band * BAND < BAND ? nbs - band * BAND : BAND;   // width of this band
   mt = r / w;
   nb = band * BAND + (r - mt * w);
+}
+
+// Scheduling pattern of one slab step with NM MFMAs, NR LDS fragment reads
+// and NV slab loads: the reads go between the MFMAs of the first half, the
+// loads between those of the second half.
+template <int NM, int NR, int NV, int M = 0>
+__device__ __forceinline__ void interleave() {
+  constexpr int H = NM / 2;
+  if constexpr (M < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    if constexpr (M < H) {
+      constexpr int ds = (M + 1) * NR / H - M * NR / H;
+      if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);   // LDS read
+    } else {
+      constexpr int vm = (M - H + 1) * NV / (NM - H) - (M - H) * NV / (NM - H);
+      if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);   // buffer load
+    }
+    interleave<NM, NR, NV, M + 1>();
+  }
 }
 
 template <int TM, int TN, bool AK, bool BKC, bool KG, int EPI>
@@ -248,15 +269,16 @@ void gemm_kernel(Args p) {
 #define MOE_ISSUE(slab_)                                                                             \
   do {                                                                                               \
     const int slab = (slab_);                                                                        \
+    const bool live_ = slab < nk;   /* a slab past the end is pushed out of range: its loads read zeros */ \
     const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a_base, a_bytes);                                  \
     const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(b_base, b_bytes);                                  \
     char* st_ = smem + (slab % STAGES) * STAGE;                                                      \
     _Pragma("unroll") for (int q = 0; q < LA; ++q)                                                   \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_t*)(st_ + (wave * LA + q) * 1024), 16, a_voff[q], \
-                                               (uint32_t)slab * a_step, 0, 0);                       \
+                                               live_ ? (uint32_t)slab * a_step : 0x80000000u, 0, 0); \
     _Pragma("unroll") for (int q = 0; q < LB; ++q)                                                   \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_t*)(st_ + SA + (wave * LB + q) * 1024), 16,      \
-                                               b_voff[q], (uint32_t)slab * b_step, 0, 0);            \
+                                               b_voff[q], live_ ? (uint32_t)slab * b_step : 0x80000000u, 0, 0); \
   } while (0)
 #else
 #define MOE_ISSUE(slab_) ((void)(slab_))
@@ -322,44 +344,45 @@ void gemm_kernel(Args p) {
 
     // Slab step it: make slab it+1 visible, refill the ring three slabs
     // ahead, and multiply slab it (registers `ca/cb`, read one step earlier)
-    // while the fragments of slab it+1 stream into `na/nb`, one LDS read per
-    // NMFMA/NREAD MFMAs.  Slab it+3 goes into the stage slab it-1 used; every
-    // wave consumed those fragments before this step's barrier.  Steps come
-    // in pairs that swap the two register sets, and no branch surrounds the
-    // MFMAs (a branch there makes the compiler copy the accumulators): the
-    // slab count is even (K of a row-grouped GEMM is a multiple of 64; a
-    // K-grouped tile rounds up and its extra slab reads zeros past the
-    // group's rows), and on the last step the wait and barrier are no-ops and
-    // the reads fetch a stage nobody writes any more.
+    // while the fragments of slab it+1 stream into `na/nb`.  Slab it+3 goes
+    // into the stage slab it-1 used; every wave consumed those fragments
+    // before this step's barrier.  The step has no branch: loads of slabs
+    // past the end are out of range (they write zeros into a stage nobody
+    // reads), so every step waits for the same count of loads, and the
+    // MFMAs, fragment reads and slab loads form one scheduling region:
+    // each MFMA is followed by its share of the reads (first half of the
+    // step) or of the loads (second half; the compiler keeps the loads
+    // behind the reads since both touch LDS).  Steps come in pairs that swap
+    // the two register sets; the slab count is even (K of a row-grouped
+    // GEMM is a multiple of 64; a K-grouped tile rounds up and its extra slab
+    // reads zeros past the group's rows).  On the last step the reads fetch a
+    // stage whose contents are never used.
 #define MOE_STEP(it_, ca, cb, na, nb_)                                                            \
   do {                                                                                          \
     const int it = (it_);                                                                       \
-    if (it + 2 < nk) wait_vmcnt<LPS>(); else wait_vmcnt<0>();                                   \
+    wait_vmcnt<LPS>();                                                                          \
     block_barrier();                                                                            \
-    if (it + STAGES - 1 < nk) MOE_ISSUE(it + STAGES - 1);                                       \
     read_frags(smem + ((it + 1) % STAGES) * STAGE, na, nb_);                                    \
+    MOE_ISSUE(it + STAGES - 1);                                                                 \
     mfmas(ca, cb);                                                                              \
-    _Pragma("unroll") for (int g_ = 0; g_ < NREAD; ++g_) {                                      \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                        \
-      __builtin_amdgcn_sched_group_barrier(0x008, NMFMA / NREAD > 0 ? NMFMA / NREAD : 1, 0);    \
-    }                                                                                           \
+    interleave<NMFMA, NREAD, LPS>();                                                            \
+    __builtin_amdgcn_sched_barrier(0);                                                          \
   } while (0)
 
-    wait_vmcnt<0>();   // previous tile's epilogue stores done: vmcnt now counts slab loads only
+    // Stores of the previous tile's epilogue may still be in flight: they are
+    // older than this tile's loads, so the load waits below cover them too.
     if (nk > 0) {
 #pragma unroll
-      for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nk) MOE_ISSUE(s);
+      for (int s = 0; s < STAGES - 1; ++s) MOE_ISSUE(s);
       bf16x8 fa0[2][FM], fb0[2][FN], fa1[2][FM], fb1[2][FN];
-      if (nk >= 3) wait_vmcnt<2 * LPS>();
-      else if (nk == 2) wait_vmcnt<LPS>();
-      else wait_vmcnt<0>();
+      wait_vmcnt<(STAGES - 2) * LPS>();
       block_barrier();
       read_frags(smem, fa0, fb0);
       for (int it2 = 0; it2 < nk; it2 += 2) {
         MOE_STEP(it2, fa0, fb0, fa1, fb1);
         MOE_STEP(it2 + 1, fa1, fb1, fa0, fb0);
       }
+      wait_vmcnt<0>();   // the out-of-range tail loads still land in the ring
       block_barrier();   // every wave is done with the ring before the epilogue stages in it
     }
 #undef MOE_STEP

@@ -139,6 +139,94 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
 }
 
 // ---------------------------------------------------------------------------
+// The same logits for E <= 16 (the few-expert layers, where the router reads
+// x once and the 64-expert tile would idle most of its MFMA columns).
+//
+// Workgroup: 16 tokens x 16 experts, 4 waves splitting d into contiguous
+// ranges of 32-wide k steps.  Each lane loads its operands straight from
+// global memory into registers, 8 steps ahead: lane l holds row l%16 (token
+// for A, expert for B) and k = 32*step + 8*(l/16) + s, s = 0..7, which is the
+// k the lane feeds to MFMA s (any fixed k permutation is the same sum).  The
+// chunk accumulator is folded every 2 steps (64 products); the 4 wave
+// partials are added in a fixed order.
+constexpr int RS_U = 8;   // k steps in flight per wave
+
+template <bool XBF16>
+__global__ __launch_bounds__(256) void router_logits_small_kernel(const void* __restrict__ xv,
+                                                                  const float* __restrict__ w,
+                                                                  const float* __restrict__ off,
+                                                                  float* __restrict__ logits, int T, int d, int E) {
+  __shared__ float sR[4][16][17];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, kq = lane >> 4;
+  const int t0 = blockIdx.x * 16, t = t0 + r;
+  const int nsteps = (d + 31) / 32;
+  const int s0 = wave * nsteps / 4, s1 = (wave + 1) * nsteps / 4;
+  const bool trow = t < T, erow = r < E;
+
+  f32x4 tot = {0.f, 0.f, 0.f, 0.f}, chk = {0.f, 0.f, 0.f, 0.f};
+  for (int st = s0; st < s1; st += RS_U) {
+    float a[RS_U][8], b[RS_U][8];
+#pragma unroll
+    for (int u = 0; u < RS_U; ++u) {
+      const int k = 32 * (st + u) + 8 * kq;
+      const bool kin = st + u < s1 && k < d;   // d % 8 == 0: the 8 values are all in or all out
+      if (XBF16) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (kin && trow) v = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(xv) + (int64_t)t * d + k);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          a[u][2 * q] = bf16_to_f32(v[q] & 0xFFFFu);
+          a[u][2 * q + 1] = bf16_to_f32(v[q] >> 16);
+        }
+      } else {
+        f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = v0;
+        if (kin && trow) {
+          const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(xv) + (int64_t)t * d + k);
+          v0 = p[0];
+          v1 = p[1];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          a[u][q] = v0[q];
+          a[u][4 + q] = v1[q];
+        }
+      }
+      f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = w0;
+      if (kin && erow) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(w + (int64_t)r * d + k);
+        w0 = p[0];
+        w1 = p[1];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        b[u][q] = w0[q];
+        b[u][4 + q] = w1[q];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < RS_U; ++u) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) chk = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u][q], b[u][q], chk, 0, 0, 0);
+      if (u & 1) {   // 2 steps x 32 k = 64 products per chunk
+        tot += chk;
+        chk = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+  // D layout of a 16x16 MFMA tile: lane holds rows 4*(lane/16)+i, column lane%16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sR[wave][4 * kq + i][r] = tot[i];
+  __syncthreads();
+  const int row = threadIdx.x >> 4, col = threadIdx.x & 15;
+  if (t0 + row < T && col < E) {
+    float v = (sR[0][row][col] + sR[1][row][col]) + (sR[2][row][col] + sR[3][row][col]);
+    if (off) v += off[col];
+    logits[(int64_t)(t0 + row) * E + col] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // One wavefront per token.  Lane l holds experts l, l+64, ...; k rounds of a
 // cross-lane argmax on (key desc, expert asc) pick the experts; lanes 0..k-1
 // then hold one chosen expert each and form the gates with wave reductions.
@@ -229,7 +317,13 @@ extern "C" moe_status moe_route(const void* x, int x_dtype, int64_t T, int64_t d
     return MOE_ENOTSUP;
   hipStream_t s = moe_stream(stream);
   dim3 g1((unsigned)ceil_div(T, RT_M), (unsigned)ceil_div(E, RT_N));
-  if (x_dtype == MOE_BF16)
+  if (E <= 16) {
+    const unsigned gs = (unsigned)ceil_div(T, 16);
+    if (x_dtype == MOE_BF16)
+      router_logits_small_kernel<true><<<gs, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
+    else
+      router_logits_small_kernel<false><<<gs, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
+  } else if (x_dtype == MOE_BF16)
     router_logits_kernel<true><<<g1, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
   else
     router_logits_kernel<false><<<g1, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);

@@ -50,7 +50,8 @@ def test_route_tiny(score):
 
 
 @pytest.mark.parametrize("T,d,E,k", [(300, 256, 16, 4), (77, 64, 1, 1), (129, 128, 96, 16), (64, 2048, 1024, 16),
-                                     (33, 64, 16, 16)])
+                                     (33, 64, 16, 16), (150, 200, 12, 3), (150, 200, 40, 5), (2100, 1032, 8, 2),
+                                     (40, 8, 17, 2)])
 def test_route_shapes(T, d, E, k):
     say(f"[route shape T={T} d={d} E={E} k={k}]")
     cfg = scaled(CONFIGS["fine"], T=T, d=d, E=E, k=k, f=64, bias="uniform")
