@@ -501,7 +501,7 @@ void gemm_kernel(Args p) {
               float dg[4], du[4];
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                const float sg = 1.0f / (1.0f + __expf(-g[q]));
+                const float sg = sigmoid_fast(g[q]);
                 dg[q] = v[q] * u[q] * sg * (1.0f + g[q] * (1.0f - sg));
                 du[q] = v[q] * g[q] * sg;
               }

@@ -27,7 +27,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// Logistic sigmoid from the hardware 2^x and reciprocal (v_exp_f32, v_rcp_f32,
+// about 1 ulp each): 1 / (1 + 2^(-z*log2(e))).  Overflow of 2^x for very
+// negative z gives 1/inf = 0, the correct limit.  Used where the result is
+// rounded to bf16 or feeds a bf16 product.
+__device__ __forceinline__ float sigmoid_fast(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.44269504088896341f));
+}
+__device__ __forceinline__ float silu_f32(float z) { return z * sigmoid_fast(z); }
 
 // Lane mask of lanes strictly below this one.
 __device__ __forceinline__ uint64_t lanemask_lt() {
