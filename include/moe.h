@@ -113,6 +113,8 @@ moe_status moe_route(const void* x, int x_dtype, int64_t T, int64_t d,
  *   counts   [E]        int32 out: assignments per expert
  *   offsets  [E+1]      int32 out: exclusive prefix sum of counts
  *   row_of   [T, k]     int32 out: row of assignment (t, j) in x_perm
+ *                       (INT32_MIN for an expert id outside [0, E): that
+ *                       assignment has no row and is skipped downstream)
  *   token_of [T*k]      int32 out: token of each x_perm row
  *   x_perm   [T*k, d]   out: x_perm[r] = x[token_of[r]] (bit copy)
  *   workspace           moe_workspace_size(MOE_CALL_PERMUTE, T, k, E, d, 0)
@@ -125,9 +127,42 @@ moe_status moe_permute(const int32_t* topk_idx, int64_t T, int k, int E,
                        void* x_perm, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_permute_capacity — moe_permute with an expert capacity.
+ * Lesson, Load balancing item 2 (expert capacity + token dropping): each
+ * expert processes at most a fixed number of tokens (C x N / E for a
+ * capacity factor C) and the overflow skips the layer.  With top-k routing
+ * the cap counts assignments; the caller passes it in rows, usually
+ * ceil(C * T * k / E).  An expert keeps its first `capacity` assignments in
+ * token order and drops the rest.
+ *   capacity  rows per expert; < 0 (or >= T*k) keeps everything, which is
+ *             exactly moe_permute
+ *   counts    [E]   every assignment per expert, dropped ones included (the
+ *                   router's demand: what moe_bias_update balances)
+ *   offsets   [E+1] exclusive prefix sum of the KEPT counts
+ *                   min(counts, capacity): expert e runs on rows
+ *                   offsets[e] .. offsets[e+1]-1, A_kept = offsets[E]
+ *   row_of    [T,k] r >= 0 for a kept assignment; ~r (< 0, not INT32_MIN)
+ *                   for a dropped one, whose row r lies in [A_kept, T*k)
+ *   token_of, x_perm  all T*k rows: the kept rows grouped by expert, then
+ *                   the dropped rows grouped by expert (experts ascending,
+ *                   tokens ascending inside each); dropped rows are still
+ *                   copied because the router weight gradient uses them
+ * A dropped slot contributes nothing to moe_combine's sum (the token skips
+ * the layer for that slot; gates are not renormalised), gets no expert
+ * gradient in moe_backward, and still passes the gate-normalisation gradient
+ * to its logit.  Workspace and errors as moe_permute.
+ */
+moe_status moe_permute_capacity(const int32_t* topk_idx, int64_t T, int k, int E, int64_t capacity,
+                                const void* x, int x_dtype, int64_t d,
+                                int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* token_of,
+                                void* x_perm, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * moe_grouped_ffn — G independent SwiGLU experts over row segments.
  * Lesson, Concept: each expert is an independent FFN, usually SwiGLU.
- * Expert g runs on rows offsets[g] .. offsets[g+1]-1 of x_rows:
+ * Expert g runs on rows offsets[g] .. offsets[g+1]-1 of x_rows (rows at or
+ * past offsets[G], e.g. those dropped by an expert capacity, are neither read
+ * nor written):
  *   G = X W_gate^T, U = X W_up^T, H = silu(G) * U, Y = H W_down^T,
  *   silu(z) = z / (1 + e^-z).
  * The shared expert of the lesson's Shared-experts section is the same call
@@ -159,7 +194,9 @@ moe_status moe_grouped_ffn(const void* x_rows, int64_t rows, int64_t d, int dtyp
  * expert's output; shared experts add their output unweighted.  The residual
  * add of the transformer block is outside this call.
  *   out[t] = shared_y[t] + sum_j topk_gate[t,j] * y_perm[row_of[t,j]]
- * summed in fp32, j ascending.
+ * summed in fp32, j ascending.  A slot with row_of[t,j] < 0 (dropped by an
+ * expert capacity, or an invalid expert id) adds nothing; its y_perm row is
+ * never read into the sum, so it may hold any bits.
  *   y_perm   [T*k, d] f32;  row_of [T, k] int32;  topk_gate [T, k] f32
  *   shared_y [T, d]   f32 or NULL
  *   out      [T, d]   out_dtype (MOE_F32, or MOE_BF16 rounded to nearest even)
@@ -228,10 +265,19 @@ typedef struct moe_bwd_args {
   float* dlogit;               /* [T, k] or NULL: dl at the chosen experts */
   void* workspace;
   size_t workspace_bytes;      /* moe_workspace_size(MOE_CALL_BACKWARD, T, k, E, d, f) */
+  /* appended; a struct_size that ends before it means NULL */
+  const int32_t* counts;       /* [E] from moe_permute_capacity, or NULL when
+                                  nothing was dropped (then x_perm holds the
+                                  kept rows only) */
 } moe_bwd_args;
 
-/* ENOTSUP: non-bf16 use, d or f not a multiple of 64, E > MOE_MAX_EXPERTS,
- * k > MOE_MAX_TOPK.  EINVAL also for struct_size != sizeof(moe_bwd_args). */
+/* With an expert capacity (row_of < 0 for dropped slots, `counts` set): a
+ * dropped slot gets dg = 0 and no dY_perm / dX_perm row; its dl (through the
+ * gate normalisation) still reaches dW_r over its dropped x_perm row and
+ * dx_r.  Expert GEMMs run on the kept rows offsets[0] .. offsets[E]-1.
+ * ENOTSUP: non-bf16 use, d or f not a multiple of 64, E > MOE_MAX_EXPERTS,
+ * k > MOE_MAX_TOPK.  EINVAL also for a struct_size other than
+ * sizeof(moe_bwd_args) or offsetof(moe_bwd_args, counts). */
 moe_status moe_backward(const moe_bwd_args* args, void* stream);
 
 /* Workspace bytes a call needs (0 if it needs none).  `which` is enum

@@ -35,12 +35,14 @@ class BwdArgs(ctypes.Structure):
         ("dx", _vp), ("dw_router", _vp), ("dw_gate_up", _vp), ("dw_down", _vp),
         ("dgate", _vp), ("dlogit", _vp),
         ("workspace", _vp), ("workspace_bytes", _sz),
+        ("counts", _vp),
     ]
 
 
 _SIGS = {
     "moe_route": [_vp, _int, _i64, _i64, _vp, _vp, _vp, _int, _int, _int, _vp, _vp, _vp, _vp],
     "moe_permute": [_vp, _i64, _int, _int, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_permute_capacity": [_vp, _i64, _int, _int, _i64, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_grouped_ffn": [_vp, _i64, _i64, _int, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_combine": [_vp, _vp, _vp, _vp, _i64, _int, _i64, _vp, _int, _vp],
     "moe_bias_update": [_vp, _vp, _int, _i64, _int, ctypes.c_float, _vp],
@@ -162,6 +164,28 @@ def moe_permute(topk_idx, x, E, counts=None, offsets=None, row_of=None, token_of
     _check("moe_permute", lib().moe_permute(_p(topk_idx), T, k, E, _p(x), _dtype_code(x), d, _p(counts),
                                             _p(offsets), _p(row_of), _p(token_of), _p(x_perm), _p(ws),
                                             ws.numel(), _stream(stream)))
+    return counts, offsets, row_of, token_of, x_perm
+
+
+def moe_permute_capacity(topk_idx, x, E, capacity, counts=None, offsets=None, row_of=None, token_of=None,
+                         x_perm=None, workspace=None, stream=None):
+    """moe_permute with an expert capacity in rows (< 0: none).  row_of holds ~r
+    for a dropped assignment; offsets cover the kept rows."""
+    T, k = topk_idx.shape
+    d = x.shape[1]
+    _req(topk_idx, "topk_idx", torch.int32)
+    _req(x, "x")
+    dev = x.device
+    A = T * k
+    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    row_of = torch.empty((T, k), dtype=torch.int32, device=dev) if row_of is None else row_of
+    token_of = torch.empty(A, dtype=torch.int32, device=dev) if token_of is None else token_of
+    x_perm = torch.empty((A, d), dtype=x.dtype, device=dev) if x_perm is None else x_perm
+    ws, n = _workspace(MOE_CALL_PERMUTE, T, k, E, d, 0, dev, workspace)
+    _check("moe_permute_capacity", lib().moe_permute_capacity(
+        _p(topk_idx), T, k, E, int(capacity), _p(x), _dtype_code(x), d, _p(counts), _p(offsets), _p(row_of),
+        _p(token_of), _p(x_perm), _p(ws), ws.numel(), _stream(stream)))
     return counts, offsets, row_of, token_of, x_perm
 
 

@@ -15,7 +15,13 @@
 //   5. wgrad up      dW_gate_up[e] = [dG|dU]^T X_perm over e's rows
 //   6. dgrad up      dX_perm = [dG|dU] W_gate_up (fp32)
 //   7. unpermute_bwd one wave per token: dx = sum_j dX_perm[row] + sum_j dl*W_r[e]
+// With an expert capacity (moe_permute_capacity), a dropped assignment has
+// no expert output: it gets dg = 0 and no dY_perm / dX_perm row, but its
+// logit still has a gradient through the gate normalisation, and the router
+// weight gradient runs over the kept and the dropped rows of x_perm.
 #include "gemm.h"
+
+#include <cstddef>
 
 moe_status moe_tile_schedule_launch(const int32_t* offsets, int G, int bm, int32_t* mt_prefix, hipStream_t s);
 
@@ -37,12 +43,13 @@ __device__ __forceinline__ float score_of(float l, int fn) {
 __global__ __launch_bounds__(256) void combine_bwd_rows_kernel(const bf16_t* __restrict__ dy, const float* __restrict__ y,
                                                                const int32_t* __restrict__ row_of,
                                                                const int32_t* __restrict__ token_of,
-                                                               const float* __restrict__ gate, int64_t A, int k,
+                                                               const float* __restrict__ gate,
+                                                               const int32_t* __restrict__ kept_rows, int64_t A, int k,
                                                                int64_t d, bf16_t* __restrict__ dy_perm,
                                                                float* __restrict__ dgp) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= A) return;
+  if (r >= A || r >= *kept_rows) return;   // rows past the kept ones have no expert output
   const int64_t t = token_of[r];
   const uint64_t hit = __ballot(lane < k && row_of[t * k + lane] == (int32_t)r);
   const int j = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
@@ -89,7 +96,8 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
   const int myr = act ? row_of[t * k + lane] : 0;
   const float myg = act ? gate[t * k + lane] : 0.f;
   const int mye = act ? idx[t * k + lane] : 0;
-  const float dg = act ? dgp[myr] : 0.f;
+  const float dg = act && myr >= 0 ? dgp[myr] : 0.f;   // a dropped slot adds nothing to the output
+  const int prow = myr >= 0 ? myr : (myr == INT32_MIN ? -1 : ~myr);   // its x_perm row, kept or dropped
   const float D = wave_sum(act ? myg * dg : 0.f);
   float dl;
   if (fn == MOE_SOFTMAX_CHOSEN) {
@@ -105,29 +113,80 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
   if (act) {
     dg_out[t * k + lane] = dg;
     dl_out[t * k + lane] = dl;
-    dl_perm[myr] = dl;
+    if (prow >= 0) dl_perm[prow] = dl;
   }
 }
 
+// Row segments of the router weight gradient: segment s < E holds the kept
+// rows of expert s (offsets), segment E+s its dropped rows, which follow all
+// kept rows (none without a capacity: counts may be NULL).  rc_prefix[s] =
+// row chunks of RCH before segment s.  One workgroup of 1024 threads, E <= 1024.
+__device__ __forceinline__ int excl_scan_1024(int v, int32_t* s_w, int& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(inc, o, MOE_WAVE);
+    if (lane >= o) inc += u;
+  }
+  if (lane == 63) s_w[wave] = inc;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) base += s_w[w];
+    total += s_w[w];
+  }
+  __syncthreads();
+  return base + inc - v;
+}
+
+__global__ __launch_bounds__(1024) void router_seg_schedule_kernel(const int32_t* __restrict__ offsets,
+                                                                   const int32_t* __restrict__ counts, int E,
+                                                                   int32_t* __restrict__ seg_beg,
+                                                                   int32_t* __restrict__ seg_end,
+                                                                   int32_t* __restrict__ rc_prefix) {
+  __shared__ int32_t s_w[16];
+  const int e = threadIdx.x;
+  const int kept = e < E ? offsets[e + 1] - offsets[e] : 0;
+  const int drop = e < E && counts ? counts[e] - kept : 0;
+  int tot_drop, tot_kp, tot_dp;
+  const int dstart = excl_scan_1024(drop, s_w, tot_drop);
+  const int kp = (kept + RCH - 1) / RCH, dp = (drop + RCH - 1) / RCH;
+  const int kpx = excl_scan_1024(kp, s_w, tot_kp);
+  const int dpx = excl_scan_1024(dp, s_w, tot_dp);
+  if (e < E) {
+    const int kept_all = offsets[E];
+    seg_beg[e] = offsets[e];
+    seg_end[e] = offsets[e + 1];
+    seg_beg[E + e] = kept_all + dstart;
+    seg_end[E + e] = kept_all + dstart + drop;
+    rc_prefix[e] = kpx;
+    rc_prefix[E + e] = tot_kp + dpx;
+  }
+  if (e == 0) rc_prefix[2 * E] = tot_kp + tot_dp;
+}
+
 // Partial router weight gradient over one chunk of at most RCH rows of one
-// expert: part[p][c] = sum over the chunk's rows of dl_perm[r] * x_perm[r][c].
+// segment: part[p][c] = sum over the chunk's rows of dl_perm[r] * x_perm[r][c].
 // Eight columns (one 16-byte vector) per thread, 2048 columns per workgroup,
 // four rows in flight per thread.
 __global__ __launch_bounds__(256) void router_wgrad_part_kernel(const bf16_t* __restrict__ x_perm,
                                                                 const float* __restrict__ dl_perm,
-                                                                const int32_t* __restrict__ offsets,
-                                                                const int32_t* __restrict__ rc_prefix, int E, int64_t d,
+                                                                const int32_t* __restrict__ seg_beg,
+                                                                const int32_t* __restrict__ seg_end,
+                                                                const int32_t* __restrict__ rc_prefix, int S, int64_t d,
                                                                 float* __restrict__ part) {
   const int p = blockIdx.x;
-  if (p >= rc_prefix[E]) return;
-  int lo = 0, hi = E;  // expert of chunk p: largest e with rc_prefix[e] <= p
+  if (p >= rc_prefix[S]) return;
+  int lo = 0, hi = S;  // segment of chunk p: largest s with rc_prefix[s] <= p
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (rc_prefix[mid] <= p) lo = mid; else hi = mid;
   }
-  const int e = lo;
-  const int64_t r0 = offsets[e] + (int64_t)(p - rc_prefix[e]) * RCH;
-  const int64_t r1 = min((int64_t)offsets[e + 1], r0 + RCH);
+  const int sg = lo;
+  const int64_t r0 = seg_beg[sg] + (int64_t)(p - rc_prefix[sg]) * RCH;
+  const int64_t r1 = min((int64_t)seg_end[sg], r0 + RCH);
   const int64_t c = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 8;
   if (c >= d) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -162,18 +221,22 @@ __global__ __launch_bounds__(256) void router_wgrad_part_kernel(const bf16_t* __
   o[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
 }
 
+// dW_r[e] = the partials of e's kept segment, then of its dropped segment, in order
 __global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* __restrict__ part,
-                                                                  const int32_t* __restrict__ rc_prefix, int64_t d,
-                                                                  float* __restrict__ dw) {
+                                                                  const int32_t* __restrict__ rc_prefix, int E,
+                                                                  int64_t d, float* __restrict__ dw) {
   const int e = blockIdx.x;
   const int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x;
   if (c >= d) return;
   float s = 0.f;
   for (int p = rc_prefix[e]; p < rc_prefix[e + 1]; ++p) s += part[(int64_t)p * d + c];
+  for (int p = rc_prefix[E + e]; p < rc_prefix[E + e + 1]; ++p) s += part[(int64_t)p * d + c];
   dw[(int64_t)e * d + c] = s;
 }
 
 // dx[t] = sum_j dx_perm[row_of[t,j]] + sum_j dl[t,j] * w_router[idx[t,j]]
+// (a dropped slot, row_of < 0, has no dx_perm row: its load goes to row 0 and
+// is replaced by zero)
 template <int K>
 __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restrict__ dx_perm,
                                                             const int32_t* __restrict__ row_of,
@@ -189,9 +252,12 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restr
   const f32x4* xr[K];
   const f32x4* wr[K];
   float w[K];
+  bool live[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    xr[j] = dx_perm + (int64_t)__shfl(myr, j, MOE_WAVE) * nv;
+    const int r = __shfl(myr, j, MOE_WAVE);
+    live[j] = r >= 0;
+    xr[j] = dx_perm + (int64_t)(live[j] ? r : 0) * nv;
     wr[j] = w_router + (int64_t)__shfl(mye, j, MOE_WAVE) * nv;
     w[j] = __shfl(myl, j, MOE_WAVE);
   }
@@ -199,7 +265,8 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restr
     f32x4 xs[K], ws[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      xs[j] = __builtin_nontemporal_load(xr[j] + v);
+      const f32x4 l = __builtin_nontemporal_load(xr[j] + v);
+      xs[j] = live[j] ? l : f32x4{0.f, 0.f, 0.f, 0.f};
       ws[j] = wr[j][v];
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -217,7 +284,7 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restr
 }
 
 struct BwdLayout {
-  size_t dy_perm, dgu, dx_perm, dg, dl, dl_perm, dgp, mt_prefix, rc_prefix, rpart, total;
+  size_t dy_perm, dgu, dx_perm, dg, dl, dl_perm, dgp, mt_prefix, rc_prefix, seg_beg, seg_end, rpart, total;
 };
 
 BwdLayout layout(int64_t T, int k, int E, int64_t d, int64_t f) {
@@ -233,8 +300,10 @@ BwdLayout layout(int64_t T, int k, int E, int64_t d, int64_t f) {
   L.dl_perm = take((size_t)A * 4);
   L.dgp = take((size_t)A * 4);
   L.mt_prefix = take((size_t)(E + 1) * 4);
-  L.rc_prefix = take((size_t)(E + 1) * 4);
-  L.rpart = take((size_t)(ceil_div(A, RCH) + E) * d * 4);
+  L.rc_prefix = take((size_t)(2 * E + 1) * 4);
+  L.seg_beg = take((size_t)2 * E * 4);
+  L.seg_end = take((size_t)2 * E * 4);
+  L.rpart = take((size_t)(ceil_div(A, RCH) + 2 * E) * d * 4);
   L.total = o;
   return L;
 }
@@ -247,7 +316,10 @@ size_t moe_backward_workspace(int64_t T, int k, int E, int64_t d, int64_t f) {
 }
 
 extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
-  if (!a || a->struct_size != sizeof(moe_bwd_args)) return MOE_EINVAL;
+  // struct_size: the full struct, or the one before `counts` was appended
+  if (!a || (a->struct_size != sizeof(moe_bwd_args) && a->struct_size != offsetof(moe_bwd_args, counts)))
+    return MOE_EINVAL;
+  const int32_t* counts = a->struct_size == sizeof(moe_bwd_args) ? a->counts : nullptr;
   const int64_t T = a->T, d = a->d, f = a->f;
   const int E = a->E, k = a->k;
   if (T < 1 || d < 1 || f < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
@@ -276,6 +348,8 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   float* dgp = reinterpret_cast<float*>(ws + Lo.dgp);
   int32_t* mt_prefix = reinterpret_cast<int32_t*>(ws + Lo.mt_prefix);
   int32_t* rc_prefix = reinterpret_cast<int32_t*>(ws + Lo.rc_prefix);
+  int32_t* seg_beg = reinterpret_cast<int32_t*>(ws + Lo.seg_beg);
+  int32_t* seg_end = reinterpret_cast<int32_t*>(ws + Lo.seg_end);
   float* rpart = reinterpret_cast<float*>(ws + Lo.rpart);
   const bf16_t* x_perm = static_cast<const bf16_t*>(a->x_perm);
   const bf16_t* wgu = static_cast<const bf16_t*>(a->w_gate_up);
@@ -283,25 +357,25 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
 
   // 1. combine backward (permuted domain) + gate backward
   combine_bwd_rows_kernel<<<(unsigned)ceil_div(A, 4), 256, 0, s>>>(static_cast<const bf16_t*>(a->dy), a->y_perm,
-                                                                     a->row_of, a->token_of, a->topk_gate, A, k, d,
-                                                                     dy_perm, dgp);
+                                                                     a->row_of, a->token_of, a->topk_gate,
+                                                                     a->offsets + E, A, k, d, dy_perm, dgp);
   MOE_LAUNCH_CHECK();
   gate_bwd_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(dgp, a->row_of, a->topk_gate, a->topk_idx, a->logits, (int)T,
                                                            k, E, a->score_fn, dg, dl, dl_perm);
   MOE_LAUNCH_CHECK();
   // 2. router weight gradient
-  moe_status st = moe_tile_schedule_launch(a->offsets, E, RCH, rc_prefix, s);
-  if (st != MOE_OK) return st;
-  router_wgrad_part_kernel<<<dim3((unsigned)(ceil_div(A, RCH) + E), (unsigned)ceil_div(d, 2048)), 256, 0, s>>>(
-      x_perm, dl_perm, a->offsets, rc_prefix, E, d, rpart);
+  router_seg_schedule_kernel<<<1, 1024, 0, s>>>(a->offsets, counts, E, seg_beg, seg_end, rc_prefix);
   MOE_LAUNCH_CHECK();
-  router_wgrad_reduce_kernel<<<dim3((unsigned)E, (unsigned)ceil_div(d, 256)), 256, 0, s>>>(rpart, rc_prefix, d,
+  router_wgrad_part_kernel<<<dim3((unsigned)(ceil_div(A, RCH) + 2 * E), (unsigned)ceil_div(d, 2048)), 256, 0, s>>>(
+      x_perm, dl_perm, seg_beg, seg_end, rc_prefix, 2 * E, d, rpart);
+  MOE_LAUNCH_CHECK();
+  router_wgrad_reduce_kernel<<<dim3((unsigned)E, (unsigned)ceil_div(d, 256)), 256, 0, s>>>(rpart, rc_prefix, E, d,
                                                                                             a->dw_router);
   MOE_LAUNCH_CHECK();
   // expert GEMMs
   using namespace moe_gemm;
   const bool large = use_large_rows(A, E, f);
-  st = moe_tile_schedule_launch(a->offsets, E, large ? BM_LARGE : BM, mt_prefix, s);
+  moe_status st = moe_tile_schedule_launch(a->offsets, E, large ? BM_LARGE : BM, mt_prefix, s);
   if (st != MOE_OK) return st;
   {  // 3. dH = dY_perm W_down -> dG|dU
     Args g{};

@@ -10,7 +10,10 @@ namespace {
 
 // One wave per token: out[t] = shared[t] + sum_j gate[t,j] * y[row_of[t,j]],
 // fp32, j ascending, 16-byte vectors along the row; the K row loads of a
-// vector are issued together.
+// vector are issued together.  A slot whose row_of is negative (dropped by
+// the expert capacity, or an invalid expert) adds nothing: its load goes to
+// row 0 and the value is replaced by zero, never multiplied (y rows that no
+// expert computed may hold anything).
 template <int K>
 __global__ __launch_bounds__(256) void combine_kernel(const f32x4* __restrict__ y, const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ gate, const f32x4* __restrict__ shared,
@@ -22,15 +25,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const f32x4* __restrict__ 
   const float myg = lane < K ? gate[t * K + lane] : 0.f;
   const f32x4* yr[K];
   float g[K];
+  bool live[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    yr[j] = y + (int64_t)__shfl(myr, j, MOE_WAVE) * nv;
+    const int r = __shfl(myr, j, MOE_WAVE);
+    live[j] = r >= 0;
+    yr[j] = y + (int64_t)(live[j] ? r : 0) * nv;
     g[j] = __shfl(myg, j, MOE_WAVE);
   }
   for (int64_t v = lane; v < nv; v += MOE_WAVE) {
     f32x4 yv[K];
 #pragma unroll
-    for (int j = 0; j < K; ++j) yv[j] = __builtin_nontemporal_load(yr[j] + v);
+    for (int j = 0; j < K; ++j) {
+      const f32x4 l = __builtin_nontemporal_load(yr[j] + v);
+      yv[j] = live[j] ? l : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     f32x4 acc = shared ? shared[t * nv + v] : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < K; ++j) {

@@ -64,6 +64,7 @@ __global__ __launch_bounds__(256) void ffn_up_f32_kernel(const float* __restrict
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (id >= rows * f) return;
   const int64_t row = id / f, n = id % f;
+  if (row >= offsets[G]) return;   // rows past the last group (e.g. dropped by a capacity) are not touched
   const int g = group_of_row(offsets, G, (int)row);
   const float* xr = X + row * d;
   const float* wg = Wgu + (int64_t)g * 2 * f * d + n * d;
@@ -86,6 +87,7 @@ __global__ __launch_bounds__(256) void ffn_down_f32_kernel(const float* __restri
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (id >= rows * d) return;
   const int64_t row = id / d, n = id % d;
+  if (row >= offsets[G]) return;
   const int g = group_of_row(offsets, G, (int)row);
   const float* hr = H + row * f;
   const float* w = Wd + (int64_t)g * d * f + n * f;

@@ -13,6 +13,15 @@
 // per-wave count and each lane's rank among equal experts in lane order.
 // Lane order is assignment order, and a token never holds an expert twice, so
 // ranks follow token order: the sort is stable and the result unique.
+//
+// Expert capacity (lesson "专家组合 (MoE)", Load balancing item 2: an expert
+// takes at most a fixed number of tokens and the overflow skips the layer):
+// with a capacity c >= 0, the first c assignments of an expert in token order
+// are kept and the rest dropped.  Kept rows fill x_perm[0, A_kept) grouped by
+// expert (offsets); dropped rows follow in x_perm[A_kept, A), grouped by
+// expert in the same order, and are still copied (the router weight gradient
+// runs over every assignment).  row_of holds r for a kept row and ~r (< 0)
+// for a dropped one; an out-of-range expert id gets INT32_MIN and no row.
 #include "moe_common.h"
 
 namespace {
@@ -81,8 +90,24 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // One workgroup of 1024 threads.  Each expert's column of the histogram is
 // turned into exclusive chunk bases (within the expert); the expert totals
 // become counts and their exclusive scan the offsets.
-__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ hist, int E, int nchunks,
-                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+__device__ __forceinline__ void block_excl_scan(int v, int E, int32_t* s_wsum, int32_t* __restrict__ out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int inc = wave_incl_scan(v);
+  if (lane == 63) s_wsum[wave] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += s_wsum[w];
+  if (tid < E) out[tid] = base + inc - v;
+  if (tid == E - 1) out[E] = base + inc;
+  __syncthreads();
+}
+
+// cap < 0: no capacity.  counts = assignments per expert (the router's
+// demand); offsets = exclusive scan of the kept counts min(counts, cap);
+// doff (capacity only) = exclusive scan of the dropped counts.
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ hist, int E, int nchunks, int cap,
+                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ doff) {
   __shared__ int32_t s_tot[MOE_MAX_EXPERTS];
   __shared__ int32_t s_wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -99,36 +124,39 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ h
     if (lane == 0) s_tot[e] = carry;
   }
   __syncthreads();
-  // exclusive scan of s_tot[0..E) (E <= 1024: one value per thread)
+  // exclusive scans over experts (E <= 1024: one value per thread)
   const int v = tid < E ? s_tot[tid] : 0;
-  const int inc = wave_incl_scan(v);
-  if (lane == 63) s_wsum[wave] = inc;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += s_wsum[w];
-  if (tid < E) {
-    counts[tid] = v;
-    offsets[tid] = base + inc - v;
-  }
-  if (tid == E - 1) offsets[E] = base + inc;
+  const int kept = cap >= 0 && v > cap ? cap : v;
+  if (tid < E) counts[tid] = v;
+  block_excl_scan(kept, E, s_wsum, offsets);
+  if (cap >= 0) block_excl_scan(v - kept, E, s_wsum, doff);
 }
 
 // row_of[i] and token_of[row] for every assignment of chunk blockIdx.x.
 __global__ __launch_bounds__(PCH) void perm_index_kernel(const int32_t* __restrict__ idx, int64_t A, int k, int E, int nchunks,
-                                                         const int32_t* __restrict__ hist, const int32_t* __restrict__ offsets,
+                                                         int cap, const int32_t* __restrict__ hist,
+                                                         const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ doff,
                                                          int32_t* __restrict__ row_of, int32_t* __restrict__ token_of) {
   __shared__ int32_t s_cnt[4][MOE_MAX_EXPERTS];
   int e;
   bool valid;
   const int rank = chunk_counts(idx, A, E, s_cnt, e, valid);
   const int64_t i = (int64_t)blockIdx.x * PCH + threadIdx.x;
-  if (i < A && !valid) row_of[i] = -1;
+  if (i < A && !valid) row_of[i] = INT32_MIN;
   if (!valid) return;
   const int wave = threadIdx.x >> 6;
-  int r = offsets[e] + hist[(int64_t)e * nchunks + blockIdx.x] + rank;
-  for (int w = 0; w < wave; ++w) r += s_cnt[w][e];
-  row_of[i] = r;
-  token_of[r] = (int32_t)(i / k);
+  int q = hist[(int64_t)e * nchunks + blockIdx.x] + rank;   // rank among expert e's assignments
+  for (int w = 0; w < wave; ++w) q += s_cnt[w][e];
+  if (cap < 0 || q < cap) {
+    const int r = offsets[e] + q;
+    row_of[i] = r;
+    token_of[r] = (int32_t)(i / k);
+  } else {
+    const int r = offsets[E] + doff[e] + (q - cap);
+    row_of[i] = ~r;
+    token_of[r] = (int32_t)(i / k);
+  }
 }
 
 // Token-major row copy: one wave per token reads its row once (16-byte
@@ -144,8 +172,9 @@ __global__ __launch_bounds__(256) void perm_copy_kernel(const u32x4* __restrict_
   bool ok = true;
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    rows[j] = __shfl(my, j, MOE_WAVE);
-    ok = ok && rows[j] >= 0;   // an out-of-range expert id left its row unset
+    const int r = __shfl(my, j, MOE_WAVE);
+    rows[j] = r >= 0 || r == INT32_MIN ? r : ~r;   // dropped rows are copied too
+    ok = ok && rows[j] >= 0;                        // an out-of-range expert id has no row
   }
   const u32x4* s = src + t * nvec;
   if (ok) {
@@ -168,12 +197,20 @@ __global__ __launch_bounds__(256) void perm_copy_kernel(const u32x4* __restrict_
 
 size_t moe_permute_workspace(int64_t T, int k, int E) {
   const int64_t nchunks = ceil_div(T * k, PCH);
-  return align256((size_t)nchunks * (size_t)E * sizeof(int32_t));
+  return align256((size_t)nchunks * (size_t)E * sizeof(int32_t)) + align256((size_t)(E + 1) * sizeof(int32_t));
 }
 
 extern "C" moe_status moe_permute(const int32_t* topk_idx, int64_t T, int k, int E, const void* x, int x_dtype, int64_t d,
                                   int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* token_of, void* x_perm,
                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return moe_permute_capacity(topk_idx, T, k, E, -1, x, x_dtype, d, counts, offsets, row_of, token_of, x_perm,
+                              workspace, workspace_bytes, stream);
+}
+
+extern "C" moe_status moe_permute_capacity(const int32_t* topk_idx, int64_t T, int k, int E, int64_t capacity,
+                                           const void* x, int x_dtype, int64_t d, int32_t* counts, int32_t* offsets,
+                                           int32_t* row_of, int32_t* token_of, void* x_perm, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
   if (!topk_idx || !x || !counts || !offsets || !row_of || !token_of || !x_perm) return MOE_EINVAL;
   if (T < 1 || d < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EINVAL;
@@ -184,12 +221,16 @@ extern "C" moe_status moe_permute(const int32_t* topk_idx, int64_t T, int k, int
   hipStream_t s = moe_stream(stream);
   const int64_t A = T * k;
   const int nchunks = (int)ceil_div(A, PCH);
+  // a capacity of A or more drops nothing: the same as none
+  const int cap = capacity < 0 || capacity >= A ? -1 : (int)capacity;
   int32_t* hist = static_cast<int32_t*>(workspace);
+  int32_t* doff = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                             align256((size_t)nchunks * (size_t)E * sizeof(int32_t)));
   perm_hist_kernel<<<nchunks, PCH, 0, s>>>(topk_idx, A, E, nchunks, hist);
   MOE_LAUNCH_CHECK();
-  perm_scan_kernel<<<1, 1024, 0, s>>>(hist, E, nchunks, counts, offsets);
+  perm_scan_kernel<<<1, 1024, 0, s>>>(hist, E, nchunks, cap, counts, offsets, doff);
   MOE_LAUNCH_CHECK();
-  perm_index_kernel<<<nchunks, PCH, 0, s>>>(topk_idx, A, k, E, nchunks, hist, offsets, row_of, token_of);
+  perm_index_kernel<<<nchunks, PCH, 0, s>>>(topk_idx, A, k, E, nchunks, cap, hist, offsets, doff, row_of, token_of);
   MOE_LAUNCH_CHECK();
   const int64_t nvec = d * es / 16;
 #define MOE_PCOPY(K)                                                                                       \

@@ -8,6 +8,8 @@ no arithmetic of its own: every step is a call into libmoe.so.
 from __future__ import annotations
 
 from dataclasses import dataclass
+from fractions import Fraction
+from math import ceil
 from typing import Optional
 
 import torch
@@ -29,6 +31,14 @@ class Shape:
     bias_update: bool = False
     gamma: float = 1e-3
     train: bool = False
+    capacity: Optional[int] = None   # rows per expert (token dropping); None: no cap
+
+
+def expert_capacity(factor: float, T: int, k: int, E: int) -> int:
+    """Rows per expert for a capacity factor C: ceil(C * T * k / E), evaluated
+    exactly on the given float C (lesson, Load balancing item 2: C x N / E
+    tokens per expert, counted here in assignments for top-k)."""
+    return int(ceil(Fraction(factor) * T * k / E))
 
 
 class CallTimer:
@@ -127,8 +137,12 @@ class MoELayer:
             L.moe_route(x, self.w_router, s.k, s.score, self.logit_offset, self.sel_bias,
                         self.idx, self.gate, self.logits, stream=stream)
         with _span(timer, "permute", stream):
-            L.moe_permute(self.idx, x, s.E, self.counts, self.offsets, self.row_of, self.token_of, self.x_perm,
-                          workspace=self.ws_perm, stream=stream)
+            if s.capacity is None:
+                L.moe_permute(self.idx, x, s.E, self.counts, self.offsets, self.row_of, self.token_of, self.x_perm,
+                              workspace=self.ws_perm, stream=stream)
+            else:
+                L.moe_permute_capacity(self.idx, x, s.E, s.capacity, self.counts, self.offsets, self.row_of,
+                                       self.token_of, self.x_perm, workspace=self.ws_perm, stream=stream)
         with _span(timer, "grouped_ffn", stream):
             L.moe_grouped_ffn(self.x_perm, self.offsets, self.w_gate_up, self.w_down, self.gu, self.h,
                               self.y_perm, workspace=self.ws_ffn, stream=stream)
@@ -158,6 +172,7 @@ class MoELayer:
                         ("dgate", self.dgate), ("dlogit", self.dlogit), ("workspace", self.ws_bwd)):
             setattr(a, name, t.data_ptr())
         a.workspace_bytes = self.ws_bwd.numel()
+        a.counts = self.counts.data_ptr() if s.capacity is not None else None
         with _span(timer, "backward", stream):
             L.moe_backward(a, stream=stream)
         return self.dx

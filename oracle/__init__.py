@@ -9,7 +9,8 @@ Sources (titles of the pages the method is taken from):
 
 * "专家组合 (MoE)" lesson, AI Engineering from Scratch (phase 7, lesson 11):
   sections Concept (the replaced FFN and the gated sum), Load balancing
-  (auxiliary-loss-free bias), Shared experts, Fine-grained experts, Build it
+  (item 2 expert capacity + token dropping, item 3 auxiliary-loss-free
+  bias), Shared experts, Fine-grained experts, Build it
   step 1 (the router function) and step 2 (the +-gamma bias controller),
   Key terms.
 * AREX article on The Ultimate MoE Training Handbook: the paragraph on router

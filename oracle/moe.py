@@ -153,29 +153,48 @@ def route_token_lesson(hidden, W_router, top_k, bias, score_fn="softmax", offset
 # permute — grouping the (token, expert) pairs by expert ahead of the expert
 # GEMMs (the "permute" the AREX article's permute-fusion paragraph refers to).
 
-def permute(idx: np.ndarray, E: int):
+def permute(idx: np.ndarray, E: int, capacity=None):
     """Stable counting sort of the T*k assignments by expert.
 
     counts[e] = number of assignments to e; offsets = exclusive prefix sum
     (length E+1).  Experts are walked in ascending order and, inside an expert,
     tokens in ascending order (the pages do not fix this order; ascending token
     order makes the permutation unique).  Assignment (t, j) takes row
-    row_of[t, j]; token_of[row] = t."""
+    row_of[t, j]; token_of[row] = t.
+
+    Expert capacity (lesson, Load balancing item 2: an expert processes at
+    most a fixed number of tokens and the overflow skips the layer): with
+    ``capacity`` c, expert e keeps its first min(counts[e], c) assignments in
+    token order and drops the others.  ``offsets`` then sums the kept counts;
+    kept rows fill 0 .. offsets[E]-1 and the dropped rows follow, grouped by
+    expert the same way.  A dropped assignment's row r is recorded as ~r
+    (negative); ``counts`` still counts every assignment."""
     idx = np.asarray(idx)
     T, k = idx.shape
     counts = np.zeros(E, np.int64)
     for e in range(E):
         counts[e] = int(np.count_nonzero(idx == e))
+    if capacity is None or capacity < 0:
+        kept = counts.copy()
+    else:
+        kept = np.minimum(counts, capacity)
+    dropped = counts - kept
     offsets = np.zeros(E + 1, np.int64)
+    dstart = np.zeros(E + 1, np.int64)
     for e in range(E):
-        offsets[e + 1] = offsets[e] + counts[e]
-    row_of = np.full((T, k), -1, np.int64)
+        offsets[e + 1] = offsets[e] + kept[e]
+        dstart[e + 1] = dstart[e] + dropped[e]
+    row_of = np.full((T, k), np.iinfo(np.int32).min, np.int64)
     token_of = np.full(T * k, -1, np.int64)
     for e in range(E):
         ts, js = np.nonzero(idx == e)      # row-major: tokens ascending
-        rows = offsets[e] + np.arange(len(ts))
-        row_of[ts, js] = rows
-        token_of[rows] = ts
+        n = int(kept[e])
+        rows = offsets[e] + np.arange(n)
+        row_of[ts[:n], js[:n]] = rows
+        token_of[rows] = ts[:n]
+        drows = offsets[E] + dstart[e] + np.arange(len(ts) - n)
+        row_of[ts[n:], js[n:]] = ~drows
+        token_of[drows] = ts[n:]
     return counts, offsets, row_of, token_of
 
 
@@ -234,11 +253,15 @@ def grouped_ffn(x_perm, offsets, w_gate_up, w_down, bf16_points: bool) -> dict:
 # experts).  The residual add sits outside the layer.
 
 def combine(y_perm, row_of, gates, shared_y=None):
+    """out[t] = shared_y[t] + sum over the kept slots j of gate[t,j] * y[row_of[t,j]];
+    a dropped slot (row_of < 0) adds nothing: the token skips the layer there."""
     y_perm = np.asarray(y_perm, np.float64)
+    gates = np.asarray(gates, np.float64)
     T, k = row_of.shape
     out = np.zeros((T, y_perm.shape[1])) if shared_y is None else np.array(shared_y, np.float64)
     for j in range(k):
-        out += np.asarray(gates, np.float64)[:, j:j + 1] * y_perm[row_of[:, j]]
+        keep = row_of[:, j] >= 0
+        out[keep] += gates[keep, j:j + 1] * y_perm[row_of[keep, j]]
     return out
 
 
@@ -268,18 +291,19 @@ def bias_update(bias, counts, T: int, k: int, gamma: float) -> np.ndarray:
 
 def forward(x, w_router, w_gate_up, w_down, k: int, score_fn: str, bf16_points: bool,
             sel_bias=None, logit_offset=None, w_gate_up_shared=None, w_down_shared=None,
-            idx=None) -> dict:
+            idx=None, capacity=None) -> dict:
     """Route, permute, run the experts, add the shared experts, combine.
 
     ``idx`` forces the expert choice (stage-isolated checks feed the GPU's own
-    choice); gates are then recomputed for that choice."""
+    choice); gates are then recomputed for that choice.  ``capacity`` caps the
+    rows of each expert (see ``permute``)."""
     E = np.asarray(w_router).shape[0]
     r = route(x, w_router, k, score_fn, sel_bias, logit_offset)
     if idx is not None:
         idx = np.asarray(idx, np.int64)
         r["idx"] = idx
         r["gates"] = _gates_for(r, idx, score_fn)
-    counts, offsets, row_of, token_of = permute(r["idx"], E)
+    counts, offsets, row_of, token_of = permute(r["idx"], E, capacity)
     x64 = _f64(x)
     x_perm = x64[token_of]
     ex = grouped_ffn(x_perm, offsets, w_gate_up, w_down, bf16_points)
@@ -385,6 +409,8 @@ def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
     gates:     dl via gate_backward; router: dW_r, dx_r via router_backward
     experts:   expert_backward_rows per expert segment
     unpermute: dx[t] = sum_j dX_perm[row_of[t,j]] + dx_r[t] (+ shared experts' dX)
+    Dropped slots (capacity) contribute to neither sum over experts; their
+    logits still get dl through the gate normalisation.
     """
     dy = _f64(dy)
     idx, gates, row_of = fwd["idx"], fwd["gates"], fwd["row_of"]
@@ -393,11 +419,12 @@ def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
     A = T * k
     d = dy.shape[1]
     y = fwd["y_perm"]
-    dg = np.empty((T, k))
+    dg = np.zeros((T, k))
     dy_perm = np.zeros((A, d))
     for j in range(k):
-        dg[:, j] = np.sum(dy * y[row_of[:, j]], axis=1)
-        dy_perm[row_of[:, j]] = gates[:, j:j + 1] * dy
+        keep = row_of[:, j] >= 0          # a dropped slot has no expert output: dg = 0
+        dg[keep, j] = np.sum(dy[keep] * y[row_of[keep, j]], axis=1)
+        dy_perm[row_of[keep, j]] = gates[keep, j:j + 1] * dy[keep]
     if bf16_points:
         dy_perm = bf16_round(dy_perm)
     tt = np.arange(T)[:, None]
@@ -421,7 +448,8 @@ def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
         dX_perm[a:b] = r["dX"]
         dGU[a:b, :f], dGU[a:b, f:] = r["dG"], r["dU"]
     for j in range(k):
-        dx += dX_perm[row_of[:, j]]
+        keep = row_of[:, j] >= 0
+        dx[keep] += dX_perm[row_of[keep, j]]
     out = {"dx": dx, "dw_router": dW_r, "dw_gate_up": dW_gu, "dw_down": dW_d,
            "dg": dg, "dl": dl, "dy_perm": dy_perm, "dx_perm": dX_perm, "dgu": dGU}
     if w_gate_up_shared is not None:

@@ -90,9 +90,9 @@ def check_route(idx, gate, logits, ref, k):
     return int(excl.sum())
 
 
-def check_permute(idx, E, counts, offsets, row_of, token_of, x_perm, x):
+def check_permute(idx, E, counts, offsets, row_of, token_of, x_perm, x, capacity=None):
     """Stage-isolated: the oracle permute fed the GPU's own choice."""
-    c, o, r, t = oracle.permute(np.asarray(idx, np.int64), E)
+    c, o, r, t = oracle.permute(np.asarray(idx, np.int64), E, capacity)
     assert np.array_equal(np.asarray(counts), c), "counts"
     assert np.array_equal(np.asarray(offsets), o), "offsets"
     assert np.array_equal(np.asarray(row_of), r), "row_of"

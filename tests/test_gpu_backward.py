@@ -16,15 +16,16 @@ from workloads import CONFIGS, make_inputs, scaled
 pytestmark = pytest.mark.gpu
 
 
-def _layer(cfg, inp):
+def _layer(cfg, inp, capacity=None):
     from mixture_experts_layer_free_amd.layer import MoELayer, Shape
-    s = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, torch.bfloat16, cfg.score, 0, 0, False, cfg.gamma, True)
+    s = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, torch.bfloat16, cfg.score, 0, 0, False, cfg.gamma, True,
+              capacity=capacity)
     return MoELayer(s, dev(inp["w_router"]), dev(inp["w_gate_up"]), dev(inp["w_down"]), dev(inp["bias"].copy()),
                     dev(inp["logit_offset"]))
 
 
-def _run(cfg, inp):
-    layer = _layer(cfg, inp)
+def _run(cfg, inp, capacity=None):
+    layer = _layer(cfg, inp, capacity)
     x = dev(inp["x"])
     layer.forward(x)
     layer.backward(x, dev(inp["dy"]))
@@ -43,6 +44,29 @@ def test_backward_small(score, T, d, E, k, f):
     idx = host(layer.idx).astype(np.int64)
     fwd = oracle.forward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], k, score, True,
                          sel_bias=inp["bias"], logit_offset=inp["logit_offset"], idx=idx)
+    g = oracle.backward(fwd, inp["dy"], inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], score, True)
+    check_close(host(layer.dgate), g["dg"], "bf16", "dg")
+    check_close(host(layer.dlogit), g["dl"], "bf16", "dl")
+    check_close(host(layer.dx), g["dx"], "bf16", "dx")
+    check_close(host(layer.dw_router), g["dw_router"], "bf16", "dW_router")
+    check_close(host(layer.dw_down), g["dw_down"], "bf16", "dW_down")
+    check_close(host(layer.dw_gate_up), g["dw_gate_up"], "bf16", "dW_gate_up")
+
+
+@pytest.mark.parametrize("score", oracle.SCORE_FNS)
+@pytest.mark.parametrize("T,d,E,k,f,cap", [(700, 256, 24, 3, 128, 40), (257, 128, 8, 8, 64, 100),
+                                           (1100, 256, 4, 2, 256, 300), (300, 128, 16, 4, 64, 0)])
+def test_backward_capacity(score, T, d, E, k, f, cap):
+    """Expert capacity in training: dropped slots get dg = 0 and no expert
+    gradient, their logits still get dl, and dW_r covers the dropped rows."""
+    say(f"[backward capacity {score} T={T} d={d} E={E} k={k} f={f} cap={cap}]")
+    cfg = scaled(CONFIGS["train"], T=T, d=d, E=E, k=k, f=f, score=score, bias="uniform")
+    inp = make_inputs(cfg)
+    layer = _run(cfg, inp, capacity=cap)
+    idx = host(layer.idx).astype(np.int64)
+    fwd = oracle.forward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], k, score, True,
+                         sel_bias=inp["bias"], logit_offset=inp["logit_offset"], idx=idx, capacity=cap)
+    assert np.array_equal(host(layer.row_of), fwd["row_of"]) and (fwd["row_of"] < 0).any()
     g = oracle.backward(fwd, inp["dy"], inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], score, True)
     check_close(host(layer.dgate), g["dg"], "bf16", "dg")
     check_close(host(layer.dlogit), g["dl"], "bf16", "dl")

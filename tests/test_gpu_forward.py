@@ -133,6 +133,42 @@ def test_permute_skew_extremes():
     _permute_case(np.tile(np.arange(E)[::-1], (T, 1)), x, E)       # k = E
 
 
+@pytest.mark.parametrize("T,E,k,d,skew", [(300, 8, 2, 64, 0.0), (1000, 37, 3, 32, 0.5), (2049, 64, 8, 128, 0.2),
+                                          (700, 16, 16, 16, 0.0), (513, 1, 1, 24, 0.0)])
+def test_permute_capacity(T, E, k, d, skew):
+    """Expert capacity: kept rows first (offsets), dropped rows after them, row_of = ~row
+    for a dropped assignment; bit-exact against the oracle for several caps."""
+    say(f"[permute capacity T={T} E={E} k={k} d={d} skew={skew}]")
+    rng = np.random.default_rng(T + 7 * E)
+    p = np.exp(-skew * np.arange(E))
+    p /= p.sum()
+    idx = np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(T)])
+    x = (rng.integers(0, 65535, (T, d))).astype(np.uint16)
+    A = T * k
+    for cap in (0, 1, max(1, A // E // 2), A // E, 2 * A // E, A, -1):
+        counts, offsets, row_of, token_of, x_perm = L.moe_permute_capacity(dev(idx.astype(np.int32)), dev(x), E, cap)
+        torch.cuda.synchronize()
+        check_permute(idx, E, host(counts), host(offsets), host(row_of), host(token_of), host(x_perm), x,
+                      capacity=cap)
+
+
+def test_permute_capacity_full_size():
+    """The 64-expert forward shape with its Zipf-skewed load at capacity factor 1.0."""
+    from mixture_experts_layer_free_amd.layer import expert_capacity
+    cfg = CONFIGS["fine"]
+    say("[permute capacity full fine]")
+    inp = make_inputs(cfg, experts=False)
+    ref = oracle.route(inp["x"], inp["w_router"], cfg.k, cfg.score, inp["bias"], inp["logit_offset"])
+    idx = ref["idx"]
+    cap = expert_capacity(1.0, cfg.T, cfg.k, cfg.E)
+    counts, offsets, row_of, token_of, x_perm = L.moe_permute_capacity(dev(idx.astype(np.int32)), dev(inp["x"]),
+                                                                       cfg.E, cap)
+    torch.cuda.synchronize()
+    assert int(host(offsets)[-1]) < cfg.T * cfg.k          # the skew makes some experts overflow
+    check_permute(idx, cfg.E, host(counts), host(offsets), host(row_of), host(token_of), host(x_perm), inp["x"],
+                  capacity=cap)
+
+
 @pytest.mark.parametrize("name", ["coarse", "fine", "dsv3", "train"])
 def test_permute_full_size(name):
     cfg = CONFIGS[name]
@@ -305,6 +341,35 @@ def test_forward_full_size(name, n_sample):
     say("  inputs generated")
     rng = np.random.default_rng(0)
     _forward_check(cfg, inp, sample=np.sort(rng.choice(cfg.T, n_sample, replace=False)))
+
+
+@pytest.mark.parametrize("name,score,cap", [("tiny", "softmax", 5), ("tiny", "sigmoid", 0), ("tiny", "sqrt_softplus", 9),
+                                            ("bf16", "sigmoid", 60), ("bf16", "softmax", 1)])
+def test_forward_capacity(name, score, cap):
+    """Layer forward with an expert capacity against the oracle fed the GPU's
+    routing: dropped slots add nothing, gates are not renormalised."""
+    say(f"[forward capacity {name} {score} cap={cap}]")
+    if name == "tiny":
+        cfg = scaled(CONFIGS["tiny"], score=score)
+    else:
+        cfg = scaled(CONFIGS["dsv3"], T=700, d=256, E=24, k=3, f=128, f_shared=192, score=score)
+    inp = make_inputs(cfg)
+    from mixture_experts_layer_free_amd.layer import MoELayer, Shape
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    sh = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, dt, cfg.score, cfg.shared, cfg.f_shared, False, cfg.gamma, False,
+               capacity=cap)
+    layer = MoELayer(sh, dev(inp["w_router"]), dev(inp["w_gate_up"]), dev(inp["w_down"]), dev(inp["bias"]),
+                     dev(inp["logit_offset"]), dev(inp.get("w_gate_up_shared")), dev(inp.get("w_down_shared")))
+    out = host(layer.forward(dev(inp["x"])))
+    torch.cuda.synchronize()
+    idx = host(layer.idx).astype(np.int64)
+    ref = oracle.forward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], cfg.k, cfg.score,
+                         cfg.dtype == "bf16", sel_bias=inp["bias"], logit_offset=inp["logit_offset"],
+                         w_gate_up_shared=inp.get("w_gate_up_shared"), w_down_shared=inp.get("w_down_shared"),
+                         idx=idx, capacity=cap)
+    assert np.array_equal(host(layer.row_of), ref["row_of"]) and np.array_equal(host(layer.counts), ref["counts"])
+    assert (ref["row_of"] < 0).any()
+    check_close(out, ref["out"], _kind(cfg), "out")
 
 
 def test_forward_deterministic():
