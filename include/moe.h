@@ -60,8 +60,11 @@ enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
  *                           experts' raw logits.
  *   MOE_SIGMOID_NORM:       score = 1/(1+e^-logit); gates = chosen scores
  *                           divided by their sum.
- *   MOE_SQRT_SOFTPLUS_NORM: score = sqrt(ln(1+e^logit)); gates as above. */
-enum moe_score { MOE_SOFTMAX_CHOSEN = 0, MOE_SIGMOID_NORM = 1, MOE_SQRT_SOFTPLUS_NORM = 2 };
+ *   MOE_SQRT_SOFTPLUS_NORM: score = sqrt(ln(1+e^logit)); gates as above.
+ *   MOE_UNIFORM_GATES:      no learned router (moe_route_hash): gates are the
+ *                           constant 1/k; only moe_backward takes it (no
+ *                           logit or router-weight gradient exists). */
+enum moe_score { MOE_SOFTMAX_CHOSEN = 0, MOE_SIGMOID_NORM = 1, MOE_SQRT_SOFTPLUS_NORM = 2, MOE_UNIFORM_GATES = 3 };
 
 /* which call a workspace is sized for */
 enum moe_call { MOE_CALL_ROUTE = 0, MOE_CALL_PERMUTE = 1, MOE_CALL_GROUPED_FFN = 2, MOE_CALL_BACKWARD = 3 };
@@ -98,6 +101,41 @@ moe_status moe_route(const void* x, int x_dtype, int64_t T, int64_t d,
                      const float* w_router, const float* logit_offset, const float* sel_bias,
                      int E, int k, int score_fn,
                      int32_t* topk_idx, float* topk_gate, float* logits_out, void* stream);
+
+/*
+ * moe_route_replay — gates and logits of a GIVEN expert choice.
+ * Lesson, Exercises item 3 (routing replay: record the experts fired at
+ * inference and force the same routing when computing gradients).  The
+ * logits are computed as in moe_route; topk_idx is an input, and the gates
+ * follow score_fn over exactly those experts.  Passing moe_route's own
+ * choice reproduces its gates.  An id outside [0, E) gets gate 0 and is left
+ * out of the normalisation (moe_permute then gives it no row).
+ *   topk_idx [T, k] int32 in;  topk_gate [T, k] f32 out;  logits_out [T, E] out
+ * Errors as moe_route.
+ */
+moe_status moe_route_replay(const void* x, int x_dtype, int64_t T, int64_t d,
+                            const float* w_router, const float* logit_offset,
+                            int E, int k, int score_fn, const int32_t* topk_idx,
+                            float* topk_gate, float* logits_out, void* stream);
+
+/*
+ * moe_route_hash — a deterministic router with nothing learned.
+ * Lesson, Exercises item 2 (replace the learned router by a hash-based
+ * one).  For token id (token_ids[t], e.g. its vocabulary id) and expert e,
+ * the key is the SplitMix64 output for state id*2^32 + e advanced salt+1
+ * times (Steele, Lea and Flood, "Fast splittable pseudorandom number
+ * generators", OOPSLA 2014):
+ *   z = id*2^32 + e + (salt+1) * 0x9E3779B97F4A7C15   (mod 2^64)
+ *   z = (z ^ z>>30) * 0xBF58476D1CE4E5B9
+ *   z = (z ^ z>>27) * 0x94D049BB133111EB
+ *   key = z ^ z>>31
+ * The token takes the k experts with the smallest keys, in ascending key
+ * order, each with gate 1/k (f32).  Use salt to give layers different maps.
+ *   token_ids [T] int32 in;  topk_idx [T, k] int32 out;  topk_gate [T, k] out
+ * ENOTSUP: E > MOE_MAX_EXPERTS, k > MOE_MAX_TOPK, T >= 2^31.
+ */
+moe_status moe_route_hash(const int32_t* token_ids, int64_t T, int E, int k, uint32_t salt,
+                          int32_t* topk_idx, float* topk_gate, void* stream);
 
 /*
  * moe_permute — group the T*k (token, expert) assignments by expert.
@@ -235,6 +273,9 @@ moe_status moe_bias_update(float* sel_bias, const int32_t* counts, int E, int64_
  *             dX_perm = dG W_gate + dU W_up
  *   unpermute: dx[t] = sum_j dX_perm[row_of[t,j]] + dx_r[t]
  * All pointers are device pointers held in a HOST struct.  bf16 layers only.
+ * score_fn MOE_UNIFORM_GATES (hash routing): dl = 0, there is no router term
+ * in dx, w_router / logits may be NULL, and dw_router (if not NULL) is
+ * set to zero.
  */
 typedef struct moe_bwd_args {
   size_t struct_size;          /* sizeof(moe_bwd_args): the ABI version */

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
-SCORE = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2}
+SCORE = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "uniform": 3}
 MOE_CALL_ROUTE, MOE_CALL_PERMUTE, MOE_CALL_GROUPED_FFN, MOE_CALL_BACKWARD = range(4)
 MAX_EXPERTS, MAX_TOPK = 1024, 16
 
@@ -41,6 +41,8 @@ class BwdArgs(ctypes.Structure):
 
 _SIGS = {
     "moe_route": [_vp, _int, _i64, _i64, _vp, _vp, _vp, _int, _int, _int, _vp, _vp, _vp, _vp],
+    "moe_route_replay": [_vp, _int, _i64, _i64, _vp, _vp, _int, _int, _int, _vp, _vp, _vp, _vp],
+    "moe_route_hash": [_vp, _i64, _int, _int, ctypes.c_uint32, _vp, _vp, _vp],
     "moe_permute": [_vp, _i64, _int, _int, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_permute_capacity": [_vp, _i64, _int, _int, _i64, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_grouped_ffn": [_vp, _i64, _i64, _int, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
@@ -145,6 +147,39 @@ def moe_route(x, w_router, k, score_fn, logit_offset=None, sel_bias=None,
                                         _p(sel_bias), E, k, sf, _p(topk_idx), _p(topk_gate),
                                         _p(logits_out), _stream(stream)))
     return topk_idx, topk_gate, logits_out
+
+
+def moe_route_replay(x, w_router, topk_idx, score_fn, logit_offset=None, topk_gate=None, logits_out=None,
+                     stream=None):
+    """Logits and gates of the given expert choice topk_idx [T, k]."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    k = topk_idx.shape[1]
+    _req(x, "x")
+    _req(w_router, "w_router", torch.float32, (E, d))
+    _req(topk_idx, "topk_idx", torch.int32, (T, k))
+    if logit_offset is not None:
+        _req(logit_offset, "logit_offset", torch.float32, (E,))
+    dev = x.device
+    topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_gate is None else topk_gate
+    logits_out = torch.empty((T, E), dtype=torch.float32, device=dev) if logits_out is None else logits_out
+    sf = SCORE[score_fn] if isinstance(score_fn, str) else int(score_fn)
+    _check("moe_route_replay", lib().moe_route_replay(_p(x), _dtype_code(x), T, d, _p(w_router), _p(logit_offset),
+                                                      E, k, sf, _p(topk_idx), _p(topk_gate), _p(logits_out),
+                                                      _stream(stream)))
+    return topk_gate, logits_out
+
+
+def moe_route_hash(token_ids, E, k, salt=0, topk_idx=None, topk_gate=None, stream=None):
+    """Hash router: the k experts with the smallest SplitMix64 keys, gates 1/k."""
+    _req(token_ids, "token_ids", torch.int32)
+    T = token_ids.shape[0]
+    dev = token_ids.device
+    topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
+    topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_gate is None else topk_gate
+    _check("moe_route_hash", lib().moe_route_hash(_p(token_ids), T, E, k, int(salt) & 0xFFFFFFFF, _p(topk_idx),
+                                                  _p(topk_gate), _stream(stream)))
+    return topk_idx, topk_gate
 
 
 def moe_permute(topk_idx, x, E, counts=None, offsets=None, row_of=None, token_of=None, x_perm=None,

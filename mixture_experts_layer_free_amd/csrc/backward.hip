@@ -100,7 +100,9 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
   const int prow = myr >= 0 ? myr : (myr == INT32_MIN ? -1 : ~myr);   // its x_perm row, kept or dropped
   const float D = wave_sum(act ? myg * dg : 0.f);
   float dl;
-  if (fn == MOE_SOFTMAX_CHOSEN) {
+  if (fn == MOE_UNIFORM_GATES) {
+    dl = 0.f;   // constant gates: no logit gradient
+  } else if (fn == MOE_SOFTMAX_CHOSEN) {
     dl = myg * (dg - D);
   } else {
     const float l = act ? logits[t * E + mye] : 0.f;
@@ -237,7 +239,7 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* _
 // dx[t] = sum_j dx_perm[row_of[t,j]] + sum_j dl[t,j] * w_router[idx[t,j]]
 // (a dropped slot, row_of < 0, has no dx_perm row: its load goes to row 0 and
 // is replaced by zero)
-template <int K>
+template <int K, bool ROUTER>
 __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restrict__ dx_perm,
                                                             const int32_t* __restrict__ row_of,
                                                             const int32_t* __restrict__ idx, const float* __restrict__ dl,
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restr
     const int r = __shfl(myr, j, MOE_WAVE);
     live[j] = r >= 0;
     xr[j] = dx_perm + (int64_t)(live[j] ? r : 0) * nv;
-    wr[j] = w_router + (int64_t)__shfl(mye, j, MOE_WAVE) * nv;
+    wr[j] = ROUTER ? w_router + (int64_t)__shfl(mye, j, MOE_WAVE) * nv : nullptr;
     w[j] = __shfl(myl, j, MOE_WAVE);
   }
   for (int64_t v = lane; v < nv; v += MOE_WAVE) {
@@ -267,13 +269,13 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restr
     for (int j = 0; j < K; ++j) {
       const f32x4 l = __builtin_nontemporal_load(xr[j] + v);
       xs[j] = live[j] ? l : f32x4{0.f, 0.f, 0.f, 0.f};
-      ws[j] = wr[j][v];
+      if (ROUTER) ws[j] = wr[j][v];
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < K; ++j) acc += xs[j];
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
+    for (int j = 0; j < K && ROUTER; ++j) {
       acc[0] = fmaf(w[j], ws[j][0], acc[0]);
       acc[1] = fmaf(w[j], ws[j][1], acc[1]);
       acc[2] = fmaf(w[j], ws[j][2], acc[2]);
@@ -281,6 +283,10 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restr
     }
     dx[t * nv + v] = acc;
   }
+}
+
+__global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
 
 struct BwdLayout {
@@ -323,11 +329,12 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   const int64_t T = a->T, d = a->d, f = a->f;
   const int E = a->E, k = a->k;
   if (T < 1 || d < 1 || f < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
-  if (a->score_fn < MOE_SOFTMAX_CHOSEN || a->score_fn > MOE_SQRT_SOFTPLUS_NORM) return MOE_EINVAL;
-  if (!a->dy || !a->x || !a->w_router || !a->logits || !a->topk_idx || !a->topk_gate || !a->row_of ||
-      !a->token_of || !a->offsets || !a->x_perm || !a->gu_saved || !a->h || !a->y_perm || !a->w_gate_up ||
-      !a->w_down || !a->dx || !a->dw_router || !a->dw_gate_up || !a->dw_down)
+  if (a->score_fn < MOE_SOFTMAX_CHOSEN || a->score_fn > MOE_UNIFORM_GATES) return MOE_EINVAL;
+  const bool router = a->score_fn != MOE_UNIFORM_GATES;
+  if (!a->dy || !a->x || !a->topk_idx || !a->topk_gate || !a->row_of || !a->token_of || !a->offsets || !a->x_perm ||
+      !a->gu_saved || !a->h || !a->y_perm || !a->w_gate_up || !a->w_down || !a->dx || !a->dw_gate_up || !a->dw_down)
     return MOE_EINVAL;
+  if (router && (!a->w_router || !a->logits || !a->dw_router)) return MOE_EINVAL;
   if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || d % 64 != 0 || f % 64 != 0 || T * k >= (1ll << 31) || T >= (1ll << 31))
     return MOE_ENOTSUP;
   // the weight-gradient GEMMs address one expert's rows of the permuted
@@ -364,14 +371,20 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
                                                            k, E, a->score_fn, dg, dl, dl_perm);
   MOE_LAUNCH_CHECK();
   // 2. router weight gradient
-  router_seg_schedule_kernel<<<1, 1024, 0, s>>>(a->offsets, counts, E, seg_beg, seg_end, rc_prefix);
-  MOE_LAUNCH_CHECK();
-  router_wgrad_part_kernel<<<dim3((unsigned)(ceil_div(A, RCH) + 2 * E), (unsigned)ceil_div(d, 2048)), 256, 0, s>>>(
-      x_perm, dl_perm, seg_beg, seg_end, rc_prefix, 2 * E, d, rpart);
-  MOE_LAUNCH_CHECK();
-  router_wgrad_reduce_kernel<<<dim3((unsigned)E, (unsigned)ceil_div(d, 256)), 256, 0, s>>>(rpart, rc_prefix, E, d,
-                                                                                            a->dw_router);
-  MOE_LAUNCH_CHECK();
+  if (router) {
+    router_seg_schedule_kernel<<<1, 1024, 0, s>>>(a->offsets, counts, E, seg_beg, seg_end, rc_prefix);
+    MOE_LAUNCH_CHECK();
+    router_wgrad_part_kernel<<<dim3((unsigned)(ceil_div(A, RCH) + 2 * E), (unsigned)ceil_div(d, 2048)), 256, 0, s>>>(
+        x_perm, dl_perm, seg_beg, seg_end, rc_prefix, 2 * E, d, rpart);
+    MOE_LAUNCH_CHECK();
+    router_wgrad_reduce_kernel<<<dim3((unsigned)E, (unsigned)ceil_div(d, 256)), 256, 0, s>>>(rpart, rc_prefix, E, d,
+                                                                                              a->dw_router);
+    MOE_LAUNCH_CHECK();
+  } else if (a->dw_router) {
+    fill_zero_kernel<<<(unsigned)std::min<int64_t>(1024, ceil_div((int64_t)E * d, 256)), 256, 0, s>>>(a->dw_router,
+                                                                                                      (int64_t)E * d);
+    MOE_LAUNCH_CHECK();
+  }
   // expert GEMMs
   using namespace moe_gemm;
   const bool large = use_large_rows(A, E, f);
@@ -420,9 +433,16 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   }
   // 7. unpermute + router input gradient
 #define MOE_UBWD(K)                                                                                             \
-  unpermute_bwd_kernel<K><<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(                                             \
-      reinterpret_cast<const f32x4*>(dx_perm), a->row_of, a->topk_idx, dl, reinterpret_cast<const f32x4*>(a->w_router), \
-      (int)T, d / 4, reinterpret_cast<f32x4*>(a->dx))
+  do {                                                                                                          \
+    if (router)                                                                                                 \
+      unpermute_bwd_kernel<K, true><<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(                                   \
+          reinterpret_cast<const f32x4*>(dx_perm), a->row_of, a->topk_idx, dl,                                  \
+          reinterpret_cast<const f32x4*>(a->w_router), (int)T, d / 4, reinterpret_cast<f32x4*>(a->dx));         \
+    else                                                                                                        \
+      unpermute_bwd_kernel<K, false><<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(                                  \
+          reinterpret_cast<const f32x4*>(dx_perm), a->row_of, a->topk_idx, dl, nullptr, (int)T, d / 4,          \
+          reinterpret_cast<f32x4*>(a->dx));                                                                     \
+  } while (0)
   MOE_DISPATCH_K(k, MOE_UBWD);
 #undef MOE_UBWD
   MOE_LAUNCH_CHECK();

@@ -243,6 +243,20 @@ __device__ __forceinline__ bool better(float v, int e, float bv, int be) {
 
 constexpr int TOPK_MAXV = MOE_MAX_EXPERTS / MOE_WAVE;  // experts per lane
 
+// Gate of the chosen expert held by an active lane (raw logit l): softmax over
+// the active lanes' logits, or the lane's score over the active lanes' sum.
+__device__ __forceinline__ float chosen_gate(float l, bool act, int fn) {
+  if (fn == MOE_SOFTMAX_CHOSEN) {
+    float m = act ? l : -INFINITY;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, MOE_WAVE));
+    const float ex = act ? expf(l - m) : 0.0f;
+    return ex / wave_sum(ex);
+  }
+  const float s = act ? score_of(l, fn) : 0.0f;
+  return s / wave_sum(s);
+}
+
 __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
                                                         int T, int E, int k, int fn, int32_t* __restrict__ idx,
                                                         float* __restrict__ gate) {
@@ -286,25 +300,96 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
   }
   // gates over the chosen experts, from the unbiased values
   const bool act = lane < k;
-  const float l = act ? lrow[mine] : 0.0f;
-  float g;
-  if (fn == MOE_SOFTMAX_CHOSEN) {
-    float m = act ? l : -INFINITY;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, MOE_WAVE));
-    const float ex = act ? expf(l - m) : 0.0f;
-    g = ex / wave_sum(ex);
-  } else {
-    const float s = act ? score_of(l, fn) : 0.0f;
-    g = s / wave_sum(s);
-  }
+  const float g = chosen_gate(act ? lrow[mine] : 0.0f, act, fn);
   if (act) {
     idx[(int64_t)t * k + lane] = mine;
     gate[(int64_t)t * k + lane] = g;
   }
 }
 
+// ---------------------------------------------------------------------------
+// Routing replay (lesson "专家组合 (MoE)", Exercises item 3: record the
+// experts fired at inference and force the same choice when computing
+// gradients): gates of a given choice, one wave per token.  An id outside
+// [0, E) gets gate 0 and takes no part in the normalisation.
+__global__ __launch_bounds__(256) void replay_gate_kernel(const float* __restrict__ logits,
+                                                          const int32_t* __restrict__ idx, int T, int E, int k, int fn,
+                                                          float* __restrict__ gate) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int e = lane < k ? idx[(int64_t)t * k + lane] : -1;
+  const bool act = lane < k && e >= 0 && e < E;
+  const float g = chosen_gate(act ? logits[(int64_t)t * E + e] : 0.0f, act, fn);
+  if (lane < k) gate[(int64_t)t * k + lane] = act ? g : 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Hash router (lesson, Exercises item 2: a deterministic router with nothing
+// learned).  Expert e's key for token id is the SplitMix64 output for the
+// state id*2^32 + e advanced (salt+1) times (Steele, Lea and Flood, "Fast
+// splittable pseudorandom number generators", 2014):
+//   z = id*2^32 + e + (salt+1)*0x9E3779B97F4A7C15
+//   z = (z ^ z>>30) * 0xBF58476D1CE4E5B9;  z = (z ^ z>>27) * 0x94D049BB133111EB;  z ^= z>>31
+// and the token goes to the k experts with the smallest keys (ascending;
+// the mix is a bijection, so keys of one token never tie), each with gate 1/k.
+__device__ __forceinline__ uint64_t splitmix_key(uint32_t id, uint32_t e, uint32_t salt) {
+  uint64_t z = ((uint64_t)id << 32 | e) + (uint64_t)(salt + 1ull) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__global__ __launch_bounds__(256) void hash_route_kernel(const int32_t* __restrict__ token_ids, int T, int E, int k,
+                                                         uint32_t salt, int32_t* __restrict__ idx,
+                                                         float* __restrict__ gate) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const uint32_t id = (uint32_t)token_ids[t];
+  const int nv = (E + MOE_WAVE - 1) / MOE_WAVE;
+  uint64_t key[TOPK_MAXV];
+#pragma unroll
+  for (int i = 0; i < TOPK_MAXV; ++i) {
+    const int e = lane + MOE_WAVE * i;
+    key[i] = i < nv && e < E ? splitmix_key(id, (uint32_t)e, salt) : ~0ull;
+  }
+  uint32_t taken = 0;
+  int mine = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t bv = ~0ull;
+    int be = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < TOPK_MAXV; ++i) {
+      const int e = lane + MOE_WAVE * i;
+      if (i < nv && e < E && !((taken >> i) & 1u) && (key[i] < bv || (key[i] == bv && e < be))) {
+        bv = key[i];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint64_t ov = ((uint64_t)(uint32_t)__shfl_xor((int)(bv >> 32), o, MOE_WAVE) << 32) |
+                          (uint32_t)__shfl_xor((int)(uint32_t)bv, o, MOE_WAVE);
+      const int oe = __shfl_xor(be, o, MOE_WAVE);
+      if (ov < bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == j) mine = be;
+  }
+  if (lane < k) {
+    idx[(int64_t)t * k + lane] = mine;
+    gate[(int64_t)t * k + lane] = 1.0f / (float)k;
+  }
+}
+
 }  // namespace
+
+static moe_status router_logits_launch(const void* x, int x_dtype, int64_t T, int64_t d, const float* w_router,
+                                       const float* logit_offset, int E, float* logits_out, hipStream_t s);
 
 extern "C" moe_status moe_route(const void* x, int x_dtype, int64_t T, int64_t d, const float* w_router,
                                 const float* logit_offset, const float* sel_bias, int E, int k, int score_fn,
@@ -316,20 +401,57 @@ extern "C" moe_status moe_route(const void* x, int x_dtype, int64_t T, int64_t d
   if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || d % 8 != 0 || T >= (1ll << 31) || d >= (1ll << 31))
     return MOE_ENOTSUP;
   hipStream_t s = moe_stream(stream);
-  dim3 g1((unsigned)ceil_div(T, RT_M), (unsigned)ceil_div(E, RT_N));
+  const moe_status st = router_logits_launch(x, x_dtype, T, d, w_router, logit_offset, E, logits_out, s);
+  if (st != MOE_OK) return st;
+  topk_gate_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(logits_out, sel_bias, (int)T, E, k, score_fn, topk_idx,
+                                                            topk_gate);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+static moe_status router_logits_launch(const void* x, int x_dtype, int64_t T, int64_t d, const float* w_router,
+                                       const float* logit_offset, int E, float* logits_out, hipStream_t s) {
   if (E <= 16) {
     const unsigned gs = (unsigned)ceil_div(T, 16);
     if (x_dtype == MOE_BF16)
       router_logits_small_kernel<true><<<gs, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
     else
       router_logits_small_kernel<false><<<gs, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
-  } else if (x_dtype == MOE_BF16)
-    router_logits_kernel<true><<<g1, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
-  else
-    router_logits_kernel<false><<<g1, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
+  } else {
+    dim3 g1((unsigned)ceil_div(T, RT_M), (unsigned)ceil_div(E, RT_N));
+    if (x_dtype == MOE_BF16)
+      router_logits_kernel<true><<<g1, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
+    else
+      router_logits_kernel<false><<<g1, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
+  }
   MOE_LAUNCH_CHECK();
-  topk_gate_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(logits_out, sel_bias, (int)T, E, k, score_fn, topk_idx,
-                                                            topk_gate);
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_route_replay(const void* x, int x_dtype, int64_t T, int64_t d, const float* w_router,
+                                       const float* logit_offset, int E, int k, int score_fn,
+                                       const int32_t* topk_idx, float* topk_gate, float* logits_out, void* stream) {
+  if (!x || !w_router || !topk_idx || !topk_gate || !logits_out) return MOE_EINVAL;
+  if (T < 1 || d < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EINVAL;
+  if (score_fn < MOE_SOFTMAX_CHOSEN || score_fn > MOE_SQRT_SOFTPLUS_NORM) return MOE_EINVAL;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || d % 8 != 0 || T >= (1ll << 31) || d >= (1ll << 31))
+    return MOE_ENOTSUP;
+  hipStream_t s = moe_stream(stream);
+  const moe_status st = router_logits_launch(x, x_dtype, T, d, w_router, logit_offset, E, logits_out, s);
+  if (st != MOE_OK) return st;
+  replay_gate_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(logits_out, topk_idx, (int)T, E, k, score_fn, topk_gate);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_route_hash(const int32_t* token_ids, int64_t T, int E, int k, uint32_t salt,
+                                     int32_t* topk_idx, float* topk_gate, void* stream) {
+  if (!token_ids || !topk_idx || !topk_gate) return MOE_EINVAL;
+  if (T < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || T >= (1ll << 31)) return MOE_ENOTSUP;
+  hash_route_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, moe_stream(stream)>>>(token_ids, (int)T, E, k, salt, topk_idx,
+                                                                             topk_gate);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -32,6 +32,8 @@ class Shape:
     gamma: float = 1e-3
     train: bool = False
     capacity: Optional[int] = None   # rows per expert (token dropping); None: no cap
+    router: str = "learned"          # "learned" (scores, top-k) or "hash" (token ids, gates 1/k)
+    salt: int = 0                    # hash router: per-layer salt
 
 
 def expert_capacity(factor: float, T: int, k: int, E: int) -> int:
@@ -131,11 +133,22 @@ class MoELayer:
             self.dlogit = z(T, k)
             self.ws_bwd = z(max(1, L.workspace_size(L.MOE_CALL_BACKWARD, T, k, E, d, f)), dtype=torch.uint8)
 
-    def forward(self, x, stream=None, timer=None):
+    def forward(self, x, stream=None, timer=None, token_ids=None, replay_idx=None):
+        """One forward.  ``replay_idx`` [T, k] int32 forces the expert choice
+        (routing replay); the hash router needs ``token_ids`` [T] int32."""
         s = self.s
         with _span(timer, "route", stream):
-            L.moe_route(x, self.w_router, s.k, s.score, self.logit_offset, self.sel_bias,
-                        self.idx, self.gate, self.logits, stream=stream)
+            if s.router == "hash":
+                if token_ids is None:
+                    raise ValueError("the hash router needs token_ids")
+                L.moe_route_hash(token_ids, s.E, s.k, s.salt, self.idx, self.gate, stream=stream)
+            elif replay_idx is not None:
+                self.idx.copy_(replay_idx)
+                L.moe_route_replay(x, self.w_router, self.idx, s.score, self.logit_offset, self.gate, self.logits,
+                                   stream=stream)
+            else:
+                L.moe_route(x, self.w_router, s.k, s.score, self.logit_offset, self.sel_bias,
+                            self.idx, self.gate, self.logits, stream=stream)
         with _span(timer, "permute", stream):
             if s.capacity is None:
                 L.moe_permute(self.idx, x, s.E, self.counts, self.offsets, self.row_of, self.token_of, self.x_perm,
@@ -162,7 +175,8 @@ class MoELayer:
     def backward(self, x, dy, stream=None, timer=None):
         s = self.s
         a = L.BwdArgs()
-        a.T, a.d, a.f, a.E, a.k, a.score_fn = s.T, s.d, s.f, s.E, s.k, L.SCORE[s.score]
+        a.T, a.d, a.f, a.E, a.k = s.T, s.d, s.f, s.E, s.k
+        a.score_fn = L.SCORE["uniform" if s.router == "hash" else s.score]
         for name, t in (("dy", dy), ("x", x), ("w_router", self.w_router), ("logits", self.logits),
                         ("topk_idx", self.idx), ("topk_gate", self.gate), ("row_of", self.row_of),
                         ("token_of", self.token_of), ("offsets", self.offsets), ("x_perm", self.x_perm),
@@ -170,7 +184,7 @@ class MoELayer:
                         ("w_gate_up", self.w_gate_up), ("w_down", self.w_down), ("dx", self.dx),
                         ("dw_router", self.dw_router), ("dw_gate_up", self.dw_gate_up), ("dw_down", self.dw_down),
                         ("dgate", self.dgate), ("dlogit", self.dlogit), ("workspace", self.ws_bwd)):
-            setattr(a, name, t.data_ptr())
+            setattr(a, name, t.data_ptr() if t is not None else None)
         a.workspace_bytes = self.ws_bwd.numel()
         a.counts = self.counts.data_ptr() if s.capacity is not None else None
         with _span(timer, "backward", stream):

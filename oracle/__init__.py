@@ -12,7 +12,7 @@ Sources (titles of the pages the method is taken from):
   (item 2 expert capacity + token dropping, item 3 auxiliary-loss-free
   bias), Shared experts, Fine-grained experts, Build it
   step 1 (the router function) and step 2 (the +-gamma bias controller),
-  Key terms.
+  Exercises items 2 (hash router) and 3 (routing replay), Key terms.
 * AREX article on The Ultimate MoE Training Handbook: the paragraph on router
   precision (fp32 router; softmax, sigmoid or sqrt(softplus) scoring) and the
   paragraph on the 64-expert top-8 teaching model (parameter counts).
@@ -28,6 +28,8 @@ from .moe import (  # noqa: F401
     score,
     route,
     route_token_lesson,
+    splitmix_key,
+    hash_route,
     permute,
     expert_ffn,
     grouped_ffn,

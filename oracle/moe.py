@@ -150,6 +150,39 @@ def route_token_lesson(hidden, W_router, top_k, bias, score_fn="softmax", offset
 
 
 # ----------------------------------------------------------------------------
+# hash router — lesson, Exercises item 2: replace the learned router by a
+# deterministic hash of the token, nothing learned.  The hash is SplitMix64
+# (Steele, Lea and Flood, "Fast splittable pseudorandom number generators",
+# OOPSLA 2014): the generator adds 0x9E3779B97F4A7C15 to its state and mixes.
+
+_GAMMA = np.uint64(0x9E3779B97F4A7C15)
+
+
+def splitmix_key(ids, experts, salt: int = 0) -> np.ndarray:
+    """Output number salt+1 of SplitMix64 started at state id*2^32 + e."""
+    ids = np.asarray(ids, np.int64).astype(np.uint32).astype(np.uint64)
+    experts = np.asarray(experts, np.uint64)
+    state = (ids << np.uint64(32)) | experts
+    with np.errstate(over="ignore"):
+        z = state + np.uint64(salt + 1) * _GAMMA                  # uint64 arithmetic wraps mod 2^64
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+    return z ^ (z >> np.uint64(31))
+
+
+def hash_route(token_ids, E: int, k: int, salt: int = 0) -> dict:
+    """Each token takes the k experts with the smallest keys splitmix_key(id, e),
+    ascending (lower expert first on a tie), with equal gates 1/k."""
+    ids = np.asarray(token_ids, np.int64)
+    T = len(ids)
+    keys = splitmix_key(ids[:, None], np.arange(E)[None, :], salt)
+    idx = np.empty((T, k), np.int64)
+    for t in range(T):
+        idx[t] = np.argsort(keys[t], kind="stable")[:k]
+    return {"idx": idx, "gates": np.full((T, k), 1.0 / k)}
+
+
+# ----------------------------------------------------------------------------
 # permute — grouping the (token, expert) pairs by expert ahead of the expert
 # GEMMs (the "permute" the AREX article's permute-fusion paragraph refers to).
 
@@ -297,9 +330,16 @@ def forward(x, w_router, w_gate_up, w_down, k: int, score_fn: str, bf16_points: 
     ``idx`` forces the expert choice (stage-isolated checks feed the GPU's own
     choice); gates are then recomputed for that choice.  ``capacity`` caps the
     rows of each expert (see ``permute``)."""
-    E = np.asarray(w_router).shape[0]
-    r = route(x, w_router, k, score_fn, sel_bias, logit_offset)
-    if idx is not None:
+    if score_fn == "uniform":           # hash routing: the choice is given, gates are 1/k
+        idx = np.asarray(idx, np.int64)
+        E = np.asarray(w_gate_up).shape[0]
+        T = idx.shape[0]
+        r = {"idx": idx, "gates": np.full((T, k), 1.0 / k), "logits": None, "scores": None,
+             "margin": np.full(T, np.inf)}
+    else:
+        E = np.asarray(w_router).shape[0]
+        r = route(x, w_router, k, score_fn, sel_bias, logit_offset)
+    if idx is not None and score_fn != "uniform":
         idx = np.asarray(idx, np.int64)
         r["idx"] = idx
         r["gates"] = _gates_for(r, idx, score_fn)
@@ -415,7 +455,7 @@ def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
     dy = _f64(dy)
     idx, gates, row_of = fwd["idx"], fwd["gates"], fwd["row_of"]
     T, k = idx.shape
-    E = np.asarray(w_router).shape[0]
+    E = len(fwd["counts"])
     A = T * k
     d = dy.shape[1]
     y = fwd["y_perm"]
@@ -427,11 +467,15 @@ def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
         dy_perm[row_of[keep, j]] = gates[keep, j:j + 1] * dy[keep]
     if bf16_points:
         dy_perm = bf16_round(dy_perm)
-    tt = np.arange(T)[:, None]
-    lc = fwd["logits"][tt, idx]
-    sc = fwd["scores"][tt, idx]
-    dl = gate_backward(dg, gates, lc, sc, score_fn)
-    dW_r, dx = router_backward(dl, idx, x, w_router)
+    if score_fn == "uniform":           # constant gates: no logit and no router gradient
+        dl = np.zeros((T, k))
+        dW_r, dx = np.zeros((E, d)), np.zeros((T, d))
+    else:
+        tt = np.arange(T)[:, None]
+        lc = fwd["logits"][tt, idx]
+        sc = fwd["scores"][tt, idx]
+        dl = gate_backward(dg, gates, lc, sc, score_fn)
+        dW_r, dx = router_backward(dl, idx, x, w_router)
     f = np.asarray(w_down).shape[2]
     dW_gu = np.zeros((E, 2 * f, d))
     dW_d = np.zeros((E, d, f))

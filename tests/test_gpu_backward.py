@@ -76,6 +76,30 @@ def test_backward_capacity(score, T, d, E, k, f, cap):
     check_close(host(layer.dw_gate_up), g["dw_gate_up"], "bf16", "dW_gate_up")
 
 
+def test_backward_hash_router():
+    """Training with the hash router: constant gates, so dl = 0, dW_r = 0, and
+    dx has no router term; the expert gradients are the usual ones."""
+    say("[backward hash router]")
+    cfg = scaled(CONFIGS["train"], T=700, d=256, E=24, k=3, f=128)
+    inp = make_inputs(cfg)
+    ids = np.random.default_rng(4).integers(0, 50000, cfg.T).astype(np.int32)
+    from mixture_experts_layer_free_amd.layer import MoELayer, Shape
+    sh = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, torch.bfloat16, cfg.score, train=True, router="hash")
+    layer = MoELayer(sh, None, dev(inp["w_gate_up"]), dev(inp["w_down"]))
+    x = dev(inp["x"])
+    layer.forward(x, token_ids=dev(ids))
+    layer.backward(x, dev(inp["dy"]))
+    torch.cuda.synchronize()
+    idx = oracle.hash_route(ids, cfg.E, cfg.k)["idx"]
+    fwd = oracle.forward(inp["x"], None, inp["w_gate_up"], inp["w_down"], cfg.k, "uniform", True, idx=idx)
+    g = oracle.backward(fwd, inp["dy"], inp["x"], None, inp["w_gate_up"], inp["w_down"], "uniform", True)
+    assert np.all(host(layer.dlogit) == 0) and np.all(host(layer.dw_router) == 0)
+    check_close(host(layer.dgate), g["dg"], "bf16", "dg")
+    check_close(host(layer.dx), g["dx"], "bf16", "dx")
+    check_close(host(layer.dw_down), g["dw_down"], "bf16", "dW_down")
+    check_close(host(layer.dw_gate_up), g["dw_gate_up"], "bf16", "dW_gate_up")
+
+
 def test_backward_empty_and_skewed_experts():
     """Experts that receive no token get exactly zero weight gradients; one
     expert holding most rows spans many K tiles."""

@@ -102,6 +102,58 @@ def test_route_full_size(name):
     assert excl <= 10
 
 
+@pytest.mark.parametrize("T,E,k,salt", [(1000, 64, 8, 0), (333, 1024, 16, 7), (77, 3, 3, 1), (4096, 256, 8, 2)])
+def test_route_hash(T, E, k, salt):
+    """Hash router: bit-exact expert choice (integer hashing), gates exactly 1/k."""
+    say(f"[route hash T={T} E={E} k={k} salt={salt}]")
+    ids = np.random.default_rng(T).integers(-2 ** 31, 2 ** 31 - 1, T).astype(np.int32)
+    idx, gate = L.moe_route_hash(dev(ids), E, k, salt)
+    torch.cuda.synchronize()
+    ref = oracle.hash_route(ids, E, k, salt)
+    assert np.array_equal(host(idx), ref["idx"])
+    assert np.all(host(gate) == np.float32(1.0 / k))
+
+
+@pytest.mark.parametrize("score", oracle.SCORE_FNS)
+def test_route_replay(score):
+    """Routing replay: the gates of moe_route's own choice are reproduced bit for
+    bit; a foreign choice gets the oracle's gates for that choice."""
+    say(f"[route replay {score}]")
+    cfg = scaled(CONFIGS["fine"], T=300, d=256, E=40, k=6, f=64, score=score, bias="uniform")
+    inp = make_inputs(cfg)
+    x, w, off = dev(inp["x"]), dev(inp["w_router"]), dev(inp["logit_offset"])
+    idx, gate, logits = L.moe_route(x, w, cfg.k, score, off, dev(inp["bias"]))
+    g2, l2 = L.moe_route_replay(x, w, idx, score, off)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(g2), host(gate)) and np.array_equal(host(l2), host(logits))
+    rng = np.random.default_rng(3)
+    ridx = np.stack([rng.permutation(cfg.E)[:cfg.k] for _ in range(cfg.T)])
+    g3, _ = L.moe_route_replay(x, w, dev(ridx.astype(np.int32)), score, off)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], cfg.k, score, True,
+                         logit_offset=inp["logit_offset"], idx=ridx)
+    check_close(host(g3), ref["gates"], "f32", "replayed gates")
+
+
+@pytest.mark.parametrize("score", oracle.SCORE_FNS)
+def test_route_fewer_experts_at_serving(score):
+    """k is a per-call argument: serving with k' < k picks the first k' of the k
+    experts and renormalises their gates."""
+    say(f"[route runtime k {score}]")
+    cfg = scaled(CONFIGS["fine"], T=500, d=128, E=64, k=8, f=64, score=score, bias="uniform")
+    inp = make_inputs(cfg, experts=False)
+    x, w, off, b = dev(inp["x"]), dev(inp["w_router"]), dev(inp["logit_offset"]), dev(inp["bias"])
+    i8, g8, _ = L.moe_route(x, w, 8, score, off, b)
+    for k in (1, 3, 5):
+        ik, gk, lk = L.moe_route(x, w, k, score, off, b)
+        torch.cuda.synchronize()
+        check_route(host(ik), host(gk), host(lk), oracle.route(inp["x"], inp["w_router"], k, score, inp["bias"],
+                                                               inp["logit_offset"]), k)
+        assert np.array_equal(host(ik), host(i8)[:, :k])      # same keys, same first k rounds
+        pre = host(g8)[:, :k].astype(np.float64)
+        np.testing.assert_allclose(host(gk), pre / pre.sum(1, keepdims=True), rtol=2e-6, atol=1e-7)
+
+
 # ---------------------------------------------------------------------------- permute
 
 def _permute_case(idx_np, x_np, E):
@@ -369,6 +421,30 @@ def test_forward_capacity(name, score, cap):
                          idx=idx, capacity=cap)
     assert np.array_equal(host(layer.row_of), ref["row_of"]) and np.array_equal(host(layer.counts), ref["counts"])
     assert (ref["row_of"] < 0).any()
+    check_close(out, ref["out"], _kind(cfg), "out")
+
+
+@pytest.mark.parametrize("name", ["tiny", "bf16"])
+def test_forward_hash_router(name):
+    """Layer forward with the hash router (token ids in, gates 1/k) against the oracle."""
+    say(f"[forward hash {name}]")
+    if name == "tiny":
+        cfg = CONFIGS["tiny"]
+    else:
+        cfg = scaled(CONFIGS["dsv3"], T=700, d=256, E=24, k=3, f=128, f_shared=192)
+    inp = make_inputs(cfg)
+    ids = np.random.default_rng(9).integers(0, 32000, cfg.T).astype(np.int32)
+    from mixture_experts_layer_free_amd.layer import MoELayer, Shape
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    sh = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, dt, cfg.score, cfg.shared, cfg.f_shared, router="hash", salt=5)
+    layer = MoELayer(sh, None, dev(inp["w_gate_up"]), dev(inp["w_down"]),
+                     w_gate_up_shared=dev(inp.get("w_gate_up_shared")), w_down_shared=dev(inp.get("w_down_shared")))
+    out = host(layer.forward(dev(inp["x"]), token_ids=dev(ids)))
+    torch.cuda.synchronize()
+    idx = oracle.hash_route(ids, cfg.E, cfg.k, 5)["idx"]
+    assert np.array_equal(host(layer.idx), idx)
+    ref = oracle.forward(inp["x"], None, inp["w_gate_up"], inp["w_down"], cfg.k, "uniform", cfg.dtype == "bf16",
+                         w_gate_up_shared=inp.get("w_gate_up_shared"), w_down_shared=inp.get("w_down_shared"), idx=idx)
     check_close(out, ref["out"], _kind(cfg), "out")
 
 
