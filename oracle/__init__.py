@@ -19,7 +19,10 @@ Sources (titles of the pages the method is taken from):
 
 Parity pins: every public function here is checked by ``tests/test_oracle_*``
 against closed forms, library routines, brute force, finite differences or
-numbers the pages print; none is "parity unpinned".
+numbers the pages print.  PARITY UNPINNED: ``aux_loss`` / ``aux_grad_logits``
+(the auxiliary load-balancing loss): the pages name the loss but give no
+formula; the Switch/GShard form is taken, and only its internal consistency
+(closed forms, finite differences, autograd) is checked.
 """
 from .moe import (  # noqa: F401
     SCORE_FNS,
@@ -30,6 +33,9 @@ from .moe import (  # noqa: F401
     route_token_lesson,
     splitmix_key,
     hash_route,
+    aux_probs,
+    aux_loss,
+    aux_grad_logits,
     permute,
     expert_ffn,
     grouped_ffn,

@@ -442,7 +442,7 @@ def expert_backward_rows(dy_rows, xr, G, U, H, w_gate_up, w_down, bf16_points: b
 
 
 def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
-             bf16_points: bool, w_gate_up_shared=None, w_down_shared=None) -> dict:
+             bf16_points: bool, w_gate_up_shared=None, w_down_shared=None, aux_alpha: float = 0.0) -> dict:
     """Gradients of sum(out * dy) with respect to x and every weight.
 
     combine:   dg[t,j] = <dy[t], Y[row_of[t,j]]>, dY_perm[row_of[t,j]] = g[t,j] dy[t]
@@ -451,6 +451,9 @@ def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
     unpermute: dx[t] = sum_j dX_perm[row_of[t,j]] + dx_r[t] (+ shared experts' dX)
     Dropped slots (capacity) contribute to neither sum over experts; their
     logits still get dl through the gate normalisation.
+    aux_alpha > 0 adds the auxiliary loss (``aux_loss``): its gradient reaches
+    every logit, so the router gradients use the dense [T, E] logit gradient
+    (returned as "dl_dense").
     """
     dy = _f64(dy)
     idx, gates, row_of = fwd["idx"], fwd["gates"], fwd["row_of"]
@@ -475,7 +478,13 @@ def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
         lc = fwd["logits"][tt, idx]
         sc = fwd["scores"][tt, idx]
         dl = gate_backward(dg, gates, lc, sc, score_fn)
-        dW_r, dx = router_backward(dl, idx, x, w_router)
+        if aux_alpha:
+            dL = np.zeros((T, E))
+            np.add.at(dL, (np.arange(T)[:, None].repeat(k, 1), idx), dl)
+            dL += aux_grad_logits(fwd["logits"], fwd["counts"], k, score_fn, aux_alpha)
+            dW_r, dx = dL.T @ _f64(x), dL @ np.asarray(w_router, np.float64)
+        else:
+            dW_r, dx = router_backward(dl, idx, x, w_router)
     f = np.asarray(w_down).shape[2]
     dW_gu = np.zeros((E, 2 * f, d))
     dW_d = np.zeros((E, d, f))
@@ -496,6 +505,8 @@ def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
         dx[keep] += dX_perm[row_of[keep, j]]
     out = {"dx": dx, "dw_router": dW_r, "dw_gate_up": dW_gu, "dw_down": dW_d,
            "dg": dg, "dl": dl, "dy_perm": dy_perm, "dx_perm": dX_perm, "dgu": dGU}
+    if aux_alpha and score_fn != "uniform":
+        out["dl_dense"] = dL
     if w_gate_up_shared is not None:
         x64 = _f64(x)
         out["dw_gate_up_shared"], out["dw_down_shared"] = [], []
@@ -506,6 +517,51 @@ def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
             out["dw_gate_up_shared"].append(r["dW_gate_up"])
             out["dw_down_shared"].append(r["dW_down"])
     return out
+
+
+# ----------------------------------------------------------------------------
+# auxiliary load-balancing loss — lesson, Load balancing item 1 (a penalty on
+# uneven expert usage, with a weight and its own gradient) and Key terms
+# (auxiliary loss).  PARITY UNPINNED: the pages give no formula.  The reading
+# taken is the Switch/GShard form
+#     L_aux = alpha * E / (T*k) * sum_e counts[e] * P[e],
+#     P[e]  = mean over tokens of p[t, e],
+# with p the router probabilities over ALL E experts (softmax of the logits
+# for softmax scoring; each score over the sum of all E scores otherwise) and
+# counts the top-k assignments (not differentiated).  Balanced counts and
+# uniform p give L_aux = alpha.
+
+def aux_probs(logits, score_fn: str) -> np.ndarray:
+    l = np.asarray(logits, np.float64)
+    if score_fn == "softmax":
+        ex = np.exp(l - l.max(axis=1, keepdims=True))
+        return ex / ex.sum(axis=1, keepdims=True)
+    s = score(l, score_fn)
+    return s / s.sum(axis=1, keepdims=True)
+
+
+def aux_loss(logits, counts, k: int, score_fn: str, alpha: float) -> float:
+    p = aux_probs(logits, score_fn)
+    T, E = p.shape
+    return float(alpha * E / (T * k) * np.sum(np.asarray(counts, np.float64) * p.mean(axis=0)))
+
+
+def aux_grad_logits(logits, counts, k: int, score_fn: str, alpha: float) -> np.ndarray:
+    """d L_aux / d logits [T, E] (counts held fixed).  With c_e = dL/dp[t,e]
+    = alpha * E / (T*k) * counts[e] / T: softmax: p_i (c_i - sum_e p_e c_e);
+    normalised scores p = s / S: (c_i - sum_e p_e c_e) / S * s'(l_i)."""
+    l = np.asarray(logits, np.float64)
+    T, E = l.shape
+    c = alpha * E / (T * k) * np.asarray(counts, np.float64) / T
+    p = aux_probs(l, score_fn)
+    pc = np.sum(p * c, axis=1, keepdims=True)
+    if score_fn == "softmax":
+        return p * (c - pc)
+    s = score(l, score_fn)
+    ds = (c - pc) / s.sum(axis=1, keepdims=True)
+    if score_fn == "sigmoid":
+        return ds * s * (1.0 - s)
+    return ds * (1.0 / (1.0 + np.exp(-l))) / (2.0 * s)
 
 
 # ----------------------------------------------------------------------------
