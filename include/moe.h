@@ -67,7 +67,8 @@ enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
 enum moe_score { MOE_SOFTMAX_CHOSEN = 0, MOE_SIGMOID_NORM = 1, MOE_SQRT_SOFTPLUS_NORM = 2, MOE_UNIFORM_GATES = 3 };
 
 /* which call a workspace is sized for */
-enum moe_call { MOE_CALL_ROUTE = 0, MOE_CALL_PERMUTE = 1, MOE_CALL_GROUPED_FFN = 2, MOE_CALL_BACKWARD = 3 };
+enum moe_call { MOE_CALL_ROUTE = 0, MOE_CALL_PERMUTE = 1, MOE_CALL_GROUPED_FFN = 2, MOE_CALL_BACKWARD = 3,
+                MOE_CALL_AUX_LOSS = 4 };
 
 /* Largest supported expert count and top-k (the handbook article's router
  * table has a model choosing 16 of 896 experts, the largest on the pages). */
@@ -257,6 +258,27 @@ moe_status moe_bias_update(float* sel_bias, const int32_t* counts, int E, int64_
                            float gamma, void* stream);
 
 /*
+ * moe_aux_loss — auxiliary load-balancing loss (the alternative to the
+ * loss-free bias).  Lesson, Load balancing item 1 and Key terms: an extra
+ * loss term that penalises uneven expert usage, with its own weight and
+ * gradient.  The pages give no formula; this is the Switch/GShard form
+ *   L_aux = alpha * E / (T*k) * sum_e counts[e] * P[e],
+ *   P[e]  = (1/T) sum_t p[t, e],
+ * p the router probabilities over ALL E experts: softmax of the logits for
+ * MOE_SOFTMAX_CHOSEN, each score over the sum of all E scores for the
+ * normalised score functions.  Balanced counts and uniform p give alpha.
+ * Reductions run in a fixed order (bit-reproducible).
+ *   logits [T, E] f32 (moe_route's logits_out);  counts [E] int32 (moe_permute)
+ *   loss_out [1] f32 device out;  p_mean_out [E] f32 out or NULL
+ *   workspace  moe_workspace_size(MOE_CALL_AUX_LOSS, T, k, E, 0, 0)
+ * Its gradient is added by moe_backward when moe_bwd_args.aux_alpha != 0.
+ * ENOTSUP: E > MOE_MAX_EXPERTS, T >= 2^31.
+ */
+moe_status moe_aux_loss(const float* logits, const int32_t* counts, int64_t T, int E, int k, int score_fn,
+                        float alpha, float* loss_out, float* p_mean_out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * moe_backward — gradients of the routed layer (training).
  * The pages give no backward formulas; this is the chain rule through the
  * forward above.  The selection bias and the logit offset get no gradient
@@ -309,16 +331,25 @@ typedef struct moe_bwd_args {
   /* appended; a struct_size that ends before it means NULL */
   const int32_t* counts;       /* [E] from moe_permute_capacity, or NULL when
                                   nothing was dropped (then x_perm holds the
-                                  kept rows only) */
+                                  kept rows only); required with aux_alpha */
+  float aux_alpha;             /* weight of the auxiliary load-balancing loss
+                                  (moe_aux_loss) whose gradient is added; 0: none */
 } moe_bwd_args;
 
-/* With an expert capacity (row_of < 0 for dropped slots, `counts` set): a
+/* With aux_alpha != 0 the gradient of moe_aux_loss (same alpha, counts
+ * and logits) is added: it reaches every logit, so dW_r = dL^T x and
+ * dx_r = dL W_r use the dense [T, E] logit gradient dL (the chosen experts'
+ * dl plus the aux part); `dlogit` still reports the main-loss dl of the
+ * chosen experts.  Needs a learned router and `counts`.
+ * With an expert capacity (row_of < 0 for dropped slots, `counts` set): a
  * dropped slot gets dg = 0 and no dY_perm / dX_perm row; its dl (through the
  * gate normalisation) still reaches dW_r over its dropped x_perm row and
  * dx_r.  Expert GEMMs run on the kept rows offsets[0] .. offsets[E]-1.
  * ENOTSUP: non-bf16 use, d or f not a multiple of 64, E > MOE_MAX_EXPERTS,
  * k > MOE_MAX_TOPK.  EINVAL also for a struct_size other than
- * sizeof(moe_bwd_args) or offsetof(moe_bwd_args, counts). */
+ * sizeof(moe_bwd_args), offsetof(moe_bwd_args, counts) or
+ * offsetof(moe_bwd_args, aux_alpha) (older callers: the missing fields
+ * read as NULL / 0). */
 moe_status moe_backward(const moe_bwd_args* args, void* stream);
 
 /* Workspace bytes a call needs (0 if it needs none).  `which` is enum

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 SCORE = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "uniform": 3}
-MOE_CALL_ROUTE, MOE_CALL_PERMUTE, MOE_CALL_GROUPED_FFN, MOE_CALL_BACKWARD = range(4)
+MOE_CALL_ROUTE, MOE_CALL_PERMUTE, MOE_CALL_GROUPED_FFN, MOE_CALL_BACKWARD, MOE_CALL_AUX_LOSS = range(5)
 MAX_EXPERTS, MAX_TOPK = 1024, 16
 
 _vp, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
@@ -35,7 +35,7 @@ class BwdArgs(ctypes.Structure):
         ("dx", _vp), ("dw_router", _vp), ("dw_gate_up", _vp), ("dw_down", _vp),
         ("dgate", _vp), ("dlogit", _vp),
         ("workspace", _vp), ("workspace_bytes", _sz),
-        ("counts", _vp),
+        ("counts", _vp), ("aux_alpha", ctypes.c_float),
     ]
 
 
@@ -48,6 +48,7 @@ _SIGS = {
     "moe_grouped_ffn": [_vp, _i64, _i64, _int, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_combine": [_vp, _vp, _vp, _vp, _i64, _int, _i64, _vp, _int, _vp],
     "moe_bias_update": [_vp, _vp, _int, _i64, _int, ctypes.c_float, _vp],
+    "moe_aux_loss": [_vp, _vp, _i64, _int, _int, _int, ctypes.c_float, _vp, _vp, _vp, _sz, _vp],
     "moe_backward": [ctypes.POINTER(BwdArgs), _vp],
     "moe_workspace_size": [_int, _i64, _int, _int, _i64, _i64],
     "moe_status_str": [_int],
@@ -266,6 +267,20 @@ def moe_bias_update(sel_bias, counts, T, k, gamma, stream=None):
     _check("moe_bias_update", lib().moe_bias_update(_p(sel_bias), _p(counts), E, T, k, float(gamma),
                                                     _stream(stream)))
     return sel_bias
+
+
+def moe_aux_loss(logits, counts, k, score_fn, alpha, loss_out=None, p_mean_out=None, workspace=None, stream=None):
+    """Auxiliary load-balancing loss (device scalar) from the logits and counts."""
+    T, E = logits.shape
+    _req(logits, "logits", torch.float32)
+    _req(counts, "counts", torch.int32, (E,))
+    dev = logits.device
+    loss_out = torch.empty(1, dtype=torch.float32, device=dev) if loss_out is None else loss_out
+    ws, n = _workspace(MOE_CALL_AUX_LOSS, T, k, E, 0, 0, dev, workspace)
+    sf = SCORE[score_fn] if isinstance(score_fn, str) else int(score_fn)
+    _check("moe_aux_loss", lib().moe_aux_loss(_p(logits), _p(counts), T, E, k, sf, float(alpha), _p(loss_out),
+                                              _p(p_mean_out), _p(ws), ws.numel(), _stream(stream)))
+    return loss_out
 
 
 def moe_backward(args: BwdArgs, stream=None):

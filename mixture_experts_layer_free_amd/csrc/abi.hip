@@ -2,6 +2,7 @@
 // per-device compute-unit count.
 #include <atomic>
 
+#include "aux.h"
 #include "moe_common.h"
 
 size_t moe_permute_workspace(int64_t T, int k, int E);
@@ -35,6 +36,8 @@ extern "C" size_t moe_workspace_size(int which, int64_t T, int k, int E, int64_t
       return moe_ffn_workspace(E);
     case MOE_CALL_BACKWARD:
       return moe_backward_workspace(T, k, E, d, f);
+    case MOE_CALL_AUX_LOSS:
+      return moe_aux_workspace(T, E);
     default:
       return 0;
   }

@@ -19,6 +19,7 @@
 // no expert output: it gets dg = 0 and no dY_perm / dX_perm row, but its
 // logit still has a gradient through the gate normalisation, and the router
 // weight gradient runs over the kept and the dropped rows of x_perm.
+#include "aux.h"
 #include "gemm.h"
 
 #include <cstddef>
@@ -290,7 +291,7 @@ __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
 }
 
 struct BwdLayout {
-  size_t dy_perm, dgu, dx_perm, dg, dl, dl_perm, dgp, mt_prefix, rc_prefix, seg_beg, seg_end, rpart, total;
+  size_t dy_perm, dgu, dx_perm, dg, dl, dl_perm, dgp, mt_prefix, rc_prefix, seg_beg, seg_end, rpart, aux, total;
 };
 
 BwdLayout layout(int64_t T, int k, int E, int64_t d, int64_t f) {
@@ -310,6 +311,7 @@ BwdLayout layout(int64_t T, int k, int E, int64_t d, int64_t f) {
   L.seg_beg = take((size_t)2 * E * 4);
   L.seg_end = take((size_t)2 * E * 4);
   L.rpart = take((size_t)(ceil_div(A, RCH) + 2 * E) * d * 4);
+  L.aux = take(moe_aux_bwd_workspace(T, E, d));
   L.total = o;
   return L;
 }
@@ -322,10 +324,12 @@ size_t moe_backward_workspace(int64_t T, int k, int E, int64_t d, int64_t f) {
 }
 
 extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
-  // struct_size: the full struct, or the one before `counts` was appended
-  if (!a || (a->struct_size != sizeof(moe_bwd_args) && a->struct_size != offsetof(moe_bwd_args, counts)))
+  // struct_size: the full struct, or one that ends before an appended field
+  if (!a || (a->struct_size != sizeof(moe_bwd_args) && a->struct_size != offsetof(moe_bwd_args, counts) &&
+             a->struct_size != offsetof(moe_bwd_args, aux_alpha)))
     return MOE_EINVAL;
-  const int32_t* counts = a->struct_size == sizeof(moe_bwd_args) ? a->counts : nullptr;
+  const int32_t* counts = a->struct_size > offsetof(moe_bwd_args, counts) ? a->counts : nullptr;
+  const float aux_alpha = a->struct_size > offsetof(moe_bwd_args, aux_alpha) ? a->aux_alpha : 0.0f;
   const int64_t T = a->T, d = a->d, f = a->f;
   const int E = a->E, k = a->k;
   if (T < 1 || d < 1 || f < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
@@ -335,6 +339,8 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
       !a->gu_saved || !a->h || !a->y_perm || !a->w_gate_up || !a->w_down || !a->dx || !a->dw_gate_up || !a->dw_down)
     return MOE_EINVAL;
   if (router && (!a->w_router || !a->logits || !a->dw_router)) return MOE_EINVAL;
+  const bool aux = aux_alpha != 0.0f;
+  if (aux && (!router || !counts)) return MOE_EINVAL;   // the aux loss needs a router and the expert counts
   if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || d % 64 != 0 || f % 64 != 0 || T * k >= (1ll << 31) || T >= (1ll << 31))
     return MOE_ENOTSUP;
   // the weight-gradient GEMMs address one expert's rows of the permuted
@@ -370,8 +376,9 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   gate_bwd_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(dgp, a->row_of, a->topk_gate, a->topk_idx, a->logits, (int)T,
                                                            k, E, a->score_fn, dg, dl, dl_perm);
   MOE_LAUNCH_CHECK();
-  // 2. router weight gradient
-  if (router) {
+  // 2. router weight gradient (with the aux loss: dense, together with dx below)
+  if (aux) {
+  } else if (router) {
     router_seg_schedule_kernel<<<1, 1024, 0, s>>>(a->offsets, counts, E, seg_beg, seg_end, rc_prefix);
     MOE_LAUNCH_CHECK();
     router_wgrad_part_kernel<<<dim3((unsigned)(ceil_div(A, RCH) + 2 * E), (unsigned)ceil_div(d, 2048)), 256, 0, s>>>(
@@ -432,6 +439,10 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
     if (st != MOE_OK) return st;
   }
   // 7. unpermute + router input gradient
+  if (aux)
+    return moe_aux_backward_launch(a->logits, counts, a->topk_idx, dl, static_cast<const bf16_t*>(a->x), a->w_router,
+                                   reinterpret_cast<const f32x4*>(dx_perm), a->row_of, T, E, k, d, a->score_fn,
+                                   aux_alpha, a->dw_router, a->dx, ws + Lo.aux, s);
 #define MOE_UBWD(K)                                                                                             \
   do {                                                                                                          \
     if (router)                                                                                                 \

@@ -34,6 +34,7 @@ class Shape:
     capacity: Optional[int] = None   # rows per expert (token dropping); None: no cap
     router: str = "learned"          # "learned" (scores, top-k) or "hash" (token ids, gates 1/k)
     salt: int = 0                    # hash router: per-layer salt
+    aux_alpha: float = 0.0           # weight of the auxiliary load-balancing loss (0: off)
 
 
 def expert_capacity(factor: float, T: int, k: int, E: int) -> int:
@@ -132,6 +133,10 @@ class MoELayer:
             self.dgate = z(T, k)
             self.dlogit = z(T, k)
             self.ws_bwd = z(max(1, L.workspace_size(L.MOE_CALL_BACKWARD, T, k, E, d, f)), dtype=torch.uint8)
+        if s.aux_alpha:
+            self.aux_loss = z(1)
+            self.aux_p = z(E)
+            self.ws_aux = z(max(1, L.workspace_size(L.MOE_CALL_AUX_LOSS, T, k, E, d, f)), dtype=torch.uint8)
 
     def forward(self, x, stream=None, timer=None, token_ids=None, replay_idx=None):
         """One forward.  ``replay_idx`` [T, k] int32 forces the expert choice
@@ -167,6 +172,10 @@ class MoELayer:
             shared_y = self.sh_y
         with _span(timer, "combine", stream):
             L.moe_combine(self.y_perm, self.row_of, self.gate, shared_y, self.out, stream=stream)
+        if s.aux_alpha:
+            with _span(timer, "aux_loss", stream):
+                L.moe_aux_loss(self.logits, self.counts, s.k, s.score, s.aux_alpha, self.aux_loss, self.aux_p,
+                               workspace=self.ws_aux, stream=stream)
         if s.bias_update and self.sel_bias is not None:
             with _span(timer, "bias_update", stream):
                 L.moe_bias_update(self.sel_bias, self.counts, s.T, s.k, s.gamma, stream=stream)
@@ -186,7 +195,8 @@ class MoELayer:
                         ("dgate", self.dgate), ("dlogit", self.dlogit), ("workspace", self.ws_bwd)):
             setattr(a, name, t.data_ptr() if t is not None else None)
         a.workspace_bytes = self.ws_bwd.numel()
-        a.counts = self.counts.data_ptr() if s.capacity is not None else None
+        a.counts = self.counts.data_ptr() if s.capacity is not None or s.aux_alpha else None
+        a.aux_alpha = s.aux_alpha
         with _span(timer, "backward", stream):
             L.moe_backward(a, stream=stream)
         return self.dx

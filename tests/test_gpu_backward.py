@@ -16,16 +16,16 @@ from workloads import CONFIGS, make_inputs, scaled
 pytestmark = pytest.mark.gpu
 
 
-def _layer(cfg, inp, capacity=None):
+def _layer(cfg, inp, capacity=None, aux_alpha=0.0):
     from mixture_experts_layer_free_amd.layer import MoELayer, Shape
     s = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, torch.bfloat16, cfg.score, 0, 0, False, cfg.gamma, True,
-              capacity=capacity)
+              capacity=capacity, aux_alpha=aux_alpha)
     return MoELayer(s, dev(inp["w_router"]), dev(inp["w_gate_up"]), dev(inp["w_down"]), dev(inp["bias"].copy()),
                     dev(inp["logit_offset"]))
 
 
-def _run(cfg, inp, capacity=None):
-    layer = _layer(cfg, inp, capacity)
+def _run(cfg, inp, capacity=None, aux_alpha=0.0):
+    layer = _layer(cfg, inp, capacity, aux_alpha)
     x = dev(inp["x"])
     layer.forward(x)
     layer.backward(x, dev(inp["dy"]))
@@ -74,6 +74,54 @@ def test_backward_capacity(score, T, d, E, k, f, cap):
     check_close(host(layer.dw_router), g["dw_router"], "bf16", "dW_router")
     check_close(host(layer.dw_down), g["dw_down"], "bf16", "dW_down")
     check_close(host(layer.dw_gate_up), g["dw_gate_up"], "bf16", "dW_gate_up")
+
+
+@pytest.mark.parametrize("score", oracle.SCORE_FNS)
+@pytest.mark.parametrize("T,d,E,k,f,cap", [(700, 256, 24, 3, 128, None), (257, 128, 8, 8, 64, 100),
+                                           (600, 128, 40, 4, 64, 40)])
+def test_backward_aux_loss(score, T, d, E, k, f, cap):
+    """With the auxiliary loss on, every logit has a gradient: dW_r and dx use
+    the dense logit gradient.  Compared with the oracle's backward (same alpha)
+    fed the GPU's routing; also with an expert capacity."""
+    say(f"[backward aux {score} T={T} d={d} E={E} k={k} f={f} cap={cap}]")
+    cfg = scaled(CONFIGS["train"], T=T, d=d, E=E, k=k, f=f, score=score, bias="uniform")
+    inp = make_inputs(cfg)
+    alpha = 0.5
+    layer = _run(cfg, inp, capacity=cap, aux_alpha=alpha)
+    idx = host(layer.idx).astype(np.int64)
+    fwd = oracle.forward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], k, score, True,
+                         sel_bias=inp["bias"], logit_offset=inp["logit_offset"], idx=idx, capacity=cap)
+    g = oracle.backward(fwd, inp["dy"], inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], score, True,
+                        aux_alpha=alpha)
+    want = oracle.aux_loss(fwd["logits"], fwd["counts"], k, score, alpha)
+    assert abs(float(host(layer.aux_loss)[0]) - want) <= 1e-5 * abs(want)
+    check_close(host(layer.dlogit), g["dl"], "bf16", "dl (main loss)")
+    check_close(host(layer.dw_router), g["dw_router"], "bf16", "dW_router")
+    check_close(host(layer.dx), g["dx"], "bf16", "dx")
+    check_close(host(layer.dw_gate_up), g["dw_gate_up"], "bf16", "dW_gate_up")
+
+
+@pytest.mark.parametrize("score", oracle.SCORE_FNS)
+def test_backward_aux_loss_contribution(score):
+    """The aux loss's own share of dW_r and dx: the GPU's (with alpha) minus
+    (without) against the oracle's dense aux logit gradient pushed through
+    the router, alpha large enough that this share is of order one."""
+    say(f"[backward aux share {score}]")
+    cfg = scaled(CONFIGS["train"], T=900, d=128, E=32, k=4, f=64, score=score, bias="uniform")
+    inp = make_inputs(cfg)
+    alpha = 0.5 * cfg.T
+    on = _run(cfg, inp, aux_alpha=alpha)
+    dw_on, dx_on = host(on.dw_router).astype(np.float64), host(on.dx).astype(np.float64)
+    off = _run(cfg, inp)
+    assert np.array_equal(host(on.idx), host(off.idx))
+    lg = host(on.logits).astype(np.float64)
+    dl_aux = oracle.aux_grad_logits(lg, host(on.counts), cfg.k, score, alpha)
+    x64 = as_f64(inp["x"])
+    want_dw = dl_aux.T @ x64
+    want_dx = dl_aux @ np.asarray(inp["w_router"], np.float64)
+    say(f"  aux share of dW_r: {np.linalg.norm(want_dw) / np.linalg.norm(dw_on):.2f}")
+    check_close(dw_on - host(off.dw_router), want_dw, "bf16", "dW_r aux share")
+    check_close(dx_on - host(off.dx), want_dx, "bf16", "dx aux share")
 
 
 def test_backward_hash_router():

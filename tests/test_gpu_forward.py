@@ -154,6 +154,30 @@ def test_route_fewer_experts_at_serving(score):
         np.testing.assert_allclose(host(gk), pre / pre.sum(1, keepdims=True), rtol=2e-6, atol=1e-7)
 
 
+@pytest.mark.parametrize("T,E,k,score", [(300, 40, 6, "softmax"), (16384, 64, 8, "sqrt_softplus"),
+                                         (4096, 256, 8, "sigmoid"), (64, 1024, 16, "softmax"), (4096, 8, 2, "softmax"),
+                                         (513, 17, 3, "sigmoid")])
+def test_aux_loss(T, E, k, score):
+    """Auxiliary load-balancing loss and the mean router probabilities against
+    the oracle fed the GPU's own logits and counts (fixed-order reductions:
+    also bit-reproducible run to run)."""
+    say(f"[aux loss T={T} E={E} k={k} {score}]")
+    cfg = scaled(CONFIGS["fine"], T=T, d=64, E=E, k=k, f=64, score=score, bias="uniform")
+    inp = make_inputs(cfg, experts=False)
+    x = dev(inp["x"])
+    idx, gate, logits = L.moe_route(x, dev(inp["w_router"]), k, score, dev(inp["logit_offset"]), dev(inp["bias"]))
+    counts = L.moe_permute(idx, x, E)[0]
+    p_mean = torch.empty(E, dtype=torch.float32, device="cuda")
+    loss = L.moe_aux_loss(logits, counts, k, score, 0.01, p_mean_out=p_mean)
+    loss2 = L.moe_aux_loss(logits, counts, k, score, 0.01)
+    torch.cuda.synchronize()
+    lg = host(logits).astype(np.float64)
+    want = oracle.aux_loss(lg, host(counts), k, score, 0.01)
+    assert abs(float(host(loss)[0]) - want) <= 1e-5 * abs(want), (float(host(loss)[0]), want)
+    check_close(host(p_mean), oracle.aux_probs(lg, score).mean(axis=0), "f32", "P")
+    assert host(loss)[0] == host(loss2)[0]
+
+
 # ---------------------------------------------------------------------------- permute
 
 def _permute_case(idx_np, x_np, E):
