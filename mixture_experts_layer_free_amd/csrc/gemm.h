@@ -393,6 +393,8 @@ void gemm_kernel(Args p) {
     // 4*(lane/32) + r%4, column lane%32) is written out, then read back as
     // 4-column chunks so every global store is a row-contiguous vector
     // (16 bytes of fp32 or 8 bytes of bf16) and the SwiGLU math runs on them.
+    // Results are stored non-temporally: they are far larger than the L2,
+    // which is left to the operand panels the neighbouring tiles reuse.
     {
       constexpr int SLD = 36;   // floats per staged row (16-byte aligned rows, spread banks)
       float* stg0 = reinterpret_cast<float*>(smem) + wave * (2 * 32 * SLD);
@@ -421,15 +423,15 @@ void gemm_kernel(Args p) {
                 uint2 h;
                 h.x = pack_bf16x2(silu_f32(g[0]) * u[0], silu_f32(g[1]) * u[1]);
                 h.y = pack_bf16x2(silu_f32(g[2]) * u[2], silu_f32(g[3]) * u[3]);
-                *reinterpret_cast<uint2*>(H + row * p.ldo + col) = h;
+                __builtin_nontemporal_store(u32x2{h.x, h.y}, reinterpret_cast<u32x2*>(H + row * p.ldo + col));
                 if (p.gu_out) {
                   uint2 gg, uu;
                   gg.x = pack_bf16x2(g[0], g[1]);
                   gg.y = pack_bf16x2(g[2], g[3]);
                   uu.x = pack_bf16x2(u[0], u[1]);
                   uu.y = pack_bf16x2(u[2], u[3]);
-                  *reinterpret_cast<uint2*>(p.gu_out + row * 2 * p.N + col) = gg;
-                  *reinterpret_cast<uint2*>(p.gu_out + row * 2 * p.N + p.N + col) = uu;
+                  __builtin_nontemporal_store(u32x2{gg.x, gg.y}, reinterpret_cast<u32x2*>(p.gu_out + row * 2 * p.N + col));
+                  __builtin_nontemporal_store(u32x2{uu.x, uu.y}, reinterpret_cast<u32x2*>(p.gu_out + row * 2 * p.N + p.N + col));
                 }
               }
             }
@@ -451,67 +453,71 @@ void gemm_kernel(Args p) {
               const int64_t col = col0 + c4;
               if (row < row_end && col < p.N) {
                 float* C = static_cast<float*>(p.out) + (KG ? (int64_t)e * p.out_group : 0);
-                *reinterpret_cast<f32x4*>(C + row * p.ldo + col) = v;
+                __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(C + row * p.ldo + col));
               }
             }
           }
         }
       } else {  // EPI_SWIGLU_BWD: dH block -> dG, dU from the saved G, U
-        // the saved G|U vectors of block b+1 are loaded while block b is
-        // computed, so only the first block waits for memory
-        uint2 gn[4], un[4];
-        auto load_gu = [&](int b, uint2 (&gb)[4], uint2 (&ub)[4]) {
+        // The saved G|U come from HBM: 16-byte loads (8 columns) issued PF
+        // blocks ahead, into the registers the fragments used in the loop, so
+        // PF blocks of loads are in flight while earlier blocks compute.
+        constexpr int NBLK = FM * FN, PF = NBLK < 4 ? NBLK : 4;
+        u32x4 gq[PF][2], uq[PF][2];
+        auto load_gu = [&](int b, u32x4 (&gb)[2], u32x4 (&ub)[2]) {
           const int mi = b / FN, ni = b % FN;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int idx = lane + 64 * j, rr = idx >> 3, c4 = (idx & 7) * 4;
+          for (int j = 0; j < 2; ++j) {
+            const int idx = lane + 64 * j, rr = idx >> 2, c8 = (idx & 3) * 8;
             const int64_t row = row0 + wm * WTM + mi * 32 + rr;
-            const int64_t col = (int64_t)nb * TN + wn * WTN + ni * 32 + c4;
-            gb[j] = ub[j] = uint2{0u, 0u};
+            const int64_t col = (int64_t)nb * TN + wn * WTN + ni * 32 + c8;
+            gb[j] = ub[j] = u32x4{0u, 0u, 0u, 0u};
             if (row < row_end && col < p.N) {
-              gb[j] = *reinterpret_cast<const uint2*>(p.gu_in + row * 2 * p.N + col);
-              ub[j] = *reinterpret_cast<const uint2*>(p.gu_in + row * 2 * p.N + p.N + col);
+              gb[j] = *reinterpret_cast<const u32x4*>(p.gu_in + row * 2 * p.N + col);
+              ub[j] = *reinterpret_cast<const u32x4*>(p.gu_in + row * 2 * p.N + p.N + col);
             }
           }
         };
-        load_gu(0, gn, un);
 #pragma unroll
-        for (int b = 0; b < FM * FN; ++b) {
+        for (int b = 0; b < PF; ++b) load_gu(b, gq[b], uq[b]);
+#pragma unroll
+        for (int b = 0; b < NBLK; ++b) {
           const int mi = b / FN, ni = b % FN;
-          uint2 gc[4], uc[4];
+          u32x4 gc[2], uc[2];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            gc[j] = gn[j];
-            uc[j] = un[j];
+          for (int j = 0; j < 2; ++j) {
+            gc[j] = gq[b % PF][j];
+            uc[j] = uq[b % PF][j];
           }
-          if (b + 1 < FM * FN) load_gu(b + 1, gn, un);
-          const int64_t col0 = (int64_t)nb * TN + wn * WTN + ni * 32;
+          if (b + PF < NBLK) load_gu(b + PF, gq[b % PF], uq[b % PF]);
           stage(stg0, acc[mi][ni]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int idx = lane + 64 * j, rr = idx >> 3, c4 = (idx & 7) * 4;
+          for (int j = 0; j < 2; ++j) {
+            const int idx = lane + 64 * j, rr = idx >> 2, c8 = (idx & 3) * 8;
             const int64_t row = row0 + wm * WTM + mi * 32 + rr;
-            const f32x4 v = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c4);
-            const int64_t col = col0 + c4;
+            const int64_t col = (int64_t)nb * TN + wn * WTN + ni * 32 + c8;
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c8);
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c8 + 4);
             if (row < row_end && col < p.N) {
-              const float g[4] = {bf16_to_f32(gc[j].x & 0xFFFFu), bf16_to_f32(gc[j].x >> 16),
-                                  bf16_to_f32(gc[j].y & 0xFFFFu), bf16_to_f32(gc[j].y >> 16)};
-              const float u[4] = {bf16_to_f32(uc[j].x & 0xFFFFu), bf16_to_f32(uc[j].x >> 16),
-                                  bf16_to_f32(uc[j].y & 0xFFFFu), bf16_to_f32(uc[j].y >> 16)};
-              float dg[4], du[4];
+              const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+              u32x4 o1, o2;
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                const float sg = sigmoid_fast(g[q]);
-                dg[q] = v[q] * u[q] * sg * (1.0f + g[q] * (1.0f - sg));
-                du[q] = v[q] * g[q] * sg;
+                float dg[2], du[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                  const uint32_t gw = gc[j][q], uw = uc[j][q];
+                  const float g = bf16_to_f32(h ? gw >> 16 : gw & 0xFFFFu);
+                  const float u = bf16_to_f32(h ? uw >> 16 : uw & 0xFFFFu);
+                  const float sg = sigmoid_fast(g);
+                  dg[h] = v[2 * q + h] * u * sg * (1.0f + g * (1.0f - sg));
+                  du[h] = v[2 * q + h] * g * sg;
+                }
+                o1[q] = pack_bf16x2(dg[0], dg[1]);
+                o2[q] = pack_bf16x2(du[0], du[1]);
               }
-              uint2 o1, o2;
-              o1.x = pack_bf16x2(dg[0], dg[1]);
-              o1.y = pack_bf16x2(dg[2], dg[3]);
-              o2.x = pack_bf16x2(du[0], du[1]);
-              o2.y = pack_bf16x2(du[2], du[3]);
-              *reinterpret_cast<uint2*>(p.gu_out + row * 2 * p.N + col) = o1;
-              *reinterpret_cast<uint2*>(p.gu_out + row * 2 * p.N + p.N + col) = o2;
+              __builtin_nontemporal_store(o1, reinterpret_cast<u32x4*>(p.gu_out + row * 2 * p.N + col));
+              __builtin_nontemporal_store(o2, reinterpret_cast<u32x4*>(p.gu_out + row * 2 * p.N + p.N + col));
             }
           }
         }
