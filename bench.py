@@ -85,6 +85,9 @@ CALL_OF = [
     ("ffn_up_f32", "grouped_ffn"), ("ffn_down_f32", "grouped_ffn"),
     ("combine_kernel", "combine"), ("bias_update_kernel", "bias_update"),
     ("combine_bwd", "backward"), ("gate_bwd", "backward"), ("router_wgrad", "backward"), ("unpermute_bwd", "backward"),
+    ("router_seg_schedule", "backward"), ("aux_dl_dense", "backward"), ("router_dense_wgrad", "backward"),
+    ("fill_zero", "backward"), ("aux_prob", "aux_loss"), ("aux_loss_final", "aux_loss"),
+    ("replay_gate", "route"), ("hash_route", "route"),
     ("gemm_kernel", "backward"),
 ]
 
@@ -394,7 +397,7 @@ def main():
         res["fwd"] = fwd_line(_lib, a, device)
     if not a.no_cpu_baseline:
         # about 10-30 s of oracle work on the host's cores
-        tokens = a.cpu_tokens or {"train": 6144, "fine": 8192, "coarse": 4096, "dsv3": 1024}[cfg.name]
+        tokens = a.cpu_tokens or {"train": 16384, "fine": 8192, "coarse": 4096, "dsv3": 1024}[cfg.name]
         log(f"[bench] cpu oracle on {tokens} tokens")
         res["cpu_baseline"] = cpu_baseline(cfg, inp, train, tokens)
     print(json.dumps(res), flush=True)
