@@ -32,8 +32,8 @@
 // the 4 waves' 32 loads queue behind one texture unit for ~500 cycles while
 // the matrix cores idle), and the tile order below is chosen for L2 reuse.
 // Two tile shapes: 256x256 (one workgroup per CU, accumulators in AGPRs,
-// half the LDS bytes per MFMA flop) for groups of >= 512 rows, 128x128 (two
-// workgroups per CU) otherwise.  The kernel is persistent: the grid is a
+// half the LDS bytes per MFMA flop) and 128x128 (two workgroups per CU);
+// use_large_rows below picks one from the rows per group.  The kernel is persistent: the grid is a
 // multiple of 8 workgroups; workgroup i runs on XCD i%8 and in each round
 // takes the tile at position i/8 of that XCD's contiguous share of the round,
 // so neighbouring tiles (sharing a weight or activation panel) meet in one
@@ -562,12 +562,19 @@ moe_status launch_gemm(const Args& a, bool large, int64_t rows, hipStream_t s) {
                : launch_cfg<BM, BN, AK, BKC, KG, EPI>(a, rows, s);
 }
 
-// Row-grouped GEMMs use the large tile when groups average at least this many
-// rows (fewer rows waste too much of a 256-row tile on ragged tails).
-constexpr int64_t LARGE_MIN_ROWS = 512;
+// Tile choice of a row-grouped GEMM by the average rows per group:
+//  * >= 512: the large tile (half the operand traffic per flop, MFMA-bound);
+//  * <= 256: the large tile too.  Such groups are bound by streaming their
+//    weights, and a 256-row tile reads each group's weights about once where
+//    128-row tiles read them once per row tile.  The MFMA work on the rows past
+//    a group's end is free when memory is the bound, and those rows cost no
+//    traffic (their loads are out of range).  Measured on 256 experts with
+//    ~128 rows each: 7.7 -> 5.6 ms for the two expert GEMMs.
+//  * in between: the small tile, whose ragged tails waste less.
+constexpr int64_t LARGE_MIN_ROWS = 512, LARGE_MAX_ROWS_WEIGHT_BOUND = 256;
 
 inline bool use_large_rows(int64_t rows, int G, int64_t f) {
-  return rows >= LARGE_MIN_ROWS * G && f % (BN_LARGE / 2) == 0;
+  return (rows >= LARGE_MIN_ROWS * G || rows <= LARGE_MAX_ROWS_WEIGHT_BOUND * G) && f % (BN_LARGE / 2) == 0;
 }
 
 }  // namespace moe_gemm

@@ -35,7 +35,8 @@ def _run(cfg, inp, capacity=None, aux_alpha=0.0):
 
 @pytest.mark.parametrize("score", oracle.SCORE_FNS)
 @pytest.mark.parametrize("T,d,E,k,f", [(700, 256, 24, 3, 128), (257, 128, 8, 8, 64), (96, 192, 40, 2, 192),
-                                       (1100, 256, 4, 2, 256), (900, 384, 3, 3, 384)])   # last two: 256x256 tiles
+                                       (1100, 256, 4, 2, 256), (900, 384, 3, 3, 384),   # 256x256 tiles
+                                       (600, 128, 4, 2, 128)])                          # 300 rows per group: 128x128 tiles
 def test_backward_small(score, T, d, E, k, f):
     say(f"[backward small {score} T={T} d={d} E={E} k={k} f={f}]")
     cfg = scaled(CONFIGS["train"], T=T, d=d, E=E, k=k, f=f, score=score, bias="uniform")

@@ -301,7 +301,8 @@ def test_ffn_tiny_f32():
 
 
 @pytest.mark.parametrize("d,f,seg", [(128, 64, [0, 1, 129, 129, 300, 557]), (256, 192, [0, 0, 0, 1000]),
-                                     (192, 128, [0, 128, 256, 384]),
+                                     (192, 128, [0, 128, 256, 384]),     # <= 256 rows per group: 256x256 tiles
+                                     (128, 128, [0, 300, 650, 1000]),    # 256..512 rows per group: 128x128 tiles
                                      # >= 512 rows per group: the 256x256 tile configuration
                                      (256, 256, [0, 600, 1300, 1301, 2600]), (384, 384, [0, 0, 2048, 2049, 2049])])
 def test_ffn_bf16_tiles_and_tails(d, f, seg):
