@@ -139,6 +139,98 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
 }
 
 // ---------------------------------------------------------------------------
+// The same logits for bf16 x on the bf16 MFMA.  Each fp32 router weight is
+// split exactly into three bf16 parts, w = hi + mid + lo (hi = w with its
+// significand cut to 8 bits, mid the next 8 bits of the remainder, lo what is
+// left; 8 + 8 + 8 bits hold the 24-bit fp32 significand).  x is bf16, so
+// every product x*hi, x*mid, x*lo is exact in fp32 and the three
+// v_mfma_f32_32x32x16_bf16 per 16-deep step add exact products in fp32 --
+// an fp32 dot product, at the bf16 matrix rate.  As in the fp32 kernel, the
+// products go into a chunk accumulator folded into the running total every
+// 64 k (every partial sum covers at most 64 x 3 exact products).
+// Workgroup: 2 waves, 32 tokens x 64 experts; wave w owns experts
+// e0 + 32w .. +31.  Operands come straight from global memory (16-byte x
+// loads, 32-byte w loads); the next four 16-deep steps load while the
+// current four multiply.
+__device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const uint32_t u = __float_as_uint(w);
+  hi = u >> 16;                                            // truncation: w - hi is exact
+  const float r1 = w - __uint_as_float(hi << 16);
+  const uint32_t v = __float_as_uint(r1);
+  mid = v >> 16;
+  const float r2 = r1 - __uint_as_float(mid << 16);        // at most 8 significant bits left
+  lo = __float_as_uint(r2) >> 16;                          // exact
+}
+
+constexpr int RB_STEPS = 4;   // 16-deep steps in flight
+
+__global__ __launch_bounds__(128) void router_logits_bf16_kernel(const bf16_t* __restrict__ x,
+                                                                 const float* __restrict__ w,
+                                                                 const float* __restrict__ off,
+                                                                 float* __restrict__ logits, int T, int d, int E) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 64 + wave * 32;
+  const int row = lane & 31, kh = 8 * (lane >> 5);        // MFMA operand layout: row l%32, k 8*(l/32)..+7
+  const int t = t0 + row, e = e0 + row;
+  const bool tin = t < T, ein = e < E;
+  const bf16_t* xr = x + (int64_t)(tin ? t : 0) * d;
+  const float* wr = w + (int64_t)(ein ? e : 0) * d;
+  f32x16 tot = {}, chk = {};
+  const int nsteps = (d + 15) / 16;
+  // batch b = steps b*RB_STEPS .. +RB_STEPS-1; batch b+1 loads while batch b multiplies
+  auto load = [&](int s0, u32x4 (&xa)[RB_STEPS], f32x4 (&wa)[RB_STEPS][2]) {
+#pragma unroll
+    for (int u = 0; u < RB_STEPS; ++u) {
+      const int k = 16 * (s0 + u) + kh;
+      const bool kin = s0 + u < nsteps && k < d;   // d % 8 == 0: the 8 values are all in or all out
+      xa[u] = kin && tin ? *reinterpret_cast<const u32x4*>(xr + k) : u32x4{0u, 0u, 0u, 0u};
+      wa[u][0] = kin && ein ? *reinterpret_cast<const f32x4*>(wr + k) : f32x4{0.f, 0.f, 0.f, 0.f};
+      wa[u][1] = kin && ein ? *reinterpret_cast<const f32x4*>(wr + k + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto compute = [&](const u32x4 (&xa)[RB_STEPS], const f32x4 (&wa)[RB_STEPS][2]) {
+#pragma unroll
+    for (int u = 0; u < RB_STEPS; ++u) {
+      uint32_t h[8], m[8], l[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        split3(wa[u][0][q], h[q], m[q], l[q]);
+        split3(wa[u][1][q], h[4 + q], m[4 + q], l[4 + q]);
+      }
+      const u32x4 hv = {h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+      const u32x4 mv = {m[0] | m[1] << 16, m[2] | m[3] << 16, m[4] | m[5] << 16, m[6] | m[7] << 16};
+      const u32x4 lv = {l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16, l[6] | l[7] << 16};
+      const bf16x8 a = __builtin_bit_cast(bf16x8, xa[u]);
+      // D[token][expert]: A = x (tokens x k), B = w parts (k x experts)
+      chk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, lv), chk, 0, 0, 0);
+      chk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, mv), chk, 0, 0, 0);
+      chk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, hv), chk, 0, 0, 0);
+    }
+    tot += chk;   // RB_STEPS * 16 = 64 k per chunk
+    chk = f32x16{};
+  };
+  u32x4 xa0[RB_STEPS], xa1[RB_STEPS];
+  f32x4 wa0[RB_STEPS][2], wa1[RB_STEPS][2];
+  load(0, xa0, wa0);
+  for (int s0 = 0; s0 < nsteps; s0 += 2 * RB_STEPS) {   // batches past the end load and add zeros
+    load(s0 + RB_STEPS, xa1, wa1);
+    compute(xa0, wa0);
+    load(s0 + 2 * RB_STEPS, xa0, wa0);
+    compute(xa1, wa1);
+  }
+  // D layout: register r of a lane = row (token) 8*(r/4) + 4*(lane/32) + r%4, column (expert) lane%32
+  const int ec = e0 + (lane & 31);
+  if (ec < E) {
+    const float o = off ? off[ec] : 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tr = t0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (tr < T) logits[(int64_t)tr * E + ec] = tot[r] + o;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // The same logits for E <= 16 (the few-expert layers, where the router reads
 // x once and the 64-expert tile would idle most of its MFMA columns).
 //
@@ -417,12 +509,12 @@ static moe_status router_logits_launch(const void* x, int x_dtype, int64_t T, in
       router_logits_small_kernel<true><<<gs, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
     else
       router_logits_small_kernel<false><<<gs, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
+  } else if (x_dtype == MOE_BF16) {
+    router_logits_bf16_kernel<<<dim3((unsigned)ceil_div(T, 32), (unsigned)ceil_div(E, 64)), 128, 0, s>>>(
+        static_cast<const bf16_t*>(x), w_router, logit_offset, logits_out, (int)T, (int)d, E);
   } else {
     dim3 g1((unsigned)ceil_div(T, RT_M), (unsigned)ceil_div(E, RT_N));
-    if (x_dtype == MOE_BF16)
-      router_logits_kernel<true><<<g1, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
-    else
-      router_logits_kernel<false><<<g1, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
+    router_logits_kernel<false><<<g1, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
   }
   MOE_LAUNCH_CHECK();
   return MOE_OK;
