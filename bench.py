@@ -79,7 +79,7 @@ def source_hash():
 
 # which library call launched a kernel (by kernel name), for per-call PMC sums
 CALL_OF = [
-    ("router_logits_kernel", "route"), ("topk_gate_kernel", "route"),
+    ("router_logits", "route"), ("topk_gate_kernel", "route"),
     ("perm_", "permute"),
     ("gemm_kernel<256, 256, true, true, false", "grouped_ffn"), ("gemm_kernel<128, 128, true, true, false", "grouped_ffn"),
     ("ffn_up_f32", "grouped_ffn"), ("ffn_down_f32", "grouped_ffn"),
