@@ -262,12 +262,76 @@ def fwd_line(_lib, a, device):
             "ms_per_step": round(ms, 4), "expert_tflops": round(expert_flops(cfg, False) / (ms * 1e-3) / 1e12, 1)}
 
 
+def bench_ep_shard(a):
+    """The grouped expert FFN on one expert-parallel rank's share: the global
+    batch is routed and permuted over all experts, and the rank's contiguous
+    expert block (its rows of X_perm and its experts' weights) goes through
+    moe_grouped_ffn, timed with HIP events on its stream.  The all-to-all
+    exchange around it is not part of this measurement."""
+    import torch
+    from mixture_experts_layer_free_amd import _lib
+    from workloads import ep_shard, expert_weight_range, make_inputs
+
+    _lib.lib()
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    cfg, e0, e1 = ep_shard(a.workload)
+    log(f"[bench] {a.workload}: routing {cfg.T} tokens over {cfg.E} experts; rank experts {e0}..{e1 - 1}")
+    inp = make_inputs(cfg, experts=False)
+    x = _dev(inp["x"], device)
+    idx, _, _ = _lib.moe_route(x, _dev(inp["w_router"], device), cfg.k, cfg.score, sel_bias=_dev(inp["bias"], device))
+    _, offsets, _, _, x_perm = _lib.moe_permute(idx, x, cfg.E)
+    off = offsets[e0:e1 + 1].cpu().numpy().astype("int64")
+    rows = int(off[-1] - off[0])
+    xs = x_perm[int(off[0]):int(off[-1])]
+    g_off = torch.from_numpy((off - off[0]).astype("int32")).to(device)
+    del x, x_perm
+    log(f"[bench] {rows} rows for {e1 - e0} experts (min {int((off[1:] - off[:-1]).min())}, "
+        f"max {int((off[1:] - off[:-1]).max())}); generating their weights")
+    wgu_np, wd_np = expert_weight_range(cfg, e0, e1)
+    wgu, wd = _dev(wgu_np, device), _dev(wd_np, device)
+    del wgu_np, wd_np
+    h = torch.empty((rows, cfg.f), dtype=torch.bfloat16, device=device)
+    y = torch.empty((rows, cfg.d), dtype=torch.float32, device=device)
+    run = lambda: _lib.moe_grouped_ffn(xs, g_off, wgu, wd, h=h, y=y)
+    for _ in range(a.warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(a.steps):
+        run()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / a.steps
+    G, d, f = e1 - e0, cfg.d, cfg.f
+    flops = 6.0 * rows * d * f
+    nbytes = rows * d * 2 + 3 * G * d * f * 2 + 2 * rows * f * 2 + rows * d * 4
+    ach = flops / (ms * 1e-3) / 1e12
+    bound = "mfma" if flops / nbytes >= PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3 else "hbm"
+    roof = ({"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(ach / PEAK_BF16_TFLOPS, 4)} if bound == "mfma" else
+            {"bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
+    roof.update({"kernel": "moe_grouped_ffn (library call, all of its kernels)", "call_ms": round(ms, 4),
+                 "flops": flops, "bytes": nbytes, "traffic": None})
+    res = {"metric": "expert FFN rows/s of one expert-parallel rank's share", "value": round(rows / (ms * 1e-3), 1),
+           "unit": "rows/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"{a.workload}: rank 0 of 8 on the 256-expert top-8 shape (d_model={d}, "
+                                  f"expert_ffn={f}): experts {e0}..{e1 - 1} of a {cfg.T}-token global batch, "
+                                  f"{rows} rows; grouped FFN only, no all-to-all",
+                      "global_batch": cfg.T, "seq_len": None, "parallelism": "ep8 (one rank's share on 1 GPU)"},
+           "expert_tflops": round(ach, 1), "roofline": roof}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="train", choices=["train", "fine", "coarse", "dsv3"])
+    ap.add_argument("--workload", default="train", choices=["train", "fine", "coarse", "dsv3", "dsv3_ep8"])
     ap.add_argument("--cpu-tokens", type=int, default=None, help="oracle sample size (tokens)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
@@ -308,6 +372,10 @@ def main():
         ms = ev[0].elapsed_time(ev[1]) / a.steps
         print(json.dumps({"copy_bytes_per_launch": 2 * n, "ms": round(ms, 4),
                           "gb_per_s": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+        return
+    from workloads import EP_SHARDS
+    if a.workload in EP_SHARDS:
+        bench_ep_shard(a)
         return
     from mixture_experts_layer_free_amd import _lib
     from mixture_experts_layer_free_amd.layer import CallTimer, MoELayer, Shape

@@ -326,6 +326,32 @@ def test_ffn_bf16_many_groups():
     _ffn_case(cfg, offsets, inp["x"], inp["w_gate_up"], inp["w_down"], rows_to_check=check)
 
 
+def test_ffn_ep8_shard():
+    """One expert-parallel rank's share of the 256-expert shape: a 32768-token
+    global batch routed and permuted on the GPU, the rank's 32 experts (about
+    1024 rows each) through the grouped FFN in the configuration the bench
+    times; every group's first and last row and a random sample against the
+    oracle's expert FFN."""
+    from workloads import ep_shard, expert_weight_range
+    cfg, e0, e1 = ep_shard("dsv3_ep8")
+    say(f"[ffn ep8 shard: experts {e0}..{e1 - 1} of {cfg.T} tokens]")
+    inp = make_inputs(cfg, experts=False)
+    x = dev(inp["x"])
+    idx, _, _ = L.moe_route(x, dev(inp["w_router"]), cfg.k, cfg.score, sel_bias=dev(inp["bias"]))
+    _, offsets, _, _, x_perm = L.moe_permute(idx, x, cfg.E)
+    off = host(offsets)[e0:e1 + 1].astype(np.int64)
+    n = off[1:] - off[:-1]
+    say(f"  rows {off[-1] - off[0]}, per expert min {n.min()} max {n.max()}")
+    assert n.min() > 0
+    xs_np = host(x_perm[int(off[0]):int(off[-1])])
+    del x, x_perm
+    wgu, wd = expert_weight_range(cfg, e0, e1)
+    g_off = off - off[0]
+    rng = np.random.default_rng(5)
+    check = np.unique(np.concatenate([g_off[:-1], g_off[1:] - 1, rng.integers(0, g_off[-1], 64)]))
+    _ffn_case(cfg, g_off, xs_np, wgu, wd, rows_to_check=check, save_gu=False)
+
+
 # ---------------------------------------------------------------------------- combine / bias
 
 @pytest.mark.parametrize("k,shared,bf16", [(2, False, False), (8, True, False), (16, False, True), (1, True, True)])

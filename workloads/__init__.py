@@ -23,6 +23,12 @@ MoE layer is measured on:
 * ``train``  the fine-grained shape at T=16384 with sqrt(softplus) scores,
               forward plus backward with dY N(0, 1) in bf16, seed 4.
 
+One expert-parallel rank's share (``ep_shard``): ``dsv3_ep8`` is rank 0 of 8
+ranks on the ``dsv3`` shape.  The global batch is 8 x 4096 tokens drawn like
+``dsv3``'s (same seed and distributions, T = 32768), routed over all 256
+experts; the rank owns experts 0..31 and their weights are ``dsv3``'s experts
+0..31.
+
 Every tensor takes its own child seed from ``SeedSequence(seed).spawn``; each
 expert's weights take a grandchild seed, so any single expert can be
 regenerated alone and the large configurations can be drawn in parallel.
@@ -147,6 +153,33 @@ def shared_weights(cfg: MoEConfig, s: int):
     gu_k, d_k = kids[_SHARED].spawn(2)
     return (_normal(gu_k.spawn(cfg.shared)[s], (2 * cfg.f_shared, cfg.d), cfg.w_std, bf),
             _normal(d_k.spawn(cfg.shared)[s], (cfg.d, cfg.f_shared), cfg.w_std, bf))
+
+
+EP_SHARDS = {"dsv3_ep8": ("dsv3", 8, 0)}
+
+
+def ep_shard(name: str):
+    """(global-batch config, first expert, end expert) of one expert-parallel
+    rank: the base shape with ranks x its tokens, and the rank's contiguous
+    block of E / ranks experts."""
+    base, ranks, rank = EP_SHARDS[name]
+    cfg = CONFIGS[base]
+    per = cfg.E // ranks
+    return replace(cfg, T=cfg.T * ranks), rank * per, (rank + 1) * per
+
+
+def expert_weight_range(cfg: MoEConfig, e0: int, e1: int, workers: Optional[int] = None):
+    """Stacked weights of routed experts e0..e1-1 (as ``make_inputs`` draws them)."""
+    dt = np.uint16 if cfg.dtype == "bf16" else np.float32
+    wgu = np.empty((e1 - e0, 2 * cfg.f, cfg.d), dt)
+    wd = np.empty((e1 - e0, cfg.d, cfg.f), dt)
+
+    def fill(e):
+        wgu[e - e0], wd[e - e0] = expert_weights(cfg, e)
+
+    with ThreadPoolExecutor(workers or _workers()) as ex:
+        list(ex.map(fill, range(e0, e1)))
+    return wgu, wd
 
 
 def make_inputs(cfg: MoEConfig, experts: bool = True, workers: Optional[int] = None) -> dict:
