@@ -208,7 +208,10 @@ moe_status moe_permute_capacity(const int32_t* topk_idx, int64_t T, int k, int E
  * with G = 1 and offsets = {0, T} over the layer input.
  *
  *   x_rows     [rows, d]     dtype
- *   offsets    [G+1]         int32, offsets[0] = 0, offsets[G] = rows
+ *   offsets    [G+1]         int32 device, nondecreasing, offsets[0] = 0,
+ *                            offsets[G] <= rows (device values, not checked:
+ *                            offsets outside that range read and write out of
+ *                            bounds)
  *   w_gate_up  [G, 2f, d]    dtype: f gate rows, then f up rows per expert
  *   w_down     [G, d, f]     dtype
  *   gu_saved   [rows, 2f]    dtype out or NULL: G (cols 0..f-1) and U

@@ -115,15 +115,33 @@ def _req(t: torch.Tensor, name: str, dtype=None, shape=None):
     return t
 
 
+def _out(t: Optional[torch.Tensor], name: str, dtype, shape, device) -> torch.Tensor:
+    """A new output tensor, or the caller's after checking that the kernels
+    can write it whole: a device tensor on the inputs' device, contiguous,
+    with the expected dtype and shape."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _req(t, name, dtype, shape)
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
+    return t
+
+
 def workspace_size(which: int, T: int, k: int, E: int, d: int = 0, f: int = 0) -> int:
     return int(lib().moe_workspace_size(which, T, k, E, d, f))
 
 
 def _workspace(which, T, k, E, d, f, device, workspace=None):
+    """(workspace tensor, its size in bytes); a caller's workspace must be a
+    contiguous device tensor on the inputs' device (the library checks its size)."""
     n = workspace_size(which, T, k, E, d, f)
     if workspace is None:
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
-    return workspace, n
+    else:
+        _req(workspace, "workspace")
+        if workspace.device != device:
+            raise ValueError(f"workspace is on {workspace.device}, the inputs on {device}")
+    return workspace, workspace.numel() * workspace.element_size()
 
 
 # ----------------------------------------------------------------------------
@@ -140,9 +158,9 @@ def moe_route(x, w_router, k, score_fn, logit_offset=None, sel_bias=None,
     if sel_bias is not None:
         _req(sel_bias, "sel_bias", torch.float32, (E,))
     dev = x.device
-    topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
-    topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_gate is None else topk_gate
-    logits_out = torch.empty((T, E), dtype=torch.float32, device=dev) if logits_out is None else logits_out
+    topk_idx = _out(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    topk_gate = _out(topk_gate, "topk_gate", torch.float32, (T, k), dev)
+    logits_out = _out(logits_out, "logits_out", torch.float32, (T, E), dev)
     sf = SCORE[score_fn] if isinstance(score_fn, str) else int(score_fn)
     _check("moe_route", lib().moe_route(_p(x), _dtype_code(x), T, d, _p(w_router), _p(logit_offset),
                                         _p(sel_bias), E, k, sf, _p(topk_idx), _p(topk_gate),
@@ -162,8 +180,8 @@ def moe_route_replay(x, w_router, topk_idx, score_fn, logit_offset=None, topk_ga
     if logit_offset is not None:
         _req(logit_offset, "logit_offset", torch.float32, (E,))
     dev = x.device
-    topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_gate is None else topk_gate
-    logits_out = torch.empty((T, E), dtype=torch.float32, device=dev) if logits_out is None else logits_out
+    topk_gate = _out(topk_gate, "topk_gate", torch.float32, (T, k), dev)
+    logits_out = _out(logits_out, "logits_out", torch.float32, (T, E), dev)
     sf = SCORE[score_fn] if isinstance(score_fn, str) else int(score_fn)
     _check("moe_route_replay", lib().moe_route_replay(_p(x), _dtype_code(x), T, d, _p(w_router), _p(logit_offset),
                                                       E, k, sf, _p(topk_idx), _p(topk_gate), _p(logits_out),
@@ -176,8 +194,8 @@ def moe_route_hash(token_ids, E, k, salt=0, topk_idx=None, topk_gate=None, strea
     _req(token_ids, "token_ids", torch.int32)
     T = token_ids.shape[0]
     dev = token_ids.device
-    topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
-    topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_gate is None else topk_gate
+    topk_idx = _out(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    topk_gate = _out(topk_gate, "topk_gate", torch.float32, (T, k), dev)
     _check("moe_route_hash", lib().moe_route_hash(_p(token_ids), T, E, k, int(salt) & 0xFFFFFFFF, _p(topk_idx),
                                                   _p(topk_gate), _stream(stream)))
     return topk_idx, topk_gate
@@ -191,15 +209,15 @@ def moe_permute(topk_idx, x, E, counts=None, offsets=None, row_of=None, token_of
     _req(x, "x")
     dev = x.device
     A = T * k
-    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
-    row_of = torch.empty((T, k), dtype=torch.int32, device=dev) if row_of is None else row_of
-    token_of = torch.empty(A, dtype=torch.int32, device=dev) if token_of is None else token_of
-    x_perm = torch.empty((A, d), dtype=x.dtype, device=dev) if x_perm is None else x_perm
+    counts = _out(counts, "counts", torch.int32, (E,), dev)
+    offsets = _out(offsets, "offsets", torch.int32, (E + 1,), dev)
+    row_of = _out(row_of, "row_of", torch.int32, (T, k), dev)
+    token_of = _out(token_of, "token_of", torch.int32, (A,), dev)
+    x_perm = _out(x_perm, "x_perm", x.dtype, (A, d), dev)
     ws, n = _workspace(MOE_CALL_PERMUTE, T, k, E, d, 0, dev, workspace)
     _check("moe_permute", lib().moe_permute(_p(topk_idx), T, k, E, _p(x), _dtype_code(x), d, _p(counts),
                                             _p(offsets), _p(row_of), _p(token_of), _p(x_perm), _p(ws),
-                                            ws.numel(), _stream(stream)))
+                                            n, _stream(stream)))
     return counts, offsets, row_of, token_of, x_perm
 
 
@@ -213,15 +231,15 @@ def moe_permute_capacity(topk_idx, x, E, capacity, counts=None, offsets=None, ro
     _req(x, "x")
     dev = x.device
     A = T * k
-    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
-    row_of = torch.empty((T, k), dtype=torch.int32, device=dev) if row_of is None else row_of
-    token_of = torch.empty(A, dtype=torch.int32, device=dev) if token_of is None else token_of
-    x_perm = torch.empty((A, d), dtype=x.dtype, device=dev) if x_perm is None else x_perm
+    counts = _out(counts, "counts", torch.int32, (E,), dev)
+    offsets = _out(offsets, "offsets", torch.int32, (E + 1,), dev)
+    row_of = _out(row_of, "row_of", torch.int32, (T, k), dev)
+    token_of = _out(token_of, "token_of", torch.int32, (A,), dev)
+    x_perm = _out(x_perm, "x_perm", x.dtype, (A, d), dev)
     ws, n = _workspace(MOE_CALL_PERMUTE, T, k, E, d, 0, dev, workspace)
     _check("moe_permute_capacity", lib().moe_permute_capacity(
         _p(topk_idx), T, k, E, int(capacity), _p(x), _dtype_code(x), d, _p(counts), _p(offsets), _p(row_of),
-        _p(token_of), _p(x_perm), _p(ws), ws.numel(), _stream(stream)))
+        _p(token_of), _p(x_perm), _p(ws), n, _stream(stream)))
     return counts, offsets, row_of, token_of, x_perm
 
 
@@ -235,14 +253,14 @@ def moe_grouped_ffn(x_rows, offsets, w_gate_up, w_down, gu_saved=None, h=None, y
     _req(w_gate_up, "w_gate_up", x_rows.dtype, (G, 2 * f, d))
     _req(w_down, "w_down", x_rows.dtype, (G, d, f))
     dev = x_rows.device
-    if save_gu and gu_saved is None:
-        gu_saved = torch.empty((rows, 2 * f), dtype=x_rows.dtype, device=dev)
-    h = torch.empty((rows, f), dtype=x_rows.dtype, device=dev) if h is None else h
-    y = torch.empty((rows, d), dtype=torch.float32, device=dev) if y is None else y
+    if save_gu or gu_saved is not None:
+        gu_saved = _out(gu_saved, "gu_saved", x_rows.dtype, (rows, 2 * f), dev)
+    h = _out(h, "h", x_rows.dtype, (rows, f), dev)
+    y = _out(y, "y", torch.float32, (rows, d), dev)
     ws, n = _workspace(MOE_CALL_GROUPED_FFN, rows, 1, G, d, f, dev, workspace)
     _check("moe_grouped_ffn", lib().moe_grouped_ffn(_p(x_rows), rows, d, _dtype_code(x_rows), _p(offsets), G, f,
                                                     _p(w_gate_up), _p(w_down), _p(gu_saved), _p(h), _p(y),
-                                                    _p(ws), ws.numel(), _stream(stream)))
+                                                    _p(ws), n, _stream(stream)))
     return gu_saved, h, y
 
 
@@ -254,7 +272,7 @@ def moe_combine(y_perm, row_of, topk_gate, shared_y=None, out=None, out_dtype=to
     _req(topk_gate, "topk_gate", torch.float32, (T, k))
     if shared_y is not None:
         _req(shared_y, "shared_y", torch.float32, (T, d))
-    out = torch.empty((T, d), dtype=out_dtype, device=y_perm.device) if out is None else out
+    out = _out(out, "out", out_dtype if out is None else out.dtype, (T, d), y_perm.device)
     _check("moe_combine", lib().moe_combine(_p(y_perm), _p(row_of), _p(topk_gate), _p(shared_y), T, k, d,
                                             _p(out), _dtype_code(out), _stream(stream)))
     return out
@@ -275,11 +293,13 @@ def moe_aux_loss(logits, counts, k, score_fn, alpha, loss_out=None, p_mean_out=N
     _req(logits, "logits", torch.float32)
     _req(counts, "counts", torch.int32, (E,))
     dev = logits.device
-    loss_out = torch.empty(1, dtype=torch.float32, device=dev) if loss_out is None else loss_out
+    loss_out = _out(loss_out, "loss_out", torch.float32, (1,), dev)
+    if p_mean_out is not None:
+        p_mean_out = _out(p_mean_out, "p_mean_out", torch.float32, (E,), dev)
     ws, n = _workspace(MOE_CALL_AUX_LOSS, T, k, E, 0, 0, dev, workspace)
     sf = SCORE[score_fn] if isinstance(score_fn, str) else int(score_fn)
     _check("moe_aux_loss", lib().moe_aux_loss(_p(logits), _p(counts), T, E, k, sf, float(alpha), _p(loss_out),
-                                              _p(p_mean_out), _p(ws), ws.numel(), _stream(stream)))
+                                              _p(p_mean_out), _p(ws), n, _stream(stream)))
     return loss_out
 
 
