@@ -364,16 +364,24 @@ def forward(x, w_router, w_gate_up, w_down, k: int, score_fn: str, bf16_points: 
 
 
 def _gates_for(r: dict, idx: np.ndarray, score_fn: str) -> np.ndarray:
+    """Gates of a given choice.  An expert id outside [0, E) (a replayed choice
+    may hold one) gets gate 0 and is left out of the normalisation; it has no
+    expert row either (``permute``)."""
     T, k = idx.shape
-    g = np.empty((T, k))
+    E = r["logits"].shape[1]
+    valid = (idx >= 0) & (idx < E)
+    g = np.zeros((T, k))
     for t in range(T):
+        v = valid[t]
+        if not v.any():
+            continue
         if score_fn == "softmax":
-            raw = r["logits"][t, idx[t]]
+            raw = r["logits"][t, idx[t, v]]
             ex = np.exp(raw - raw.max())
-            g[t] = ex / ex.sum()
+            g[t, v] = ex / ex.sum()
         else:
-            sc = r["scores"][t, idx[t]]
-            g[t] = sc / sc.sum()
+            sc = r["scores"][t, idx[t, v]]
+            g[t, v] = sc / sc.sum()
     return g
 
 
@@ -474,17 +482,22 @@ def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
         dl = np.zeros((T, k))
         dW_r, dx = np.zeros((E, d)), np.zeros((T, d))
     else:
+        # a slot whose expert id lies outside [0, E) has gate 0 and is out of
+        # the normalisation: score 0 there, and no logit gradient
+        valid = (idx >= 0) & (idx < E)
+        safe = np.where(valid, idx, 0)
         tt = np.arange(T)[:, None]
-        lc = fwd["logits"][tt, idx]
-        sc = fwd["scores"][tt, idx]
-        dl = gate_backward(dg, gates, lc, sc, score_fn)
+        lc = fwd["logits"][tt, safe]
+        sc = np.where(valid, fwd["scores"][tt, safe], 0.0)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            dl = np.where(valid, gate_backward(dg, gates, lc, sc, score_fn), 0.0)
         if aux_alpha:
             dL = np.zeros((T, E))
-            np.add.at(dL, (np.arange(T)[:, None].repeat(k, 1), idx), dl)
+            np.add.at(dL, (np.arange(T)[:, None].repeat(k, 1), safe), dl)
             dL += aux_grad_logits(fwd["logits"], fwd["counts"], k, score_fn, aux_alpha)
             dW_r, dx = dL.T @ _f64(x), dL @ np.asarray(w_router, np.float64)
         else:
-            dW_r, dx = router_backward(dl, idx, x, w_router)
+            dW_r, dx = router_backward(dl, safe, x, w_router)
     f = np.asarray(w_down).shape[2]
     dW_gu = np.zeros((E, 2 * f, d))
     dW_d = np.zeros((E, d, f))
