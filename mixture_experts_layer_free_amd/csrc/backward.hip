@@ -84,7 +84,8 @@ __global__ __launch_bounds__(256) void combine_bwd_rows_kernel(const bf16_t* __r
 }
 
 // Gate backward, one wave per token (lanes 0..k-1 hold the chosen experts):
-// dl on the chosen experts from dg = dgp[row_of[t,j]].
+// dl on the chosen experts from dg = dgp[row_of[t,j]].  dg and dl are
+// written for every slot (0 for an expert id outside [0, E)).
 __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__ dgp, const int32_t* __restrict__ row_of,
                                                        const float* __restrict__ gate, const int32_t* __restrict__ idx,
                                                        const float* __restrict__ logits, int T, int k, int E, int fn,
@@ -93,10 +94,14 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const bool act = lane < k;
-  const int myr = act ? row_of[t * k + lane] : 0;
+  // a slot whose expert id lies outside [0, E) (a replayed choice) has gate 0,
+  // is out of the normalisation and gets no gradient
+  const bool slot = lane < k;
+  const int e_in = slot ? idx[t * k + lane] : -1;
+  const bool act = slot && e_in >= 0 && e_in < E;
+  const int myr = slot ? row_of[t * k + lane] : 0;
   const float myg = act ? gate[t * k + lane] : 0.f;
-  const int mye = act ? idx[t * k + lane] : 0;
+  const int mye = act ? e_in : 0;
   const float dg = act && myr >= 0 ? dgp[myr] : 0.f;   // a dropped slot adds nothing to the output
   const int prow = myr >= 0 ? myr : (myr == INT32_MIN ? -1 : ~myr);   // its x_perm row, kept or dropped
   const float D = wave_sum(act ? myg * dg : 0.f);
@@ -113,10 +118,10 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
     if (fn == MOE_SIGMOID_NORM) dl = ds * s * (1.0f - s);
     else dl = ds * (1.0f / (1.0f + expf(-l))) / (2.0f * s);
   }
-  if (act) {
-    dg_out[t * k + lane] = dg;
-    dl_out[t * k + lane] = dl;
-    if (prow >= 0) dl_perm[prow] = dl;
+  if (slot) {
+    dg_out[t * k + lane] = act ? dg : 0.f;
+    dl_out[t * k + lane] = act ? dl : 0.f;
+    if (act && prow >= 0) dl_perm[prow] = dl;
   }
 }
 
@@ -244,13 +249,14 @@ template <int K, bool ROUTER>
 __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restrict__ dx_perm,
                                                             const int32_t* __restrict__ row_of,
                                                             const int32_t* __restrict__ idx, const float* __restrict__ dl,
-                                                            const f32x4* __restrict__ w_router, int T, int64_t nv,
-                                                            f32x4* __restrict__ dx) {
+                                                            const f32x4* __restrict__ w_router, int T, int E,
+                                                            int64_t nv, f32x4* __restrict__ dx) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int myr = lane < K ? row_of[t * K + lane] : 0;
-  const int mye = lane < K ? idx[t * K + lane] : 0;
+  const int e_in = lane < K ? idx[t * K + lane] : 0;
+  const int mye = e_in >= 0 && e_in < E ? e_in : 0;   // an id outside [0, E) has dl = 0: any row serves
   const float myl = lane < K ? dl[t * K + lane] : 0.f;
   const f32x4* xr[K];
   const f32x4* wr[K];
@@ -448,10 +454,10 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
     if (router)                                                                                                 \
       unpermute_bwd_kernel<K, true><<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(                                   \
           reinterpret_cast<const f32x4*>(dx_perm), a->row_of, a->topk_idx, dl,                                  \
-          reinterpret_cast<const f32x4*>(a->w_router), (int)T, d / 4, reinterpret_cast<f32x4*>(a->dx));         \
+          reinterpret_cast<const f32x4*>(a->w_router), (int)T, E, d / 4, reinterpret_cast<f32x4*>(a->dx));      \
     else                                                                                                        \
       unpermute_bwd_kernel<K, false><<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(                                  \
-          reinterpret_cast<const f32x4*>(dx_perm), a->row_of, a->topk_idx, dl, nullptr, (int)T, d / 4,          \
+          reinterpret_cast<const f32x4*>(dx_perm), a->row_of, a->topk_idx, dl, nullptr, (int)T, E, d / 4,       \
           reinterpret_cast<f32x4*>(a->dx));                                                                     \
   } while (0)
   MOE_DISPATCH_K(k, MOE_UBWD);

@@ -214,3 +214,36 @@ def test_backward_full_training_shape():
         say(f"  expert {e}: {b - a} rows")
         check_close(host(layer.dw_down[e]), r["dW_down"], "bf16", f"dW_down[{e}]")
         check_close(host(layer.dw_gate_up[e]), r["dW_gate_up"], "bf16", f"dW_gate_up[{e}]")
+
+
+@pytest.mark.parametrize("score", oracle.SCORE_FNS)
+def test_backward_replay_invalid_ids(score):
+    """Training on a replayed choice in which some expert ids lie outside
+    [0, E): those slots have gate 0, no row and no gradient, and every other
+    gradient is the oracle's for the same choice."""
+    say(f"[backward replay with invalid ids {score}]")
+    cfg = scaled(CONFIGS["train"], T=500, d=128, E=16, k=4, f=64, score=score, bias="uniform")
+    inp = make_inputs(cfg)
+    rng = np.random.default_rng(7)
+    ridx = np.stack([rng.permutation(cfg.E)[:cfg.k] for _ in range(cfg.T)]).astype(np.int64)
+    bad = rng.random(ridx.shape) < 0.2
+    ridx[bad] = rng.choice([-1, -100, cfg.E, 1 << 20], int(bad.sum()))
+    ridx[:3] = -1                                   # tokens with no valid slot
+    layer = _layer(cfg, inp)
+    x = dev(inp["x"])
+    layer.forward(x, replay_idx=dev(ridx.astype(np.int32)))
+    layer.backward(x, dev(inp["dy"]))
+    torch.cuda.synchronize()
+    fwd = oracle.forward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], cfg.k, score, True,
+                         logit_offset=inp["logit_offset"], idx=ridx)
+    g = oracle.backward(fwd, inp["dy"], inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], score, True)
+    valid = (ridx >= 0) & (ridx < cfg.E)
+    assert np.all(host(layer.gate)[~valid] == 0) and np.all(host(layer.dlogit)[~valid] == 0)
+    assert np.all(host(layer.dgate)[~valid] == 0)
+    check_close(host(layer.out), fwd["out"], "bf16", "out")
+    check_close(host(layer.dgate), g["dg"], "bf16", "dg")
+    check_close(host(layer.dlogit), g["dl"], "bf16", "dl")
+    check_close(host(layer.dx), g["dx"], "bf16", "dx")
+    check_close(host(layer.dw_router), g["dw_router"], "bf16", "dW_router")
+    check_close(host(layer.dw_down), g["dw_down"], "bf16", "dW_down")
+    check_close(host(layer.dw_gate_up), g["dw_gate_up"], "bf16", "dW_gate_up")
