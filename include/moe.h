@@ -298,6 +298,9 @@ moe_status moe_aux_loss(const float* logits, const int32_t* counts, int64_t T, i
  *             dX_perm = dG W_gate + dU W_up
  *   unpermute: dx[t] = sum_j dX_perm[row_of[t,j]] + dx_r[t]
  * All pointers are device pointers held in a HOST struct.  bf16 layers only.
+ * A slot whose expert id lies outside [0, E) (a choice replayed through
+ * moe_route_replay) has gate 0 and no row: it gets dg = dl = 0 and adds
+ * nothing to any gradient.
  * score_fn MOE_UNIFORM_GATES (hash routing): dl = 0, there is no router term
  * in dx, w_router / logits may be NULL, and dw_router (if not NULL) is
  * set to zero.
