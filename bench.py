@@ -176,17 +176,19 @@ def measured_traffic(workload):
     return t.get("workloads", {}).get(workload)
 
 
-def algorithmic(cfg):
+def algorithmic(cfg, fused=False):
     """Per library call: (flops, bytes, peak TFLOP/s of its arithmetic) that
     the method itself needs -- every tensor read or written once, weights
-    once, intermediates written once and read once."""
+    once, intermediates written once and read once.  fused: the permute is
+    fused into the expert GEMM (indices only; the GEMM reads x, not X_perm)."""
     T, d, E, k, f, A = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.T * cfg.k
     xb = 2 if cfg.dtype == "bf16" else 4
     gu = A * 2 * f * 2 if cfg.train else 0                  # saved G|U (training)
+    rows_in = T * d * xb if fused else A * d * xb           # the up-projection's input rows
     out = {
         "route": (2.0 * T * d * E, T * d * xb + E * d * 4 + T * E * 4 + T * k * 8, 157.3),
-        "permute": (0, T * d * xb + A * d * xb + T * k * 8 + A * 4, None),
-        "grouped_ffn": (6.0 * A * d * f, A * d * xb + 3 * E * d * f * xb + 2 * A * f * xb + A * d * 4 + gu,
+        "permute": (0, (0 if fused else T * d * xb + A * d * xb) + T * k * 8 + A * 4, None),
+        "grouped_ffn": (6.0 * A * d * f, rows_in + 3 * E * d * f * xb + 2 * A * f * xb + A * d * 4 + gu,
                         PEAK_BF16_TFLOPS),
         "combine": (0, A * d * 4 + T * d * 4 * (2 if cfg.shared else 1) + T * k * 8, None),
         "bias_update": (0, E * 12, None),
@@ -258,7 +260,8 @@ def fwd_line(_lib, a, device):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / a.steps * 1e3
     log(f"[bench] forward line: {ms:.3f} ms/step")
-    return {"workload": describe(cfg, False), "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+    return {"workload": describe(cfg, False) + ", permute fused into the expert GEMM",
+            "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
             "ms_per_step": round(ms, 4), "expert_tflops": round(expert_flops(cfg, False) / (ms * 1e-3) / 1e12, 1)}
 
 
@@ -336,6 +339,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--no-fwd", action="store_true", help="skip the forward-only line on the 64-expert shape")
+    ap.add_argument("--no-fuse-permute", action="store_true",
+                    help="forward workloads: copy X_perm (moe_permute) instead of the expert GEMM gathering x rows")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs of this bench into profiles/traffic.json")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "STEPS"),
@@ -390,7 +395,7 @@ def main():
     inp = make_inputs(cfg)
     d = lambda k: _dev(inp.get(k), device)
     shape = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, torch.bfloat16, cfg.score, cfg.shared, cfg.f_shared,
-                  cfg.bias_update, cfg.gamma, train)
+                  cfg.bias_update, cfg.gamma, train, fuse_permute=not a.no_fuse_permute)
     layer = MoELayer(shape, d("w_router"), d("w_gate_up"), d("w_down"), d("bias"), d("logit_offset"),
                      d("w_gate_up_shared"), d("w_down_shared"), device=device)
     x = d("x")
@@ -436,7 +441,8 @@ def main():
     # per-call rooflines: algorithmic work per call / the call's event time
     traffic = measured_traffic(cfg.name)
     rooflines = {}
-    for call, (flops, nbytes, peak_flops) in algorithmic(cfg).items():
+    fused = not train and not a.no_fuse_permute
+    for call, (flops, nbytes, peak_flops) in algorithmic(cfg, fused).items():
         if call not in calls:
             continue
         t = calls[call] * 1e-3
@@ -456,7 +462,9 @@ def main():
     res = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
            "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": describe(cfg, train), "global_batch": cfg.T, "seq_len": None,
+           "config": {"workload": describe(cfg, train) + (", permute fused into the expert GEMM"
+                                                          if not a.no_fuse_permute and not train else ""),
+                      "global_batch": cfg.T, "seq_len": None,
                       "parallelism": "none (1 GPU)"},
            "eager_ms_per_step": round(eager_ms, 4), "step_mode": "eager" if a.no_graph else "hip_graph_replay",
            "calls_ms": calls, "expert_tflops": round(expert_flops(cfg, train) / (ms * 1e-3) / 1e12, 1),

@@ -155,7 +155,9 @@ moe_status moe_route_hash(const int32_t* token_ids, int64_t T, int E, int k, uin
  *                       (INT32_MIN for an expert id outside [0, E): that
  *                       assignment has no row and is skipped downstream)
  *   token_of [T*k]      int32 out: token of each x_perm row
- *   x_perm   [T*k, d]   out: x_perm[r] = x[token_of[r]] (bit copy)
+ *   x_perm   [T*k, d]   out: x_perm[r] = x[token_of[r]] (bit copy), or NULL:
+ *                       indices only, no copy (for moe_grouped_ffn_gather,
+ *                       which reads x through token_of); x may then be NULL
  *   workspace           moe_workspace_size(MOE_CALL_PERMUTE, T, k, E, d, 0)
  * ENOTSUP: E > MOE_MAX_EXPERTS, k > MOE_MAX_TOPK, T*k >= 2^31, d*elem not a
  * multiple of 16 bytes.
@@ -229,6 +231,27 @@ moe_status moe_grouped_ffn(const void* x_rows, int64_t rows, int64_t d, int dtyp
                            const void* w_gate_up, const void* w_down,
                            void* gu_saved, void* h, float* y,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_grouped_ffn_gather — moe_grouped_ffn on the unpermuted input: GEMM
+ * row r reads row token_of[r] of x (the permute fused into the expert GEMM's
+ * operand loads).  The AREX article on The Ultimate MoE Training Handbook, in
+ * its paragraph on the handbook's section 3.7, reports that fusing the
+ * permute cut the permute/copy kernels' share of the step; with this call a
+ * forward pass runs moe_permute with x_perm = NULL and never writes X_perm.
+ *   x          [T, d]        dtype, the layer input
+ *   token_of   [rows]        int32 device, from moe_permute (values in
+ *                            [0, T); an index outside reads as a zero row)
+ *   rows, offsets, w_gate_up, w_down, gu_saved, h, y, workspace: as
+ *                            moe_grouped_ffn (h, y, gu_saved in permuted
+ *                            row order)
+ * Errors as moe_grouped_ffn; EINVAL for a NULL token_of; ENOTSUP (bf16) when
+ * T*d*2 >= 2^31 (x is addressed through one buffer resource).
+ */
+moe_status moe_grouped_ffn_gather(const void* x, int64_t T, const int32_t* token_of, int64_t rows, int64_t d,
+                                  int dtype, const int32_t* offsets, int G, int64_t f,
+                                  const void* w_gate_up, const void* w_down, void* gu_saved, void* h, float* y,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * moe_combine — gate-weighted sum of each token's expert outputs.

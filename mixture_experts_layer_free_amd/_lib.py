@@ -46,6 +46,8 @@ _SIGS = {
     "moe_permute": [_vp, _i64, _int, _int, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_permute_capacity": [_vp, _i64, _int, _int, _i64, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_grouped_ffn": [_vp, _i64, _i64, _int, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_grouped_ffn_gather": [_vp, _i64, _vp, _i64, _i64, _int, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                               _vp],
     "moe_combine": [_vp, _vp, _vp, _vp, _i64, _int, _i64, _vp, _int, _vp],
     "moe_bias_update": [_vp, _vp, _int, _i64, _int, ctypes.c_float, _vp],
     "moe_aux_loss": [_vp, _vp, _i64, _int, _int, _int, ctypes.c_float, _vp, _vp, _vp, _sz, _vp],
@@ -202,7 +204,8 @@ def moe_route_hash(token_ids, E, k, salt=0, topk_idx=None, topk_gate=None, strea
 
 
 def moe_permute(topk_idx, x, E, counts=None, offsets=None, row_of=None, token_of=None, x_perm=None,
-                workspace=None, stream=None):
+                workspace=None, stream=None, copy=True):
+    """copy=False: indices only (x_perm is not written and comes back None)."""
     T, k = topk_idx.shape
     d = x.shape[1]
     _req(topk_idx, "topk_idx", torch.int32)
@@ -213,8 +216,10 @@ def moe_permute(topk_idx, x, E, counts=None, offsets=None, row_of=None, token_of
     offsets = _out(offsets, "offsets", torch.int32, (E + 1,), dev)
     row_of = _out(row_of, "row_of", torch.int32, (T, k), dev)
     token_of = _out(token_of, "token_of", torch.int32, (A,), dev)
-    x_perm = _out(x_perm, "x_perm", x.dtype, (A, d), dev)
+    x_perm = _out(x_perm, "x_perm", x.dtype, (A, d), dev) if copy else None
     ws, n = _workspace(MOE_CALL_PERMUTE, T, k, E, d, 0, dev, workspace)
+    if not copy:
+        x_perm = None
     _check("moe_permute", lib().moe_permute(_p(topk_idx), T, k, E, _p(x), _dtype_code(x), d, _p(counts),
                                             _p(offsets), _p(row_of), _p(token_of), _p(x_perm), _p(ws),
                                             n, _stream(stream)))
@@ -222,9 +227,10 @@ def moe_permute(topk_idx, x, E, counts=None, offsets=None, row_of=None, token_of
 
 
 def moe_permute_capacity(topk_idx, x, E, capacity, counts=None, offsets=None, row_of=None, token_of=None,
-                         x_perm=None, workspace=None, stream=None):
+                         x_perm=None, workspace=None, stream=None, copy=True):
     """moe_permute with an expert capacity in rows (< 0: none).  row_of holds ~r
-    for a dropped assignment; offsets cover the kept rows."""
+    for a dropped assignment; offsets cover the kept rows.  copy=False: indices
+    only."""
     T, k = topk_idx.shape
     d = x.shape[1]
     _req(topk_idx, "topk_idx", torch.int32)
@@ -235,8 +241,10 @@ def moe_permute_capacity(topk_idx, x, E, capacity, counts=None, offsets=None, ro
     offsets = _out(offsets, "offsets", torch.int32, (E + 1,), dev)
     row_of = _out(row_of, "row_of", torch.int32, (T, k), dev)
     token_of = _out(token_of, "token_of", torch.int32, (A,), dev)
-    x_perm = _out(x_perm, "x_perm", x.dtype, (A, d), dev)
+    x_perm = _out(x_perm, "x_perm", x.dtype, (A, d), dev) if copy else None
     ws, n = _workspace(MOE_CALL_PERMUTE, T, k, E, d, 0, dev, workspace)
+    if not copy:
+        x_perm = None
     _check("moe_permute_capacity", lib().moe_permute_capacity(
         _p(topk_idx), T, k, E, int(capacity), _p(x), _dtype_code(x), d, _p(counts), _p(offsets), _p(row_of),
         _p(token_of), _p(x_perm), _p(ws), n, _stream(stream)))
@@ -261,6 +269,30 @@ def moe_grouped_ffn(x_rows, offsets, w_gate_up, w_down, gu_saved=None, h=None, y
     _check("moe_grouped_ffn", lib().moe_grouped_ffn(_p(x_rows), rows, d, _dtype_code(x_rows), _p(offsets), G, f,
                                                     _p(w_gate_up), _p(w_down), _p(gu_saved), _p(h), _p(y),
                                                     _p(ws), n, _stream(stream)))
+    return gu_saved, h, y
+
+
+def moe_grouped_ffn_gather(x, token_of, offsets, w_gate_up, w_down, gu_saved=None, h=None, y=None, save_gu=False,
+                           workspace=None, stream=None):
+    """moe_grouped_ffn on rows token_of[r] of x (the permute fused into the GEMM)."""
+    T, d = x.shape
+    rows = token_of.shape[0]
+    G = offsets.shape[0] - 1
+    f = w_down.shape[2]
+    _req(x, "x")
+    _req(token_of, "token_of", torch.int32, (rows,))
+    _req(offsets, "offsets", torch.int32)
+    _req(w_gate_up, "w_gate_up", x.dtype, (G, 2 * f, d))
+    _req(w_down, "w_down", x.dtype, (G, d, f))
+    dev = x.device
+    if save_gu or gu_saved is not None:
+        gu_saved = _out(gu_saved, "gu_saved", x.dtype, (rows, 2 * f), dev)
+    h = _out(h, "h", x.dtype, (rows, f), dev)
+    y = _out(y, "y", torch.float32, (rows, d), dev)
+    ws, n = _workspace(MOE_CALL_GROUPED_FFN, rows, 1, G, d, f, dev, workspace)
+    _check("moe_grouped_ffn_gather", lib().moe_grouped_ffn_gather(
+        _p(x), T, _p(token_of), rows, d, _dtype_code(x), _p(offsets), G, f, _p(w_gate_up), _p(w_down),
+        _p(gu_saved), _p(h), _p(y), _p(ws), n, _stream(stream)))
     return gu_saved, h, y
 
 

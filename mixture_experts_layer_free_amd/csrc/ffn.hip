@@ -7,19 +7,19 @@
 // finer experts mean smaller GEMMs that cost step time: the kernels below are
 // built so that many small, unequal expert GEMMs still fill the chip.
 //
-// bf16 path: two grouped GEMMs on v_mfma_f32_32x32x16_bf16 with fp32
-// accumulation, both "NT" (activations and nn.Linear weights are both
+// bf16 path: two grouped GEMMs (gemm.h) on v_mfma_f32_32x32x16_bf16 with
+// fp32 accumulation, both "NT" (activations and nn.Linear weights are both
 // contiguous along the reduction dimension):
 //   up:   [G | U] = X W_gu^T, epilogue H = silu(G) * U (bf16), optionally G, U
 //   down: Y = H W_down^T (fp32 out)
-// Tiles are 128 rows x 128 weight rows x 64 deep, 4 waves of 64x64, LDS
-// double-buffered with a register prefetch.  The tile list is built on the
-// device from the expert offsets (no host sync): expert e owns
-// ceil(n_e/128) row tiles; tiles are ordered (expert, column block, row
-// tile), so consecutive tiles share the weight panel.  The kernel is
-// persistent: workgroup i sits on XCD i%8 and takes, in each round, a tile
-// from that XCD's contiguous share of the round, so tiles that reuse a weight
-// panel run on one XCD and hit its L2.
+// The row-tile prefix sums are built on the device from the expert offsets
+// (no host sync); the GEMM kernel is persistent and XCD-aware (gemm.h).
+//
+// Fused permute (moe_grouped_ffn_gather): the AREX article on The Ultimate
+// MoE Training Handbook reports, in its paragraph on the handbook's section
+// 3.7, that fusing the permute shrank the permute/copy kernels' share of the
+// step.  Here the up-projection's operand loads fetch row token_of[r] of x
+// for GEMM row r, so no permuted copy of x is written or read.
 #include "gemm.h"
 
 namespace {
@@ -57,7 +57,10 @@ __device__ __forceinline__ int group_of_row(const int32_t* __restrict__ offsets,
   return lo;
 }
 
+// row_token (or null): GEMM row r reads row row_token[r] of X, which has
+// x_total rows (an index outside [0, x_total) reads as a zero row)
 __global__ __launch_bounds__(256) void ffn_up_f32_kernel(const float* __restrict__ X, int64_t rows, int64_t d,
+                                                         const int32_t* __restrict__ row_token, int64_t x_total,
                                                          const int32_t* __restrict__ offsets, int G, int64_t f,
                                                          const float* __restrict__ Wgu, float* __restrict__ gu,
                                                          float* __restrict__ H) {
@@ -66,11 +69,13 @@ __global__ __launch_bounds__(256) void ffn_up_f32_kernel(const float* __restrict
   const int64_t row = id / f, n = id % f;
   if (row >= offsets[G]) return;   // rows past the last group (e.g. dropped by a capacity) are not touched
   const int g = group_of_row(offsets, G, (int)row);
-  const float* xr = X + row * d;
+  const int64_t xrow = row_token ? (int64_t)row_token[row] : row;
+  const bool in = xrow >= 0 && xrow < x_total;
+  const float* xr = X + (in ? xrow : 0) * d;
   const float* wg = Wgu + (int64_t)g * 2 * f * d + n * d;
   const float* wu = wg + f * d;
   float a = 0.f, b = 0.f;
-  for (int64_t i = 0; i < d; ++i) {
+  for (int64_t i = 0; in && i < d; ++i) {
     a = fmaf(xr[i], wg[i], a);
     b = fmaf(xr[i], wu[i], b);
   }
@@ -119,9 +124,11 @@ moe_status moe_tile_schedule_launch(const int32_t* offsets, int G, int bm, int32
 }
 
 // Tile schedule plus the two bf16 expert GEMMs of a grouped SwiGLU FFN.
-moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, const int32_t* offsets, int32_t* mt_prefix,
-                               int G, int64_t f, const bf16_t* wgu, const bf16_t* wd, bf16_t* gu, bf16_t* h, float* y,
-                               hipStream_t s) {
+// row_token (or null): GEMM row r of the up-projection reads row
+// row_token[r] of x_rows, which then has x_total rows.
+moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, const int32_t* row_token, int64_t x_total,
+                               const int32_t* offsets, int32_t* mt_prefix, int G, int64_t f, const bf16_t* wgu,
+                               const bf16_t* wd, bf16_t* gu, bf16_t* h, float* y, hipStream_t s) {
   using namespace moe_gemm;
   const bool large = use_large_rows(rows, G, f);
   moe_status st = moe_tile_schedule_launch(offsets, G, large ? BM_LARGE : BM, mt_prefix, s);
@@ -141,6 +148,8 @@ moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, co
   a.out = h;
   a.ldo = f;
   a.gu_out = gu;
+  a.a_rows = row_token;
+  a.a_rows_total = x_total;
   st = launch_gemm<true, true, false, EPI_SWIGLU>(a, large, rows, s);
   if (st != MOE_OK) return st;
   Args b{};
@@ -160,30 +169,53 @@ moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, co
   return launch_gemm<true, true, false, EPI_F32>(b, large, rows, s);
 }
 
-extern "C" moe_status moe_grouped_ffn(const void* x_rows, int64_t rows, int64_t d, int dtype, const int32_t* offsets, int G,
-                                      int64_t f, const void* w_gate_up, const void* w_down, void* gu_saved, void* h, float* y,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
-  if (!x_rows || !offsets || !w_gate_up || !w_down || !h || !y) return MOE_EINVAL;
-  if (rows < 1 || d < 1 || f < 1 || G < 1) return MOE_EINVAL;
+namespace {
+
+moe_status grouped_ffn_impl(const void* x, int64_t x_total, const int32_t* row_token, int64_t rows, int64_t d,
+                            int dtype, const int32_t* offsets, int G, int64_t f, const void* w_gate_up,
+                            const void* w_down, void* gu_saved, void* h, float* y, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!x || !offsets || !w_gate_up || !w_down || !h || !y) return MOE_EINVAL;
+  if (rows < 1 || d < 1 || f < 1 || G < 1 || x_total < 1) return MOE_EINVAL;
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EINVAL;
   if (G > MOE_MAX_EXPERTS || rows >= (1ll << 31)) return MOE_ENOTSUP;
   hipStream_t s = moe_stream(stream);
   if (dtype == MOE_BF16) {
     if (d % 64 != 0 || f % 64 != 0) return MOE_ENOTSUP;
     if (2 * f * d * 2 >= (1ll << 31)) return MOE_ENOTSUP;   // one expert's weight must fit a buffer resource
+    // gathered rows are addressed through one buffer resource over all of x
+    if (row_token && x_total * d * 2 >= (1ll << 31)) return MOE_ENOTSUP;
     if (!workspace || workspace_bytes < moe_ffn_workspace(G)) return MOE_EWORKSPACE;
     int32_t* mt_prefix = static_cast<int32_t*>(workspace);
-    return moe_ffn_bf16_launch(static_cast<const bf16_t*>(x_rows), rows, d, offsets, mt_prefix, G, f,
+    return moe_ffn_bf16_launch(static_cast<const bf16_t*>(x), rows, d, row_token, x_total, offsets, mt_prefix, G, f,
                                static_cast<const bf16_t*>(w_gate_up), static_cast<const bf16_t*>(w_down),
                                static_cast<bf16_t*>(gu_saved), static_cast<bf16_t*>(h), y, s);
   }
   if (d % 4 != 0) return MOE_ENOTSUP;
   ffn_up_f32_kernel<<<(unsigned)ceil_div(rows * f, 256), 256, 0, s>>>(
-      static_cast<const float*>(x_rows), rows, d, offsets, G, f, static_cast<const float*>(w_gate_up),
+      static_cast<const float*>(x), rows, d, row_token, x_total, offsets, G, f, static_cast<const float*>(w_gate_up),
       static_cast<float*>(gu_saved), static_cast<float*>(h));
   MOE_LAUNCH_CHECK();
   ffn_down_f32_kernel<<<(unsigned)ceil_div(rows * d, 256), 256, 0, s>>>(static_cast<const float*>(h), rows, d, offsets, G,
                                                                         f, static_cast<const float*>(w_down), y);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" moe_status moe_grouped_ffn(const void* x_rows, int64_t rows, int64_t d, int dtype, const int32_t* offsets, int G,
+                                      int64_t f, const void* w_gate_up, const void* w_down, void* gu_saved, void* h, float* y,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return grouped_ffn_impl(x_rows, rows, nullptr, rows, d, dtype, offsets, G, f, w_gate_up, w_down, gu_saved, h, y,
+                          workspace, workspace_bytes, stream);
+}
+
+extern "C" moe_status moe_grouped_ffn_gather(const void* x, int64_t T, const int32_t* token_of, int64_t rows, int64_t d,
+                                             int dtype, const int32_t* offsets, int G, int64_t f, const void* w_gate_up,
+                                             const void* w_down, void* gu_saved, void* h, float* y, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  if (!token_of) return MOE_EINVAL;
+  return grouped_ffn_impl(x, T, token_of, rows, d, dtype, offsets, G, f, w_gate_up, w_down, gu_saved, h, y, workspace,
+                          workspace_bytes, stream);
 }

@@ -75,6 +75,10 @@ struct Args {
   int64_t out_group;         // K-grouped: elements between groups' outputs
   const bf16_t* gu_in;       // SwiGLU-bwd: saved [rows, 2N] G|U
   bf16_t* gu_out;            // SwiGLU: G|U save (or null); SwiGLU-bwd: dG|dU out
+  // SwiGLU (up-projection) only: when set, GEMM row r reads row a_rows[r] of
+  // A, which has a_rows_total rows (the permute fused into the operand load)
+  const int32_t* a_rows;
+  int64_t a_rows_total;
 };
 
 typedef __attribute__((address_space(3))) void lds_t;
@@ -84,6 +88,18 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int n = bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0 : (int)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+// Wave-uniform copies of values that are uniform by construction: a buffer
+// resource the compiler cannot prove uniform costs a loop over the lanes at
+// every load that uses it.
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+__device__ __forceinline__ int64_t uni(int64_t v) {
+  const uint32_t lo = uni((uint32_t)(uint64_t)v), hi = uni((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ const void* uni(const void* ptr) {
+  return reinterpret_cast<const void*>((uintptr_t)uni((int64_t)(uintptr_t)ptr));
 }
 
 template <int N>
@@ -204,7 +220,19 @@ void gemm_kernel(Args p) {
     int64_t a_bytes, b_bytes;
     uint32_t a_voff[LA], b_voff[LB];
     uint32_t a_step, b_step;   // bytes per slab
-    if (AK) {
+    if (AK && !KG && EPI == EPI_SWIGLU && p.a_rows) {   // only the up-projection gathers
+      // gathered rows: the buffer spans all of A, a row past the group's end
+      // gets an offset past the buffer (its loads read zeros)
+      a_base = p.A;
+      a_bytes = p.a_rows_total * p.lda * 2;
+      a_step = BK * 2;
+#pragma unroll
+      for (int q = 0; q < LA; ++q) {
+        const int r = (wave * LA + q) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swz_kc(r);
+        a_voff[q] = row0 + r < row_end ? (uint32_t)((int64_t)p.a_rows[row0 + r] * p.lda * 2 + c * 16) : 0x80000000u;
+      }
+    } else if (AK) {
       const int64_t a_rows = row_end - row0 < TM ? row_end - row0 : TM;
       a_base = p.A + row0 * p.lda;
       a_bytes = a_rows * p.lda * 2;
@@ -265,13 +293,13 @@ void gemm_kernel(Args p) {
     // lane-linearly.  The host compilation pass only needs this kernel's
     // signature (for its launch stub) and cannot type the LDS-pointer cast,
     // so the statement exists in the device pass only.
+    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(uni(a_base), uni(a_bytes));
+    const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(uni(b_base), uni(b_bytes));
 #if defined(__HIP_DEVICE_COMPILE__)
 #define MOE_ISSUE(slab_)                                                                             \
   do {                                                                                               \
     const int slab = (slab_);                                                                        \
     const bool live_ = slab < nk;   /* a slab past the end is pushed out of range: its loads read zeros */ \
-    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a_base, a_bytes);                                  \
-    const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(b_base, b_bytes);                                  \
     char* st_ = smem + (slab % STAGES) * STAGE;                                                      \
     _Pragma("unroll") for (int q = 0; q < LA; ++q)                                                   \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_t*)(st_ + (wave * LA + q) * 1024), 16, a_voff[q], \

@@ -211,7 +211,9 @@ extern "C" moe_status moe_permute_capacity(const int32_t* topk_idx, int64_t T, i
                                            const void* x, int x_dtype, int64_t d, int32_t* counts, int32_t* offsets,
                                            int32_t* row_of, int32_t* token_of, void* x_perm, void* workspace,
                                            size_t workspace_bytes, void* stream) {
-  if (!topk_idx || !x || !counts || !offsets || !row_of || !token_of || !x_perm) return MOE_EINVAL;
+  // x_perm NULL: indices only (a consumer that gathers rows through token_of
+  // needs no copy), and then x may be NULL too
+  if (!topk_idx || !counts || !offsets || !row_of || !token_of || (x_perm && !x)) return MOE_EINVAL;
   if (T < 1 || d < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EINVAL;
   const int64_t es = x_dtype == MOE_BF16 ? 2 : 4;
@@ -232,6 +234,7 @@ extern "C" moe_status moe_permute_capacity(const int32_t* topk_idx, int64_t T, i
   MOE_LAUNCH_CHECK();
   perm_index_kernel<<<nchunks, PCH, 0, s>>>(topk_idx, A, k, E, nchunks, cap, hist, offsets, doff, row_of, token_of);
   MOE_LAUNCH_CHECK();
+  if (!x_perm) return MOE_OK;
   const int64_t nvec = d * es / 16;
 #define MOE_PCOPY(K)                                                                                       \
   perm_copy_kernel<K><<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(static_cast<const u32x4*>(x), T, nvec, row_of, \

@@ -73,6 +73,24 @@ def test_grouped_ffn_validation(L):
     assert lib.moe_grouped_ffn(*a(wsb=0)) == L.MOE_EWORKSPACE
 
 
+def test_grouped_ffn_gather_validation(L):
+    lib = L.lib()
+    need = L.workspace_size(L.MOE_CALL_GROUPED_FFN, 512, 1, 4, 128, 128)
+    a = lambda **kw: [P, kw.get("T", 256), kw.get("tok", P), 512, kw.get("d", 128), 1, P, 4, 128, P, P, None, P, P,
+                      P, need, None]
+    assert lib.moe_grouped_ffn_gather(*a(tok=None)) == L.MOE_EINVAL
+    assert lib.moe_grouped_ffn_gather(*a(T=0)) == L.MOE_EINVAL
+    assert lib.moe_grouped_ffn_gather(*a(d=96)) == L.MOE_ENOTSUP
+    assert lib.moe_grouped_ffn_gather(*a(T=1 << 23, d=128)) == L.MOE_ENOTSUP   # x past one buffer resource
+
+
+def test_permute_without_copy_needs_no_x(L):
+    lib = L.lib()
+    need = L.workspace_size(L.MOE_CALL_PERMUTE, 1000, 8, 64)
+    # a copy needs x; indices only do not (that call would enqueue, so only the rejection is exercised here)
+    assert lib.moe_permute(P, 1000, 8, 64, None, 1, 64, P, P, P, P, P, P, need, None) == L.MOE_EINVAL
+
+
 def test_combine_and_bias_validation(L):
     lib = L.lib()
     assert lib.moe_combine(None, P, P, None, 10, 2, 64, P, 0, None) == L.MOE_EINVAL

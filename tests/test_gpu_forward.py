@@ -326,6 +326,60 @@ def test_ffn_bf16_many_groups():
     _ffn_case(cfg, offsets, inp["x"], inp["w_gate_up"], inp["w_down"], rows_to_check=check)
 
 
+@pytest.mark.parametrize("T,d,E,k,f", [(300, 128, 8, 2, 64), (1500, 256, 4, 2, 256), (700, 192, 24, 3, 128),
+                                       (64, 32, 8, 2, 64)])
+def test_ffn_gather_equals_permuted_rows(T, d, E, k, f):
+    """The fused permute: moe_grouped_ffn_gather on x through token_of gives
+    bit for bit what moe_grouped_ffn gives on the copied X_perm, and both match
+    the oracle's expert FFN on sampled rows (fp32 for the d = 32 case)."""
+    say(f"[ffn gather T={T} d={d} E={E} k={k} f={f}]")
+    base = CONFIGS["tiny"] if d == 32 else CONFIGS["fine"]
+    cfg = scaled(base, T=T, d=d, E=E, k=k, f=f, bias="uniform", zipf_s=None)
+    inp = make_inputs(cfg)
+    x = dev(inp["x"])
+    idx, _, _ = L.moe_route(x, dev(inp["w_router"]), cfg.k, cfg.score, sel_bias=dev(inp["bias"]))
+    counts, offsets, row_of, token_of, x_perm = L.moe_permute(idx, x, cfg.E)
+    c2, o2, r2, t2, none = L.moe_permute(idx, x, cfg.E, copy=False)
+    torch.cuda.synchronize()
+    assert none is None
+    for u, v in ((counts, c2), (offsets, o2), (row_of, r2), (token_of, t2)):
+        assert torch.equal(u, v)
+    wgu, wd = dev(inp["w_gate_up"]), dev(inp["w_down"])
+    g1, h1, y1 = L.moe_grouped_ffn(x_perm, offsets, wgu, wd, save_gu=True)
+    g2, h2, y2 = L.moe_grouped_ffn_gather(x, token_of, offsets, wgu, wd, save_gu=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(h1, h2) and torch.equal(g1, g2)
+    A = T * k
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([[0, A - 1], rng.integers(0, A, 48)]))
+    off = host(offsets).astype(np.int64)
+    grp = np.searchsorted(off, rows, side="right") - 1
+    xp = host(x_perm)
+    y = host(y2)
+    ref = np.zeros((len(rows), d))
+    for g in np.unique(grp):
+        sel = grp == g
+        ref[sel] = oracle.expert_ffn(xp[rows[sel]], inp["w_gate_up"][g], inp["w_down"][g], cfg.dtype == "bf16")["Y"]
+    check_close(y[rows], ref, _kind(cfg), "Y (gathered)")
+
+
+def test_ffn_gather_out_of_range_token_reads_zero():
+    """A token index outside [0, T) reads as a zero row (bf16 and fp32)."""
+    for base in ("fine", "tiny"):
+        d = 128 if base == "fine" else 32
+        cfg = scaled(CONFIGS[base], T=200, d=d, E=2, k=1, f=64)
+        inp = make_inputs(cfg)
+        tok = np.arange(200, dtype=np.int32)
+        tok[[3, 150]] = [-5, 1 << 20]
+        offsets = np.array([0, 100, 200], np.int32)
+        _, h, y = L.moe_grouped_ffn_gather(dev(inp["x"]), dev(tok), dev(offsets), dev(inp["w_gate_up"]),
+                                           dev(inp["w_down"]))
+        torch.cuda.synchronize()
+        yh = host(y)
+        assert np.all(yh[[3, 150]] == 0) and np.all(host(h).astype(np.float64)[[3, 150]] == 0)
+        assert np.count_nonzero(yh[4]) > 0
+
+
 def test_ffn_ep8_shard():
     """One expert-parallel rank's share of the 256-expert shape: a 32768-token
     global batch routed and permuted on the GPU, the rank's 32 experts (about
@@ -499,6 +553,30 @@ def test_forward_hash_router(name):
     check_close(out, ref["out"], _kind(cfg), "out")
 
 
+@pytest.mark.parametrize("name", ["tiny", "bf16"])
+def test_forward_fused_permute(name):
+    """The layer with the permute fused into the expert GEMM (no X_perm) gives
+    the same output as with the copy, and the oracle's."""
+    from mixture_experts_layer_free_amd.layer import MoELayer, Shape
+    cfg = CONFIGS["tiny"] if name == "tiny" else scaled(CONFIGS["fine"], T=900, d=256, E=24, k=3, f=128)
+    say(f"[forward fused permute {name}]")
+    inp = make_inputs(cfg)
+    dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    outs = []
+    for fuse in (False, True):
+        sh = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, dt, cfg.score, fuse_permute=fuse)
+        layer = MoELayer(sh, dev(inp["w_router"]), dev(inp["w_gate_up"]), dev(inp["w_down"]), dev(inp["bias"]),
+                         dev(inp["logit_offset"]))
+        assert (layer.x_perm is None) == fuse
+        outs.append(host(layer.forward(dev(inp["x"]))).copy())
+    torch.cuda.synchronize()
+    assert np.array_equal(outs[0], outs[1])
+    ref = oracle.forward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], cfg.k, cfg.score,
+                         cfg.dtype == "bf16", sel_bias=inp["bias"], logit_offset=inp["logit_offset"])
+    keep = ref["margin"] >= 1e-6
+    check_close(outs[1][keep], ref["out"][keep], _kind(cfg), "out (fused permute)")
+
+
 def test_forward_deterministic():
     say("[forward determinism]")
     cfg = scaled(CONFIGS["fine"], T=1000, d=256, E=32, k=4, f=128)
@@ -509,4 +587,5 @@ def test_forward_deterministic():
     oa = host(a.forward(x)).copy()
     ob = host(b.forward(x))
     assert np.array_equal(oa, ob)
-    assert np.array_equal(host(a.x_perm), host(b.x_perm))
+    assert np.array_equal(host(a.token_of), host(b.token_of))
+    assert np.array_equal(host(a.y_perm), host(b.y_perm))
