@@ -1,5 +1,7 @@
 // Permute: group the T*k (token, expert) assignments by expert, stably and
-// without atomics, and copy each token's row to its k expert rows.
+// without atomics, and copy each token's row to its k expert rows (or, with
+// x_perm NULL, only the indices: an expert GEMM that gathers rows through
+// token_of needs no copy).
 //
 // The expert GEMMs want every expert's rows contiguous; this is the permute
 // whose fusion the AREX article on The Ultimate MoE Training Handbook reports
