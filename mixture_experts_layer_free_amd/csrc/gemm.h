@@ -39,6 +39,7 @@
 // so neighbouring tiles (sharing a weight or activation panel) meet in one
 // XCD's L2.
 #pragma once
+#include <atomic>
 
 #include "moe_common.h"
 
@@ -558,8 +559,22 @@ void gemm_kernel(Args p) {
 // Persistent grid: at most `per_cu` workgroups per CU, a multiple of 8.
 int grid_for(int64_t tiles_upper, int per_cu);
 
-// Raises a kernel's dynamic-LDS limit (once per kernel, at its first launch).
+// Raises a kernel's dynamic-LDS limit on the current device.
 moe_status lds_attr(const void* fn, int bytes);
+
+// Per device (the current one): 0 not yet set, 1 set, 2 failed.
+constexpr int kMaxAttrDevices = 64;
+template <typename K>
+moe_status lds_attr_once(std::atomic<int> (&done)[kMaxAttrDevices], K* fn, int bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxAttrDevices) dev = 0;
+  int st = done[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    st = lds_attr(reinterpret_cast<const void*>(fn), bytes) == MOE_OK ? 1 : 2;
+    done[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? MOE_OK : MOE_EHIP;
+}
 
 // Fills in the tile counts of `a` for a TM x TN tile and launches.  `rows`
 // (row-grouped only) bounds the row tiles: sum over groups of
@@ -576,8 +591,8 @@ moe_status launch_cfg(Args a, int64_t rows, hipStream_t s) {
     tiles = (ceil_div(rows, TM) + a.G) * a.NB;
   }
   constexpr int lds = lds_bytes<TM, TN>();
-  static const moe_status attr =
-      lds_attr(reinterpret_cast<const void*>(&gemm_kernel<TM, TN, AK, BKC, KG, EPI>), lds);
+  static std::atomic<int> attr_done[kMaxAttrDevices];
+  const moe_status attr = lds_attr_once(attr_done, &gemm_kernel<TM, TN, AK, BKC, KG, EPI>, lds);
   if (attr != MOE_OK) return attr;
   gemm_kernel<TM, TN, AK, BKC, KG, EPI><<<grid_for(tiles, TM * TN > 128 * 128 ? 1 : 2), 256, lds, s>>>(a);
   MOE_LAUNCH_CHECK();

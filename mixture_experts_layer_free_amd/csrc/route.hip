@@ -148,10 +148,13 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
 // an fp32 dot product, at the bf16 matrix rate.  As in the fp32 kernel, the
 // products go into a chunk accumulator folded into the running total every
 // 64 k (every partial sum covers at most 64 x 3 exact products).
-// Workgroup: 2 waves, 32 tokens x 64 experts; wave w owns experts
-// e0 + 32w .. +31.  Operands come straight from global memory (16-byte x
-// loads, 32-byte w loads); the next four 16-deep steps load while the
-// current four multiply.
+// Workgroup: 2 x RKS waves, 32 tokens x 64 experts; wave w owns experts
+// e0 + 32(w%2) .. +31 and the (w/2)-th of RKS contiguous ranges of the
+// reduction.  RKS = 4 when the grid would otherwise hold fewer than 1024
+// waves (e.g. 8192 tokens x 64 experts), so a small grid still keeps the
+// SIMDs busy; 1 otherwise (more waves measured slower there).  Operands come straight from global memory (16-byte x loads,
+// 32-byte w loads); the next four 16-deep steps load while the current four
+// multiply.  The RKS partial tiles are added in range order through LDS.
 __device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
   const uint32_t u = __float_as_uint(w);
   hi = u >> 16;                                            // truncation: w - hi is exact
@@ -164,19 +167,26 @@ __device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uin
 
 constexpr int RB_STEPS = 4;   // 16-deep steps in flight
 
-__global__ __launch_bounds__(128) void router_logits_bf16_kernel(const bf16_t* __restrict__ x,
-                                                                 const float* __restrict__ w,
-                                                                 const float* __restrict__ off,
-                                                                 float* __restrict__ logits, int T, int d, int E) {
+template <int RKS>
+__global__ __launch_bounds__(128 * RKS) void router_logits_bf16_kernel(const bf16_t* __restrict__ x,
+                                                                       const float* __restrict__ w,
+                                                                       const float* __restrict__ off,
+                                                                       float* __restrict__ logits, int T, int d, int E) {
+  __shared__ f32x4 s_part[RKS > 1 ? RKS - 1 : 1][2][4][64];   // partial tiles of ranges 1..RKS-1
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 64 + wave * 32;
+  const int eh = wave & 1, ks = wave >> 1;
+  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 64 + eh * 32;
   const int row = lane & 31, kh = 8 * (lane >> 5);        // MFMA operand layout: row l%32, k 8*(l/32)..+7
   const int t = t0 + row, e = e0 + row;
   const bool tin = t < T, ein = e < E;
   const bf16_t* xr = x + (int64_t)(tin ? t : 0) * d;
   const float* wr = w + (int64_t)(ein ? e : 0) * d;
   f32x16 tot = {}, chk = {};
-  const int nsteps = (d + 15) / 16;
+  // this wave's steps: range ks of RKS, each a whole number of load batches
+  const int nall = (d + 15) / 16;
+  const int per = ((nall + RKS - 1) / RKS + RB_STEPS - 1) / RB_STEPS * RB_STEPS;
+  const int sbeg = ks * per < nall ? ks * per : nall;
+  const int nsteps = sbeg + per < nall ? sbeg + per : nall;   // end of the range
   // batch b = steps b*RB_STEPS .. +RB_STEPS-1; batch b+1 loads while batch b multiplies
   auto load = [&](int s0, u32x4 (&xa)[RB_STEPS], f32x4 (&wa)[RB_STEPS][2]) {
 #pragma unroll
@@ -211,13 +221,26 @@ __global__ __launch_bounds__(128) void router_logits_bf16_kernel(const bf16_t* _
   };
   u32x4 xa0[RB_STEPS], xa1[RB_STEPS];
   f32x4 wa0[RB_STEPS][2], wa1[RB_STEPS][2];
-  load(0, xa0, wa0);
-  for (int s0 = 0; s0 < nsteps; s0 += 2 * RB_STEPS) {   // batches past the end load and add zeros
+  load(sbeg, xa0, wa0);
+  for (int s0 = sbeg; s0 < nsteps; s0 += 2 * RB_STEPS) {   // batches past the end load and add zeros
     load(s0 + RB_STEPS, xa1, wa1);
     compute(xa0, wa0);
     load(s0 + 2 * RB_STEPS, xa0, wa0);
     compute(xa1, wa1);
   }
+  // add the ranges' partial tiles in range order (deterministic)
+  if (RKS > 1 && ks > 0)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s_part[ks - 1][eh][q][lane] = f32x4{tot[4 * q], tot[4 * q + 1], tot[4 * q + 2], tot[4 * q + 3]};
+  if (RKS > 1) __syncthreads();
+  if (ks > 0) return;
+#pragma unroll
+  for (int j = 0; j < RKS - 1; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = s_part[j][eh][q][lane];
+      tot[4 * q] += v[0]; tot[4 * q + 1] += v[1]; tot[4 * q + 2] += v[2]; tot[4 * q + 3] += v[3];
+    }
   // D layout: register r of a lane = row (token) 8*(r/4) + 4*(lane/32) + r%4, column (expert) lane%32
   const int ec = e0 + (lane & 31);
   if (ec < E) {
@@ -510,8 +533,13 @@ static moe_status router_logits_launch(const void* x, int x_dtype, int64_t T, in
     else
       router_logits_small_kernel<false><<<gs, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
   } else if (x_dtype == MOE_BF16) {
-    router_logits_bf16_kernel<<<dim3((unsigned)ceil_div(T, 32), (unsigned)ceil_div(E, 64)), 128, 0, s>>>(
-        static_cast<const bf16_t*>(x), w_router, logit_offset, logits_out, (int)T, (int)d, E);
+    const dim3 g((unsigned)ceil_div(T, 32), (unsigned)ceil_div(E, 64));
+    if ((int64_t)g.x * g.y * 2 < 1024)
+      router_logits_bf16_kernel<4><<<g, 128 * 4, 0, s>>>(static_cast<const bf16_t*>(x), w_router, logit_offset,
+                                                          logits_out, (int)T, (int)d, E);
+    else
+      router_logits_bf16_kernel<1><<<g, 128, 0, s>>>(static_cast<const bf16_t*>(x), w_router, logit_offset,
+                                                      logits_out, (int)T, (int)d, E);
   } else {
     dim3 g1((unsigned)ceil_div(T, RT_M), (unsigned)ceil_div(E, RT_N));
     router_logits_kernel<false><<<g1, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
