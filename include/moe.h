@@ -21,15 +21,19 @@
  *     nn.Linear layout [out, in].  bf16 tensors are raw 16-bit bf16 values.
  *   - Indices and counts are int32; sizes are int64 where they can pass 2^31.
  *   - Arguments are checked before anything is enqueued: MOE_EINVAL for a
- *     NULL required pointer, a non-positive size, k outside [1, E] or a
- *     workspace smaller than moe_workspace_size asks for; MOE_ENOTSUP for
- *     shapes outside the supported set (stated per call); MOE_EHIP when a
- *     kernel launch fails.  Nothing is enqueued when a call fails.
+ *     NULL required pointer, a non-positive size or k outside [1, E];
+ *     MOE_EWORKSPACE for a NULL workspace or one smaller than
+ *     moe_workspace_size asks for; MOE_ENOTSUP for shapes outside the
+ *     supported set (stated per call).  A call that fails these checks
+ *     enqueues nothing.  MOE_EHIP: a kernel launch (or setting a kernel's
+ *     LDS limit) failed; kernels the call enqueued before it may still run.
  *   - Values that must agree between calls (offsets[G] == rows, the expert
  *     indices being in [0, E)) live on the device and are not checked.
  *   - NaN or Inf inputs give undefined expert selection.
- *   - Calls on different streams with disjoint buffers may run concurrently;
- *     the library has no mutable global state.
+ *   - Calls on different streams (or host threads) with disjoint buffers may
+ *     run concurrently.  The only global state is a per-device cache (the
+ *     compute-unit count, the kernels' LDS limits), filled once per device
+ *     under atomics.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -224,7 +228,9 @@ moe_status moe_permute_capacity(const int32_t* topk_idx, int64_t T, int k, int E
  *   workspace                moe_workspace_size(MOE_CALL_GROUPED_FFN, rows, 1, G, d, f)
  * bf16 uses MFMA with fp32 accumulation; f32 uses fp32 FMA.
  * ENOTSUP: G > MOE_MAX_EXPERTS, rows >= 2^31; bf16 needs d and f to be
- * multiples of 64; f32 needs d a multiple of 4.
+ * multiples of 64 and one expert's gate/up weight under 2 GiB
+ * (2f*d*2 < 2^31 bytes: it is addressed through one buffer resource); f32
+ * needs d a multiple of 4.
  */
 moe_status moe_grouped_ffn(const void* x_rows, int64_t rows, int64_t d, int dtype,
                            const int32_t* offsets, int G, int64_t f,
@@ -375,7 +381,9 @@ typedef struct moe_bwd_args {
  * gate normalisation) still reaches dW_r over its dropped x_perm row and
  * dx_r.  Expert GEMMs run on the kept rows offsets[0] .. offsets[E]-1.
  * ENOTSUP: non-bf16 use, d or f not a multiple of 64, E > MOE_MAX_EXPERTS,
- * k > MOE_MAX_TOPK.  EINVAL also for a struct_size other than
+ * k > MOE_MAX_TOPK, T*k >= 2^31, and buffers the GEMMs address through one
+ * buffer resource reaching 2 GiB: T*k*max(d, 2f)*2 >= 2^31 or
+ * 2f*d*2 >= 2^31 bytes.  EINVAL also for a struct_size other than
  * sizeof(moe_bwd_args), offsetof(moe_bwd_args, counts) or
  * offsetof(moe_bwd_args, aux_alpha) (older callers: the missing fields
  * read as NULL / 0). */

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 @pytest.fixture(scope="module")
-def L():
+def built():
     from mixture_experts_layer_free_amd import _lib
     if not os.path.exists(_lib.LIB_PATH):
         from mixture_experts_layer_free_amd import build
@@ -19,12 +19,24 @@ def L():
     return _lib
 
 
-def test_exports_every_declared_entry_point(L):
+@pytest.fixture(scope="module")
+def L(built):
+    """The binding, for argument checks that must fail before any launch.
+    They pass a stand-in device pointer, so where a GPU is visible a call that
+    unexpectedly passed its checks would launch on it: skipped there (the
+    driver of these checks is the CPU suite)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("host-only argument checks (stand-in pointers) are not run where a GPU is visible")
+    return built
+
+
+def test_exports_every_declared_entry_point(built):
     hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
     names = sorted(set(re.findall(r"^\s*(?:moe_status|size_t|const char\*)\s+(moe_\w+)\s*\(", hdr, re.M)))
     assert {"moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_bias_update", "moe_backward",
             "moe_workspace_size", "moe_status_str"} <= set(names)
-    lib = L.lib()
+    lib = built.lib()
     for n in names:
         assert hasattr(lib, n), n
 
@@ -71,6 +83,10 @@ def test_grouped_ffn_validation(L):
     assert lib.moe_grouped_ffn(*a(f=100)) == L.MOE_ENOTSUP
     assert lib.moe_grouped_ffn(*a(G=2000)) == L.MOE_ENOTSUP
     assert lib.moe_grouped_ffn(*a(wsb=0)) == L.MOE_EWORKSPACE
+    assert lib.moe_grouped_ffn(*a(ws=None)) == L.MOE_EWORKSPACE
+    # one expert's gate/up weight of 2 GiB: past one buffer resource
+    assert lib.moe_grouped_ffn(*a(d=16384, f=32768)) == L.MOE_ENOTSUP
+    assert lib.moe_grouped_ffn(*a(d=16384, f=32704, wsb=0)) == L.MOE_EWORKSPACE   # just under: the shape passes
 
 
 def test_grouped_ffn_gather_validation(L):
@@ -99,6 +115,81 @@ def test_combine_and_bias_validation(L):
     assert lib.moe_combine(P, P, P, None, 10, 2, 64, P, 5, None) == L.MOE_EINVAL
     assert lib.moe_bias_update(None, P, 8, 64, 2, 1e-3, None) == L.MOE_EINVAL
     assert lib.moe_bias_update(P, P, 8, 64, 9, 1e-3, None) == L.MOE_EINVAL
+
+
+def test_route_variants_validation(L):
+    lib = L.lib()
+    # moe_route_replay: the score function must be a learned one
+    r = lambda **kw: [P, 1, kw.get("T", 64), kw.get("d", 64), P, None, kw.get("E", 8), kw.get("k", 2),
+                      kw.get("sf", 0), kw.get("idx", P), P, P, None]
+    assert lib.moe_route_replay(*r(idx=None)) == L.MOE_EINVAL
+    assert lib.moe_route_replay(*r(sf=3)) == L.MOE_EINVAL
+    assert lib.moe_route_replay(*r(d=12)) == L.MOE_ENOTSUP
+    assert lib.moe_route_replay(*r(E=2048)) == L.MOE_ENOTSUP
+    # moe_route_hash
+    assert lib.moe_route_hash(None, 64, 8, 2, 0, P, P, None) == L.MOE_EINVAL
+    assert lib.moe_route_hash(P, 64, 8, 9, 0, P, P, None) == L.MOE_EINVAL
+    assert lib.moe_route_hash(P, 64, 64, 17, 0, P, P, None) == L.MOE_ENOTSUP
+    assert lib.moe_route_hash(P, 1 << 31, 8, 2, 0, P, P, None) == L.MOE_ENOTSUP
+
+
+def test_permute_capacity_validation(L):
+    lib = L.lib()
+    need = L.workspace_size(L.MOE_CALL_PERMUTE, 1000, 8, 64)
+    a = lambda **kw: [P, 1000, kw.get("k", 8), 64, kw.get("cap", 200), P, 1, kw.get("d", 64), P, P,
+                      kw.get("row_of", P), P, P, P, kw.get("wsb", need), None]
+    assert lib.moe_permute_capacity(*a(row_of=None)) == L.MOE_EINVAL
+    assert lib.moe_permute_capacity(*a(k=65)) == L.MOE_EINVAL
+    assert lib.moe_permute_capacity(*a(d=4)) == L.MOE_ENOTSUP
+    assert lib.moe_permute_capacity(*a(wsb=need - 1)) == L.MOE_EWORKSPACE
+
+
+def test_aux_loss_validation(L):
+    lib = L.lib()
+    need = L.workspace_size(L.MOE_CALL_AUX_LOSS, 1000, 8, 64)
+    a = lambda **kw: [kw.get("lg", P), P, kw.get("T", 1000), kw.get("E", 64), kw.get("k", 8), kw.get("sf", 1),
+                      0.01, P, None, P, kw.get("wsb", need), None]
+    assert need > 0
+    assert lib.moe_aux_loss(*a(lg=None)) == L.MOE_EINVAL
+    assert lib.moe_aux_loss(*a(k=65)) == L.MOE_EINVAL
+    assert lib.moe_aux_loss(*a(sf=3)) == L.MOE_EINVAL      # hash routing has no router probabilities
+    assert lib.moe_aux_loss(*a(E=2048, k=8)) == L.MOE_ENOTSUP
+    assert lib.moe_aux_loss(*a(wsb=need - 1)) == L.MOE_EWORKSPACE
+
+
+def _bwd_args(L, **kw):
+    a = L.BwdArgs()
+    a.struct_size = kw.get("struct_size", ctypes.sizeof(L.BwdArgs))
+    a.T, a.d, a.f = kw.get("T", 1000), kw.get("d", 256), kw.get("f", 128)
+    a.E, a.k, a.score_fn = kw.get("E", 64), kw.get("k", 8), kw.get("score_fn", 2)
+    for name in ("dy", "x", "w_router", "logits", "topk_idx", "topk_gate", "row_of", "token_of", "offsets",
+                 "x_perm", "gu_saved", "h", "y_perm", "w_gate_up", "w_down", "dx", "dw_router", "dw_gate_up",
+                 "dw_down", "workspace"):
+        setattr(a, name, kw.get(name, P.value))
+    a.workspace_bytes = kw.get("workspace_bytes", L.workspace_size(L.MOE_CALL_BACKWARD, a.T, a.k, a.E, a.d, a.f))
+    a.counts = kw.get("counts", None)
+    a.aux_alpha = kw.get("aux_alpha", 0.0)
+    return a
+
+
+def test_backward_validation(L):
+    lib = L.lib()
+    bwd = lambda **kw: lib.moe_backward(ctypes.byref(_bwd_args(L, **kw)), None)
+    assert bwd(struct_size=8) == L.MOE_EINVAL
+    assert bwd(k=65) == L.MOE_EINVAL
+    assert bwd(score_fn=4) == L.MOE_EINVAL
+    assert bwd(dy=None) == L.MOE_EINVAL
+    assert bwd(w_router=None) == L.MOE_EINVAL                     # a learned router needs its weight
+    assert bwd(aux_alpha=0.01) == L.MOE_EINVAL                    # the aux gradient needs the counts
+    assert bwd(score_fn=3, aux_alpha=0.01, counts=P.value) == L.MOE_EINVAL   # and a learned router
+    assert bwd(d=96) == L.MOE_ENOTSUP
+    assert bwd(f=100) == L.MOE_ENOTSUP
+    assert bwd(E=2048, k=8) == L.MOE_ENOTSUP
+    assert bwd(T=1 << 20, d=1024, workspace_bytes=1 << 50) == L.MOE_ENOTSUP   # X_perm past 2 GiB
+    assert bwd(workspace_bytes=0) == L.MOE_EWORKSPACE
+    assert bwd(workspace=None) == L.MOE_EWORKSPACE
+    # an older caller's struct, ending before `counts`, passes the size check
+    assert bwd(struct_size=L.BwdArgs.counts.offset, workspace_bytes=0) == L.MOE_EWORKSPACE
 
 
 def test_status_strings(L):
