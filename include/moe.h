@@ -100,7 +100,8 @@ enum moe_call { MOE_CALL_ROUTE = 0, MOE_CALL_PERMUTE = 1, MOE_CALL_GROUPED_FFN =
  *                        the backward
  * Logits are computed in fp32 from x (bf16 widened exactly) and W_r, with
  * blocked accumulation (partial sums of at most 64 products).
- * ENOTSUP: E > MOE_MAX_EXPERTS, k > MOE_MAX_TOPK, d not a multiple of 8.
+ * ENOTSUP: E > MOE_MAX_EXPERTS, k > MOE_MAX_TOPK, d not a multiple of 8,
+ * d >= 2^24, T >= 2^31.
  */
 moe_status moe_route(const void* x, int x_dtype, int64_t T, int64_t d,
                      const float* w_router, const float* logit_offset, const float* sel_bias,

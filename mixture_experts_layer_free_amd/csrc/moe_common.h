@@ -38,6 +38,25 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
 }
 __device__ __forceinline__ float silu_f32(float z) { return z * sigmoid_fast(z); }
 
+// Raw buffer resource over [base, base + bytes), bytes >= 0: loads at
+// offsets past the end read zeros (offsets of 2^31 and up are always past it).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0 : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+// Wave-uniform copies of values that are uniform by construction: a buffer
+// resource the compiler cannot prove uniform costs a loop over the lanes at
+// every load that uses it.
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+__device__ __forceinline__ int64_t uni(int64_t v) {
+  const uint32_t lo = uni((uint32_t)(uint64_t)v), hi = uni((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ const void* uni(const void* ptr) {
+  return reinterpret_cast<const void*>((uintptr_t)uni((int64_t)(uintptr_t)ptr));
+}
+
 // Lane mask of lanes strictly below this one.
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int l = threadIdx.x & (MOE_WAVE - 1);

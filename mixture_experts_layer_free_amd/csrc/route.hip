@@ -152,17 +152,25 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
 // e0 + 32(w%2) .. +31 and the (w/2)-th of RKS contiguous ranges of the
 // reduction.  RKS = 4 when the grid would otherwise hold fewer than 1024
 // waves (e.g. 8192 tokens x 64 experts), so a small grid still keeps the
-// SIMDs busy; 1 otherwise (more waves measured slower there).  Operands come straight from global memory (16-byte x loads,
-// 32-byte w loads); the next four 16-deep steps load while the current four
+// SIMDs busy; 1 otherwise (more waves measured slower there).  Operands come
+// straight from global memory by buffer loads in the MFMA operand layout
+// (16-byte x loads, 32-byte w loads, 32-bit offsets within the tile's rows, so
+// d < 2^24); the next four 16-deep steps load while the current four
 // multiply.  The RKS partial tiles are added in range order through LDS.
-__device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-  const uint32_t u = __float_as_uint(w);
-  hi = u >> 16;                                            // truncation: w - hi is exact
-  const float r1 = w - __uint_as_float(hi << 16);
-  const uint32_t v = __float_as_uint(r1);
-  mid = v >> 16;
-  const float r2 = r1 - __uint_as_float(mid << 16);        // at most 8 significant bits left
-  lo = __float_as_uint(r2) >> 16;                          // exact
+// Splits two fp32 weights a, b into their bf16 parts, packed in pairs (a in
+// the low half): hi = the top 16 bits (truncation, so w - hi is exact), mid
+// = the top 16 bits of r1 = w - hi, lo = the top 16 bits of r2 = r1 - mid,
+// which has at most 8 significant bits left and so is exact.  Each pair is
+// one byte permutation of the two words.
+__device__ __forceinline__ void split3x2(float a, float b, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  constexpr uint32_t TOP = 0x07060302u;   // bytes 2, 3 of the second operand, then of the first
+  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+  hi = __builtin_amdgcn_perm(ub, ua, TOP);
+  const float ra = a - __uint_as_float(ua & 0xFFFF0000u), rb = b - __uint_as_float(ub & 0xFFFF0000u);
+  const uint32_t va = __float_as_uint(ra), vb = __float_as_uint(rb);
+  mid = __builtin_amdgcn_perm(vb, va, TOP);
+  const float sa = ra - __uint_as_float(va & 0xFFFF0000u), sb = rb - __uint_as_float(vb & 0xFFFF0000u);
+  lo = __builtin_amdgcn_perm(__float_as_uint(sb), __float_as_uint(sa), TOP);
 }
 
 constexpr int RB_STEPS = 4;   // 16-deep steps in flight
@@ -173,14 +181,21 @@ __global__ __launch_bounds__(128 * RKS) void router_logits_bf16_kernel(const bf1
                                                                        const float* __restrict__ off,
                                                                        float* __restrict__ logits, int T, int d, int E) {
   __shared__ f32x4 s_part[RKS > 1 ? RKS - 1 : 1][2][4][64];   // partial tiles of ranges 1..RKS-1
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = (int)uni((uint32_t)(threadIdx.x >> 6));   // uniform: scalar offsets
   const int eh = wave & 1, ks = wave >> 1;
   const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 64 + eh * 32;
   const int row = lane & 31, kh = 8 * (lane >> 5);        // MFMA operand layout: row l%32, k 8*(l/32)..+7
-  const int t = t0 + row, e = e0 + row;
-  const bool tin = t < T, ein = e < E;
-  const bf16_t* xr = x + (int64_t)(tin ? t : 0) * d;
-  const float* wr = w + (int64_t)(ein ? e : 0) * d;
+  // Buffer resources over the tile's 32 token rows of x and 32 expert rows of
+  // W_r: a row past T (E) lies past the resource and reads zeros.  A lane's
+  // x offset is pushed past the end for a k beyond d or a step beyond this
+  // wave's range, so its products are zero whatever W_r holds there.
+  const __amdgpu_buffer_rsrc_t rx =
+      make_rsrc(uni((const void*)(x + (int64_t)t0 * d)), uni((int64_t)(T - t0 < 32 ? T - t0 : 32) * d * 2));
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(uni((const void*)(w + (int64_t)(e0 < E ? e0 : 0) * d)),
+                uni((int64_t)(E - e0 < 32 ? (E - e0 > 0 ? E - e0 : 0) : 32) * d * 4));
+  const uint32_t xo = (uint32_t)(row * d + kh) * 2u, wo = (uint32_t)(row * d + kh) * 4u;
+  const int klim = d - kh;   // this lane's k = 16*s + kh is inside d while 16*s < klim
   f32x16 tot = {}, chk = {};
   // this wave's steps: range ks of RKS, each a whole number of load batches
   const int nall = (d + 15) / 16;
@@ -191,25 +206,24 @@ __global__ __launch_bounds__(128 * RKS) void router_logits_bf16_kernel(const bf1
   auto load = [&](int s0, u32x4 (&xa)[RB_STEPS], f32x4 (&wa)[RB_STEPS][2]) {
 #pragma unroll
     for (int u = 0; u < RB_STEPS; ++u) {
-      const int k = 16 * (s0 + u) + kh;
-      const bool kin = s0 + u < nsteps && k < d;   // d % 8 == 0: the 8 values are all in or all out
-      xa[u] = kin && tin ? *reinterpret_cast<const u32x4*>(xr + k) : u32x4{0u, 0u, 0u, 0u};
-      wa[u][0] = kin && ein ? *reinterpret_cast<const f32x4*>(wr + k) : f32x4{0.f, 0.f, 0.f, 0.f};
-      wa[u][1] = kin && ein ? *reinterpret_cast<const f32x4*>(wr + k + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const int st = s0 + u;
+      const bool kin = st < nsteps && 16 * st < klim;   // d % 8 == 0: the 8 values are all in or all out
+      const uint32_t so = (uint32_t)st * 32u;           // bytes of x per 16-deep step (W_r: twice that)
+      xa[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, kin ? xo : 0x80000000u, so, 0));
+      wa[u][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo, 2 * so, 0));
+      wa[u][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo + 16u, 2 * so, 0));
     }
   };
   auto compute = [&](const u32x4 (&xa)[RB_STEPS], const f32x4 (&wa)[RB_STEPS][2]) {
 #pragma unroll
     for (int u = 0; u < RB_STEPS; ++u) {
-      uint32_t h[8], m[8], l[8];
+      uint32_t h[4], m[4], l[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        split3(wa[u][0][q], h[q], m[q], l[q]);
-        split3(wa[u][1][q], h[4 + q], m[4 + q], l[4 + q]);
+      for (int q = 0; q < 2; ++q) {
+        split3x2(wa[u][0][2 * q], wa[u][0][2 * q + 1], h[q], m[q], l[q]);
+        split3x2(wa[u][1][2 * q], wa[u][1][2 * q + 1], h[2 + q], m[2 + q], l[2 + q]);
       }
-      const u32x4 hv = {h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
-      const u32x4 mv = {m[0] | m[1] << 16, m[2] | m[3] << 16, m[4] | m[5] << 16, m[6] | m[7] << 16};
-      const u32x4 lv = {l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16, l[6] | l[7] << 16};
+      const u32x4 hv = {h[0], h[1], h[2], h[3]}, mv = {m[0], m[1], m[2], m[3]}, lv = {l[0], l[1], l[2], l[3]};
       const bf16x8 a = __builtin_bit_cast(bf16x8, xa[u]);
       // D[token][expert]: A = x (tokens x k), B = w parts (k x experts)
       chk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, lv), chk, 0, 0, 0);
@@ -513,7 +527,7 @@ extern "C" moe_status moe_route(const void* x, int x_dtype, int64_t T, int64_t d
   if (T < 1 || d < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EINVAL;
   if (score_fn < MOE_SOFTMAX_CHOSEN || score_fn > MOE_SQRT_SOFTPLUS_NORM) return MOE_EINVAL;
-  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || d % 8 != 0 || T >= (1ll << 31) || d >= (1ll << 31))
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || d % 8 != 0 || T >= (1ll << 31) || d >= (1ll << 24))
     return MOE_ENOTSUP;
   hipStream_t s = moe_stream(stream);
   const moe_status st = router_logits_launch(x, x_dtype, T, d, w_router, logit_offset, E, logits_out, s);
@@ -555,7 +569,7 @@ extern "C" moe_status moe_route_replay(const void* x, int x_dtype, int64_t T, in
   if (T < 1 || d < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EINVAL;
   if (score_fn < MOE_SOFTMAX_CHOSEN || score_fn > MOE_SQRT_SOFTPLUS_NORM) return MOE_EINVAL;
-  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || d % 8 != 0 || T >= (1ll << 31) || d >= (1ll << 31))
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || d % 8 != 0 || T >= (1ll << 31) || d >= (1ll << 24))
     return MOE_ENOTSUP;
   hipStream_t s = moe_stream(stream);
   const moe_status st = router_logits_launch(x, x_dtype, T, d, w_router, logit_offset, E, logits_out, s);

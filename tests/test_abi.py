@@ -58,6 +58,7 @@ def test_route_validation(L):
     assert lib.moe_route(*args(E=1025, k=2)) == L.MOE_ENOTSUP
     assert lib.moe_route(*args(E=64, k=17)) == L.MOE_ENOTSUP
     assert lib.moe_route(*args(d=60)) == L.MOE_ENOTSUP
+    assert lib.moe_route(*args(d=1 << 24)) == L.MOE_ENOTSUP   # 32-bit offsets within a 32-row tile
 
 
 def test_permute_validation(L):
