@@ -148,6 +148,9 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
 // an fp32 dot product, at the bf16 matrix rate.  As in the fp32 kernel, the
 // products go into a chunk accumulator folded into the running total every
 // 64 k (every partial sum covers at most 64 x 3 exact products).
+// This kernel serves the grids too small for the LDS-shared kernel below
+// (fewer than 256 tiles of 64 x 64, e.g. 8192 tokens x 64 experts) and
+// d >= 2^22.
 // Workgroup: 2 x RKS waves, 32 tokens x 64 experts; wave w owns experts
 // e0 + 32(w%2) .. +31 and the (w/2)-th of RKS contiguous ranges of the
 // reduction.  RKS = 4 when the grid would otherwise hold fewer than 1024
@@ -262,6 +265,149 @@ __global__ __launch_bounds__(128 * RKS) void router_logits_bf16_kernel(const bf1
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int tr = t0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (tr < T) logits[(int64_t)tr * E + ec] = tot[r] + o;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The same logits and the same sums (bit for bit) on larger grids, with the
+// operands shared through LDS.  The kernel above is bound by its texture
+// addresser: each wave fetches its own fragments in the MFMA operand layout
+// (32 rows per load), and the two waves of a workgroup fetch the same x rows.
+// Here a 4-wave workgroup owns 64 tokens x 64 experts (wave w: tokens
+// 32(w/2).., experts 32(w%2)..) and stages each 64-deep batch of x and W_r
+// once, with every load covering whole 128-byte lines; W_r is split into its
+// three bf16 parts once, on the way into LDS (three [64][64] bf16 planes).
+// Each 16-deep step then reads one x and three W_r fragments from LDS and
+// issues the same three MFMAs, in the same order, on the same lane-to-k
+// mapping as the kernel above; the chunk accumulator folds every 64 k.
+// Batches run two ahead in registers; the LDS holds two stages (64 KB).
+// Offsets are 32-bit within the tile's rows: d < 2^22.
+constexpr int RL_T = 64, RL_E = 64, RL_K = 64;                  // tile and batch depth
+
+// LDS writes done, then the workgroup barrier; the compiler moves no memory
+// access across either.
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+constexpr int RL_XB = RL_T * RL_K * 2, RL_PB = RL_E * RL_K * 2;  // bytes: x stage, one W_r plane
+constexpr int RL_STAGE = RL_XB + 3 * RL_PB;                      // 32 KB
+
+__device__ __forceinline__ int rl_swz(int row) { return (row >> 1) & 7; }   // 16-byte chunk swizzle, [64][64] bf16
+
+__global__ __launch_bounds__(256) void router_logits_lds_kernel(const bf16_t* __restrict__ x,
+                                                                const float* __restrict__ w,
+                                                                const float* __restrict__ off,
+                                                                float* __restrict__ logits, int T, int d, int E) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * RL_STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = (int)uni((uint32_t)(tid >> 6));
+  const int tm = wave >> 1, te = wave & 1;
+  const int ntb = (T + RL_T - 1) / RL_T;
+  const int t0 = (int)(blockIdx.x % ntb) * RL_T, e0 = (int)(blockIdx.x / ntb) * RL_E;
+  const int nb = (d + RL_K - 1) / RL_K;   // 64-deep batches
+
+  // Loads: x rows of 128 bytes (8 chunks) -> thread chunks c = tid, tid+256
+  // (row c/8, chunk c%8); W_r rows of 256 bytes (16 chunks of 4 floats) ->
+  // c = tid + 256j, j < 4 (row c/16, chunk c%16).  Rows past T (E) lie past
+  // the buffer resource and read zeros; an x chunk past d is pushed past it
+  // too, so its products are zero whatever W_r holds there.
+  const __amdgpu_buffer_rsrc_t rx =
+      make_rsrc(uni((const void*)(x + (int64_t)t0 * d)), uni((int64_t)(T - t0 < RL_T ? T - t0 : RL_T) * d * 2));
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(uni((const void*)(w + (int64_t)e0 * d)), uni((int64_t)(E - e0 < RL_E ? E - e0 : RL_E) * d * 4));
+  uint32_t xo[2], wo[4];
+  int xk[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = tid + 256 * j, r = c >> 3, ch = c & 7;
+    xo[j] = (uint32_t)(r * d + 8 * ch) * 2u;
+    xk[j] = 8 * ch;   // k of the chunk inside its batch
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = tid + 256 * j, r = c >> 4, ch = c & 15;
+    wo[j] = (uint32_t)(r * d + 4 * ch) * 4u;
+  }
+  auto gload = [&](int b, u32x4 (&xr)[2], f32x4 (&wr)[4]) {
+    const int kb = (int)uni((uint32_t)(b * RL_K));   // uniform: a scalar offset, no loop over the lanes
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      xr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rx, kb + xk[j] < d ? xo[j] : 0x80000000u, (uint32_t)kb * 2u, 0));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      wr[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo[j], (uint32_t)kb * 4u, 0));
+  };
+  // LDS stage: x [64][64] bf16, then the hi, mid, lo planes of W_r [64][64] bf16
+  auto swrite = [&](char* st, const u32x4 (&xr)[2], const f32x4 (&wr)[4]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = tid + 256 * j, r = c >> 3, ch = c & 7;
+      *reinterpret_cast<u32x4*>(st + r * 128 + ((ch ^ rl_swz(r)) << 4)) = xr[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = tid + 256 * j, r = c >> 4, ch = c & 15;   // 4 floats: half of a 16-byte plane chunk
+      const int o = r * 128 + (((ch >> 1) ^ rl_swz(r)) << 4) + 8 * (ch & 1);
+      uint32_t h0, m0, l0, h1, m1, l1;
+      split3x2(wr[j][0], wr[j][1], h0, m0, l0);
+      split3x2(wr[j][2], wr[j][3], h1, m1, l1);
+      *reinterpret_cast<u32x2*>(st + RL_XB + o) = u32x2{h0, h1};
+      *reinterpret_cast<u32x2*>(st + RL_XB + RL_PB + o) = u32x2{m0, m1};
+      *reinterpret_cast<u32x2*>(st + RL_XB + 2 * RL_PB + o) = u32x2{l0, l1};
+    }
+  };
+  // fragments: row l%32 of the wave's 32, k 8*(l/32).. of the 16-deep step
+  const int fr = lane & 31, fsw = rl_swz(fr);
+  const int xa_row = (32 * tm + fr) * 128, wb_row = (32 * te + fr) * 128;
+  f32x16 tot = {}, chk = {};
+  auto compute = [&](const char* st) {
+#pragma unroll
+    for (int u = 0; u < RL_K / 16; ++u) {
+      const int ch = ((2 * u + (lane >> 5)) ^ fsw) << 4;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + xa_row + ch);
+      const bf16x8 hv = *reinterpret_cast<const bf16x8*>(st + RL_XB + wb_row + ch);
+      const bf16x8 mv = *reinterpret_cast<const bf16x8*>(st + RL_XB + RL_PB + wb_row + ch);
+      const bf16x8 lv = *reinterpret_cast<const bf16x8*>(st + RL_XB + 2 * RL_PB + wb_row + ch);
+      chk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, lv, chk, 0, 0, 0);
+      chk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, mv, chk, 0, 0, 0);
+      chk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, hv, chk, 0, 0, 0);
+    }
+    tot += chk;
+    chk = f32x16{};
+  };
+  // batch j lives in register set j % 2 until it is written to LDS stage j % 2
+  u32x4 xr0[2], xr1[2];
+  f32x4 wr0[4], wr1[4];
+  gload(0, xr0, wr0);
+  gload(1, xr1, wr1);   // a batch past the end reads zeros
+  swrite(smem, xr0, wr0);
+  wait_lgkm0();
+  lds_barrier();
+  for (int b = 0; b < nb; b += 2) {
+    gload(b + 2, xr0, wr0);
+    compute(smem);
+    swrite(smem + RL_STAGE, xr1, wr1);
+    wait_lgkm0();
+    lds_barrier();
+    if (b + 1 >= nb) break;
+    gload(b + 3, xr1, wr1);
+    compute(smem + RL_STAGE);
+    swrite(smem, xr0, wr0);
+    wait_lgkm0();
+    lds_barrier();
+  }
+  // D layout: register r of a lane = row (token) 8*(r/4) + 4*(lane/32) + r%4, column (expert) lane%32
+  const int ec = e0 + 32 * te + (lane & 31);
+  if (ec < E) {
+    const float o = off ? off[ec] : 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tr = t0 + 32 * tm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       if (tr < T) logits[(int64_t)tr * E + ec] = tot[r] + o;
     }
   }
@@ -546,6 +692,11 @@ static moe_status router_logits_launch(const void* x, int x_dtype, int64_t T, in
       router_logits_small_kernel<true><<<gs, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
     else
       router_logits_small_kernel<false><<<gs, 256, 0, s>>>(x, w_router, logit_offset, logits_out, (int)T, (int)d, E);
+  } else if (x_dtype == MOE_BF16 && d < (1 << 22) && ceil_div(T, RL_T) * ceil_div(E, RL_E) >= 256) {
+    // enough 64 x 64 tiles to fill the CUs: operands shared through LDS
+    const unsigned g = (unsigned)(ceil_div(T, RL_T) * ceil_div(E, RL_E));
+    router_logits_lds_kernel<<<g, 256, 0, s>>>(static_cast<const bf16_t*>(x), w_router, logit_offset, logits_out,
+                                               (int)T, (int)d, E);
   } else if (x_dtype == MOE_BF16) {
     const dim3 g((unsigned)ceil_div(T, 32), (unsigned)ceil_div(E, 64));
     if ((int64_t)g.x * g.y * 2 < 1024)

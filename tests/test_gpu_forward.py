@@ -51,7 +51,9 @@ def test_route_tiny(score):
 
 @pytest.mark.parametrize("T,d,E,k", [(300, 256, 16, 4), (77, 64, 1, 1), (129, 128, 96, 16), (64, 2048, 1024, 16),
                                      (33, 64, 16, 16), (150, 200, 12, 3), (150, 200, 40, 5), (2100, 1032, 8, 2),
-                                     (40, 8, 17, 2)])
+                                     (40, 8, 17, 2),
+                                     # >= 256 tiles of 64 x 64: the LDS-shared router, ragged T, E and d
+                                     (16383, 200, 100, 5), (4100, 72, 300, 8)])
 def test_route_shapes(T, d, E, k):
     say(f"[route shape T={T} d={d} E={E} k={k}]")
     cfg = scaled(CONFIGS["fine"], T=T, d=d, E=E, k=k, f=64, bias="uniform")
