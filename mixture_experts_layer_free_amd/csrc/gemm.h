@@ -33,7 +33,11 @@
 // the matrix cores idle), and the tile order below is chosen for L2 reuse.
 // Two tile shapes: 256x256 (one workgroup per CU, accumulators in AGPRs,
 // half the LDS bytes per MFMA flop) and 128x128 (two workgroups per CU);
-// use_large_rows below picks one from the rows per group.  The kernel is persistent: the grid is a
+// use_large_rows below picks one from the rows per group.  A row-grouped
+// 256x256 tile whose group ends within its first 128 rows runs as 128x256
+// with the four waves side by side (each 128 x 64), so small experts and
+// ragged last tiles do half the MFMA work per wave and half the A loads
+// while still reading their weights once.  The kernel is persistent: the grid is a
 // multiple of 8 workgroups; workgroup i runs on XCD i%8 and in each round
 // takes the tile at position i/8 of that XCD's contiguous share of the round,
 // so neighbouring tiles (sharing a weight or activation panel) meet in one
@@ -146,19 +150,373 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
+// One output tile: TM x TN, the four waves WM x WN (WM = 4 / WN), each
+// (TM / WM) x (TN / WN) of 32x32 MFMA blocks; operand slabs, main loop and
+// epilogue as described at the top of this file.
+template <int TM, int TN, int WN, bool AK, bool BKC, bool KG, int EPI>
+__device__ __forceinline__ void gemm_tile(const Args& p, char* smem, int e, int nb, int64_t row0, int64_t row_end,
+                                          int64_t kbeg, int64_t kend) {
+  constexpr int WTM = TM / (4 / WN), WTN = TN / WN, FM = WTM / 32, FN = WTN / 32;
+  constexpr int SA = TM * BK * 2, SB = TN * BK * 2, STAGE = SA + SB;   // bytes
+  constexpr int LA = SA / 4096, LB = SB / 4096;                         // 1 KB loads per wave per slab
+  constexpr int LPS = LA + LB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  // slabs: K / BK for a row-grouped GEMM (even: K is a multiple of 64);
+  // rounded up to even for a K-grouped one (the extra slab reads zeros)
+  const int nk = KG ? (int)((kend - kbeg + 2 * BK - 1) / (2 * BK)) * 2 : (int)((kend - kbeg) / BK);
+
+  // ---- buffer resources and per-lane byte offsets of this tile's loads.
+  // A K-contiguous: rows row0.. of A, bounded at the group's last row.
+  // A K-strided:    rows kbeg.. of A, bounded at kend; columns from row0.
+  const void* a_base;
+  const void* b_base;
+  int64_t a_bytes, b_bytes;
+  uint32_t a_voff[LA], b_voff[LB];
+  uint32_t a_step, b_step;   // bytes per slab
+  if (AK && !KG && EPI == EPI_SWIGLU && p.a_rows) {   // only the up-projection gathers
+    // gathered rows: the buffer spans all of A, a row past the group's end
+    // gets an offset past the buffer (its loads read zeros)
+    a_base = p.A;
+    a_bytes = p.a_rows_total * p.lda * 2;
+    a_step = BK * 2;
+#pragma unroll
+    for (int q = 0; q < LA; ++q) {
+      const int r = (wave * LA + q) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ swz_kc(r);
+      a_voff[q] = row0 + r < row_end ? (uint32_t)((int64_t)p.a_rows[row0 + r] * p.lda * 2 + c * 16) : 0x80000000u;
+    }
+  } else if (AK) {
+    const int64_t a_rows = row_end - row0 < TM ? row_end - row0 : TM;
+    a_base = p.A + row0 * p.lda;
+    a_bytes = a_rows * p.lda * 2;
+    a_step = BK * 2;
+#pragma unroll
+    for (int q = 0; q < LA; ++q) {
+      const int r = (wave * LA + q) * 16 + (lane >> 2);      // tile row of this lane
+      const int c = (lane & 3) ^ swz_kc(r);                  // logical chunk it fetches
+      a_voff[q] = (uint32_t)((int64_t)r * p.lda * 2 + c * 16);
+    }
+  } else {
+    a_base = p.A + kbeg * p.lda;
+    a_bytes = (kend - kbeg) * p.lda * 2;
+    a_step = (uint32_t)(BK * p.lda * 2);
+    constexpr int CPR = TM / 8;                              // chunks per slab row
+#pragma unroll
+    for (int q = 0; q < LA; ++q) {
+      const int idx = (wave * LA + q) * 64 + lane;           // physical chunk index in the slab
+      const int k = idx / CPR, pc = idx % CPR;
+      const int c = pc ^ swz_ks(k);
+      a_voff[q] = (uint32_t)((int64_t)k * p.lda * 2 + (row0 + c * 8) * 2);
+    }
+  }
+  if (BKC) {
+    b_base = p.B + (int64_t)e * p.b_group;
+    b_bytes = p.b_rows * p.ldb * 2;
+    b_step = BK * 2;
+#pragma unroll
+    for (int q = 0; q < LB; ++q) {
+      const int r = (wave * LB + q) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ swz_kc(r);
+      int64_t n;
+      if (EPI == EPI_SWIGLU) {
+        const int jb = r >> 5;   // 32-row blocks of the tile: gate, up, gate, up, ...
+        n = ((jb & 1) ? p.N : 0) + (int64_t)nb * (TN / 2) + (jb >> 1) * 32 + (r & 31);
+      } else {
+        n = (int64_t)nb * TN + r;   // rows past the weight read as zeros
+      }
+      b_voff[q] = (uint32_t)(n * p.ldb * 2 + c * 16);
+    }
+  } else {
+    const bf16_t* Bk = KG ? p.B + kbeg * p.ldb : p.B + (int64_t)e * p.b_group;
+    b_base = Bk;
+    b_bytes = (KG ? (kend - kbeg) : p.K) * p.ldb * 2;
+    b_step = (uint32_t)(BK * p.ldb * 2);
+    constexpr int CPR = TN / 8;
+#pragma unroll
+    for (int q = 0; q < LB; ++q) {
+      const int idx = (wave * LB + q) * 64 + lane;
+      const int k = idx / CPR, pc = idx % CPR;
+      const int c = pc ^ swz_ks(k);
+      b_voff[q] = (uint32_t)((int64_t)k * p.ldb * 2 + ((int64_t)nb * TN + c * 8) * 2);
+    }
+  }
+
+  // Loads of one BK-deep slab into its ring stage: LA (LB) 1 KB
+  // buffer->LDS loads per wave for A (B), 16 bytes per lane placed
+  // lane-linearly.  The host compilation pass only needs this kernel's
+  // signature (for its launch stub) and cannot type the LDS-pointer cast,
+  // so the statement exists in the device pass only.
+  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(uni(a_base), uni(a_bytes));
+  const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(uni(b_base), uni(b_bytes));
+#if defined(__HIP_DEVICE_COMPILE__)
+#define MOE_ISSUE(slab_)                                                                             \
+do {                                                                                               \
+  const int slab = (slab_);                                                                        \
+  const bool live_ = slab < nk;   /* a slab past the end is pushed out of range: its loads read zeros */ \
+  char* st_ = smem + (slab % STAGES) * STAGE;                                                      \
+  _Pragma("unroll") for (int q = 0; q < LA; ++q)                                                   \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_t*)(st_ + (wave * LA + q) * 1024), 16, a_voff[q], \
+                                             live_ ? (uint32_t)slab * a_step : 0x80000000u, 0, 0); \
+  _Pragma("unroll") for (int q = 0; q < LB; ++q)                                                   \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_t*)(st_ + SA + (wave * LB + q) * 1024), 16,      \
+                                             b_voff[q], live_ ? (uint32_t)slab * b_step : 0x80000000u, 0, 0); \
+} while (0)
+#else
+#define MOE_ISSUE(slab_) ((void)(slab_))
+#endif
+
+  // fragment byte offsets inside a stage for the 16-deep step kk
+  auto frag_kc = [&](int region, int row, int kk) -> int {   // K-contiguous slab: ds_read_b128
+    const int c = (kk >> 3) + (lane >> 5);
+    return region + row * (BK * 2) + ((c ^ swz_kc(row)) << 4);
+  };
+  auto frag_ks = [&](int region, int T, int col0, int kk, int t) -> int {   // K-strided slab: ds_read_b64_tr_b16
+    const int g = lane >> 4, a = lane & 15;
+    const int k = kk + 8 * (g >> 1) + 4 * t + (a >> 2);
+    const int m = col0 + 16 * (g & 1) + 4 * (a & 3);
+    return region + k * (T * 2) + (((m >> 3) ^ swz_ks(k)) << 4) + ((m & 7) << 1);
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni) acc[mi][ni] = f32x16{};
+
+  // Fragment reads of one slab into a register set (both 16-deep steps).
+  auto read_frags = [&](const char* st, bf16x8 (&fa)[2][FM], bf16x8 (&fb)[2][FN]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kk = 16 * h;
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi) {
+        const int m0 = wm * WTM + mi * 32;
+        if (AK) {
+          fa[h][mi] = *reinterpret_cast<const bf16x8*>(st + frag_kc(0, m0 + (lane & 31), kk));
+        } else {
+          fa[h][mi] = join8(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + frag_ks(0, TM, m0, kk, 0))),
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + frag_ks(0, TM, m0, kk, 1))));
+        }
+      }
+#pragma unroll
+      for (int ni = 0; ni < FN; ++ni) {
+        const int n0 = wn * WTN + ni * 32;
+        if (BKC) {
+          fb[h][ni] = *reinterpret_cast<const bf16x8*>(st + frag_kc(SA, n0 + (lane & 31), kk));
+        } else {
+          fb[h][ni] = join8(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + frag_ks(SA, TN, n0, kk, 0))),
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + frag_ks(SA, TN, n0, kk, 1))));
+        }
+      }
+    }
+  };
+  auto mfmas = [&](const bf16x8 (&fa)[2][FM], const bf16x8 (&fb)[2][FN]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < FN; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[h][mi], fb[h][ni], acc[mi][ni], 0, 0, 0);
+  };
+  // LDS reads per slab (a transposing fragment takes two) and MFMAs per slab
+  constexpr int NREAD = 2 * (FM * (AK ? 1 : 2) + FN * (BKC ? 1 : 2));
+  constexpr int NMFMA = 2 * FM * FN;
+
+  // Slab step it: make slab it+1 visible, refill the ring three slabs
+  // ahead, and multiply slab it (registers `ca/cb`, read one step earlier)
+  // while the fragments of slab it+1 stream into `na/nb`.  Slab it+3 goes
+  // into the stage slab it-1 used; every wave consumed those fragments
+  // before this step's barrier.  The step has no branch: loads of slabs
+  // past the end are out of range (they write zeros into a stage nobody
+  // reads), so every step waits for the same count of loads, and the
+  // MFMAs, fragment reads and slab loads form one scheduling region:
+  // each MFMA is followed by its share of the reads (first half of the
+  // step) or of the loads (second half; the compiler keeps the loads
+  // behind the reads since both touch LDS).  Steps come in pairs that swap
+  // the two register sets; the slab count is even (K of a row-grouped
+  // GEMM is a multiple of 64; a K-grouped tile rounds up and its extra slab
+  // reads zeros past the group's rows).  On the last step the reads fetch a
+  // stage whose contents are never used.
+#define MOE_STEP(it_, ca, cb, na, nb_)                                                            \
+do {                                                                                          \
+  const int it = (it_);                                                                       \
+  wait_vmcnt<LPS>();                                                                          \
+  block_barrier();                                                                            \
+  read_frags(smem + ((it + 1) % STAGES) * STAGE, na, nb_);                                    \
+  MOE_ISSUE(it + STAGES - 1);                                                                 \
+  mfmas(ca, cb);                                                                              \
+  interleave<NMFMA, NREAD, LPS>();                                                            \
+  __builtin_amdgcn_sched_barrier(0);                                                          \
+} while (0)
+
+  // Stores of the previous tile's epilogue may still be in flight: they are
+  // older than this tile's loads, so the load waits below cover them too.
+  if (nk > 0) {
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) MOE_ISSUE(s);
+    bf16x8 fa0[2][FM], fb0[2][FN], fa1[2][FM], fb1[2][FN];
+    wait_vmcnt<(STAGES - 2) * LPS>();
+    block_barrier();
+    read_frags(smem, fa0, fb0);
+    for (int it2 = 0; it2 < nk; it2 += 2) {
+      MOE_STEP(it2, fa0, fb0, fa1, fb1);
+      MOE_STEP(it2 + 1, fa1, fb1, fa0, fb0);
+    }
+    wait_vmcnt<0>();   // the out-of-range tail loads still land in the ring
+    block_barrier();   // every wave is done with the ring before the epilogue stages in it
+  }
+#undef MOE_STEP
+#undef MOE_ISSUE
+
+  // ---- epilogue.  Each 32x32 result block goes through LDS (the ring is
+  // idle now): the MFMA layout (register r of a lane = row 8*(r/4) +
+  // 4*(lane/32) + r%4, column lane%32) is written out, then read back as
+  // 4-column chunks so every global store is a row-contiguous vector
+  // (16 bytes of fp32 or 8 bytes of bf16) and the SwiGLU math runs on them.
+  // Results are stored non-temporally: they are far larger than the L2,
+  // which is left to the operand panels the neighbouring tiles reuse.
+  {
+    constexpr int SLD = 36;   // floats per staged row (16-byte aligned rows, spread banks)
+    float* stg0 = reinterpret_cast<float*>(smem) + wave * (2 * 32 * SLD);
+    float* stg1 = stg0 + 32 * SLD;
+    auto stage = [&](float* stg, const f32x16& v) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) stg[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * SLD + (lane & 31)] = v[r];
+    };
+    if (EPI == EPI_SWIGLU) {
+      bf16_t* H = static_cast<bf16_t*>(p.out);
+#pragma unroll
+      for (int pi = 0; pi < FN / 2; ++pi) {   // wave column blocks come in (gate, up) pairs
+        const int64_t col0 = (int64_t)nb * (TN / 2) + (wn * (WTN / 64) + pi) * 32;
+#pragma unroll
+        for (int mi = 0; mi < FM; ++mi) {
+          stage(stg0, acc[mi][2 * pi]);
+          stage(stg1, acc[mi][2 * pi + 1]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int idx = lane + 64 * j, rr = idx >> 3, c4 = (idx & 7) * 4;
+            const int64_t row = row0 + wm * WTM + mi * 32 + rr;
+            const f32x4 g = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c4);
+            const f32x4 u = *reinterpret_cast<const f32x4*>(stg1 + rr * SLD + c4);
+            if (row < row_end) {
+              const int64_t col = col0 + c4;
+              uint2 h;
+              h.x = pack_bf16x2(silu_f32(g[0]) * u[0], silu_f32(g[1]) * u[1]);
+              h.y = pack_bf16x2(silu_f32(g[2]) * u[2], silu_f32(g[3]) * u[3]);
+              __builtin_nontemporal_store(u32x2{h.x, h.y}, reinterpret_cast<u32x2*>(H + row * p.ldo + col));
+              if (p.gu_out) {
+                uint2 gg, uu;
+                gg.x = pack_bf16x2(g[0], g[1]);
+                gg.y = pack_bf16x2(g[2], g[3]);
+                uu.x = pack_bf16x2(u[0], u[1]);
+                uu.y = pack_bf16x2(u[2], u[3]);
+                __builtin_nontemporal_store(u32x2{gg.x, gg.y}, reinterpret_cast<u32x2*>(p.gu_out + row * 2 * p.N + col));
+                __builtin_nontemporal_store(u32x2{uu.x, uu.y}, reinterpret_cast<u32x2*>(p.gu_out + row * 2 * p.N + p.N + col));
+              }
+            }
+          }
+        }
+      }
+    } else if (EPI == EPI_F32) {
+#pragma unroll
+      for (int ni = 0; ni < FN; ++ni) {
+        const int64_t col0 = (int64_t)nb * TN + wn * WTN + ni * 32;
+        if (col0 >= p.N) continue;
+#pragma unroll
+        for (int mi = 0; mi < FM; ++mi) {
+          stage(stg0, acc[mi][ni]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int idx = lane + 64 * j, rr = idx >> 3, c4 = (idx & 7) * 4;
+            const int64_t row = row0 + wm * WTM + mi * 32 + rr;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c4);
+            const int64_t col = col0 + c4;
+            if (row < row_end && col < p.N) {
+              float* C = static_cast<float*>(p.out) + (KG ? (int64_t)e * p.out_group : 0);
+              __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(C + row * p.ldo + col));
+            }
+          }
+        }
+      }
+    } else {  // EPI_SWIGLU_BWD: dH block -> dG, dU from the saved G, U
+      // The saved G|U come from HBM: 16-byte loads (8 columns) issued PF
+      // blocks ahead, into the registers the fragments used in the loop, so
+      // PF blocks of loads are in flight while earlier blocks compute.
+      constexpr int NBLK = FM * FN, PF = NBLK < 4 ? NBLK : 4;
+      u32x4 gq[PF][2], uq[PF][2];
+      auto load_gu = [&](int b, u32x4 (&gb)[2], u32x4 (&ub)[2]) {
+        const int mi = b / FN, ni = b % FN;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int idx = lane + 64 * j, rr = idx >> 2, c8 = (idx & 3) * 8;
+          const int64_t row = row0 + wm * WTM + mi * 32 + rr;
+          const int64_t col = (int64_t)nb * TN + wn * WTN + ni * 32 + c8;
+          gb[j] = ub[j] = u32x4{0u, 0u, 0u, 0u};
+          if (row < row_end && col < p.N) {
+            gb[j] = *reinterpret_cast<const u32x4*>(p.gu_in + row * 2 * p.N + col);
+            ub[j] = *reinterpret_cast<const u32x4*>(p.gu_in + row * 2 * p.N + p.N + col);
+          }
+        }
+      };
+#pragma unroll
+      for (int b = 0; b < PF; ++b) load_gu(b, gq[b], uq[b]);
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b) {
+        const int mi = b / FN, ni = b % FN;
+        u32x4 gc[2], uc[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          gc[j] = gq[b % PF][j];
+          uc[j] = uq[b % PF][j];
+        }
+        if (b + PF < NBLK) load_gu(b + PF, gq[b % PF], uq[b % PF]);
+        stage(stg0, acc[mi][ni]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int idx = lane + 64 * j, rr = idx >> 2, c8 = (idx & 3) * 8;
+          const int64_t row = row0 + wm * WTM + mi * 32 + rr;
+          const int64_t col = (int64_t)nb * TN + wn * WTN + ni * 32 + c8;
+          const f32x4 v0 = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c8);
+          const f32x4 v1 = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c8 + 4);
+          if (row < row_end && col < p.N) {
+            const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            u32x4 o1, o2;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float dg[2], du[2];
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const uint32_t gw = gc[j][q], uw = uc[j][q];
+                const float g = bf16_to_f32(h ? gw >> 16 : gw & 0xFFFFu);
+                const float u = bf16_to_f32(h ? uw >> 16 : uw & 0xFFFFu);
+                const float sg = sigmoid_fast(g);
+                dg[h] = v[2 * q + h] * u * sg * (1.0f + g * (1.0f - sg));
+                du[h] = v[2 * q + h] * g * sg;
+              }
+              o1[q] = pack_bf16x2(dg[0], dg[1]);
+              o2[q] = pack_bf16x2(du[0], du[1]);
+            }
+            __builtin_nontemporal_store(o1, reinterpret_cast<u32x4*>(p.gu_out + row * 2 * p.N + col));
+            __builtin_nontemporal_store(o2, reinterpret_cast<u32x4*>(p.gu_out + row * 2 * p.N + p.N + col));
+          }
+        }
+      }
+    }
+  }
+  block_barrier();   // staging areas sit in the ring: free them before the next tile's loads
+}
+
 template <int TM, int TN, bool AK, bool BKC, bool KG, int EPI>
 __global__ __launch_bounds__(256, (TM * TN > 128 * 128) ? 1 : 2)
 __attribute__((amdgpu_waves_per_eu((TM * TN > 128 * 128) ? 1 : 2, (TM * TN > 128 * 128) ? 1 : 2)))
 void gemm_kernel(Args p) {
-  constexpr int WTM = TM / 2, WTN = TN / 2, FM = WTM / 32, FN = WTN / 32;
-  constexpr int SA = TM * BK * 2, SB = TN * BK * 2, STAGE = SA + SB;   // bytes
-  constexpr int LA = SA / 4096, LB = SB / 4096;                         // 1 KB loads per wave per slab
-  constexpr int LPS = LA + LB;
+  constexpr int STAGE = (TM + TN) * BK * 2;   // bytes of one ring stage
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int32_t* s_pref = reinterpret_cast<int32_t*>(smem + STAGES * STAGE);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x;
   if (!KG) {
     for (int i = tid; i <= p.G; i += 256) s_pref[i] = p.mt_prefix[i];
     __syncthreads();
@@ -192,350 +550,17 @@ void gemm_kernel(Args p) {
       kbeg = 0;
       kend = p.K;
     }
-    // slabs: K / BK for a row-grouped GEMM (even: K is a multiple of 64);
-    // rounded up to even for a K-grouped one (the extra slab reads zeros)
-    const int nk = KG ? (int)((kend - kbeg + 2 * BK - 1) / (2 * BK)) * 2 : (int)((kend - kbeg) / BK);
-
-    // ---- buffer resources and per-lane byte offsets of this tile's loads.
-    // A K-contiguous: rows row0.. of A, bounded at the group's last row.
-    // A K-strided:    rows kbeg.. of A, bounded at kend; columns from row0.
-    const void* a_base;
-    const void* b_base;
-    int64_t a_bytes, b_bytes;
-    uint32_t a_voff[LA], b_voff[LB];
-    uint32_t a_step, b_step;   // bytes per slab
-    if (AK && !KG && EPI == EPI_SWIGLU && p.a_rows) {   // only the up-projection gathers
-      // gathered rows: the buffer spans all of A, a row past the group's end
-      // gets an offset past the buffer (its loads read zeros)
-      a_base = p.A;
-      a_bytes = p.a_rows_total * p.lda * 2;
-      a_step = BK * 2;
-#pragma unroll
-      for (int q = 0; q < LA; ++q) {
-        const int r = (wave * LA + q) * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ swz_kc(r);
-        a_voff[q] = row0 + r < row_end ? (uint32_t)((int64_t)p.a_rows[row0 + r] * p.lda * 2 + c * 16) : 0x80000000u;
-      }
-    } else if (AK) {
-      const int64_t a_rows = row_end - row0 < TM ? row_end - row0 : TM;
-      a_base = p.A + row0 * p.lda;
-      a_bytes = a_rows * p.lda * 2;
-      a_step = BK * 2;
-#pragma unroll
-      for (int q = 0; q < LA; ++q) {
-        const int r = (wave * LA + q) * 16 + (lane >> 2);      // tile row of this lane
-        const int c = (lane & 3) ^ swz_kc(r);                  // logical chunk it fetches
-        a_voff[q] = (uint32_t)((int64_t)r * p.lda * 2 + c * 16);
-      }
-    } else {
-      a_base = p.A + kbeg * p.lda;
-      a_bytes = (kend - kbeg) * p.lda * 2;
-      a_step = (uint32_t)(BK * p.lda * 2);
-      constexpr int CPR = TM / 8;                              // chunks per slab row
-#pragma unroll
-      for (int q = 0; q < LA; ++q) {
-        const int idx = (wave * LA + q) * 64 + lane;           // physical chunk index in the slab
-        const int k = idx / CPR, pc = idx % CPR;
-        const int c = pc ^ swz_ks(k);
-        a_voff[q] = (uint32_t)((int64_t)k * p.lda * 2 + (row0 + c * 8) * 2);
+    // A 256-row tile whose group ends within its first 128 rows (a small
+    // expert, or a group's ragged last tile) runs as 128 x 256 with the waves
+    // side by side: half the MFMA work on each wave's path and half the A
+    // loads, the same weight reads.
+    if constexpr (TM == 256 && TN == 256 && AK && !KG) {
+      if (uni(row_end - row0) <= TM / 2) {
+        gemm_tile<TM / 2, TN, 4, AK, BKC, KG, EPI>(p, smem, e, nb, row0, row_end, kbeg, kend);
+        continue;
       }
     }
-    if (BKC) {
-      b_base = p.B + (int64_t)e * p.b_group;
-      b_bytes = p.b_rows * p.ldb * 2;
-      b_step = BK * 2;
-#pragma unroll
-      for (int q = 0; q < LB; ++q) {
-        const int r = (wave * LB + q) * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ swz_kc(r);
-        int64_t n;
-        if (EPI == EPI_SWIGLU) {
-          const int jb = r >> 5;   // 32-row blocks of the tile: gate, up, gate, up, ...
-          n = ((jb & 1) ? p.N : 0) + (int64_t)nb * (TN / 2) + (jb >> 1) * 32 + (r & 31);
-        } else {
-          n = (int64_t)nb * TN + r;   // rows past the weight read as zeros
-        }
-        b_voff[q] = (uint32_t)(n * p.ldb * 2 + c * 16);
-      }
-    } else {
-      const bf16_t* Bk = KG ? p.B + kbeg * p.ldb : p.B + (int64_t)e * p.b_group;
-      b_base = Bk;
-      b_bytes = (KG ? (kend - kbeg) : p.K) * p.ldb * 2;
-      b_step = (uint32_t)(BK * p.ldb * 2);
-      constexpr int CPR = TN / 8;
-#pragma unroll
-      for (int q = 0; q < LB; ++q) {
-        const int idx = (wave * LB + q) * 64 + lane;
-        const int k = idx / CPR, pc = idx % CPR;
-        const int c = pc ^ swz_ks(k);
-        b_voff[q] = (uint32_t)((int64_t)k * p.ldb * 2 + ((int64_t)nb * TN + c * 8) * 2);
-      }
-    }
-
-    // Loads of one BK-deep slab into its ring stage: LA (LB) 1 KB
-    // buffer->LDS loads per wave for A (B), 16 bytes per lane placed
-    // lane-linearly.  The host compilation pass only needs this kernel's
-    // signature (for its launch stub) and cannot type the LDS-pointer cast,
-    // so the statement exists in the device pass only.
-    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(uni(a_base), uni(a_bytes));
-    const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(uni(b_base), uni(b_bytes));
-#if defined(__HIP_DEVICE_COMPILE__)
-#define MOE_ISSUE(slab_)                                                                             \
-  do {                                                                                               \
-    const int slab = (slab_);                                                                        \
-    const bool live_ = slab < nk;   /* a slab past the end is pushed out of range: its loads read zeros */ \
-    char* st_ = smem + (slab % STAGES) * STAGE;                                                      \
-    _Pragma("unroll") for (int q = 0; q < LA; ++q)                                                   \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_t*)(st_ + (wave * LA + q) * 1024), 16, a_voff[q], \
-                                               live_ ? (uint32_t)slab * a_step : 0x80000000u, 0, 0); \
-    _Pragma("unroll") for (int q = 0; q < LB; ++q)                                                   \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_t*)(st_ + SA + (wave * LB + q) * 1024), 16,      \
-                                               b_voff[q], live_ ? (uint32_t)slab * b_step : 0x80000000u, 0, 0); \
-  } while (0)
-#else
-#define MOE_ISSUE(slab_) ((void)(slab_))
-#endif
-
-    // fragment byte offsets inside a stage for the 16-deep step kk
-    auto frag_kc = [&](int region, int row, int kk) -> int {   // K-contiguous slab: ds_read_b128
-      const int c = (kk >> 3) + (lane >> 5);
-      return region + row * (BK * 2) + ((c ^ swz_kc(row)) << 4);
-    };
-    auto frag_ks = [&](int region, int T, int col0, int kk, int t) -> int {   // K-strided slab: ds_read_b64_tr_b16
-      const int g = lane >> 4, a = lane & 15;
-      const int k = kk + 8 * (g >> 1) + 4 * t + (a >> 2);
-      const int m = col0 + 16 * (g & 1) + 4 * (a & 3);
-      return region + k * (T * 2) + (((m >> 3) ^ swz_ks(k)) << 4) + ((m & 7) << 1);
-    };
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < FN; ++ni) acc[mi][ni] = f32x16{};
-
-    // Fragment reads of one slab into a register set (both 16-deep steps).
-    auto read_frags = [&](const char* st, bf16x8 (&fa)[2][FM], bf16x8 (&fb)[2][FN]) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kk = 16 * h;
-#pragma unroll
-        for (int mi = 0; mi < FM; ++mi) {
-          const int m0 = wm * WTM + mi * 32;
-          if (AK) {
-            fa[h][mi] = *reinterpret_cast<const bf16x8*>(st + frag_kc(0, m0 + (lane & 31), kk));
-          } else {
-            fa[h][mi] = join8(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + frag_ks(0, TM, m0, kk, 0))),
-                              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + frag_ks(0, TM, m0, kk, 1))));
-          }
-        }
-#pragma unroll
-        for (int ni = 0; ni < FN; ++ni) {
-          const int n0 = wn * WTN + ni * 32;
-          if (BKC) {
-            fb[h][ni] = *reinterpret_cast<const bf16x8*>(st + frag_kc(SA, n0 + (lane & 31), kk));
-          } else {
-            fb[h][ni] = join8(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + frag_ks(SA, TN, n0, kk, 0))),
-                              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + frag_ks(SA, TN, n0, kk, 1))));
-          }
-        }
-      }
-    };
-    auto mfmas = [&](const bf16x8 (&fa)[2][FM], const bf16x8 (&fb)[2][FN]) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < FN; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[h][mi], fb[h][ni], acc[mi][ni], 0, 0, 0);
-    };
-    // LDS reads per slab (a transposing fragment takes two) and MFMAs per slab
-    constexpr int NREAD = 2 * (FM * (AK ? 1 : 2) + FN * (BKC ? 1 : 2));
-    constexpr int NMFMA = 2 * FM * FN;
-
-    // Slab step it: make slab it+1 visible, refill the ring three slabs
-    // ahead, and multiply slab it (registers `ca/cb`, read one step earlier)
-    // while the fragments of slab it+1 stream into `na/nb`.  Slab it+3 goes
-    // into the stage slab it-1 used; every wave consumed those fragments
-    // before this step's barrier.  The step has no branch: loads of slabs
-    // past the end are out of range (they write zeros into a stage nobody
-    // reads), so every step waits for the same count of loads, and the
-    // MFMAs, fragment reads and slab loads form one scheduling region:
-    // each MFMA is followed by its share of the reads (first half of the
-    // step) or of the loads (second half; the compiler keeps the loads
-    // behind the reads since both touch LDS).  Steps come in pairs that swap
-    // the two register sets; the slab count is even (K of a row-grouped
-    // GEMM is a multiple of 64; a K-grouped tile rounds up and its extra slab
-    // reads zeros past the group's rows).  On the last step the reads fetch a
-    // stage whose contents are never used.
-#define MOE_STEP(it_, ca, cb, na, nb_)                                                            \
-  do {                                                                                          \
-    const int it = (it_);                                                                       \
-    wait_vmcnt<LPS>();                                                                          \
-    block_barrier();                                                                            \
-    read_frags(smem + ((it + 1) % STAGES) * STAGE, na, nb_);                                    \
-    MOE_ISSUE(it + STAGES - 1);                                                                 \
-    mfmas(ca, cb);                                                                              \
-    interleave<NMFMA, NREAD, LPS>();                                                            \
-    __builtin_amdgcn_sched_barrier(0);                                                          \
-  } while (0)
-
-    // Stores of the previous tile's epilogue may still be in flight: they are
-    // older than this tile's loads, so the load waits below cover them too.
-    if (nk > 0) {
-#pragma unroll
-      for (int s = 0; s < STAGES - 1; ++s) MOE_ISSUE(s);
-      bf16x8 fa0[2][FM], fb0[2][FN], fa1[2][FM], fb1[2][FN];
-      wait_vmcnt<(STAGES - 2) * LPS>();
-      block_barrier();
-      read_frags(smem, fa0, fb0);
-      for (int it2 = 0; it2 < nk; it2 += 2) {
-        MOE_STEP(it2, fa0, fb0, fa1, fb1);
-        MOE_STEP(it2 + 1, fa1, fb1, fa0, fb0);
-      }
-      wait_vmcnt<0>();   // the out-of-range tail loads still land in the ring
-      block_barrier();   // every wave is done with the ring before the epilogue stages in it
-    }
-#undef MOE_STEP
-#undef MOE_ISSUE
-
-    // ---- epilogue.  Each 32x32 result block goes through LDS (the ring is
-    // idle now): the MFMA layout (register r of a lane = row 8*(r/4) +
-    // 4*(lane/32) + r%4, column lane%32) is written out, then read back as
-    // 4-column chunks so every global store is a row-contiguous vector
-    // (16 bytes of fp32 or 8 bytes of bf16) and the SwiGLU math runs on them.
-    // Results are stored non-temporally: they are far larger than the L2,
-    // which is left to the operand panels the neighbouring tiles reuse.
-    {
-      constexpr int SLD = 36;   // floats per staged row (16-byte aligned rows, spread banks)
-      float* stg0 = reinterpret_cast<float*>(smem) + wave * (2 * 32 * SLD);
-      float* stg1 = stg0 + 32 * SLD;
-      auto stage = [&](float* stg, const f32x16& v) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) stg[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * SLD + (lane & 31)] = v[r];
-      };
-      if (EPI == EPI_SWIGLU) {
-        bf16_t* H = static_cast<bf16_t*>(p.out);
-#pragma unroll
-        for (int pi = 0; pi < FN / 2; ++pi) {   // wave column blocks come in (gate, up) pairs
-          const int64_t col0 = (int64_t)nb * (TN / 2) + (wn * (WTN / 64) + pi) * 32;
-#pragma unroll
-          for (int mi = 0; mi < FM; ++mi) {
-            stage(stg0, acc[mi][2 * pi]);
-            stage(stg1, acc[mi][2 * pi + 1]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int idx = lane + 64 * j, rr = idx >> 3, c4 = (idx & 7) * 4;
-              const int64_t row = row0 + wm * WTM + mi * 32 + rr;
-              const f32x4 g = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c4);
-              const f32x4 u = *reinterpret_cast<const f32x4*>(stg1 + rr * SLD + c4);
-              if (row < row_end) {
-                const int64_t col = col0 + c4;
-                uint2 h;
-                h.x = pack_bf16x2(silu_f32(g[0]) * u[0], silu_f32(g[1]) * u[1]);
-                h.y = pack_bf16x2(silu_f32(g[2]) * u[2], silu_f32(g[3]) * u[3]);
-                __builtin_nontemporal_store(u32x2{h.x, h.y}, reinterpret_cast<u32x2*>(H + row * p.ldo + col));
-                if (p.gu_out) {
-                  uint2 gg, uu;
-                  gg.x = pack_bf16x2(g[0], g[1]);
-                  gg.y = pack_bf16x2(g[2], g[3]);
-                  uu.x = pack_bf16x2(u[0], u[1]);
-                  uu.y = pack_bf16x2(u[2], u[3]);
-                  __builtin_nontemporal_store(u32x2{gg.x, gg.y}, reinterpret_cast<u32x2*>(p.gu_out + row * 2 * p.N + col));
-                  __builtin_nontemporal_store(u32x2{uu.x, uu.y}, reinterpret_cast<u32x2*>(p.gu_out + row * 2 * p.N + p.N + col));
-                }
-              }
-            }
-          }
-        }
-      } else if (EPI == EPI_F32) {
-#pragma unroll
-        for (int ni = 0; ni < FN; ++ni) {
-          const int64_t col0 = (int64_t)nb * TN + wn * WTN + ni * 32;
-          if (col0 >= p.N) continue;
-#pragma unroll
-          for (int mi = 0; mi < FM; ++mi) {
-            stage(stg0, acc[mi][ni]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int idx = lane + 64 * j, rr = idx >> 3, c4 = (idx & 7) * 4;
-              const int64_t row = row0 + wm * WTM + mi * 32 + rr;
-              const f32x4 v = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c4);
-              const int64_t col = col0 + c4;
-              if (row < row_end && col < p.N) {
-                float* C = static_cast<float*>(p.out) + (KG ? (int64_t)e * p.out_group : 0);
-                __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(C + row * p.ldo + col));
-              }
-            }
-          }
-        }
-      } else {  // EPI_SWIGLU_BWD: dH block -> dG, dU from the saved G, U
-        // The saved G|U come from HBM: 16-byte loads (8 columns) issued PF
-        // blocks ahead, into the registers the fragments used in the loop, so
-        // PF blocks of loads are in flight while earlier blocks compute.
-        constexpr int NBLK = FM * FN, PF = NBLK < 4 ? NBLK : 4;
-        u32x4 gq[PF][2], uq[PF][2];
-        auto load_gu = [&](int b, u32x4 (&gb)[2], u32x4 (&ub)[2]) {
-          const int mi = b / FN, ni = b % FN;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int idx = lane + 64 * j, rr = idx >> 2, c8 = (idx & 3) * 8;
-            const int64_t row = row0 + wm * WTM + mi * 32 + rr;
-            const int64_t col = (int64_t)nb * TN + wn * WTN + ni * 32 + c8;
-            gb[j] = ub[j] = u32x4{0u, 0u, 0u, 0u};
-            if (row < row_end && col < p.N) {
-              gb[j] = *reinterpret_cast<const u32x4*>(p.gu_in + row * 2 * p.N + col);
-              ub[j] = *reinterpret_cast<const u32x4*>(p.gu_in + row * 2 * p.N + p.N + col);
-            }
-          }
-        };
-#pragma unroll
-        for (int b = 0; b < PF; ++b) load_gu(b, gq[b], uq[b]);
-#pragma unroll
-        for (int b = 0; b < NBLK; ++b) {
-          const int mi = b / FN, ni = b % FN;
-          u32x4 gc[2], uc[2];
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            gc[j] = gq[b % PF][j];
-            uc[j] = uq[b % PF][j];
-          }
-          if (b + PF < NBLK) load_gu(b + PF, gq[b % PF], uq[b % PF]);
-          stage(stg0, acc[mi][ni]);
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int idx = lane + 64 * j, rr = idx >> 2, c8 = (idx & 3) * 8;
-            const int64_t row = row0 + wm * WTM + mi * 32 + rr;
-            const int64_t col = (int64_t)nb * TN + wn * WTN + ni * 32 + c8;
-            const f32x4 v0 = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c8);
-            const f32x4 v1 = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c8 + 4);
-            if (row < row_end && col < p.N) {
-              const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-              u32x4 o1, o2;
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                float dg[2], du[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                  const uint32_t gw = gc[j][q], uw = uc[j][q];
-                  const float g = bf16_to_f32(h ? gw >> 16 : gw & 0xFFFFu);
-                  const float u = bf16_to_f32(h ? uw >> 16 : uw & 0xFFFFu);
-                  const float sg = sigmoid_fast(g);
-                  dg[h] = v[2 * q + h] * u * sg * (1.0f + g * (1.0f - sg));
-                  du[h] = v[2 * q + h] * g * sg;
-                }
-                o1[q] = pack_bf16x2(dg[0], dg[1]);
-                o2[q] = pack_bf16x2(du[0], du[1]);
-              }
-              __builtin_nontemporal_store(o1, reinterpret_cast<u32x4*>(p.gu_out + row * 2 * p.N + col));
-              __builtin_nontemporal_store(o2, reinterpret_cast<u32x4*>(p.gu_out + row * 2 * p.N + p.N + col));
-            }
-          }
-        }
-      }
-    }
-    block_barrier();   // staging areas sit in the ring: free them before the next tile's loads
+    gemm_tile<TM, TN, 2, AK, BKC, KG, EPI>(p, smem, e, nb, row0, row_end, kbeg, kend);
   }
 }
 
