@@ -539,6 +539,36 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* lrow = logits + (int64_t)t * E;
+  if (E <= MOE_WAVE) {
+    // One key per lane: each lane counts the keys that beat its own (a
+    // larger key, or an equal key at a lower expert index), which is its
+    // place in the selection order; one permute then hands the k best to
+    // lanes 0..k-1.  The order is read on a 64-bit integer: an
+    // order-preserving image of the key (-0 taken as +0) above the
+    // complemented lane, so ties go to the lower index and no two lanes tie.
+    const bool valid = lane < E;
+    const float kf = valid ? score_of(lrow[lane], fn) + (bias ? bias[lane] : 0.0f) + 0.0f : 0.0f;
+    const uint32_t u = __float_as_uint(kf);
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint64_t mykey = valid ? ((uint64_t)ord << 32) | (uint32_t)(MOE_WAVE - 1 - lane) : 0ull;
+    const uint32_t khi = (uint32_t)(mykey >> 32), klo = (uint32_t)mykey;
+    int rank = 0;
+#pragma unroll
+    for (int m = 0; m < MOE_WAVE; ++m) {
+      const uint64_t km = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, m) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)klo, m);
+      rank += km > mykey ? 1 : 0;
+    }
+    // lanes past E keep their own id (their ranks are >= E, never sent)
+    const int mine = __builtin_amdgcn_ds_permute((valid ? rank : lane) * 4, lane);
+    const bool act = lane < k;
+    const float g = chosen_gate(act ? lrow[mine] : 0.0f, act, fn);
+    if (act) {
+      idx[(int64_t)t * k + lane] = mine;
+      gate[(int64_t)t * k + lane] = g;
+    }
+    return;
+  }
   const int nv = (E + MOE_WAVE - 1) / MOE_WAVE;
 
   float key[TOPK_MAXV];
