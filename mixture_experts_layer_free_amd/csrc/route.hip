@@ -271,6 +271,15 @@ __global__ __launch_bounds__(128 * RKS) void router_logits_bf16_kernel(const bf1
 }
 
 // ---------------------------------------------------------------------------
+// LDS writes done, then the workgroup barrier; the compiler moves no memory
+// access across either.
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // The same logits and the same sums (bit for bit) on larger grids, with the
 // operands shared through LDS.  The kernel above is bound by its texture
 // addresser: each wave fetches its own fragments in the MFMA operand layout
@@ -285,15 +294,6 @@ __global__ __launch_bounds__(128 * RKS) void router_logits_bf16_kernel(const bf1
 // Batches run two ahead in registers; the LDS holds two stages (64 KB).
 // Offsets are 32-bit within the tile's rows: d < 2^22.
 constexpr int RL_T = 64, RL_E = 64, RL_K = 64;                  // tile and batch depth
-
-// LDS writes done, then the workgroup barrier; the compiler moves no memory
-// access across either.
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 constexpr int RL_XB = RL_T * RL_K * 2, RL_PB = RL_E * RL_K * 2;  // bytes: x stage, one W_r plane
 constexpr int RL_STAGE = RL_XB + 3 * RL_PB;                      // 32 KB
 
