@@ -444,6 +444,34 @@ def test_bias_update_bit_exact():
         assert np.array_equal(host(tb), oracle.bias_update(b, counts, T, k, 1e-3))
 
 
+def test_bias_trajectory_over_steps():
+    """The loss-free controller's feedback loop (lesson, Load balancing item 3
+    and Build it step 2): five steps of route -> permute -> bias update on the
+    GPU, each step's bias steering the next selection.  Every step: the
+    routing against the oracle fed the GPU's current bias (near-ties
+    excluded), the counts of the GPU's choice bit-exact, and the updated bias
+    bit-exact."""
+    say("[bias trajectory]")
+    cfg = scaled(CONFIGS["fine"], T=2048, d=256, E=64, k=8, f=64)
+    inp = make_inputs(cfg, experts=False)
+    w, o = dev(inp["w_router"]), inp["logit_offset"]
+    bias = np.zeros(cfg.E, np.float32)
+    tb = dev(bias.copy())
+    for step in range(5):
+        x_np = make_inputs(scaled(cfg, seed=1000 + step), experts=False)["x"]
+        x = dev(x_np)
+        idx, gate, logits = L.moe_route(x, w, cfg.k, cfg.score, dev(o), tb)
+        ref = oracle.route(x_np, inp["w_router"], cfg.k, cfg.score, bias, o)
+        check_route(host(idx), host(gate), host(logits), ref, cfg.k)
+        counts = L.moe_permute(idx, x, cfg.E, copy=False)[0]
+        c = host(counts)
+        assert np.array_equal(c, oracle.permute(host(idx), cfg.E)[0])
+        L.moe_bias_update(tb, counts, cfg.T, cfg.k, cfg.gamma)
+        bias = oracle.bias_update(bias, c, cfg.T, cfg.k, cfg.gamma)
+        assert np.array_equal(host(tb), bias), step
+    assert np.count_nonzero(bias) > cfg.E // 2   # the controller moved most experts
+
+
 # ---------------------------------------------------------------------------- whole layer
 
 def _layer(cfg, inp, train=False):
