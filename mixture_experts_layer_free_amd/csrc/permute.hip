@@ -113,15 +113,25 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ h
   __shared__ int32_t s_tot[MOE_MAX_EXPERTS];
   __shared__ int32_t s_wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int SB = 8;   // 64-chunk groups whose loads are issued together
   for (int e = wave; e < E; e += 16) {
     int32_t* col = hist + (int64_t)e * nchunks;
     int carry = 0;
-    for (int c0 = 0; c0 < nchunks; c0 += 64) {
-      const int c = c0 + lane;
-      const int v = c < nchunks ? col[c] : 0;
-      const int inc = wave_incl_scan(v);
-      if (c < nchunks) col[c] = carry + inc - v;
-      carry += __shfl(inc, 63, MOE_WAVE);
+    for (int c0 = 0; c0 < nchunks; c0 += 64 * SB) {
+      int v[SB];
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        const int c = c0 + 64 * b + lane;
+        v[b] = c < nchunks ? col[c] : 0;
+      }
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        if (c0 + 64 * b >= nchunks) break;   // empty groups past the column's end
+        const int c = c0 + 64 * b + lane;
+        const int inc = wave_incl_scan(v[b]);
+        if (c < nchunks) col[c] = carry + inc - v[b];
+        carry += __shfl(inc, 63, MOE_WAVE);
+      }
     }
     if (lane == 0) s_tot[e] = carry;
   }
