@@ -400,7 +400,7 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   }
   // expert GEMMs
   using namespace moe_gemm;
-  const bool large = use_large_rows(A, E, f);
+  const bool large = use_large_tile(f);
   moe_status st = moe_tile_schedule_launch(a->offsets, E, large ? BM_LARGE : BM, mt_prefix, s);
   if (st != MOE_OK) return st;
   {  // 3. dH = dY_perm W_down -> dG|dU

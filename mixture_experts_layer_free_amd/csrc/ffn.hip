@@ -130,7 +130,7 @@ moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, co
                                const int32_t* offsets, int32_t* mt_prefix, int G, int64_t f, const bf16_t* wgu,
                                const bf16_t* wd, bf16_t* gu, bf16_t* h, float* y, hipStream_t s) {
   using namespace moe_gemm;
-  const bool large = use_large_rows(rows, G, f);
+  const bool large = use_large_tile(f);
   moe_status st = moe_tile_schedule_launch(offsets, G, large ? BM_LARGE : BM, mt_prefix, s);
   if (st != MOE_OK) return st;
   Args a{};

@@ -33,7 +33,7 @@
 // the matrix cores idle), and the tile order below is chosen for L2 reuse.
 // Two tile shapes: 256x256 (one workgroup per CU, accumulators in AGPRs,
 // half the LDS bytes per MFMA flop) and 128x128 (two workgroups per CU);
-// use_large_rows below picks one from the rows per group.  A row-grouped
+// use_large_tile below picks one (the large one where it fits).  A row-grouped
 // 256x256 tile whose group ends within its first 128 rows runs as 128x256
 // with the four waves side by side (each 128 x 64), so small experts and
 // ragged last tiles do half the MFMA work per wave and half the A loads
@@ -613,19 +613,15 @@ moe_status launch_gemm(const Args& a, bool large, int64_t rows, hipStream_t s) {
                : launch_cfg<BM, BN, AK, BKC, KG, EPI>(a, rows, s);
 }
 
-// Tile choice of a row-grouped GEMM by the average rows per group:
-//  * >= 512: the large tile (half the operand traffic per flop, MFMA-bound);
-//  * <= 256: the large tile too.  Such groups are bound by streaming their
-//    weights, and a 256-row tile reads each group's weights about once where
-//    128-row tiles read them once per row tile.  The MFMA work on the rows past
-//    a group's end is free when memory is the bound, and those rows cost no
-//    traffic (their loads are out of range).  Measured on 256 experts with
-//    ~128 rows each: 7.7 -> 5.6 ms for the two expert GEMMs.
-//  * in between: the small tile, whose ragged tails waste less.
-constexpr int64_t LARGE_MIN_ROWS = 512, LARGE_MAX_ROWS_WEIGHT_BOUND = 256;
-
-inline bool use_large_rows(int64_t rows, int G, int64_t f) {
-  return (rows >= LARGE_MIN_ROWS * G || rows <= LARGE_MAX_ROWS_WEIGHT_BOUND * G) && f % (BN_LARGE / 2) == 0;
-}
+// Tile choice of a row-grouped GEMM: the large tile whenever the SwiGLU
+// columns allow it (f a multiple of 128).  It moves half the operand bytes
+// per flop of the small one, reads each group's weights once per 256 rows
+// (the small tile: once per 128), and a tile whose group ends within its
+// first 128 rows runs as 128 x 256, so ragged tails waste little.  Measured
+// on 64 experts (d = 2048, f = 1024), large against small, both expert GEMMs:
+// 130-250 rows per expert 0.28 against 0.35 ms, 300-470 rows 0.50 against
+// 0.58, 400-511 rows 0.52 against 0.68, 257-320 rows even; on 256 experts of
+// ~128 rows, 7.7 -> 5.6 ms.  The small tile serves the other widths.
+inline bool use_large_tile(int64_t f) { return f % (BN_LARGE / 2) == 0; }
 
 }  // namespace moe_gemm
