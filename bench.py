@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -65,15 +66,23 @@ CSRC = os.path.join(ROOT, "mixture_experts_layer_free_amd", "csrc")
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def _code_only(text):
+    """Source text without comments and with whitespace runs collapsed: an
+    edit that changes no code leaves it unchanged."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash():
-    """sha256 over the HIP sources: measured HBM traffic is only reported for
-    the kernels it was measured on."""
+    """sha256 over the code of the HIP sources (comments and layout left out):
+    measured HBM traffic is only reported for the kernels it was measured on."""
     import hashlib
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
         if f.endswith((".hip", ".h")):
             h.update(f.encode())
-            h.update(open(os.path.join(CSRC, f), "rb").read())
+            h.update(_code_only(open(os.path.join(CSRC, f), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -25,7 +25,8 @@
 //     gather 4 consecutive k of one column per lane (the transpose happens in
 //     the LDS read, none in registers).
 //
-// Workgroup: 4 waves in 2x2, each wave (TM/2) x (TN/2) of 32x32 MFMA blocks.
+// Workgroup: 4 waves in 2x2, each wave (TM/2) x (TN/2) of 32x32 MFMA blocks
+// (1x4 for the half tiles below).
 // Measured on MI355X, the loop is bound by the operand stream from L2 into
 // LDS (removing the in-loop loads alone lifts it from ~1.07 to ~1.75 PF/s):
 // the slab loads of a step are spread between its MFMAs (issued together,
@@ -37,11 +38,11 @@
 // 256x256 tile whose group ends within its first 128 rows runs as 128x256
 // with the four waves side by side (each 128 x 64), so small experts and
 // ragged last tiles do half the MFMA work per wave and half the A loads
-// while still reading their weights once.  The kernel is persistent: the grid is a
-// multiple of 8 workgroups; workgroup i runs on XCD i%8 and in each round
-// takes the tile at position i/8 of that XCD's contiguous share of the round,
-// so neighbouring tiles (sharing a weight or activation panel) meet in one
-// XCD's L2.
+// while still reading their weights once.  The kernel is persistent: the
+// grid is a multiple of 8 workgroups; workgroup i runs on XCD i%8 and in each
+// round takes the tile at position i/8 of that XCD's contiguous share of the
+// round, so neighbouring tiles (sharing a weight or activation panel) meet in
+// one XCD's L2.
 #pragma once
 #include <atomic>
 
