@@ -8,7 +8,8 @@
 //   1. combine_bwd   one wave per expert row: dg = <dy, y_perm[row]>,
 //                    dY_perm = bf16(g*dy); then one wave per token for the
 //                    gate backward (dl on the chosen experts)
-//   2. router wgrad  dW_r[e] = sum over e's rows of dl * x_perm (row-chunk
+//   2. router wgrad  dW_r[e] = sum over e's rows of dl * x_perm, read from x
+//                    through token_of (row-chunk
 //                    partials, then an ordered reduction: deterministic)
 //   3. dgrad down    dH = dY_perm W_down, epilogue SwiGLU backward -> dG|dU
 //   4. wgrad down    dW_down[e] = dY_perm^T H over e's rows
@@ -177,9 +178,13 @@ __global__ __launch_bounds__(1024) void router_seg_schedule_kernel(const int32_t
 
 // Partial router weight gradient over one chunk of at most RCH rows of one
 // segment: part[p][c] = sum over the chunk's rows of dl_perm[r] * x_perm[r][c].
+// Row r of x_perm is row token_of[r] of x, and x is read there: the k copies
+// of a token row come from one row of x, which stays in the caches, instead
+// of k rows streamed from HBM (147 -> 69 us on 16384 tokens, top-8).
 // Eight columns (one 16-byte vector) per thread, 2048 columns per workgroup,
 // four rows in flight per thread.
-__global__ __launch_bounds__(256) void router_wgrad_part_kernel(const bf16_t* __restrict__ x_perm,
+__global__ __launch_bounds__(256) void router_wgrad_part_kernel(const bf16_t* __restrict__ x,
+                                                                const int32_t* __restrict__ token_of,
                                                                 const float* __restrict__ dl_perm,
                                                                 const int32_t* __restrict__ seg_beg,
                                                                 const int32_t* __restrict__ seg_end,
@@ -204,7 +209,7 @@ __global__ __launch_bounds__(256) void router_wgrad_part_kernel(const bf16_t* __
     float w[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      xv[u] = *reinterpret_cast<const u32x4*>(x_perm + (r + u) * d + c);
+      xv[u] = *reinterpret_cast<const u32x4*>(x + (int64_t)token_of[r + u] * d + c);
       w[u] = dl_perm[r + u];
     }
 #pragma unroll
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(256) void router_wgrad_part_kernel(const bf16_t* __
       }
   }
   for (; r < r1; ++r) {
-    const u32x4 xv = *reinterpret_cast<const u32x4*>(x_perm + r * d + c);
+    const u32x4 xv = *reinterpret_cast<const u32x4*>(x + (int64_t)token_of[r] * d + c);
     const float w = dl_perm[r];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -388,7 +393,7 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
     router_seg_schedule_kernel<<<1, 1024, 0, s>>>(a->offsets, counts, E, seg_beg, seg_end, rc_prefix);
     MOE_LAUNCH_CHECK();
     router_wgrad_part_kernel<<<dim3((unsigned)(ceil_div(A, RCH) + 2 * E), (unsigned)ceil_div(d, 2048)), 256, 0, s>>>(
-        x_perm, dl_perm, seg_beg, seg_end, rc_prefix, 2 * E, d, rpart);
+        static_cast<const bf16_t*>(a->x), a->token_of, dl_perm, seg_beg, seg_end, rc_prefix, 2 * E, d, rpart);
     MOE_LAUNCH_CHECK();
     router_wgrad_reduce_kernel<<<dim3((unsigned)E, (unsigned)ceil_div(d, 256)), 256, 0, s>>>(rpart, rc_prefix, E, d,
                                                                                               a->dw_router);
