@@ -9,8 +9,8 @@
 //                    dY_perm = bf16(g*dy); then one wave per token for the
 //                    gate backward (dl on the chosen experts)
 //   2. router wgrad  dW_r[e] = sum over e's rows of dl * x_perm, read from x
-//                    through token_of (row-chunk
-//                    partials, then an ordered reduction: deterministic)
+//                    through token_of (row-chunk partials, then an ordered
+//                    reduction: deterministic)
 //   3. dgrad down    dH = dY_perm W_down, epilogue SwiGLU backward -> dG|dU
 //   4. wgrad down    dW_down[e] = dY_perm^T H over e's rows
 //   5. wgrad up      dW_gate_up[e] = [dG|dU]^T X_perm over e's rows
