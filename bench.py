@@ -185,15 +185,17 @@ def measured_traffic(workload):
     return t.get("workloads", {}).get(workload)
 
 
-def algorithmic(cfg, fused=False):
+def algorithmic(cfg, fused=False, gather=None):
     """Per library call: (flops, bytes, peak TFLOP/s of its arithmetic) that
     the method itself needs -- every tensor read or written once, weights
-    once, intermediates written once and read once.  fused: the permute is
-    fused into the expert GEMM (indices only; the GEMM reads x, not X_perm)."""
+    once, intermediates written once and read once.  fused: the permute moves
+    indices only (no X_perm).  gather (default: fused): the up-projection
+    reads its rows from x through token_of, not from X_perm."""
+    gather = fused if gather is None else gather
     T, d, E, k, f, A = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.T * cfg.k
     xb = 2 if cfg.dtype == "bf16" else 4
     gu = A * 2 * f * 2 if cfg.train else 0                  # saved G|U (training)
-    rows_in = T * d * xb if fused else A * d * xb           # the up-projection's input rows
+    rows_in = T * d * xb if gather else A * d * xb          # the up-projection's input rows
     out = {
         "route": (2.0 * T * d * E, T * d * xb + E * d * 4 + T * E * 4 + T * k * 8, 157.3),
         "permute": (0, (0 if fused else T * d * xb + A * d * xb) + T * k * 8 + A * 4, None),
@@ -349,7 +351,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--no-fwd", action="store_true", help="skip the forward-only line on the 64-expert shape")
     ap.add_argument("--no-fuse-permute", action="store_true",
-                    help="forward workloads: copy X_perm (moe_permute) instead of the expert GEMM gathering x rows")
+                    help="the up-projection reads X_perm rows instead of gathering x rows through token_of (forward workloads then copy X_perm)")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs of this bench into profiles/traffic.json")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "STEPS"),
@@ -450,8 +452,9 @@ def main():
     # per-call rooflines: algorithmic work per call / the call's event time
     traffic = measured_traffic(cfg.name)
     rooflines = {}
-    fused = not train and not a.no_fuse_permute
-    for call, (flops, nbytes, peak_flops) in algorithmic(cfg, fused).items():
+    gather = not a.no_fuse_permute                 # the up-projection reads x through token_of
+    fused = gather and not train                   # and then no X_perm is written (training keeps it)
+    for call, (flops, nbytes, peak_flops) in algorithmic(cfg, fused, gather).items():
         if call not in calls:
             continue
         t = calls[call] * 1e-3
@@ -472,7 +475,9 @@ def main():
            "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": describe(cfg, train) + (", permute fused into the expert GEMM"
-                                                          if not a.no_fuse_permute and not train else ""),
+                                                          if fused else
+                                                          ", up-projection reads x through token_of"
+                                                          if gather else ""),
                       "global_batch": cfg.T, "seq_len": None,
                       "parallelism": "none (1 GPU)"},
            "eager_ms_per_step": round(eager_ms, 4), "step_mode": "eager" if a.no_graph else "hip_graph_replay",

@@ -35,7 +35,7 @@ class Shape:
     router: str = "learned"          # "learned" (scores, top-k) or "hash" (token ids, gates 1/k)
     salt: int = 0                    # hash router: per-layer salt
     aux_alpha: float = 0.0           # weight of the auxiliary load-balancing loss (0: off)
-    fuse_permute: bool = True        # forward only: the expert GEMM gathers x rows, no X_perm copy
+    fuse_permute: bool = True        # the up-projection gathers x rows (forward only: no X_perm copy)
 
 
 def expert_capacity(factor: float, T: int, k: int, E: int) -> int:
@@ -109,10 +109,11 @@ class MoELayer:
         self.offsets = z(E + 1, dtype=torch.int32)
         self.row_of = z(T, k, dtype=torch.int32)
         self.token_of = z(A, dtype=torch.int32)
-        # a forward-only layer fuses the permute into the expert GEMM (it reads
-        # x through token_of); training keeps X_perm for the weight gradients
-        self.gather = s.fuse_permute and not s.train
-        self.x_perm = None if self.gather else z(A, d, dtype=dt)
+        # the up-projection reads x through token_of (the permute fused into
+        # the expert GEMM); a forward-only layer then writes no X_perm, and
+        # training still writes it for the weight gradient of W_gate_up
+        self.gather = s.fuse_permute
+        self.x_perm = None if (self.gather and not s.train) else z(A, d, dtype=dt)
         self.gu = z(A, 2 * f, dtype=dt) if s.train else None
         self.h = z(A, f, dtype=dt)
         self.y_perm = z(A, d)
@@ -161,11 +162,11 @@ class MoELayer:
         with _span(timer, "permute", stream):
             if s.capacity is None:
                 L.moe_permute(self.idx, x, s.E, self.counts, self.offsets, self.row_of, self.token_of, self.x_perm,
-                              workspace=self.ws_perm, stream=stream, copy=not self.gather)
+                              workspace=self.ws_perm, stream=stream, copy=self.x_perm is not None)
             else:
                 L.moe_permute_capacity(self.idx, x, s.E, s.capacity, self.counts, self.offsets, self.row_of,
                                        self.token_of, self.x_perm, workspace=self.ws_perm, stream=stream,
-                                       copy=not self.gather)
+                                       copy=self.x_perm is not None)
         with _span(timer, "grouped_ffn", stream):
             if self.gather:
                 L.moe_grouped_ffn_gather(x, self.token_of, self.offsets, self.w_gate_up, self.w_down, self.gu,
