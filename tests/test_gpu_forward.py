@@ -78,6 +78,28 @@ def test_route_ties_go_to_lower_index():
     assert np.all(idx[strong] == np.array([2, 7]))
 
 
+@pytest.mark.parametrize("E", [64, 40, 17, 100])
+def test_route_all_keys_equal(E):
+    """Zero input rows give every expert the same key: the choice is experts
+    0..k-1 in index order with equal gates (the tie rule read into the
+    lesson's Build it step 1: lower index first), both on the one-key-per-lane
+    path (E <= 64) and
+    on the argmax rounds (E > 64); the other rows follow the oracle."""
+    say(f"[route all keys equal E={E}]")
+    T, d, k = 96, 64, 8
+    r = np.random.default_rng(E)
+    x = r.standard_normal((T, d)).astype(np.float32)
+    x[::2] = 0.0
+    w = (r.standard_normal((E, d)) * 0.1).astype(np.float32)
+    for score in oracle.SCORE_FNS:
+        idx, gate, logits = L.moe_route(dev(x), dev(w), k, score, None, None)
+        idx, gate = host(idx), host(gate)
+        assert np.all(idx[::2] == np.arange(k)), score
+        assert np.allclose(gate[::2], 1.0 / k, rtol=0, atol=1e-7), score
+        ref = oracle.route(x, w, k, score)
+        check_route(idx, gate, host(logits), ref, k)
+
+
 def test_route_fp32_not_bf16_winner():
     """fp32-distinct, bf16-equal router rows: the GPU router picks the true
     winner, which a bf16 router would not."""
