@@ -83,8 +83,8 @@ def test_route_all_keys_equal(E):
     """Zero input rows give every expert the same key: the choice is experts
     0..k-1 in index order with equal gates (the tie rule read into the
     lesson's Build it step 1: lower index first), both on the one-key-per-lane
-    path (E <= 64) and
-    on the argmax rounds (E > 64); the other rows follow the oracle."""
+    path (E <= 64) and on the argmax rounds (E > 64); the other rows follow
+    the oracle."""
     say(f"[route all keys equal E={E}]")
     T, d, k = 96, 64, 8
     r = np.random.default_rng(E)
