@@ -324,10 +324,11 @@ def test_ffn_tiny_f32():
     _ffn_case(cfg, offsets, x, inp["w_gate_up"], inp["w_down"])
 
 
-@pytest.mark.parametrize("d,f,seg", [(128, 64, [0, 1, 129, 129, 300, 557]), (256, 192, [0, 0, 0, 1000]),
-                                     (192, 128, [0, 128, 256, 384]),     # <= 256 rows per group: 256x256 tiles
-                                     (128, 128, [0, 300, 650, 1000]),    # 256..512 rows per group: 128x128 tiles
-                                     # >= 512 rows per group: the 256x256 tile configuration
+@pytest.mark.parametrize("d,f,seg", [# f not a multiple of 128: 128x128 tiles
+                                     (128, 64, [0, 1, 129, 129, 300, 557]), (256, 192, [0, 0, 0, 1000]),
+                                     # f a multiple of 128: 256x256 tiles; groups and ragged ends of at
+                                     # most 128 rows run as 128x256 half tiles
+                                     (192, 128, [0, 128, 256, 384]), (128, 128, [0, 300, 650, 1000]),
                                      (256, 256, [0, 600, 1300, 1301, 2600]), (384, 384, [0, 0, 2048, 2049, 2049])])
 def test_ffn_bf16_tiles_and_tails(d, f, seg):
     say(f"[ffn bf16 d={d} f={f} seg={seg}]")
@@ -337,10 +338,13 @@ def test_ffn_bf16_tiles_and_tails(d, f, seg):
     _ffn_case(cfg, np.array(seg), inp["x"], inp["w_gate_up"], inp["w_down"])
 
 
-def test_ffn_bf16_many_groups():
-    say("[ffn bf16 300 groups]")
+@pytest.mark.parametrize("f", [64, 128])
+def test_ffn_bf16_many_groups(f):
+    """300 groups of 0..299 rows: 128x128 tiles (f = 64), and 256x256 tiles
+    with most groups on 128x256 half tiles (f = 128)."""
+    say(f"[ffn bf16 300 groups f={f}]")
     rng = np.random.default_rng(3)
-    G, d, f = 300, 128, 64
+    G, d = 300, 128
     n = rng.integers(0, 300, G)
     n[::7] = 0
     offsets = np.concatenate([[0], np.cumsum(n)])
