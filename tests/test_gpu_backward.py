@@ -149,11 +149,13 @@ def test_backward_hash_router():
     check_close(host(layer.dw_gate_up), g["dw_gate_up"], "bf16", "dW_gate_up")
 
 
-def test_backward_empty_and_skewed_experts():
+@pytest.mark.parametrize("f", [64, 128])
+def test_backward_empty_and_skewed_experts(f):
     """Experts that receive no token get exactly zero weight gradients; one
-    expert holding most rows spans many K tiles."""
-    say("[backward skew]")
-    cfg = scaled(CONFIGS["train"], T=600, d=128, E=16, k=2, f=64, score="sigmoid")
+    expert holding most rows spans many K tiles.  f = 128 puts the data
+    gradients on 256x256 tiles, the few-row experts on half tiles."""
+    say(f"[backward skew f={f}]")
+    cfg = scaled(CONFIGS["train"], T=600, d=128, E=16, k=2, f=f, score="sigmoid")
     inp = make_inputs(cfg)
     off = np.zeros(cfg.E, np.float32)
     off[3], off[7] = 6.0, 5.0          # nearly every token picks experts 3 and 7
