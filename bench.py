@@ -190,7 +190,8 @@ def algorithmic(cfg, fused=False, gather=None):
     the method itself needs -- every tensor read or written once, weights
     once, intermediates written once and read once.  fused: the permute moves
     indices only (no X_perm).  gather (default: fused): the up-projection
-    reads its rows from x through token_of, not from X_perm."""
+    (and in training W_gate_up's weight gradient) reads its rows from x
+    through token_of, not from X_perm."""
     gather = fused if gather is None else gather
     T, d, E, k, f, A = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.T * cfg.k
     xb = 2 if cfg.dtype == "bf16" else 4
@@ -209,8 +210,9 @@ def algorithmic(cfg, fused=False, gather=None):
         out["shared_ffn"] = (6.0 * T * d * fs, T * d * xb + 3 * d * fs * xb + 2 * T * fs * xb + T * d * 4,
                              PEAK_BF16_TFLOPS)
     if cfg.train:
-        # inputs dY, Y, X_perm, G|U, H, weights; outputs dx, dW; dY_perm, dG|U, dX_perm written and read once
-        nbytes = (T * d * 2 + A * d * 4 + A * d * 2 + A * 2 * f * 2 + A * f * 2 + 3 * E * d * f * 2
+        # inputs dY, Y, x (or X_perm), G|U, H, weights; outputs dx, dW; dY_perm, dG|U, dX_perm written and
+        # read once
+        nbytes = (T * d * 2 + A * d * 4 + rows_in + A * 2 * f * 2 + A * f * 2 + 3 * E * d * f * 2
                   + T * d * 4 + 3 * E * d * f * 4 + 2 * (A * d * 2 + A * 2 * f * 2 + A * d * 4))
         out["backward"] = (12.0 * A * d * f + 4.0 * A * d, nbytes, PEAK_BF16_TFLOPS)
     return out
@@ -351,7 +353,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--no-fwd", action="store_true", help="skip the forward-only line on the 64-expert shape")
     ap.add_argument("--no-fuse-permute", action="store_true",
-                    help="the up-projection reads X_perm rows instead of gathering x rows through token_of (forward workloads then copy X_perm)")
+                    help="the permute copies X_perm, and the up-projection and W_gate_up's weight gradient read it, "
+                         "instead of gathering x rows through token_of")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs of this bench into profiles/traffic.json")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "STEPS"),
@@ -452,8 +455,8 @@ def main():
     # per-call rooflines: algorithmic work per call / the call's event time
     traffic = measured_traffic(cfg.name)
     rooflines = {}
-    gather = not a.no_fuse_permute                 # the up-projection reads x through token_of
-    fused = gather and not train                   # and then no X_perm is written (training keeps it)
+    gather = not a.no_fuse_permute                 # the expert GEMMs read x through token_of
+    fused = gather                                 # and then no X_perm is written
     for call, (flops, nbytes, peak_flops) in algorithmic(cfg, fused, gather).items():
         if call not in calls:
             continue
@@ -474,10 +477,8 @@ def main():
     res = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
            "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": describe(cfg, train) + (", permute fused into the expert GEMM"
-                                                          if fused else
-                                                          ", up-projection reads x through token_of"
-                                                          if gather else ""),
+           "config": {"workload": describe(cfg, train) + (", permute fused into the expert GEMMs"
+                                                          if fused else ""),
                       "global_batch": cfg.T, "seq_len": None,
                       "parallelism": "none (1 GPU)"},
            "eager_ms_per_step": round(eager_ms, 4), "step_mode": "eager" if a.no_graph else "hip_graph_replay",

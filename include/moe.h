@@ -349,7 +349,9 @@ typedef struct moe_bwd_args {
   const int32_t* row_of;       /* [T, k] */
   const int32_t* token_of;     /* [T*k] */
   const int32_t* offsets;      /* [E+1] */
-  const void* x_perm;          /* [T*k, d] bf16 */
+  const void* x_perm;          /* [T*k, d] bf16, or NULL: the weight gradient
+                                  of W_gate_up then reads row token_of[r] of x
+                                  for row r (no X_perm buffer needed) */
   const void* gu_saved;        /* [T*k, 2f] bf16 */
   const void* h;               /* [T*k, f] bf16 */
   const float* y_perm;         /* [T*k, d] f32 */

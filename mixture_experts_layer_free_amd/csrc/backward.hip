@@ -13,7 +13,9 @@
 //                    reduction: deterministic)
 //   3. dgrad down    dH = dY_perm W_down, epilogue SwiGLU backward -> dG|dU
 //   4. wgrad down    dW_down[e] = dY_perm^T H over e's rows
-//   5. wgrad up      dW_gate_up[e] = [dG|dU]^T X_perm over e's rows
+//   5. wgrad up      dW_gate_up[e] = [dG|dU]^T X_perm over e's rows (with
+//                    no X_perm given, its rows are read from x through
+//                    token_of inside the GEMM's slab loads)
 //   6. dgrad up      dX_perm = [dG|dU] W_gate_up (fp32)
 //   7. unpermute_bwd one wave per token: dx = sum_j dX_perm[row] + sum_j dl*W_r[e]
 // With an expert capacity (moe_permute_capacity), a dropped assignment has
@@ -346,7 +348,7 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   if (T < 1 || d < 1 || f < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
   if (a->score_fn < MOE_SOFTMAX_CHOSEN || a->score_fn > MOE_UNIFORM_GATES) return MOE_EINVAL;
   const bool router = a->score_fn != MOE_UNIFORM_GATES;
-  if (!a->dy || !a->x || !a->topk_idx || !a->topk_gate || !a->row_of || !a->token_of || !a->offsets || !a->x_perm ||
+  if (!a->dy || !a->x || !a->topk_idx || !a->topk_gate || !a->row_of || !a->token_of || !a->offsets ||
       !a->gu_saved || !a->h || !a->y_perm || !a->w_gate_up || !a->w_down || !a->dx || !a->dw_gate_up || !a->dw_down)
     return MOE_EINVAL;
   if (router && (!a->w_router || !a->logits || !a->dw_router)) return MOE_EINVAL;
@@ -432,11 +434,20 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   {  // 5. dW_gate_up[e] = [dG|dU]^T X_perm
     Args g{};
     g.A = dgu; g.lda = 2 * f;
-    g.B = x_perm; g.ldb = d;
+    g.ldb = d;
     g.M = 2 * f; g.N = d;
     g.offsets = a->offsets; g.G = E;
     g.out = a->dw_gate_up; g.ldo = d; g.out_group = 2 * f * d;
-    st = launch_gemm<false, false, true, EPI_F32>(g, 2 * f >= BM_LARGE && d >= BN_LARGE, 0, s);
+    const bool large = 2 * f >= BM_LARGE && d >= BN_LARGE;
+    if (x_perm) {
+      g.B = x_perm;
+      st = launch_gemm<false, false, true, EPI_F32>(g, large, 0, s);
+    } else {
+      g.B = static_cast<const bf16_t*>(a->x);
+      g.b_gather = a->token_of;
+      g.b_gather_rows = T;
+      st = launch_gemm<false, false, true, EPI_F32, true>(g, large, 0, s);
+    }
     if (st != MOE_OK) return st;
   }
   {  // 6. dX_perm = [dG|dU] W_gate_up

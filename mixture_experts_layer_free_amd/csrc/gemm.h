@@ -85,7 +85,23 @@ struct Args {
   // A, which has a_rows_total rows (the permute fused into the operand load)
   const int32_t* a_rows;
   int64_t a_rows_total;
+  // K-grouped with a K-strided B only (GB kernels): reduction row r reads
+  // row b_gather[r] of B, which has b_gather_rows rows
+  const int32_t* b_gather;
+  int64_t b_gather_rows;
 };
+
+// p[i] for a wave-uniform i, loaded through the scalar cache (constant
+// address space): p must not change while the kernel runs.
+__device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p, int64_t i) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef const __attribute__((address_space(4))) int32_t* cptr;
+  return reinterpret_cast<cptr>(reinterpret_cast<uintptr_t>(p))[i];
+#else
+  (void)p, (void)i;   // the host pass never runs device code
+  return 0;
+#endif
+}
 
 typedef __attribute__((address_space(3))) void lds_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -154,7 +170,7 @@ __device__ __forceinline__ void interleave() {
 // One output tile: TM x TN, the four waves WM x WN (WM = 4 / WN), each
 // (TM / WM) x (TN / WN) of 32x32 MFMA blocks; operand slabs, main loop and
 // epilogue as described at the top of this file.
-template <int TM, int TN, int WN, bool AK, bool BKC, bool KG, int EPI>
+template <int TM, int TN, int WN, bool AK, bool BKC, bool KG, int EPI, bool GB>
 __device__ __forceinline__ void gemm_tile(const Args& p, char* smem, int e, int nb, int64_t row0, int64_t row_end,
                                           int64_t kbeg, int64_t kend) {
   constexpr int WTM = TM / (4 / WN), WTN = TN / WN, FM = WTM / 32, FN = WTN / 32;
@@ -228,6 +244,20 @@ __device__ __forceinline__ void gemm_tile(const Args& p, char* smem, int e, int 
       }
       b_voff[q] = (uint32_t)(n * p.ldb * 2 + c * 16);
     }
+  } else if (GB) {
+    // gathered rows: the buffer spans all of B; b_voff holds the column part
+    // of each load, the row part comes per slab from b_gather (gb_rows below)
+    b_base = p.B;
+    b_bytes = p.b_gather_rows * p.ldb * 2;
+    b_step = 0;
+    constexpr int CPR = TN / 8;
+#pragma unroll
+    for (int q = 0; q < LB; ++q) {
+      const int idx = (wave * LB + q) * 64 + lane;
+      const int k = idx / CPR, pc = idx % CPR;
+      const int c = pc ^ swz_ks(k);
+      b_voff[q] = (uint32_t)(((int64_t)nb * TN + c * 8) * 2);
+    }
   } else {
     const bf16_t* Bk = KG ? p.B + kbeg * p.ldb : p.B + (int64_t)e * p.b_group;
     b_base = Bk;
@@ -250,21 +280,66 @@ __device__ __forceinline__ void gemm_tile(const Args& p, char* smem, int e, int 
   // so the statement exists in the device pass only.
   const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(uni(a_base), uni(a_bytes));
   const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(uni(b_base), uni(b_bytes));
+
+  // Gathered B (GB): a wave's loads of one slab cover its rows 8*wave ..
+  // 8*wave+7 (BK/4 rows, since each wave moves a quarter of the slab).  Their
+  // row indices are read with scalar loads one slab ahead (gb_rows); a row
+  // past the group's end gets -1.  gb_voffs turns them into the per-lane
+  // byte offsets of a slab's loads; a row outside B (or -1) gets an offset
+  // past the buffer, so its load reads zeros.
+  static_assert(!GB || (KG && !BKC && LB * 64 / (TN / 8) == 8), "gathered B: K-grouped, K-strided, 8 rows per wave");
+  const int wv = (int)uni((uint32_t)wave);
+  // (held as a vector value, not an array: a lane-dependent choice between
+  // two elements of an array becomes an indexed load from scratch memory)
+  typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+  // The loaded values are first used a step later (gb_voffs), so the wait
+  // for the scalar loads never holds up a step's LDS reads.
+  auto gb_row0 = [&](int slab) -> int64_t { return uni(kbeg + (int64_t)uni((uint32_t)slab) * BK + 8 * wv); };
+  auto gb_rows = [&](int slab) -> i32x8 {
+    const int64_t r0 = gb_row0(slab);
+    i32x8 t;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = r0 + i;
+      t[i] = scalar_load_i32(p.b_gather, r < kend ? r : kbeg);   // kbeg < kend: a row of the group
+    }
+    return t;
+  };
+  // each load of a wave covers RPL consecutive rows of its 8 (64 lanes of
+  // 16 bytes, TN / 8 lanes per row): lane l of load q takes row q*RPL + l/(TN/8)
+  constexpr int RPL = 64 / (TN / 8);
+  static_assert(!GB || RPL == 2 || RPL == 4, "gathered B: 2 or 4 rows per load");
+  const bool gb_b0 = (lane / (TN / 8)) & 1, gb_b1 = (lane / (TN / 8)) & 2;
+  const uint32_t gb_rb = (uint32_t)(p.ldb * 2), gb_nrows = (uint32_t)p.b_gather_rows;
+  auto gb_voffs = [&](int slab, i32x8 t, uint32_t (&vo)[LB]) {
+    const int64_t r0 = gb_row0(slab);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = r0 + i < kend ? t[i] : -1;   // rows past the group's end
+#pragma unroll
+    for (int q = 0; q < LB; ++q) {
+      int32_t row = gb_b0 ? t[q * RPL + 1] : t[q * RPL];
+      if constexpr (RPL == 4) row = gb_b1 ? (gb_b0 ? t[q * RPL + 3] : t[q * RPL + 2]) : row;
+      // B has under 2^31 bytes, so a row inside it gives a 32-bit offset;
+      // -1 and any row outside B go past the buffer
+      vo[q] = (uint32_t)row < gb_nrows ? (uint32_t)row * gb_rb + b_voff[q] : 0x80000000u;
+    }
+  };
 #if defined(__HIP_DEVICE_COMPILE__)
-#define MOE_ISSUE(slab_)                                                                             \
+#define MOE_ISSUE(slab_, gvo_)                                                                       \
 do {                                                                                               \
   const int slab = (slab_);                                                                        \
   const bool live_ = slab < nk;   /* a slab past the end is pushed out of range: its loads read zeros */ \
   char* st_ = smem + (slab % STAGES) * STAGE;                                                      \
   _Pragma("unroll") for (int q = 0; q < LA; ++q)                                                   \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_t*)(st_ + (wave * LA + q) * 1024), 16, a_voff[q], \
-                                             live_ ? (uint32_t)slab * a_step : 0x80000000u, 0, 0); \
+                                             uni(live_ ? (uint32_t)slab * a_step : 0x80000000u), 0, 0); \
   _Pragma("unroll") for (int q = 0; q < LB; ++q)                                                   \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_t*)(st_ + SA + (wave * LB + q) * 1024), 16,      \
-                                             b_voff[q], live_ ? (uint32_t)slab * b_step : 0x80000000u, 0, 0); \
+                                             GB ? (gvo_)[q] : b_voff[q],                           \
+                                             uni(GB ? 0u : live_ ? (uint32_t)slab * b_step : 0x80000000u), 0, 0); \
 } while (0)
 #else
-#define MOE_ISSUE(slab_) ((void)(slab_))
+#define MOE_ISSUE(slab_, gvo_) ((void)(slab_), (void)(gvo_))
 #endif
 
   // fragment byte offsets inside a stage for the 16-deep step kk
@@ -340,13 +415,23 @@ do {                                                                            
   // GEMM is a multiple of 64; a K-grouped tile rounds up and its extra slab
   // reads zeros past the group's rows).  On the last step the reads fetch a
   // stage whose contents are never used.
-#define MOE_STEP(it_, ca, cb, na, nb_)                                                            \
+  // With a gathered B, the step first turns the row indices read one step
+  // earlier (tc) into load offsets, in a scheduling region of its own (its
+  // wait for the scalar loads then covers those loads only), and starts the
+  // scalar loads of the next slab's rows (tn).
+#define MOE_STEP(it_, ca, cb, na, nb_, tc, tn)                                                    \
 do {                                                                                          \
   const int it = (it_);                                                                       \
   wait_vmcnt<LPS>();                                                                          \
   block_barrier();                                                                            \
+  uint32_t gvo[LB];                                                                           \
+  if constexpr (GB) {                                                                         \
+    gb_voffs(it + STAGES - 1, tc, gvo);                                                       \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+    tn = gb_rows(it + STAGES);                                                                \
+  }                                                                                           \
   read_frags(smem + ((it + 1) % STAGES) * STAGE, na, nb_);                                    \
-  MOE_ISSUE(it + STAGES - 1);                                                                 \
+  MOE_ISSUE(it + STAGES - 1, gvo);                                                            \
   mfmas(ca, cb);                                                                              \
   interleave<NMFMA, NREAD, LPS>();                                                            \
   __builtin_amdgcn_sched_barrier(0);                                                          \
@@ -355,15 +440,29 @@ do {                                                                            
   // Stores of the previous tile's epilogue may still be in flight: they are
   // older than this tile's loads, so the load waits below cover them too.
   if (nk > 0) {
+    i32x8 tk0 = {}, tk1 = {};   // gathered B: row indices of the slab the next step loads, and of the one after
+    if constexpr (GB) {
+      static_assert(STAGES == 4, "gathered-B prologue");
+      const i32x8 t0 = gb_rows(0), t1 = gb_rows(1), t2 = gb_rows(2);
+      uint32_t v0[LB], v1[LB], v2[LB];
+      gb_voffs(0, t0, v0);
+      gb_voffs(1, t1, v1);
+      gb_voffs(2, t2, v2);
+      tk0 = gb_rows(3);
+      MOE_ISSUE(0, v0);
+      MOE_ISSUE(1, v1);
+      MOE_ISSUE(2, v2);
+    } else {
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) MOE_ISSUE(s);
+      for (int s = 0; s < STAGES - 1; ++s) MOE_ISSUE(s, b_voff);
+    }
     bf16x8 fa0[2][FM], fb0[2][FN], fa1[2][FM], fb1[2][FN];
     wait_vmcnt<(STAGES - 2) * LPS>();
     block_barrier();
     read_frags(smem, fa0, fb0);
     for (int it2 = 0; it2 < nk; it2 += 2) {
-      MOE_STEP(it2, fa0, fb0, fa1, fb1);
-      MOE_STEP(it2 + 1, fa1, fb1, fa0, fb0);
+      MOE_STEP(it2, fa0, fb0, fa1, fb1, tk0, tk1);
+      MOE_STEP(it2 + 1, fa1, fb1, fa0, fb0, tk1, tk0);
     }
     wait_vmcnt<0>();   // the out-of-range tail loads still land in the ring
     block_barrier();   // every wave is done with the ring before the epilogue stages in it
@@ -509,7 +608,7 @@ do {                                                                            
   block_barrier();   // staging areas sit in the ring: free them before the next tile's loads
 }
 
-template <int TM, int TN, bool AK, bool BKC, bool KG, int EPI>
+template <int TM, int TN, bool AK, bool BKC, bool KG, int EPI, bool GB>
 __global__ __launch_bounds__(256, (TM * TN > 128 * 128) ? 1 : 2)
 __attribute__((amdgpu_waves_per_eu((TM * TN > 128 * 128) ? 1 : 2, (TM * TN > 128 * 128) ? 1 : 2)))
 void gemm_kernel(Args p) {
@@ -557,11 +656,11 @@ void gemm_kernel(Args p) {
     // loads, the same weight reads.
     if constexpr (TM == 256 && TN == 256 && AK && !KG) {
       if (uni(row_end - row0) <= TM / 2) {
-        gemm_tile<TM / 2, TN, 4, AK, BKC, KG, EPI>(p, smem, e, nb, row0, row_end, kbeg, kend);
+        gemm_tile<TM / 2, TN, 4, AK, BKC, KG, EPI, GB>(p, smem, e, nb, row0, row_end, kbeg, kend);
         continue;
       }
     }
-    gemm_tile<TM, TN, 2, AK, BKC, KG, EPI>(p, smem, e, nb, row0, row_end, kbeg, kend);
+    gemm_tile<TM, TN, 2, AK, BKC, KG, EPI, GB>(p, smem, e, nb, row0, row_end, kbeg, kend);
   }
 }
 
@@ -589,7 +688,7 @@ moe_status lds_attr_once(std::atomic<int> (&done)[kMaxAttrDevices], K* fn, int b
 // (row-grouped only) bounds the row tiles: sum over groups of
 // ceil(n_g/TM) <= ceil(rows/TM) + G.  a.mt_prefix must have been built with
 // bm = TM.
-template <int TM, int TN, bool AK, bool BKC, bool KG, int EPI>
+template <int TM, int TN, bool AK, bool BKC, bool KG, int EPI, bool GB = false>
 moe_status launch_cfg(Args a, int64_t rows, hipStream_t s) {
   a.NB = EPI == EPI_SWIGLU ? (int)(a.N / (TN / 2)) : (int)ceil_div(a.N, TN);
   int64_t tiles;
@@ -601,17 +700,17 @@ moe_status launch_cfg(Args a, int64_t rows, hipStream_t s) {
   }
   constexpr int lds = lds_bytes<TM, TN>();
   static std::atomic<int> attr_done[kMaxAttrDevices];
-  const moe_status attr = lds_attr_once(attr_done, &gemm_kernel<TM, TN, AK, BKC, KG, EPI>, lds);
+  const moe_status attr = lds_attr_once(attr_done, &gemm_kernel<TM, TN, AK, BKC, KG, EPI, GB>, lds);
   if (attr != MOE_OK) return attr;
-  gemm_kernel<TM, TN, AK, BKC, KG, EPI><<<grid_for(tiles, TM * TN > 128 * 128 ? 1 : 2), 256, lds, s>>>(a);
+  gemm_kernel<TM, TN, AK, BKC, KG, EPI, GB><<<grid_for(tiles, TM * TN > 128 * 128 ? 1 : 2), 256, lds, s>>>(a);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
 
-template <bool AK, bool BKC, bool KG, int EPI>
+template <bool AK, bool BKC, bool KG, int EPI, bool GB = false>
 moe_status launch_gemm(const Args& a, bool large, int64_t rows, hipStream_t s) {
-  return large ? launch_cfg<BM_LARGE, BN_LARGE, AK, BKC, KG, EPI>(a, rows, s)
-               : launch_cfg<BM, BN, AK, BKC, KG, EPI>(a, rows, s);
+  return large ? launch_cfg<BM_LARGE, BN_LARGE, AK, BKC, KG, EPI, GB>(a, rows, s)
+               : launch_cfg<BM, BN, AK, BKC, KG, EPI, GB>(a, rows, s);
 }
 
 // Tile choice of a row-grouped GEMM: the large tile whenever the SwiGLU

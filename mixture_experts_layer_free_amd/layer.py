@@ -35,7 +35,7 @@ class Shape:
     router: str = "learned"          # "learned" (scores, top-k) or "hash" (token ids, gates 1/k)
     salt: int = 0                    # hash router: per-layer salt
     aux_alpha: float = 0.0           # weight of the auxiliary load-balancing loss (0: off)
-    fuse_permute: bool = True        # the up-projection gathers x rows (forward only: no X_perm copy)
+    fuse_permute: bool = True        # the up-projection and W_gate_up's weight gradient gather x rows: no X_perm copy
 
 
 def expert_capacity(factor: float, T: int, k: int, E: int) -> int:
@@ -113,7 +113,7 @@ class MoELayer:
         # the expert GEMM); a forward-only layer then writes no X_perm, and
         # training still writes it for the weight gradient of W_gate_up
         self.gather = s.fuse_permute
-        self.x_perm = None if (self.gather and not s.train) else z(A, d, dtype=dt)
+        self.x_perm = None if self.gather else z(A, d, dtype=dt)
         self.gu = z(A, 2 * f, dtype=dt) if s.train else None
         self.h = z(A, f, dtype=dt)
         self.y_perm = z(A, d)

@@ -16,16 +16,16 @@ from workloads import CONFIGS, make_inputs, scaled
 pytestmark = pytest.mark.gpu
 
 
-def _layer(cfg, inp, capacity=None, aux_alpha=0.0):
+def _layer(cfg, inp, capacity=None, aux_alpha=0.0, fuse_permute=True):
     from mixture_experts_layer_free_amd.layer import MoELayer, Shape
     s = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, torch.bfloat16, cfg.score, 0, 0, False, cfg.gamma, True,
-              capacity=capacity, aux_alpha=aux_alpha)
+              capacity=capacity, aux_alpha=aux_alpha, fuse_permute=fuse_permute)
     return MoELayer(s, dev(inp["w_router"]), dev(inp["w_gate_up"]), dev(inp["w_down"]), dev(inp["bias"].copy()),
                     dev(inp["logit_offset"]))
 
 
-def _run(cfg, inp, capacity=None, aux_alpha=0.0):
-    layer = _layer(cfg, inp, capacity, aux_alpha)
+def _run(cfg, inp, capacity=None, aux_alpha=0.0, fuse_permute=True):
+    layer = _layer(cfg, inp, capacity, aux_alpha, fuse_permute)
     x = dev(inp["x"])
     layer.forward(x)
     layer.backward(x, dev(inp["dy"]))
@@ -147,6 +147,24 @@ def test_backward_hash_router():
     check_close(host(layer.dx), g["dx"], "bf16", "dx")
     check_close(host(layer.dw_down), g["dw_down"], "bf16", "dW_down")
     check_close(host(layer.dw_gate_up), g["dw_gate_up"], "bf16", "dW_gate_up")
+
+
+@pytest.mark.parametrize("T,d,E,k,f,cap", [(700, 256, 24, 3, 128, None), (1100, 256, 4, 2, 256, None),
+                                           (257, 128, 8, 8, 64, None), (600, 128, 6, 2, 128, 180)])
+def test_backward_gathered_rows_equal_x_perm(T, d, E, k, f, cap):
+    """W_gate_up's weight gradient reading x through token_of (no X_perm)
+    adds the same products in the same order as the one reading X_perm, on
+    both tile shapes, ragged group ends and with dropped slots: every output
+    is bit-identical."""
+    say(f"[backward gathered vs X_perm T={T} d={d} E={E} k={k} f={f} cap={cap}]")
+    cfg = scaled(CONFIGS["train"], T=T, d=d, E=E, k=k, f=f, score="sqrt_softplus", bias="uniform")
+    inp = make_inputs(cfg)
+    a = _run(cfg, inp, capacity=cap, fuse_permute=True)
+    b = _run(cfg, inp, capacity=cap, fuse_permute=False)
+    assert a.x_perm is None and b.x_perm is not None
+    for name in ("dw_gate_up", "dw_down", "dw_router", "dx", "dgate"):
+        u, v = host(getattr(a, name)), host(getattr(b, name))
+        assert np.array_equal(u.view(np.uint32), v.view(np.uint32)), name
 
 
 @pytest.mark.parametrize("f", [64, 128])
