@@ -244,8 +244,9 @@ moe_status moe_grouped_ffn(const void* x_rows, int64_t rows, int64_t d, int dtyp
  * row r reads row token_of[r] of x (the permute fused into the expert GEMM's
  * operand loads).  The AREX article on The Ultimate MoE Training Handbook, in
  * its paragraph on the handbook's section 3.7, reports that fusing the
- * permute cut the permute/copy kernels' share of the step; with this call a
- * forward pass runs moe_permute with x_perm = NULL and never writes X_perm.
+ * permute cut the permute/copy kernels' share of the step; with this call
+ * (and moe_backward with x_perm = NULL) a forward or training step runs
+ * moe_permute with x_perm = NULL and never writes X_perm.
  *   x          [T, d]        dtype, the layer input
  *   token_of   [rows]        int32 device, from moe_permute (values in
  *                            [0, T); an index outside reads as a zero row)
