@@ -109,9 +109,9 @@ class MoELayer:
         self.offsets = z(E + 1, dtype=torch.int32)
         self.row_of = z(T, k, dtype=torch.int32)
         self.token_of = z(A, dtype=torch.int32)
-        # the up-projection reads x through token_of (the permute fused into
-        # the expert GEMM); a forward-only layer then writes no X_perm, and
-        # training still writes it for the weight gradient of W_gate_up
+        # the up-projection, and in training the weight gradient of W_gate_up,
+        # read x through token_of (the permute fused into the expert GEMMs):
+        # then no X_perm is written
         self.gather = s.fuse_permute
         self.x_perm = None if self.gather else z(A, d, dtype=dt)
         self.gu = z(A, 2 * f, dtype=dt) if s.train else None
