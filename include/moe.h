@@ -114,8 +114,13 @@ moe_status moe_route(const void* x, int x_dtype, int64_t T, int64_t d,
  * inference and force the same routing when computing gradients).  The
  * logits are computed as in moe_route; topk_idx is an input, and the gates
  * follow score_fn over exactly those experts.  Passing moe_route's own
- * choice reproduces its gates.  An id outside [0, E) gets gate 0 and is left
- * out of the normalisation (moe_permute then gives it no row).
+ * choice reproduces its gates.
+ * Precondition: a replayed choice is one a router made, so each row holds k
+ * distinct ids in [0, E).  The library does not check this on the device.
+ * For a row that breaks it the gates, the expert rows and the gradients of
+ * that token are unspecified; the kernels never use such an id as an index,
+ * so every call stays inside its buffers, and the outputs and input
+ * gradients of the other tokens are unaffected.
  *   topk_idx [T, k] int32 in;  topk_gate [T, k] f32 out;  logits_out [T, E] out
  * Errors as moe_route.
  */
@@ -329,9 +334,8 @@ moe_status moe_aux_loss(const float* logits, const int32_t* counts, int64_t T, i
  *             dX_perm = dG W_gate + dU W_up
  *   unpermute: dx[t] = sum_j dX_perm[row_of[t,j]] + dx_r[t]
  * All pointers are device pointers held in a HOST struct.  bf16 layers only.
- * A slot whose expert id lies outside [0, E) (a choice replayed through
- * moe_route_replay) has gate 0 and no row: it gets dg = dl = 0 and adds
- * nothing to any gradient.
+ * An expert id outside [0, E) (which moe_route_replay's precondition rules
+ * out) gives that token unspecified gradients and stays in bounds.
  * score_fn MOE_UNIFORM_GATES (hash routing): dl = 0, there is no router term
  * in dx, w_router / logits may be NULL, and dw_router (if not NULL) is
  * set to zero.

@@ -88,7 +88,8 @@ __global__ __launch_bounds__(256) void combine_bwd_rows_kernel(const bf16_t* __r
 
 // Gate backward, one wave per token (lanes 0..k-1 hold the chosen experts):
 // dl on the chosen experts from dg = dgp[row_of[t,j]].  dg and dl are
-// written for every slot (0 for an expert id outside [0, E)).
+// written for every slot.  An expert id outside [0, E) is invalid input (its
+// token's results are unspecified); such a slot is never used as an index.
 __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__ dgp, const int32_t* __restrict__ row_of,
                                                        const float* __restrict__ gate, const int32_t* __restrict__ idx,
                                                        const float* __restrict__ logits, int T, int k, int E, int fn,
@@ -97,8 +98,8 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  // a slot whose expert id lies outside [0, E) (a replayed choice) has gate 0,
-  // is out of the normalisation and gets no gradient
+  // an expert id outside [0, E) is never used as an index: its slot is left
+  // out of the sums below
   const bool slot = lane < k;
   const int e_in = slot ? idx[t * k + lane] : -1;
   const bool act = slot && e_in >= 0 && e_in < E;
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restr
   if (t >= T) return;
   const int myr = lane < K ? row_of[t * K + lane] : 0;
   const int e_in = lane < K ? idx[t * K + lane] : 0;
-  const int mye = e_in >= 0 && e_in < E ? e_in : 0;   // an id outside [0, E) has dl = 0: any row serves
+  const int mye = e_in >= 0 && e_in < E ? e_in : 0;   // an invalid id is never used as an index
   const float myl = lane < K ? dl[t * K + lane] : 0.f;
   const f32x4* xr[K];
   const f32x4* wr[K];

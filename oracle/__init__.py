@@ -30,7 +30,6 @@ from .moe import (  # noqa: F401
     bf16_from_bits,
     score,
     route,
-    route_token_lesson,
     splitmix_key,
     hash_route,
     aux_probs,

@@ -13,7 +13,6 @@ leaves the layer stay in high precision.
 """
 from __future__ import annotations
 
-import math
 from typing import Optional
 
 import numpy as np
@@ -115,38 +114,6 @@ def route(x, w_router, k: int, score_fn: str, sel_bias=None, logit_offset=None) 
             gates[t] = sc / sc.sum()
     return {"idx": idx, "gates": gates, "logits": logits, "scores": s,
             "keys": keys, "margin": margin}
-
-
-def route_token_lesson(hidden, W_router, top_k, bias, score_fn="softmax", offset=None):
-    """One token routed with plain Python lists and loops (lesson, Build it
-    step 1): E dot products, bias added for the ranking only, a stable sort,
-    then gates from the unbiased values of the chosen experts."""
-    E = len(W_router)
-    raw = []
-    for e in range(E):
-        acc = 0.0
-        for h, w in zip(hidden, W_router[e]):
-            acc += float(h) * float(w)
-        if offset is not None:
-            acc += float(offset[e])
-        raw.append(acc)
-    if score_fn == "softmax":
-        sc = raw[:]
-    elif score_fn == "sigmoid":
-        sc = [1.0 / (1.0 + math.exp(-v)) for v in raw]
-    else:
-        sc = [math.sqrt(max(v, 0.0) + math.log1p(math.exp(-abs(v)))) for v in raw]
-    biased = [sc[e] + float(bias[e]) for e in range(E)]
-    top = sorted(range(E), key=lambda e: -biased[e])[:top_k]
-    if score_fn == "softmax":
-        chosen = [raw[e] for e in top]
-        m = max(chosen)
-        ex = [math.exp(c - m) for c in chosen]
-        tot = sum(ex)
-        return top, [v / tot for v in ex]
-    chosen = [sc[e] for e in top]
-    tot = sum(chosen)
-    return top, [v / tot for v in chosen]
 
 
 # ----------------------------------------------------------------------------
@@ -364,25 +331,32 @@ def forward(x, w_router, w_gate_up, w_down, k: int, score_fn: str, bf16_points: 
 
 
 def _gates_for(r: dict, idx: np.ndarray, score_fn: str) -> np.ndarray:
-    """Gates of a given choice.  An expert id outside [0, E) (a replayed choice
-    may hold one) gets gate 0 and is left out of the normalisation; it has no
-    expert row either (``permute``)."""
+    """Gates of a given choice (routing replay, lesson Exercises item 3: the
+    experts that fired are recorded and the same routing is forced later).
+    A replayed choice is one the router made, so every id lies in [0, E) and a
+    token holds each expert at most once; anything else is not a choice and
+    is rejected."""
     T, k = idx.shape
     E = r["logits"].shape[1]
-    valid = (idx >= 0) & (idx < E)
+    _check_choice(idx, E)
     g = np.zeros((T, k))
     for t in range(T):
-        v = valid[t]
-        if not v.any():
-            continue
         if score_fn == "softmax":
-            raw = r["logits"][t, idx[t, v]]
+            raw = r["logits"][t, idx[t]]
             ex = np.exp(raw - raw.max())
-            g[t, v] = ex / ex.sum()
+            g[t] = ex / ex.sum()
         else:
-            sc = r["scores"][t, idx[t, v]]
-            g[t, v] = sc / sc.sum()
+            sc = r["scores"][t, idx[t]]
+            g[t] = sc / sc.sum()
     return g
+
+
+def _check_choice(idx: np.ndarray, E: int) -> None:
+    if np.any((idx < 0) | (idx >= E)):
+        raise ValueError("an expert id outside [0, E) is not a routing choice")
+    s = np.sort(idx, axis=1)
+    if s.shape[1] > 1 and np.any(s[:, 1:] == s[:, :-1]):
+        raise ValueError("a token holds the same expert twice")
 
 
 # ----------------------------------------------------------------------------
@@ -482,22 +456,18 @@ def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
         dl = np.zeros((T, k))
         dW_r, dx = np.zeros((E, d)), np.zeros((T, d))
     else:
-        # a slot whose expert id lies outside [0, E) has gate 0 and is out of
-        # the normalisation: score 0 there, and no logit gradient
-        valid = (idx >= 0) & (idx < E)
-        safe = np.where(valid, idx, 0)
+        _check_choice(idx, E)
         tt = np.arange(T)[:, None]
-        lc = fwd["logits"][tt, safe]
-        sc = np.where(valid, fwd["scores"][tt, safe], 0.0)
-        with np.errstate(divide="ignore", invalid="ignore"):
-            dl = np.where(valid, gate_backward(dg, gates, lc, sc, score_fn), 0.0)
+        lc = fwd["logits"][tt, idx]
+        sc = fwd["scores"][tt, idx]
+        dl = gate_backward(dg, gates, lc, sc, score_fn)
         if aux_alpha:
             dL = np.zeros((T, E))
-            np.add.at(dL, (np.arange(T)[:, None].repeat(k, 1), safe), dl)
+            np.add.at(dL, (np.arange(T)[:, None].repeat(k, 1), idx), dl)
             dL += aux_grad_logits(fwd["logits"], fwd["counts"], k, score_fn, aux_alpha)
             dW_r, dx = dL.T @ _f64(x), dL @ np.asarray(w_router, np.float64)
         else:
-            dW_r, dx = router_backward(dl, safe, x, w_router)
+            dW_r, dx = router_backward(dl, idx, x, w_router)
     f = np.asarray(w_down).shape[2]
     dW_gu = np.zeros((E, 2 * f, d))
     dW_d = np.zeros((E, d, f))

@@ -156,20 +156,6 @@ def test_bias_moves_selection_not_gates(fn):
         np.testing.assert_allclose(r2["gates"][t], p, rtol=1e-13)
 
 
-@pytest.mark.parametrize("fn", oracle.SCORE_FNS)
-def test_lesson_router_equals_vectorised_router(fn):
-    """The per-token list-and-loop router against the array router."""
-    cfg = CONFIGS["tiny"]
-    inp = make_inputs(cfg)
-    x, w, b = inp["x"], inp["w_router"], inp["bias"]
-    o = np.random.default_rng(9).uniform(-0.2, 0.2, cfg.E)
-    r = oracle.route(x, w, cfg.k, fn, sel_bias=b, logit_offset=o)
-    for t in range(cfg.T):
-        top, g = oracle.route_token_lesson(x[t].tolist(), w.tolist(), cfg.k, b.tolist(), fn, o.tolist())
-        assert top == r["idx"][t].tolist()
-        np.testing.assert_allclose(g, r["gates"][t], rtol=1e-12)
-
-
 def test_margin_definition():
     x = np.array([[1.0, 0.0]])
     w = np.array([[3.0, 0], [2.0, 0], [1.0, 0], [2.0 + 1e-7, 0]])

@@ -125,69 +125,27 @@ def test_hash_layer_backward_matches_finite_differences_and_autograd():
         np.testing.assert_allclose(g[gk], t[k].grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=k)
 
 
-# ---------------------------------------------------------------------------- replayed ids outside [0, E)
+# ---------------------------------------------------------------------------- a replayed choice must be a choice
 
-def _replay_with_invalid(cfg, seed):
-    rng = np.random.default_rng(seed)
-    idx = np.stack([rng.permutation(cfg.E)[:cfg.k] for _ in range(cfg.T)]).astype(np.int64)
-    bad = rng.random(idx.shape) < 0.25
-    idx[bad] = rng.choice([-1, -7, cfg.E, cfg.E + 5], int(bad.sum()))
-    idx[0] = -1                          # a token with no valid slot at all
-    return idx
-
-
-@pytest.mark.parametrize("score", oracle.SCORE_FNS)
-def test_replay_invalid_ids_equal_the_choice_without_them(score):
-    """A replayed slot whose expert id lies outside [0, E) has gate 0, no row
-    and no share of the normalisation: each token's output equals the replay
-    of its valid ids alone (a token without any has output 0)."""
-    cfg = scaled(CONFIGS["tiny"], T=30, score=score)
+@pytest.mark.parametrize("bad", [-1, 8, 1 << 20])
+def test_replay_rejects_ids_outside_the_experts(bad):
+    """Routing replay (lesson, Exercises item 3) forces experts that fired, so
+    each id names one of the E experts; an id outside [0, E) is not a routing
+    choice and the oracle gives it no meaning."""
+    cfg = scaled(CONFIGS["tiny"], T=6)
     inp = make_inputs(cfg)
-    idx = _replay_with_invalid(cfg, 1)
-    a = (inp["w_router"], inp["w_gate_up"], inp["w_down"])
-    o = oracle.forward(inp["x"], *a, cfg.k, score, False, idx=idx)
-    valid = (idx >= 0) & (idx < cfg.E)
-    assert np.all(o["gates"][~valid] == 0) and np.all(o["row_of"][~valid] == np.iinfo(np.int32).min)
-    assert o["counts"].sum() == valid.sum()
-    for t in range(cfg.T):
-        ids = idx[t][valid[t]]
-        if len(ids) == 0:
-            assert np.all(o["out"][t] == 0)
-            continue
-        r = oracle.forward(inp["x"][t:t + 1], *a, len(ids), score, False, idx=ids[None, :])
-        np.testing.assert_allclose(o["out"][t], r["out"][0], rtol=1e-12, atol=1e-14)
-        np.testing.assert_allclose(o["gates"][t][valid[t]], r["gates"][0], rtol=1e-13, atol=0)
+    idx = np.stack([np.arange(cfg.k) + t % 3 for t in range(cfg.T)]).astype(np.int64)
+    idx[2, 1] = bad
+    with pytest.raises(ValueError):
+        oracle.forward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], cfg.k, "softmax", False, idx=idx)
 
 
-@pytest.mark.parametrize("score", oracle.SCORE_FNS)
-def test_replay_invalid_ids_backward_matches_finite_differences(score):
-    """The backward of a replayed choice with invalid slots: such slots pass no
-    gradient to any logit, and the others' gradients match finite differences
-    of the forward with the same choice held fixed."""
-    cfg = scaled(CONFIGS["tiny"], T=16, seed=3, score=score)
+def test_replay_rejects_a_repeated_expert():
+    """A token picks k distinct experts (the lesson's top-k): a replayed row
+    naming one expert twice is not a choice."""
+    cfg = scaled(CONFIGS["tiny"], T=4)
     inp = make_inputs(cfg)
-    idx = _replay_with_invalid(cfg, 2)
-    p = {k: np.asarray(inp[k], np.float64) for k in ("x", "w_router", "w_gate_up", "w_down")}
-    dy = np.random.default_rng(9).standard_normal((cfg.T, cfg.d))
-
-    def run():
-        return oracle.forward(p["x"], p["w_router"], p["w_gate_up"], p["w_down"], cfg.k, score, False, idx=idx)
-
-    fwd = run()
-    g = oracle.backward(fwd, dy, p["x"], p["w_router"], p["w_gate_up"], p["w_down"], score, False)
-    valid = (idx >= 0) & (idx < cfg.E)
-    assert np.all(g["dl"][~valid] == 0) and np.all(g["dg"][~valid] == 0)
-    rng = np.random.default_rng(6)
-    h = 1e-6
-    for name, gname in (("x", "dx"), ("w_router", "dw_router"), ("w_gate_up", "dw_gate_up"), ("w_down", "dw_down")):
-        arr, grad = p[name], g[gname]
-        for _ in range(8):
-            i = tuple(int(rng.integers(0, s)) for s in arr.shape)
-            old = arr[i]
-            arr[i] = old + h
-            lp = float(np.sum(run()["out"] * dy))
-            arr[i] = old - h
-            lm = float(np.sum(run()["out"] * dy))
-            arr[i] = old
-            fd = (lp - lm) / (2 * h)
-            assert abs(fd - grad[i]) <= 1e-7 + 1e-6 * abs(fd), (name, i, fd, grad[i])
+    idx = np.tile(np.arange(cfg.k, dtype=np.int64), (cfg.T, 1))
+    idx[1] = 3
+    with pytest.raises(ValueError):
+        oracle.forward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], cfg.k, "sigmoid", False, idx=idx)
