@@ -208,6 +208,28 @@ moe_status moe_permute_capacity(const int32_t* topk_idx, int64_t T, int k, int E
                                 int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* token_of,
                                 void* x_perm, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the static device scratch behind moe_permute_noalloc. */
+#define MOE_PERMUTE_NOALLOC_SCRATCH (4u << 20)
+
+/*
+ * moe_permute_noalloc — moe_permute with no workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  It calls no allocator:
+ * its scratch (the per-chunk expert histogram) is a static device array of
+ * MOE_PERMUTE_NOALLOC_SCRATCH bytes, one per GPU, held until the process
+ * ends.  Arguments, results and errors as moe_permute (no capacity), plus
+ * ENOTSUP when the histogram, ceil(T*k/256) * E * 4 bytes, exceeds that
+ * size (T*k = 2^20 assignments fit with E up to 256, 2^18 with E up to
+ * 1024); EHIP when the scratch address cannot be looked up.  Every call on one GPU uses that
+ * GPU's one scratch array: calls that may overlap on one GPU (different
+ * streams, host threads) race and give wrong results; order them on one
+ * stream.  Nothing in the scratch has to start at zero.
+ */
+moe_status moe_permute_noalloc(const int32_t* topk_idx, int64_t T, int k, int E,
+                               const void* x, int x_dtype, int64_t d,
+                               int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* token_of,
+                               void* x_perm, void* stream);
+
 /*
  * moe_grouped_ffn — G independent SwiGLU experts over row segments.
  * Lesson, Concept: each expert is an independent FFN, usually SwiGLU.

@@ -21,6 +21,7 @@ MOE_F32, MOE_BF16 = 0, 1
 SCORE = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "uniform": 3}
 MOE_CALL_ROUTE, MOE_CALL_PERMUTE, MOE_CALL_GROUPED_FFN, MOE_CALL_BACKWARD, MOE_CALL_AUX_LOSS = range(5)
 MAX_EXPERTS, MAX_TOPK = 1024, 16
+PERMUTE_NOALLOC_SCRATCH = 4 << 20   # bytes of moe_permute_noalloc's static device scratch
 
 _vp, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
 
@@ -44,6 +45,7 @@ _SIGS = {
     "moe_route_replay": [_vp, _int, _i64, _i64, _vp, _vp, _int, _int, _int, _vp, _vp, _vp, _vp],
     "moe_route_hash": [_vp, _i64, _int, _int, ctypes.c_uint32, _vp, _vp, _vp],
     "moe_permute": [_vp, _i64, _int, _int, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_permute_noalloc": [_vp, _i64, _int, _int, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_permute_capacity": [_vp, _i64, _int, _int, _i64, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_grouped_ffn": [_vp, _i64, _i64, _int, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_grouped_ffn_gather": [_vp, _i64, _vp, _i64, _i64, _int, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
@@ -223,6 +225,28 @@ def moe_permute(topk_idx, x, E, counts=None, offsets=None, row_of=None, token_of
     _check("moe_permute", lib().moe_permute(_p(topk_idx), T, k, E, _p(x), _dtype_code(x), d, _p(counts),
                                             _p(offsets), _p(row_of), _p(token_of), _p(x_perm), _p(ws),
                                             n, _stream(stream)))
+    return counts, offsets, row_of, token_of, x_perm
+
+
+def moe_permute_noalloc(topk_idx, x, E, counts=None, offsets=None, row_of=None, token_of=None, x_perm=None,
+                        stream=None, copy=True):
+    """moe_permute without a workspace: the library's static per-GPU scratch
+    is used (calls that overlap on one GPU race).  Outputs a caller passes in
+    are written in place; copy=False: indices only."""
+    T, k = topk_idx.shape
+    d = x.shape[1]
+    _req(topk_idx, "topk_idx", torch.int32)
+    _req(x, "x")
+    dev = x.device
+    A = T * k
+    counts = _out(counts, "counts", torch.int32, (E,), dev)
+    offsets = _out(offsets, "offsets", torch.int32, (E + 1,), dev)
+    row_of = _out(row_of, "row_of", torch.int32, (T, k), dev)
+    token_of = _out(token_of, "token_of", torch.int32, (A,), dev)
+    x_perm = _out(x_perm, "x_perm", x.dtype, (A, d), dev) if copy else None
+    _check("moe_permute_noalloc", lib().moe_permute_noalloc(_p(topk_idx), T, k, E, _p(x), _dtype_code(x), d,
+                                                            _p(counts), _p(offsets), _p(row_of), _p(token_of),
+                                                            _p(x_perm), _stream(stream)))
     return counts, offsets, row_of, token_of, x_perm
 
 

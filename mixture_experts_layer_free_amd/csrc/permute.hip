@@ -24,6 +24,8 @@
 // expert in the same order, and are still copied (the router weight gradient
 // runs over every assignment).  row_of holds r for a kept row and ~r (< 0)
 // for a dropped one; an out-of-range expert id gets INT32_MIN and no row.
+#include <atomic>
+
 #include "moe_common.h"
 
 namespace {
@@ -219,27 +221,21 @@ extern "C" moe_status moe_permute(const int32_t* topk_idx, int64_t T, int k, int
                               workspace, workspace_bytes, stream);
 }
 
-extern "C" moe_status moe_permute_capacity(const int32_t* topk_idx, int64_t T, int k, int E, int64_t capacity,
-                                           const void* x, int x_dtype, int64_t d, int32_t* counts, int32_t* offsets,
-                                           int32_t* row_of, int32_t* token_of, void* x_perm, void* workspace,
-                                           size_t workspace_bytes, void* stream) {
-  // x_perm NULL: indices only (a consumer that gathers rows through token_of
-  // needs no copy), and then x may be NULL too
-  if (!topk_idx || !counts || !offsets || !row_of || !token_of || (x_perm && !x)) return MOE_EINVAL;
-  if (T < 1 || d < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
-  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EINVAL;
-  const int64_t es = x_dtype == MOE_BF16 ? 2 : 4;
-  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || T * k >= (1ll << 31) || (d * es) % 16 != 0) return MOE_ENOTSUP;
-  const size_t need = moe_permute_workspace(T, k, E);
-  if (!workspace || workspace_bytes < need) return MOE_EWORKSPACE;
-  hipStream_t s = moe_stream(stream);
+// Scratch of moe_permute_noalloc: one copy per GPU, for the life of the
+// process.  Host code never names it: it takes the address that
+// hipGetSymbolAddress returns for the current device (noalloc_scratch).
+static __device__ __align__(256) int32_t scratch[MOE_PERMUTE_NOALLOC_SCRATCH / sizeof(int32_t)];
+
+namespace {
+
+// The permute's kernels after the argument checks; hist/doff: its scratch
+// (the chunk histogram, then the dropped-row bases), nothing of which has to
+// start at zero (every entry is written before it is read).
+moe_status permute_launch(const int32_t* topk_idx, int64_t T, int k, int E, int cap, const void* x, int64_t es,
+                          int64_t d, int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* token_of,
+                          void* x_perm, int32_t* hist, int32_t* doff, hipStream_t s) {
   const int64_t A = T * k;
   const int nchunks = (int)ceil_div(A, PCH);
-  // a capacity of A or more drops nothing: the same as none
-  const int cap = capacity < 0 || capacity >= A ? -1 : (int)capacity;
-  int32_t* hist = static_cast<int32_t*>(workspace);
-  int32_t* doff = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                             align256((size_t)nchunks * (size_t)E * sizeof(int32_t)));
   perm_hist_kernel<<<nchunks, PCH, 0, s>>>(topk_idx, A, E, nchunks, hist);
   MOE_LAUNCH_CHECK();
   perm_scan_kernel<<<1, 1024, 0, s>>>(hist, E, nchunks, cap, counts, offsets, doff);
@@ -255,4 +251,75 @@ extern "C" moe_status moe_permute_capacity(const int32_t* topk_idx, int64_t T, i
 #undef MOE_PCOPY
   MOE_LAUNCH_CHECK();
   return MOE_OK;
+}
+
+// Argument checks shared by every permute entry point; es = element bytes.
+moe_status permute_check(const int32_t* topk_idx, int64_t T, int k, int E, const void* x, int x_dtype, int64_t d,
+                         const int32_t* counts, const int32_t* offsets, const int32_t* row_of,
+                         const int32_t* token_of, const void* x_perm, int64_t& es) {
+  // x_perm NULL: indices only (a consumer that gathers rows through token_of
+  // needs no copy), and then x may be NULL too
+  if (!topk_idx || !counts || !offsets || !row_of || !token_of || (x_perm && !x)) return MOE_EINVAL;
+  if (T < 1 || d < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EINVAL;
+  es = x_dtype == MOE_BF16 ? 2 : 4;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || T * k >= (1ll << 31) || (d * es) % 16 != 0) return MOE_ENOTSUP;
+  return MOE_OK;
+}
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<uintptr_t> g_scratch[kMaxScratchDevices];   // 0: not yet looked up
+
+// This device's copy of `scratch` (looked up once per device, with that
+// device current), or nullptr if the lookup failed.
+int32_t* noalloc_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  uintptr_t p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == 0) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    p = reinterpret_cast<uintptr_t>(ptr);
+    g_scratch[dev].store(p, std::memory_order_release);   // racing first calls store the same address
+  }
+  return reinterpret_cast<int32_t*>(p);
+}
+
+}  // namespace
+
+extern "C" moe_status moe_permute_capacity(const int32_t* topk_idx, int64_t T, int k, int E, int64_t capacity,
+                                           const void* x, int x_dtype, int64_t d, int32_t* counts, int32_t* offsets,
+                                           int32_t* row_of, int32_t* token_of, void* x_perm, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  int64_t es = 0;
+  const moe_status st = permute_check(topk_idx, T, k, E, x, x_dtype, d, counts, offsets, row_of, token_of, x_perm, es);
+  if (st != MOE_OK) return st;
+  const size_t need = moe_permute_workspace(T, k, E);
+  if (!workspace || workspace_bytes < need) return MOE_EWORKSPACE;
+  const int64_t A = T * k;
+  // a capacity of A or more drops nothing: the same as none
+  const int cap = capacity < 0 || capacity >= A ? -1 : (int)capacity;
+  int32_t* hist = static_cast<int32_t*>(workspace);
+  int32_t* doff = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                             align256((size_t)ceil_div(A, PCH) * (size_t)E * sizeof(int32_t)));
+  return permute_launch(topk_idx, T, k, E, cap, x, es, d, counts, offsets, row_of, token_of, x_perm, hist, doff,
+                        moe_stream(stream));
+}
+
+extern "C" moe_status moe_permute_noalloc(const int32_t* topk_idx, int64_t T, int k, int E, const void* x, int x_dtype,
+                                          int64_t d, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                                          int32_t* token_of, void* x_perm, void* stream) {
+  int64_t es = 0;
+  const moe_status st = permute_check(topk_idx, T, k, E, x, x_dtype, d, counts, offsets, row_of, token_of, x_perm, es);
+  if (st != MOE_OK) return st;
+  // the histogram must fit the static scratch (no capacity: doff is not used)
+  const size_t hist_bytes = (size_t)ceil_div(T * k, PCH) * (size_t)E * sizeof(int32_t);
+  if (hist_bytes > MOE_PERMUTE_NOALLOC_SCRATCH) return MOE_ENOTSUP;
+  int32_t* hist = noalloc_scratch();
+  if (!hist) return MOE_EHIP;
+  return permute_launch(topk_idx, T, k, E, -1, x, es, d, counts, offsets, row_of, token_of, x_perm, hist, nullptr,
+                        moe_stream(stream));
 }
