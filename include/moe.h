@@ -72,7 +72,7 @@ enum moe_score { MOE_SOFTMAX_CHOSEN = 0, MOE_SIGMOID_NORM = 1, MOE_SQRT_SOFTPLUS
 
 /* which call a workspace is sized for */
 enum moe_call { MOE_CALL_ROUTE = 0, MOE_CALL_PERMUTE = 1, MOE_CALL_GROUPED_FFN = 2, MOE_CALL_BACKWARD = 3,
-                MOE_CALL_AUX_LOSS = 4 };
+                MOE_CALL_AUX_LOSS = 4, MOE_CALL_BACKWARD_SHARED = 5 };
 
 /* Largest supported expert count and top-k (the handbook article's router
  * table has a model choosing 16 of 896 experts, the largest on the pages). */
@@ -256,7 +256,9 @@ moe_status moe_permute_noalloc(const int32_t* topk_idx, int64_t T, int k, int E,
  *   workspace                moe_workspace_size(MOE_CALL_GROUPED_FFN, rows, 1, G, d, f)
  * bf16 uses MFMA with fp32 accumulation; f32 uses fp32 FMA.
  * ENOTSUP: G > MOE_MAX_EXPERTS, rows >= 2^31; bf16 needs d and f to be
- * multiples of 64 and one expert's gate/up weight under 2 GiB
+ * multiples of 64 (the GEMM loops run over pairs of 32-deep slabs and the
+ * SwiGLU tiles pair 64-column gate and up blocks; there is no tail path
+ * along d or f) and one expert's gate/up weight under 2 GiB
  * (2f*d*2 < 2^31 bytes: it is addressed through one buffer resource); f32
  * needs d a multiple of 4.
  */
@@ -399,7 +401,42 @@ typedef struct moe_bwd_args {
                                   kept rows only); required with aux_alpha */
   float aux_alpha;             /* weight of the auxiliary load-balancing loss
                                   (moe_aux_loss) whose gradient is added; 0: none */
+  /* appended: the shared expert (lesson, Shared experts section: an expert
+     every token passes through, its output added with weight 1).  NULL
+     w_gate_up_shared: the layer has none and the other shared fields are
+     ignored.  Its backward is the expert chain rule above with dY_perm = dy
+     and X = x over all T rows; its input gradient is added to dx. */
+  int64_t f_shared;            /* shared expert FFN width (a multiple of 64) */
+  const void* w_gate_up_shared;   /* [2fs, d] bf16 */
+  const void* w_down_shared;      /* [d, fs] bf16 */
+  const void* gu_shared;       /* [T, 2fs] bf16: G|U saved by the forward
+                                  (moe_grouped_ffn's gu_saved) */
+  const void* h_shared;        /* [T, fs] bf16: the forward's H */
+  float* dw_gate_up_shared;    /* [2fs, d] out */
+  float* dw_down_shared;       /* [d, fs] out */
+  void* workspace_shared;      /* moe_workspace_size(MOE_CALL_BACKWARD_SHARED,
+                                  T, 1, 1, d, f_shared) bytes */
+  size_t workspace_shared_bytes;
+  /* appended: per-stage timing.  NULL, or a HOST array of MOE_BWD_STAGES
+     hipEvent_t (as void*): event s is recorded on the stream after stage s
+     (enum moe_bwd_stage), so a caller that records one event before the call
+     can time every stage with hipEventElapsedTime.  Stages the call does not
+     run (e.g. the shared expert's without one) still record their event. */
+  void* const* stage_events;
 } moe_bwd_args;
+
+/* Stages of moe_backward, in stream order (for moe_bwd_args.stage_events). */
+enum moe_bwd_stage {
+  MOE_BWD_COMBINE = 0,      /* combine backward and gate backward (dg, dl) */
+  MOE_BWD_ROUTER = 1,       /* router weight gradient */
+  MOE_BWD_DGRAD_DOWN = 2,   /* tile schedule; dH = dY_perm W_down, SwiGLU backward -> dG|dU */
+  MOE_BWD_WGRAD_DOWN = 3,   /* dW_down = dY_perm^T H */
+  MOE_BWD_WGRAD_UP = 4,     /* dW_gate_up = [dG|dU]^T X */
+  MOE_BWD_DGRAD_UP = 5,     /* dX_perm = [dG|dU] W_gate_up */
+  MOE_BWD_SHARED = 6,       /* the shared expert's four GEMMs */
+  MOE_BWD_UNPERMUTE = 7,    /* dx = sum_j dX_perm rows + router and shared terms */
+  MOE_BWD_STAGES = 8
+};
 
 /* With aux_alpha != 0 the gradient of moe_aux_loss (same alpha, counts
  * and logits) is added: it reaches every logit, so dW_r = dL^T x and
@@ -410,13 +447,17 @@ typedef struct moe_bwd_args {
  * dropped slot gets dg = 0 and no dY_perm / dX_perm row; its dl (through the
  * gate normalisation) still reaches dW_r over its dropped x_perm row and
  * dx_r.  Expert GEMMs run on the kept rows offsets[0] .. offsets[E]-1.
- * ENOTSUP: non-bf16 use, d or f not a multiple of 64, E > MOE_MAX_EXPERTS,
- * k > MOE_MAX_TOPK, T*k >= 2^31, and buffers the GEMMs address through one
- * buffer resource reaching 2 GiB: T*k*max(d, 2f)*2 >= 2^31 or
- * 2f*d*2 >= 2^31 bytes.  EINVAL also for a struct_size other than
- * sizeof(moe_bwd_args), offsetof(moe_bwd_args, counts) or
- * offsetof(moe_bwd_args, aux_alpha) (older callers: the missing fields
- * read as NULL / 0). */
+ * ENOTSUP: non-bf16 use, d, f or f_shared not a multiple of 64,
+ * E > MOE_MAX_EXPERTS, k > MOE_MAX_TOPK, T*k >= 2^31, and buffers the GEMMs
+ * address through one buffer resource reaching 2 GiB: T*k*max(d, 2f)*2 >=
+ * 2^31 or 2f*d*2 >= 2^31 bytes (for the shared expert T*max(d, 2fs)*2 and
+ * 2fs*d*2).  The multiples of 64: the GEMM loops run over pairs of
+ * 32-deep slabs and the SwiGLU tiles pair 64-column gate and up blocks,
+ * with no tail path along d or f.  EINVAL also
+ * for a struct_size other than sizeof(moe_bwd_args) or the offset of one of
+ * the appended fields counts, aux_alpha, f_shared or stage_events (older
+ * callers: the missing fields read as NULL / 0); EWORKSPACE for a missing
+ * or small workspace_shared when a shared expert is given. */
 moe_status moe_backward(const moe_bwd_args* args, void* stream);
 
 /* Workspace bytes a call needs (0 if it needs none).  `which` is enum

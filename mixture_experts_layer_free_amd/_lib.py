@@ -19,7 +19,10 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 SCORE = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "uniform": 3}
-MOE_CALL_ROUTE, MOE_CALL_PERMUTE, MOE_CALL_GROUPED_FFN, MOE_CALL_BACKWARD, MOE_CALL_AUX_LOSS = range(5)
+(MOE_CALL_ROUTE, MOE_CALL_PERMUTE, MOE_CALL_GROUPED_FFN, MOE_CALL_BACKWARD, MOE_CALL_AUX_LOSS,
+ MOE_CALL_BACKWARD_SHARED) = range(6)
+# stages of moe_backward (enum moe_bwd_stage), in stream order
+BWD_STAGES = ("combine", "router", "dgrad_down", "wgrad_down", "wgrad_up", "dgrad_up", "shared", "unpermute")
 MAX_EXPERTS, MAX_TOPK = 1024, 16
 PERMUTE_NOALLOC_SCRATCH = 4 << 20   # bytes of moe_permute_noalloc's static device scratch
 
@@ -37,6 +40,10 @@ class BwdArgs(ctypes.Structure):
         ("dgate", _vp), ("dlogit", _vp),
         ("workspace", _vp), ("workspace_bytes", _sz),
         ("counts", _vp), ("aux_alpha", ctypes.c_float),
+        ("f_shared", _i64), ("w_gate_up_shared", _vp), ("w_down_shared", _vp), ("gu_shared", _vp),
+        ("h_shared", _vp), ("dw_gate_up_shared", _vp), ("dw_down_shared", _vp),
+        ("workspace_shared", _vp), ("workspace_shared_bytes", _sz),
+        ("stage_events", ctypes.POINTER(_vp)),
     ]
 
 
@@ -359,6 +366,17 @@ def moe_aux_loss(logits, counts, k, score_fn, alpha, loss_out=None, p_mean_out=N
     return loss_out
 
 
-def moe_backward(args: BwdArgs, stream=None):
+def moe_backward(args: BwdArgs, stream=None, stage_events=None):
+    """stage_events: None, or len(BWD_STAGES) torch.cuda.Event objects, each
+    recorded once before (so that it exists); the library records event s on
+    the stream after stage s."""
     args.struct_size = ctypes.sizeof(BwdArgs)
+    keep = None
+    if stage_events is not None:
+        if len(stage_events) != len(BWD_STAGES):
+            raise ValueError(f"stage_events needs {len(BWD_STAGES)} events")
+        keep = (_vp * len(BWD_STAGES))(*[ev.cuda_event for ev in stage_events])
+        args.stage_events = ctypes.cast(keep, ctypes.POINTER(_vp))
+    else:
+        args.stage_events = None
     _check("moe_backward", lib().moe_backward(ctypes.byref(args), _stream(stream)))

@@ -8,6 +8,7 @@
 size_t moe_permute_workspace(int64_t T, int k, int E);
 size_t moe_ffn_workspace(int G);
 size_t moe_backward_workspace(int64_t T, int k, int E, int64_t d, int64_t f);
+size_t moe_backward_shared_workspace(int64_t T, int64_t d, int64_t fs);
 
 namespace {
 constexpr int kMaxDevices = 64;
@@ -38,6 +39,8 @@ extern "C" size_t moe_workspace_size(int which, int64_t T, int k, int E, int64_t
       return moe_backward_workspace(T, k, E, d, f);
     case MOE_CALL_AUX_LOSS:
       return moe_aux_workspace(T, E);
+    case MOE_CALL_BACKWARD_SHARED:
+      return moe_backward_shared_workspace(T, d, f);
     default:
       return 0;
   }

@@ -232,7 +232,8 @@ template <int K>
 __global__ __launch_bounds__(256) void unpermute_bwd_dense_kernel(const f32x4* __restrict__ dx_perm,
                                                                   const int32_t* __restrict__ row_of,
                                                                   const float* __restrict__ dl_dense,
-                                                                  const f32x4* __restrict__ w_router, int T, int E,
+                                                                  const f32x4* __restrict__ w_router,
+                                                                  const f32x4* __restrict__ extra, int T, int E,
                                                                   int64_t nv, f32x4* __restrict__ dx) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(256) void unpermute_bwd_dense_kernel(const f32x4* _
   }
   const float* dlr = dl_dense + t * E;
   for (int64_t v = lane; v < nv; v += MOE_WAVE) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc = extra ? __builtin_nontemporal_load(extra + t * nv + v) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const f32x4 l = __builtin_nontemporal_load(xr[j] + v);
@@ -276,8 +277,8 @@ size_t moe_aux_bwd_workspace(int64_t T, int E, int64_t d) {
 
 moe_status moe_aux_backward_launch(const float* logits, const int32_t* counts, const int32_t* idx, const float* dl,
                                    const bf16_t* x, const float* w_router, const f32x4* dx_perm,
-                                   const int32_t* row_of, int64_t T, int E, int k, int64_t d, int fn, float alpha,
-                                   float* dw_router, float* dx, void* ws, hipStream_t s) {
+                                   const f32x4* extra, const int32_t* row_of, int64_t T, int E, int k, int64_t d,
+                                   int fn, float alpha, float* dw_router, float* dx, void* ws, hipStream_t s) {
   float* dl_dense = static_cast<float*>(ws);
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align256((size_t)T * E * sizeof(float)));
   aux_dl_dense_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(logits, counts, idx, dl, (int)T, E, k, fn, alpha,
@@ -292,7 +293,7 @@ moe_status moe_aux_backward_launch(const float* logits, const int32_t* counts, c
   MOE_LAUNCH_CHECK();
 #define MOE_UBWD_DENSE(K)                                                                                  \
   unpermute_bwd_dense_kernel<K><<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(                                  \
-      dx_perm, row_of, dl_dense, reinterpret_cast<const f32x4*>(w_router), (int)T, E, d / 4,               \
+      dx_perm, row_of, dl_dense, reinterpret_cast<const f32x4*>(w_router), extra, (int)T, E, d / 4,        \
       reinterpret_cast<f32x4*>(dx))
   MOE_DISPATCH_K(k, MOE_UBWD_DENSE);
 #undef MOE_UBWD_DENSE

@@ -250,14 +250,16 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* _
   dw[(int64_t)e * d + c] = s;
 }
 
-// dx[t] = sum_j dx_perm[row_of[t,j]] + sum_j dl[t,j] * w_router[idx[t,j]]
+// dx[t] = extra[t] + sum_j dx_perm[row_of[t,j]] + sum_j dl[t,j] * w_router[idx[t,j]]
+// (extra: the shared expert's input gradient, or null)
 // (a dropped slot, row_of < 0, has no dx_perm row: its load goes to row 0 and
 // is replaced by zero)
 template <int K, bool ROUTER>
 __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restrict__ dx_perm,
                                                             const int32_t* __restrict__ row_of,
                                                             const int32_t* __restrict__ idx, const float* __restrict__ dl,
-                                                            const f32x4* __restrict__ w_router, int T, int E,
+                                                            const f32x4* __restrict__ w_router,
+                                                            const f32x4* __restrict__ extra, int T, int E,
                                                             int64_t nv, f32x4* __restrict__ dx) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restr
       xs[j] = live[j] ? l : f32x4{0.f, 0.f, 0.f, 0.f};
       if (ROUTER) ws[j] = wr[j][v];
     }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc = extra ? __builtin_nontemporal_load(extra + t * nv + v) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < K; ++j) acc += xs[j];
 #pragma unroll
@@ -298,6 +300,11 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restr
     }
     dx[t * nv + v] = acc;
   }
+}
+
+// offsets {0, T} of the shared expert's one row group
+__global__ void shared_offsets_kernel(int32_t* __restrict__ o, int32_t T) {
+  if (threadIdx.x < 2) o[threadIdx.x] = threadIdx.x ? T : 0;
 }
 
 __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -330,6 +337,24 @@ BwdLayout layout(int64_t T, int k, int E, int64_t d, int64_t f) {
   return L;
 }
 
+// Workspace of the shared expert's backward: dG|dU [T, 2fs] bf16, its input
+// gradient [T, d] f32, and its one-group offsets and tile prefix.
+struct SharedLayout {
+  size_t dgu, dx, offs, mt_prefix, total;
+};
+
+SharedLayout shared_layout(int64_t T, int64_t d, int64_t fs) {
+  SharedLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
+  L.dgu = take((size_t)T * 2 * fs * 2);
+  L.dx = take((size_t)T * d * 4);
+  L.offs = take(2 * 4);
+  L.mt_prefix = take(2 * 4);
+  L.total = o;
+  return L;
+}
+
 }  // namespace
 
 size_t moe_backward_workspace(int64_t T, int k, int E, int64_t d, int64_t f) {
@@ -337,13 +362,22 @@ size_t moe_backward_workspace(int64_t T, int k, int E, int64_t d, int64_t f) {
   return layout(T, k, E, d, f).total;
 }
 
+size_t moe_backward_shared_workspace(int64_t T, int64_t d, int64_t fs) {
+  if (d < 1 || fs < 1) return 0;
+  return shared_layout(T, d, fs).total;
+}
+
 extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   // struct_size: the full struct, or one that ends before an appended field
   if (!a || (a->struct_size != sizeof(moe_bwd_args) && a->struct_size != offsetof(moe_bwd_args, counts) &&
-             a->struct_size != offsetof(moe_bwd_args, aux_alpha)))
+             a->struct_size != offsetof(moe_bwd_args, aux_alpha) &&
+             a->struct_size != offsetof(moe_bwd_args, f_shared) &&
+             a->struct_size != offsetof(moe_bwd_args, stage_events)))
     return MOE_EINVAL;
   const int32_t* counts = a->struct_size > offsetof(moe_bwd_args, counts) ? a->counts : nullptr;
   const float aux_alpha = a->struct_size > offsetof(moe_bwd_args, aux_alpha) ? a->aux_alpha : 0.0f;
+  const bool shared = a->struct_size > offsetof(moe_bwd_args, f_shared) && a->w_gate_up_shared;
+  void* const* events = a->struct_size > offsetof(moe_bwd_args, stage_events) ? a->stage_events : nullptr;
   const int64_t T = a->T, d = a->d, f = a->f;
   const int E = a->E, k = a->k;
   if (T < 1 || d < 1 || f < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
@@ -361,9 +395,31 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   // activations, and the data-gradient GEMMs one expert's weight, through
   // 32-bit buffer resources
   if (T * k * std::max(d, 2 * f) * 2 >= (1ll << 31) || 2 * f * d * 2 >= (1ll << 31)) return MOE_ENOTSUP;
+  const int64_t fs = shared ? a->f_shared : 0;
+  if (shared) {
+    if (!a->w_down_shared || !a->gu_shared || !a->h_shared || !a->dw_gate_up_shared || !a->dw_down_shared || fs < 1)
+      return MOE_EINVAL;
+    if (fs % 64 != 0 || T * std::max(d, 2 * fs) * 2 >= (1ll << 31) || 2 * fs * d * 2 >= (1ll << 31))
+      return MOE_ENOTSUP;
+  }
   const BwdLayout Lo = layout(T, k, E, d, f);
   if (!a->workspace || a->workspace_bytes < Lo.total) return MOE_EWORKSPACE;
+  const SharedLayout Ls = shared_layout(T, d, fs);
+  if (shared && (!a->workspace_shared || a->workspace_shared_bytes < Ls.total)) return MOE_EWORKSPACE;
   hipStream_t s = moe_stream(stream);
+  // event of stage st (enum moe_bwd_stage), recorded after the stage's kernels
+  auto mark = [&](int st) -> moe_status {
+    if (events && events[st] && hipEventRecord(static_cast<hipEvent_t>(events[st]), s) != hipSuccess) {
+      (void)hipGetLastError();
+      return MOE_EHIP;
+    }
+    return MOE_OK;
+  };
+#define MOE_MARK(st_)                      \
+  do {                                     \
+    const moe_status m_ = mark(st_);       \
+    if (m_ != MOE_OK) return m_;           \
+  } while (0)
   const int64_t A = T * k;
   char* ws = static_cast<char*>(a->workspace);
   bf16_t* dy_perm = reinterpret_cast<bf16_t*>(ws + Lo.dy_perm);
@@ -390,6 +446,7 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   gate_bwd_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(dgp, a->row_of, a->topk_gate, a->topk_idx, a->logits, (int)T,
                                                            k, E, a->score_fn, dg, dl, dl_perm);
   MOE_LAUNCH_CHECK();
+  MOE_MARK(MOE_BWD_COMBINE);
   // 2. router weight gradient (with the aux loss: dense, together with dx below)
   if (aux) {
   } else if (router) {
@@ -406,6 +463,7 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
                                                                                                       (int64_t)E * d);
     MOE_LAUNCH_CHECK();
   }
+  MOE_MARK(MOE_BWD_ROUTER);
   // expert GEMMs
   using namespace moe_gemm;
   const bool large = use_large_tile(f);
@@ -422,6 +480,7 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
     st = launch_gemm<true, false, false, EPI_SWIGLU_BWD>(g, large, A, s);
     if (st != MOE_OK) return st;
   }
+  MOE_MARK(MOE_BWD_DGRAD_DOWN);
   {  // 4. dW_down[e] = dY_perm^T H
     Args g{};
     g.A = dy_perm; g.lda = d;
@@ -432,6 +491,7 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
     st = launch_gemm<false, false, true, EPI_F32>(g, d >= BM_LARGE && f >= BN_LARGE, 0, s);
     if (st != MOE_OK) return st;
   }
+  MOE_MARK(MOE_BWD_WGRAD_DOWN);
   {  // 5. dW_gate_up[e] = [dG|dU]^T X_perm
     Args g{};
     g.A = dgu; g.lda = 2 * f;
@@ -451,6 +511,7 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
     }
     if (st != MOE_OK) return st;
   }
+  MOE_MARK(MOE_BWD_WGRAD_UP);
   {  // 6. dX_perm = [dG|dU] W_gate_up
     Args g{};
     g.A = dgu; g.lda = 2 * f;
@@ -461,24 +522,89 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
     st = launch_gemm<true, false, false, EPI_F32>(g, large, A, s);
     if (st != MOE_OK) return st;
   }
-  // 7. unpermute + router input gradient
-  if (aux)
-    return moe_aux_backward_launch(a->logits, counts, a->topk_idx, dl, static_cast<const bf16_t*>(a->x), a->w_router,
-                                   reinterpret_cast<const f32x4*>(dx_perm), a->row_of, T, E, k, d, a->score_fn,
-                                   aux_alpha, a->dw_router, a->dx, ws + Lo.aux, s);
+  MOE_MARK(MOE_BWD_DGRAD_UP);
+  // shared expert: the same four products over all T rows with dY_perm = dy
+  // and X = x (gate 1), on one row group {0, T}
+  char* wss = static_cast<char*>(a->workspace_shared);
+  float* dx_sh = shared ? reinterpret_cast<float*>(wss + Ls.dx) : nullptr;
+  if (shared) {
+    bf16_t* dgu_sh = reinterpret_cast<bf16_t*>(wss + Ls.dgu);
+    int32_t* offs_sh = reinterpret_cast<int32_t*>(wss + Ls.offs);
+    int32_t* mt_sh = reinterpret_cast<int32_t*>(wss + Ls.mt_prefix);
+    const bf16_t* dyb = static_cast<const bf16_t*>(a->dy);
+    const bf16_t* xb = static_cast<const bf16_t*>(a->x);
+    const bool large_sh = use_large_tile(fs);
+    shared_offsets_kernel<<<1, 64, 0, s>>>(offs_sh, (int32_t)T);
+    MOE_LAUNCH_CHECK();
+    st = moe_tile_schedule_launch(offs_sh, 1, large_sh ? BM_LARGE : BM, mt_sh, s);
+    if (st != MOE_OK) return st;
+    {  // dH = dy W_down_sh -> dG|dU (SwiGLU backward from the saved G|U)
+      Args g{};
+      g.A = dyb; g.lda = d;
+      g.B = static_cast<const bf16_t*>(a->w_down_shared); g.ldb = fs;
+      g.K = d; g.N = fs;
+      g.offsets = offs_sh; g.mt_prefix = mt_sh; g.G = 1;
+      g.gu_in = static_cast<const bf16_t*>(a->gu_shared);
+      g.gu_out = dgu_sh;
+      st = launch_gemm<true, false, false, EPI_SWIGLU_BWD>(g, large_sh, T, s);
+      if (st != MOE_OK) return st;
+    }
+    {  // dW_down_sh = dy^T H_sh
+      Args g{};
+      g.A = dyb; g.lda = d;
+      g.B = static_cast<const bf16_t*>(a->h_shared); g.ldb = fs;
+      g.M = d; g.N = fs;
+      g.offsets = offs_sh; g.G = 1;
+      g.out = a->dw_down_shared; g.ldo = fs; g.out_group = 0;
+      st = launch_gemm<false, false, true, EPI_F32>(g, d >= BM_LARGE && fs >= BN_LARGE, 0, s);
+      if (st != MOE_OK) return st;
+    }
+    {  // dW_gate_up_sh = [dG|dU]^T x
+      Args g{};
+      g.A = dgu_sh; g.lda = 2 * fs;
+      g.B = xb; g.ldb = d;
+      g.M = 2 * fs; g.N = d;
+      g.offsets = offs_sh; g.G = 1;
+      g.out = a->dw_gate_up_shared; g.ldo = d; g.out_group = 0;
+      st = launch_gemm<false, false, true, EPI_F32>(g, 2 * fs >= BM_LARGE && d >= BN_LARGE, 0, s);
+      if (st != MOE_OK) return st;
+    }
+    {  // dx_sh = [dG|dU] W_gate_up_sh (f32; added to dx by the unpermute below)
+      Args g{};
+      g.A = dgu_sh; g.lda = 2 * fs;
+      g.B = static_cast<const bf16_t*>(a->w_gate_up_shared); g.ldb = d; g.b_group = 0;
+      g.K = 2 * fs; g.N = d;
+      g.offsets = offs_sh; g.mt_prefix = mt_sh; g.G = 1;
+      g.out = dx_sh; g.ldo = d;
+      st = launch_gemm<true, false, false, EPI_F32>(g, large_sh, T, s);
+      if (st != MOE_OK) return st;
+    }
+  }
+  MOE_MARK(MOE_BWD_SHARED);
+  // 7. unpermute + router input gradient (+ the shared expert's)
+  if (aux) {
+    st = moe_aux_backward_launch(a->logits, counts, a->topk_idx, dl, static_cast<const bf16_t*>(a->x), a->w_router,
+                                 reinterpret_cast<const f32x4*>(dx_perm), reinterpret_cast<const f32x4*>(dx_sh),
+                                 a->row_of, T, E, k, d, a->score_fn, aux_alpha, a->dw_router, a->dx, ws + Lo.aux, s);
+    if (st != MOE_OK) return st;
+  } else {
 #define MOE_UBWD(K)                                                                                             \
   do {                                                                                                          \
     if (router)                                                                                                 \
       unpermute_bwd_kernel<K, true><<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(                                   \
           reinterpret_cast<const f32x4*>(dx_perm), a->row_of, a->topk_idx, dl,                                  \
-          reinterpret_cast<const f32x4*>(a->w_router), (int)T, E, d / 4, reinterpret_cast<f32x4*>(a->dx));      \
+          reinterpret_cast<const f32x4*>(a->w_router), reinterpret_cast<const f32x4*>(dx_sh), (int)T, E, d / 4, \
+          reinterpret_cast<f32x4*>(a->dx));                                                                     \
     else                                                                                                        \
       unpermute_bwd_kernel<K, false><<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(                                  \
-          reinterpret_cast<const f32x4*>(dx_perm), a->row_of, a->topk_idx, dl, nullptr, (int)T, E, d / 4,       \
-          reinterpret_cast<f32x4*>(a->dx));                                                                     \
+          reinterpret_cast<const f32x4*>(dx_perm), a->row_of, a->topk_idx, dl, nullptr,                        \
+          reinterpret_cast<const f32x4*>(dx_sh), (int)T, E, d / 4, reinterpret_cast<f32x4*>(a->dx));            \
   } while (0)
-  MOE_DISPATCH_K(k, MOE_UBWD);
+    MOE_DISPATCH_K(k, MOE_UBWD);
 #undef MOE_UBWD
-  MOE_LAUNCH_CHECK();
+    MOE_LAUNCH_CHECK();
+  }
+  MOE_MARK(MOE_BWD_UNPERMUTE);
+#undef MOE_MARK
   return MOE_OK;
 }

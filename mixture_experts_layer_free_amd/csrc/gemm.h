@@ -192,8 +192,9 @@ __device__ __forceinline__ void gemm_tile(const Args& p, char* smem, int e, int 
   uint32_t a_voff[LA], b_voff[LB];
   uint32_t a_step, b_step;   // bytes per slab
   if (AK && !KG && EPI == EPI_SWIGLU && p.a_rows) {   // only the up-projection gathers
-    // gathered rows: the buffer spans all of A, a row past the group's end
-    // gets an offset past the buffer (its loads read zeros)
+    // gathered rows: the buffer spans all of A (under 2^31 bytes), a row past
+    // the group's end or an index outside [0, a_rows_total) gets an offset
+    // past the buffer (its loads read zeros); a valid index's offset fits 32 bits
     a_base = p.A;
     a_bytes = p.a_rows_total * p.lda * 2;
     a_step = BK * 2;
@@ -201,7 +202,8 @@ __device__ __forceinline__ void gemm_tile(const Args& p, char* smem, int e, int 
     for (int q = 0; q < LA; ++q) {
       const int r = (wave * LA + q) * 16 + (lane >> 2);
       const int c = (lane & 3) ^ swz_kc(r);
-      a_voff[q] = row0 + r < row_end ? (uint32_t)((int64_t)p.a_rows[row0 + r] * p.lda * 2 + c * 16) : 0x80000000u;
+      const uint32_t src = row0 + r < row_end ? (uint32_t)p.a_rows[row0 + r] : 0xFFFFFFFFu;
+      a_voff[q] = src < (uint32_t)p.a_rows_total ? src * (uint32_t)(p.lda * 2) + c * 16 : 0x80000000u;
     }
   } else if (AK) {
     const int64_t a_rows = row_end - row0 < TM ? row_end - row0 : TM;

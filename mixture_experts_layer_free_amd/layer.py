@@ -130,6 +130,12 @@ class MoELayer:
             self.sh_h = z(T, fs, dtype=dt)
             self.sh_y = z(T, d)
             self.ws_sh = z(max(1, L.workspace_size(L.MOE_CALL_GROUPED_FFN, T, 1, 1, d, fs)), dtype=torch.uint8)
+            self.sh_gu = z(T, 2 * fs, dtype=dt) if s.train else None
+            if s.train:
+                self.dw_gate_up_shared = z(2 * fs, d)
+                self.dw_down_shared = z(d, fs)
+                self.ws_bwd_sh = z(max(1, L.workspace_size(L.MOE_CALL_BACKWARD_SHARED, T, 1, 1, d, fs)),
+                                   dtype=torch.uint8)
         if s.train:
             self.dx = z(T, d)
             self.dw_router = z(E, d)
@@ -177,8 +183,8 @@ class MoELayer:
         shared_y = None
         if s.shared:
             with _span(timer, "shared_ffn", stream):
-                L.moe_grouped_ffn(x, self.sh_offsets, self.w_gate_up_shared, self.w_down_shared, None, self.sh_h,
-                                  self.sh_y, workspace=self.ws_sh, stream=stream)
+                L.moe_grouped_ffn(x, self.sh_offsets, self.w_gate_up_shared, self.w_down_shared, self.sh_gu,
+                                  self.sh_h, self.sh_y, workspace=self.ws_sh, stream=stream)
             shared_y = self.sh_y
         with _span(timer, "combine", stream):
             L.moe_combine(self.y_perm, self.row_of, self.gate, shared_y, self.out, stream=stream)
@@ -191,7 +197,8 @@ class MoELayer:
                 L.moe_bias_update(self.sel_bias, self.counts, s.T, s.k, s.gamma, stream=stream)
         return self.out
 
-    def backward(self, x, dy, stream=None, timer=None):
+    def backward(self, x, dy, stream=None, timer=None, stage_events=None):
+        """Gradients of the last forward; stage_events as in _lib.moe_backward."""
         s = self.s
         a = L.BwdArgs()
         a.T, a.d, a.f, a.E, a.k = s.T, s.d, s.f, s.E, s.k
@@ -207,8 +214,16 @@ class MoELayer:
         a.workspace_bytes = self.ws_bwd.numel()
         a.counts = self.counts.data_ptr() if s.capacity is not None or s.aux_alpha else None
         a.aux_alpha = s.aux_alpha
+        if s.shared:
+            a.f_shared = s.f_shared
+            for name, t in (("w_gate_up_shared", self.w_gate_up_shared[0]), ("w_down_shared", self.w_down_shared[0]),
+                            ("gu_shared", self.sh_gu), ("h_shared", self.sh_h),
+                            ("dw_gate_up_shared", self.dw_gate_up_shared), ("dw_down_shared", self.dw_down_shared),
+                            ("workspace_shared", self.ws_bwd_sh)):
+                setattr(a, name, t.data_ptr())
+            a.workspace_shared_bytes = self.ws_bwd_sh.numel()
         with _span(timer, "backward", stream):
-            L.moe_backward(a, stream=stream)
+            L.moe_backward(a, stream=stream, stage_events=stage_events)
         return self.dx
 
     def capture(self, x, dy=None):

@@ -170,6 +170,13 @@ def _bwd_args(L, **kw):
     a.workspace_bytes = kw.get("workspace_bytes", L.workspace_size(L.MOE_CALL_BACKWARD, a.T, a.k, a.E, a.d, a.f))
     a.counts = kw.get("counts", None)
     a.aux_alpha = kw.get("aux_alpha", 0.0)
+    if kw.get("shared"):
+        a.f_shared = kw.get("f_shared", 128)
+        for name in ("w_gate_up_shared", "w_down_shared", "gu_shared", "h_shared", "dw_gate_up_shared",
+                     "dw_down_shared", "workspace_shared"):
+            setattr(a, name, kw.get(name, P.value))
+        a.workspace_shared_bytes = kw.get("workspace_shared_bytes", L.workspace_size(
+            L.MOE_CALL_BACKWARD_SHARED, a.T, 1, 1, a.d, a.f_shared))
     return a
 
 
@@ -191,8 +198,28 @@ def test_backward_validation(L):
     assert bwd(T=1 << 20, d=1024, workspace_bytes=1 << 50) == L.MOE_ENOTSUP   # X_perm past 2 GiB
     assert bwd(workspace_bytes=0) == L.MOE_EWORKSPACE
     assert bwd(workspace=None) == L.MOE_EWORKSPACE
-    # an older caller's struct, ending before `counts`, passes the size check
-    assert bwd(struct_size=L.BwdArgs.counts.offset, workspace_bytes=0) == L.MOE_EWORKSPACE
+    # an older caller's struct, ending before an appended field, passes the size check
+    for field in ("counts", "aux_alpha", "f_shared", "stage_events"):
+        assert bwd(struct_size=getattr(L.BwdArgs, field).offset, workspace_bytes=0) == L.MOE_EWORKSPACE, field
+    assert bwd(struct_size=L.BwdArgs.f_shared.offset + 8) == L.MOE_EINVAL
+    # the shared expert's fields
+    assert bwd(shared=True, h_shared=None) == L.MOE_EINVAL
+    assert bwd(shared=True, f_shared=0) == L.MOE_EINVAL
+    assert bwd(shared=True, f_shared=96) == L.MOE_ENOTSUP
+    assert bwd(shared=True, workspace_shared=None) == L.MOE_EWORKSPACE
+    assert bwd(shared=True, workspace_shared_bytes=1) == L.MOE_EWORKSPACE
+    # an older caller's struct ending before f_shared ignores the shared fields
+    assert bwd(shared=True, f_shared=96, struct_size=L.BwdArgs.f_shared.offset, workspace_bytes=0) == \
+        L.MOE_EWORKSPACE
+
+
+def test_backward_shared_workspace_size(built):
+    """The shared expert's backward workspace: dG|dU (bf16) and its input
+    gradient (f32) over T rows, plus small index arrays."""
+    T, d, fs = 1000, 256, 128
+    n = built.workspace_size(built.MOE_CALL_BACKWARD_SHARED, T, 1, 1, d, fs)
+    assert n >= T * 2 * fs * 2 + T * d * 4
+    assert n < T * 2 * fs * 2 + T * d * 4 + 4096
 
 
 def test_status_strings(L):

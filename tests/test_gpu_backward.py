@@ -18,10 +18,10 @@ pytestmark = pytest.mark.gpu
 
 def _layer(cfg, inp, capacity=None, aux_alpha=0.0, fuse_permute=True):
     from mixture_experts_layer_free_amd.layer import MoELayer, Shape
-    s = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, torch.bfloat16, cfg.score, 0, 0, False, cfg.gamma, True,
-              capacity=capacity, aux_alpha=aux_alpha, fuse_permute=fuse_permute)
+    s = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, torch.bfloat16, cfg.score, cfg.shared, cfg.f_shared, False,
+              cfg.gamma, True, capacity=capacity, aux_alpha=aux_alpha, fuse_permute=fuse_permute)
     return MoELayer(s, dev(inp["w_router"]), dev(inp["w_gate_up"]), dev(inp["w_down"]), dev(inp["bias"].copy()),
-                    dev(inp["logit_offset"]))
+                    dev(inp["logit_offset"]), dev(inp.get("w_gate_up_shared")), dev(inp.get("w_down_shared")))
 
 
 def _run(cfg, inp, capacity=None, aux_alpha=0.0, fuse_permute=True):
@@ -270,3 +270,67 @@ def test_backward_replay_invalid_ids_stay_local(score):
     check_close(host(layer.dgate)[sel], g["dg"], "bf16", "dg (valid tokens)")
     check_close(host(layer.dlogit)[sel], g["dl"], "bf16", "dl (valid tokens)")
     check_close(host(layer.dx)[sel], g["dx"], "bf16", "dx (valid tokens)")
+
+
+@pytest.mark.parametrize("score,T,d,E,k,f,fs,aux", [
+    ("sigmoid", 700, 256, 16, 4, 128, 128, 0.0),        # 256x256 tiles for the shared expert
+    ("sqrt_softplus", 500, 128, 8, 2, 64, 192, 0.0),   # 128x128 tiles
+    ("softmax", 300, 256, 24, 3, 128, 256, 0.01),      # with the auxiliary-loss gradient
+])
+def test_backward_shared_expert(score, T, d, E, k, f, fs, aux):
+    """A training step of a layer with one shared expert (lesson, Shared
+    experts section): every gradient, the shared expert's weight gradients
+    included, against the oracle's chain rule through the shared expert."""
+    say(f"[backward shared expert {score} T={T} d={d} E={E} k={k} f={f} fs={fs} aux={aux}]")
+    cfg = scaled(CONFIGS["train"], T=T, d=d, E=E, k=k, f=f, score=score, bias="uniform", shared=1, f_shared=fs)
+    inp = make_inputs(cfg)
+    layer = _layer(cfg, inp, aux_alpha=aux)
+    x = dev(inp["x"])
+    layer.forward(x)
+    layer.backward(x, dev(inp["dy"]))
+    torch.cuda.synchronize()
+    idx = host(layer.idx).astype(np.int64)
+    fwd = oracle.forward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], k, score, True,
+                         sel_bias=inp["bias"], logit_offset=inp["logit_offset"], idx=idx,
+                         w_gate_up_shared=inp["w_gate_up_shared"], w_down_shared=inp["w_down_shared"])
+    check_close(host(layer.out), fwd["out"], "bf16", "out")
+    g = oracle.backward(fwd, inp["dy"], inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], score, True,
+                        w_gate_up_shared=inp["w_gate_up_shared"], w_down_shared=inp["w_down_shared"],
+                        aux_alpha=aux)
+    check_close(host(layer.dx), g["dx"], "bf16", "dx")
+    check_close(host(layer.dw_gate_up_shared), g["dw_gate_up_shared"][0], "bf16", "dW_gate_up_shared")
+    check_close(host(layer.dw_down_shared), g["dw_down_shared"][0], "bf16", "dW_down_shared")
+    check_close(host(layer.dw_router), g["dw_router"], "bf16", "dW_router")
+    check_close(host(layer.dw_down), g["dw_down"], "bf16", "dW_down")
+    check_close(host(layer.dw_gate_up), g["dw_gate_up"], "bf16", "dW_gate_up")
+
+
+def test_backward_stage_events():
+    """moe_bwd_args.stage_events: each stage's event is recorded after the
+    stage, in order, and the stage times add up to the call's time; the
+    gradients are the same with and without events."""
+    from mixture_experts_layer_free_amd import _lib as L
+    cfg = scaled(CONFIGS["train"], T=1000, d=256, E=8, k=2, f=128, shared=1, f_shared=128)
+    inp = make_inputs(cfg)
+    layer = _layer(cfg, inp)
+    x, dy = dev(inp["x"]), dev(inp["dy"])
+    layer.forward(x)
+    layer.backward(x, dy)
+    torch.cuda.synchronize()
+    ref = {n: host(getattr(layer, n)).copy() for n in ("dx", "dw_gate_up", "dw_down", "dw_gate_up_shared")}
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(L.BWD_STAGES) + 1)]
+    for e in evs:
+        e.record()                       # the events exist before the library records them
+    torch.cuda.synchronize()
+    evs[0].record()
+    layer.backward(x, dy, stage_events=evs[1:])
+    end = torch.cuda.Event(enable_timing=True)
+    end.record()
+    torch.cuda.synchronize()
+    ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(len(L.BWD_STAGES))]
+    say("  stage ms: " + ", ".join(f"{n} {t:.4f}" for n, t in zip(L.BWD_STAGES, ms)))
+    assert all(t >= 0 for t in ms)
+    total = evs[0].elapsed_time(end)
+    assert sum(ms) <= total + 1e-3 and sum(ms) >= 0.5 * total, (sum(ms), total)
+    for n, v in ref.items():
+        assert np.array_equal(host(getattr(layer, n)), v), n

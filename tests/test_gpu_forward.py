@@ -392,19 +392,23 @@ def test_ffn_gather_equals_permuted_rows(T, d, E, k, f):
 
 
 def test_ffn_gather_out_of_range_token_reads_zero():
-    """A token index outside [0, T) reads as a zero row (bf16 and fp32)."""
+    """A token index outside [0, T) reads as a zero row (bf16 and fp32),
+    including indices whose byte offset is a multiple of 2^32 plus a valid
+    row's offset (they must not wrap onto a row of x)."""
     for base in ("fine", "tiny"):
         d = 128 if base == "fine" else 32
         cfg = scaled(CONFIGS[base], T=200, d=d, E=2, k=1, f=64)
         inp = make_inputs(cfg)
         tok = np.arange(200, dtype=np.int32)
-        tok[[3, 150]] = [-5, 1 << 20]
+        wrap = (1 << 32) // (d * 2)                    # rows per 2^32 bytes of bf16 x
+        bad = [3, 150, 151, 152, 153]
+        tok[bad] = [-5, 1 << 20, wrap, wrap + 7, -(1 << 31)]
         offsets = np.array([0, 100, 200], np.int32)
         _, h, y = L.moe_grouped_ffn_gather(dev(inp["x"]), dev(tok), dev(offsets), dev(inp["w_gate_up"]),
                                            dev(inp["w_down"]))
         torch.cuda.synchronize()
         yh = host(y)
-        assert np.all(yh[[3, 150]] == 0) and np.all(host(h).astype(np.float64)[[3, 150]] == 0)
+        assert np.all(yh[bad] == 0) and np.all(host(h).astype(np.float64)[bad] == 0)
         assert np.count_nonzero(yh[4]) > 0
 
 
