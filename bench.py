@@ -10,10 +10,15 @@ seeded input already resident in HBM:
     logit offset: forward + bias update;
   * "coarse" (8 experts top-2) and "dsv3" (256+1 shared, top-8) forwards.
 
-Prints one JSON line (rank 0).  ``roofline`` covers the dominant library
-call, timed with HIP events on its stream inside the timed region;
-``cpu_baseline`` times the CPU oracle on a bounded sample of the same
-workload.  Progress goes to stderr.
+Prints one JSON line.  ``value`` is tokens/s of the median step of graph
+replays timed between two device synchronisations.  ``roofline`` covers the
+dominant kernel (the longest backward stage, one GEMM launch, timed with the
+HIP events moe_backward records on its stream after each stage);
+``rooflines`` covers every library call and ``kernel_rooflines`` every
+backward stage.  ``fwd_lines`` repeats the measurement for the forward-only
+workloads (8 experts top-2, 64 experts top-8, 256 + 1 shared top-8).
+``cpu_baseline`` times the CPU oracle on a bounded sample of each workload.
+Progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -133,17 +138,26 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload
     n = 1 << 31
     ff = copy_factor(copy_fetch_dir, "FETCH_SIZE", n)
     fw = copy_factor(copy_write_dir, "WRITE_SIZE", n)
-    calls = {}
+    calls, kernels, nk = {}, {}, {}
     for d, counter, fac, key in ((fetch_dir, "FETCH_SIZE", ff, "read"), (write_dir, "WRITE_SIZE", fw, "write")):
         for (_, name), kib in per_kernel(d, counter).items():
             c = call_of(name)
             if c:
                 calls.setdefault(c, {"read": 0.0, "write": 0.0})[key] += kib * 1024.0 * fac
+                sn = short_name(name)
+                kernels.setdefault(sn, {"read": 0.0, "write": 0.0})[key] += kib * 1024.0 * fac
+                if key == "read":
+                    nk[sn] = nk.get(sn, 0) + 1
     out = json.load(open(TRAFFIC)) if os.path.exists(TRAFFIC) else {}
+    if out.get("source_sha") != source_hash():
+        out["workloads"], out["kernels"] = {}, {}   # records of other code are dropped
     out["source_sha"] = source_hash()
     out["calibration"] = {"fetch_factor": round(ff, 4), "write_factor": round(fw, 4),
                           "note": "bytes = counter KiB x 1024 x factor; factor = 2 GiB / counter of a plain 2 GiB copy"}
     out.setdefault("workloads", {})[workload] = {c: {k: int(v / launches) for k, v in rw.items()} for c, rw in calls.items()}
+    # per kernel: bytes per launch (the average over its dispatches)
+    out.setdefault("kernels", {})[workload] = {k: {kk: int(v / nk[k]) for kk, v in rw.items()}
+                                               for k, rw in kernels.items() if nk.get(k)}
     os.makedirs(os.path.dirname(TRAFFIC), exist_ok=True)
     json.dump(out, open(TRAFFIC, "w"), indent=1)
     print(json.dumps(out["workloads"][workload]))
@@ -176,13 +190,49 @@ def summarize_stats(stats_csv, steps, title):
 
 
 def measured_traffic(workload):
+    """Per-call HBM bytes per step measured on the current kernels (None when
+    the HIP code changed since the counters were taken); the per-kernel
+    bytes per launch are under the key "kernels"."""
     try:
         t = json.load(open(TRAFFIC))
     except (OSError, ValueError):
         return None
     if t.get("source_sha") != source_hash():
         return None
-    return t.get("workloads", {}).get(workload)
+    w = t.get("workloads", {}).get(workload)
+    if w is None:
+        return None
+    return dict(w, kernels=t.get("kernels", {}).get(workload, {}))
+
+
+def summarize_counters(files):
+    """Per-kernel table of rocprofv3 --pmc runs (one counter_collection.csv
+    per pass, each run of the same program): every counter summed over a
+    kernel's dispatches, divided by the dispatch count.  Derived columns:
+    MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SQ_BUSY_CU_CYCLES), clock from
+    GRBM_GUI_ACTIVE over the kernel's average duration (when the run also
+    traced kernels), LDS bank conflicts per LDS instruction."""
+    import csv
+    per = {}
+    dur = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            k = short_name(r["Kernel_Name"])
+            d = per.setdefault(k, {})
+            key = r["Counter_Name"]
+            d.setdefault(key, {})
+            d[key][r["Dispatch_Id"]] = d[key].get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+            if "Start_Timestamp" in r and r.get("End_Timestamp"):
+                dur.setdefault(k, {})[r["Dispatch_Id"]] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    cols = sorted({c for d in per.values() for c in d})
+    print("| kernel | " + " | ".join(cols) + " |")
+    print("|---|" + "---:|" * len(cols))
+    for k, d in sorted(per.items(), key=lambda kv: -sum(len(v) for v in kv[1].values())):
+        vals = []
+        for c in cols:
+            v = d.get(c)
+            vals.append(f"{sum(v.values()) / len(v):.4g}" if v else "")
+        print(f"| `{k}` | " + " | ".join(vals) + " |")
 
 
 def algorithmic(cfg, fused=False, gather=None):
@@ -218,18 +268,62 @@ def algorithmic(cfg, fused=False, gather=None):
     return out
 
 
-def blas_threads():
+def blas_info():
+    """BLAS library, version and thread count numpy uses (threadpoolctl)."""
     try:
         from threadpoolctl import threadpool_info
-        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-        return max(n) if n else 1
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return {"library": i.get("internal_api"), "version": i.get("version"),
+                        "threads": i.get("num_threads")}
     except Exception:  # pragma: no cover
-        return 1
+        pass
+    return {"library": None, "version": None, "threads": None}
+
+
+def host_cores():
+    return len(os.sched_getaffinity(0))
+
+
+ONE_CORE_SNIPPET = r"""
+import json, os, sys, time
+os.sched_setaffinity(0, {min(os.sched_getaffinity(0))})
+sys.path.insert(0, sys.argv[1])
+import numpy as np
+import oracle
+from workloads import CONFIGS, make_inputs
+cfg = CONFIGS["tiny"]
+inp = make_inputs(cfg)
+n, t0 = 0, time.perf_counter()
+while time.perf_counter() - t0 < 3.0:
+    oracle.forward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], cfg.k, cfg.score, False,
+                   sel_bias=inp["bias"])
+    n += 1
+dt = time.perf_counter() - t0
+print(json.dumps({"value": round(n * cfg.T / dt, 1), "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+                  "calls": n}))
+"""
+
+
+def oracle_one_core():
+    """The oracle's forward on the tiny fp32 workload (T=64, 8 experts top-2)
+    on one host core with single-threaded BLAS, in a child process started
+    before this process touches the GPU."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    try:
+        r = subprocess.run([sys.executable, "-c", ONE_CORE_SNIPPET, ROOT], env=env, capture_output=True, text=True,
+                           timeout=120)
+        out = json.loads(r.stdout.strip().splitlines()[-1])
+        out.update(kind="oracle", sample="tiny workload (T=64 d=32 E=8 top-2 fp32) forward, repeated for 3 s, "
+                                         "one core, BLAS single-threaded")
+        return out
+    except Exception as e:  # pragma: no cover
+        return {"error": str(e)[:200]}
 
 
 def cpu_baseline(cfg, inp, train, tokens):
     """The oracle, as it stands, on the first `tokens` tokens of the workload."""
-    import numpy as np
     import oracle
     sl = slice(0, tokens)
     x = inp["x"][sl]
@@ -242,40 +336,245 @@ def cpu_baseline(cfg, inp, train, tokens):
     if train:
         oracle.backward(fwd, inp["dy"][sl], x, inp["w_router"], inp["w_gate_up"], inp["w_down"], cfg.score, True)
     dt = time.perf_counter() - t0
-    return {"value": round(tokens / dt, 2), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+    return {"value": round(tokens / dt, 2), "unit": "tokens/s", "cores": host_cores(), "blas": blas_info(),
+            "kind": "oracle",
             "sample": f"first {tokens} of {cfg.T} tokens of the same workload, "
                       f"{'forward+backward' if train else 'forward'} in fp64 numpy ({dt:.1f} s)"}
 
 
-def fwd_line(_lib, a, device):
-    """Forward-only tokens/s on the 64-expert top-8 shape (T=8192, sigmoid
-    router with the Zipf-skewed logit offset, bias update), graph replays."""
+def routing_stats(cfg, inp, idx_gpu, counts_gpu):
+    """Expert load of the first forward (max and min over mean of the counts)
+    and, from the oracle's fp64 router on every token, the tokens excluded as
+    near-ties (k-th and (k+1)-th keys within 1e-6 relative) and the tokens
+    outside them whose expert set differs from the GPU's (expected 0)."""
+    import numpy as np
+    import oracle
+    c = np.asarray(counts_gpu, np.float64)
+    mean = c.mean()
+    r = oracle.route(inp["x"], inp["w_router"], cfg.k, cfg.score, inp["bias"], inp["logit_offset"])
+    excl = r["margin"] < 1e-6
+    g = np.sort(np.asarray(idx_gpu, np.int64), axis=1)
+    o = np.sort(r["idx"], axis=1)
+    mism = int((np.any(g != o, axis=1) & ~excl).sum())
+    return {"load_max_over_mean": round(float(c.max() / mean), 3), "load_min_over_mean": round(float(c.min() / mean), 3),
+            "near_tie_excluded": int(excl.sum()), "idx_mismatch_outside_near_ties": mism}
+
+
+def time_replays(graph, steps, warmup):
+    """Graph replays: `warmup` untimed, then exactly `steps` timed between
+    two device synchronisations.  Events on the replay stream around every
+    replay give per-step times; returns (median ms, mean ms of the events,
+    wall-clock ms per step)."""
+    import statistics
+    import torch
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i].record()
+        graph.replay()
+    ev[steps].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return statistics.median(per), sum(per) / steps, wall
+
+
+def stage_algorithmic(cfg):
+    """Per backward stage (moe_bwd_stage): (flops, bytes, peak TFLOP/s or
+    None for a memory-bound stage) -- each tensor read or written once."""
+    T, d, E, k, f, A = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.T * cfg.k
+    fs = cfg.f_shared * cfg.shared
+    return {
+        "combine": (0, A * d * 4 + T * d * 2 + A * d * 2 + T * k * 12, None),
+        "router": (2.0 * A * d, T * d * 2 + A * 4 + E * d * 4, None),
+        "dgrad_down": (2.0 * A * d * f, A * d * 2 + E * d * f * 2 + 2 * A * 2 * f * 2, PEAK_BF16_TFLOPS),
+        "wgrad_down": (2.0 * A * d * f, A * d * 2 + A * f * 2 + E * d * f * 4, PEAK_BF16_TFLOPS),
+        "wgrad_up": (4.0 * A * d * f, A * 2 * f * 2 + T * d * 2 + E * 2 * f * d * 4, PEAK_BF16_TFLOPS),
+        "dgrad_up": (4.0 * A * d * f, A * 2 * f * 2 + E * 2 * f * d * 2 + A * d * 4, PEAK_BF16_TFLOPS),
+        "shared": (12.0 * T * d * fs, 0, PEAK_BF16_TFLOPS),
+        "unpermute": (0, A * d * 4 + T * d * 4 + E * d * 4 + T * k * 12, None),
+    }
+
+
+# kernel of each backward stage that dominates it (for the per-kernel roofline
+# and its PMC traffic record)
+STAGE_KERNEL = {
+    "dgrad_down": "gemm_kernel<256, 256, true, false, false, 2, false>",
+    "wgrad_down": "gemm_kernel<256, 256, false, false, true, 1, false>",
+    "wgrad_up": "gemm_kernel<256, 256, false, false, true, 1, true>",
+    "dgrad_up": "gemm_kernel<256, 256, true, false, false, 1, false>",
+    "combine": "combine_bwd_rows_kernel",
+    "unpermute": "unpermute_bwd_kernel<8, true>",
+}
+
+
+def roofline_entry(flops, nbytes, peak_flops, ms, traffic=None):
+    t = ms * 1e-3
+    if flops and peak_flops and (not nbytes or flops / nbytes >= peak_flops / PEAK_HBM_GBS * 1e3):
+        ach = flops / t / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 1), "peak": peak_flops, "unit": "TFLOP/s",
+                "frac": round(ach / peak_flops, 4), "ms": round(ms, 4), "flops": flops, "bytes": nbytes,
+                "peak_dtype": "fp32" if peak_flops < PEAK_BF16_TFLOPS else "bf16", "traffic": traffic}
+    ach = nbytes / t / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "ms": round(ms, 4), "flops": flops, "bytes": nbytes,
+            "peak_dtype": None, "traffic": traffic}
+
+
+def build_layer(cfg, inp, device, fuse=True):
     import torch
     from mixture_experts_layer_free_amd.layer import MoELayer, Shape
-    from workloads import CONFIGS, make_inputs
-    cfg = CONFIGS["fine"]
-    log(f"[bench] forward line: generating inputs for {cfg.name}")
-    inp = make_inputs(cfg)
     d = lambda k: _dev(inp.get(k), device)
-    layer = MoELayer(Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, torch.bfloat16, cfg.score, 0, 0, cfg.bias_update,
-                           cfg.gamma, False), d("w_router"), d("w_gate_up"), d("w_down"), d("bias"),
-                     d("logit_offset"), device=device)
-    x = d("x")
+    shape = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, torch.bfloat16, cfg.score, cfg.shared, cfg.f_shared,
+                  cfg.bias_update, cfg.gamma, cfg.train, fuse_permute=fuse)
+    layer = MoELayer(shape, d("w_router"), d("w_gate_up"), d("w_down"), d("bias"), d("logit_offset"),
+                     d("w_gate_up_shared"), d("w_down_shared"), device=device)
+    return layer, d("x"), (d("dy") if cfg.train else None)
+
+
+def measure(cfg, a, device, fuse=True, cpu_tokens=None, graph=True):
+    """One workload: tokens/s from graph replays (median step), per-call and
+    per-backward-stage times from an eager timed region with HIP events on
+    the calls' stream, routing statistics of the first forward, and the
+    oracle on a bounded sample."""
+    import statistics
+    import numpy as np
+    import torch
+    from mixture_experts_layer_free_amd import _lib
+    from mixture_experts_layer_free_amd.layer import CallTimer
+    train = cfg.train
+    inp = None
+    log(f"[bench] {cfg.name}: generating inputs")
+    from workloads import make_inputs
+    inp = make_inputs(cfg)
+    layer, x, dy = build_layer(cfg, inp, device, fuse)
+
+    def step(timer=None, stage_events=None):
+        layer.forward(x, timer=timer)
+        if train:
+            layer.backward(x, dy, timer=timer, stage_events=stage_events)
+
+    # first forward: the routing under the initial bias
+    layer.forward(x)
+    torch.cuda.synchronize()
+    idx0 = layer.idx.cpu().numpy()
+    counts0 = layer.counts.cpu().numpy()
+    if train:
+        layer.backward(x, dy)
+    log(f"[bench] {cfg.name}: warmup {a.warmup}")
     for _ in range(a.warmup):
-        layer.forward(x)
-    graph = layer.capture(x)
-    for _ in range(a.warmup):
-        graph.replay()
+        step()
+    torch.cuda.synchronize()
+    # eager timed region: events around every library call and every backward stage
+    timer = CallTimer()
+    nst = len(_lib.BWD_STAGES)
+    stage_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(a.steps)]
+    for evs in stage_ev:
+        for e in evs:
+            e.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(a.steps):
-        graph.replay()
+    for i in range(a.steps):
+        if train:
+            layer.forward(x, timer=timer)
+            stage_ev[i][0].record()
+            layer.backward(x, dy, timer=timer, stage_events=stage_ev[i][1:])
+        else:
+            step(timer)
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) / a.steps * 1e3
-    log(f"[bench] forward line: {ms:.3f} ms/step")
-    return {"workload": describe(cfg, False) + ", permute fused into the expert GEMM",
-            "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
-            "ms_per_step": round(ms, 4), "expert_tflops": round(expert_flops(cfg, False) / (ms * 1e-3) / 1e12, 1)}
+    eager_ms = (time.perf_counter() - t0) / a.steps * 1e3
+    calls = {n: round(statistics.median(ea.elapsed_time(eb) for ea, eb in timer.pairs[n]), 4) for n in timer.pairs}
+    stages = {}
+    if train:
+        for si, name in enumerate(_lib.BWD_STAGES):
+            stages[name] = round(statistics.median(stage_ev[i][si].elapsed_time(stage_ev[i][si + 1])
+                                                   for i in range(a.steps)), 4)
+    log(f"[bench] {cfg.name}: eager {eager_ms:.3f} ms/step; calls {calls}; backward stages {stages}")
+    if graph:
+        g = layer.capture(x, dy)
+        log(f"[bench] {cfg.name}: timing {a.steps} graph replays")
+        med, mean, wall = time_replays(g, a.steps, a.warmup)
+        del g
+    else:
+        med = mean = wall = eager_ms
+    log(f"[bench] {cfg.name}: {med:.4f} ms/step (median), mean {mean:.4f}, wall {wall:.4f}")
+    traffic = measured_traffic(cfg.name)
+    ktraffic = (traffic or {}).get("kernels", {})
+    rooflines = {}
+    for call, (flops, nbytes, peak_flops) in algorithmic(cfg, fuse, fuse).items():
+        if call in calls:
+            tr = traffic.get(call) if traffic else None
+            rooflines[call] = roofline_entry(flops, nbytes, peak_flops, calls[call],
+                                             (tr["read"] + tr["write"]) if tr else None)
+    kernels = {}
+    for name, (flops, nbytes, peak_flops) in stage_algorithmic(cfg).items():
+        if name in stages and (flops or nbytes):
+            kn = STAGE_KERNEL.get(name)
+            tr = ktraffic.get(kn) if kn else None
+            kernels[name] = roofline_entry(flops, nbytes, peak_flops, stages[name],
+                                           (tr["read"] + tr["write"]) if tr else None)
+            if kn:
+                kernels[name]["kernel"] = kn
+    res = {"ms_per_step": round(med, 4), "ms_per_step_mean": round(mean, 4), "ms_per_step_wall": round(wall, 4),
+           "tokens_per_s": round(cfg.T / (med * 1e-3), 1), "eager_ms_per_step": round(eager_ms, 4),
+           "calls_ms": calls, "rooflines": rooflines,
+           "expert_tflops": round(expert_flops(cfg, train) / (med * 1e-3) / 1e12, 1)}
+    if train:
+        res["backward_stages_ms"] = stages
+        res["kernel_rooflines"] = kernels
+    res["routing"] = routing_stats(cfg, inp, idx0, counts0)
+    log(f"[bench] {cfg.name}: routing {res['routing']}")
+    del layer, x, dy
+    torch.cuda.empty_cache()
+    if cpu_tokens:
+        log(f"[bench] {cfg.name}: cpu oracle on {cpu_tokens} tokens")
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, train, cpu_tokens)
+    del inp
+    return res
+
+
+# hipBLASLt (torch.mm) GEMMs with the M, N, K of the six expert GEMMs of the
+# training step, each dense over all A = T*k rows (the weight gradients as
+# one product with K = A): the same flops as the grouped kernels, bf16 out.
+LIB_GEMMS = ("up", "down", "dgrad_down", "wgrad_down", "wgrad_up", "dgrad_up")
+
+
+def library_gemms(cfg, steps, device):
+    import torch
+    A, d, f = cfg.T * cfg.k, cfg.d, cfg.f
+    g = torch.Generator(device=device).manual_seed(0)
+    r = lambda *s: (torch.randn(*s, device=device, generator=g) * 0.5).to(torch.bfloat16)
+    X, Wgu, Wd = r(A, d), r(2 * f, d), r(d, f)
+    Hh, dYp, dGU = r(A, f), r(A, d), r(A, 2 * f)
+    ops = {
+        "up": lambda: torch.mm(X, Wgu.t()),            # [A,d] x [d,2f]
+        "down": lambda: torch.mm(Hh, Wd.t()),          # [A,f] x [f,d]
+        "dgrad_down": lambda: torch.mm(dYp, Wd),       # [A,d] x [d,f]
+        "wgrad_down": lambda: torch.mm(dYp.t(), Hh),   # [d,A] x [A,f]
+        "wgrad_up": lambda: torch.mm(dGU.t(), X),      # [2f,A] x [A,d]
+        "dgrad_up": lambda: torch.mm(dGU, Wgu),        # [A,2f] x [2f,d]
+    }
+    flops = {"up": 4.0 * A * d * f, "down": 2.0 * A * d * f, "dgrad_down": 2.0 * A * d * f,
+             "wgrad_down": 2.0 * A * d * f, "wgrad_up": 4.0 * A * d * f, "dgrad_up": 4.0 * A * d * f}
+    out = {}
+    for name in LIB_GEMMS:
+        fn = ops[name]
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        out[name] = {"ms": round(ms, 4), "tflops": round(flops[name] / (ms * 1e-3) / 1e12, 1)}
+        log(f"[bench] hipBLASLt {name}: {ms:.4f} ms, {out[name]['tflops']} TFLOP/s")
+    return out
 
 
 def bench_ep_shard(a):
@@ -342,16 +641,24 @@ def bench_ep_shard(a):
     print(json.dumps(res), flush=True)
 
 
+CPU_TOKENS = {"train": 16384, "train_skew": 16384, "fine": 4096, "coarse": 512, "dsv3": 16}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="train", choices=["train", "fine", "coarse", "dsv3", "dsv3_ep8"])
-    ap.add_argument("--cpu-tokens", type=int, default=None, help="oracle sample size (tokens)")
+    ap.add_argument("--workload", default="train",
+                    choices=["train", "train_skew", "fine", "coarse", "dsv3", "dsv3_ep8"])
+    ap.add_argument("--fwd-lines", default="fine,coarse,dsv3",
+                    help="forward-only workloads measured after the training line (comma-separated; '' for none)")
+    ap.add_argument("--cpu-tokens", type=int, default=None, help="oracle sample size of the headline (tokens)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
-    ap.add_argument("--no-fwd", action="store_true", help="skip the forward-only line on the 64-expert shape")
+    ap.add_argument("--no-fwd", action="store_true", help="skip the forward-only lines")
+    ap.add_argument("--library-gemms", action="store_true",
+                    help="also time hipBLASLt GEMMs with the M, N, K of the training step's six expert GEMMs")
     ap.add_argument("--no-fuse-permute", action="store_true",
                     help="the permute copies X_perm, and the up-projection and W_gate_up's weight gradient read it, "
                          "instead of gathering x rows through token_of")
@@ -359,6 +666,8 @@ def main():
                     help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs of this bench into profiles/traffic.json")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("KERNEL_STATS_CSV", "STEPS"),
                     help="print a rocprofv3 kernel_stats.csv of this bench as a markdown table")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="COUNTER_CSV",
+                    help="print rocprofv3 --pmc counter_collection.csv files (one per pass) as a per-kernel table")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 2 GiB device-to-device copy (HBM reference and PMC byte calibration)")
     a = ap.parse_args()
@@ -367,12 +676,22 @@ def main():
         return
     if a.summarize_pmc:
         # the profiled run is `bench.py --no-graph --no-fwd --no-cpu-baseline` with the same --steps/--warmup
-        summarize_pmc(*a.summarize_pmc, workload=a.workload, launches=a.steps + a.warmup)
+        # (plus one first forward/backward before the warm-up)
+        summarize_pmc(*a.summarize_pmc, workload=a.workload, launches=a.steps + a.warmup + 1)
+        return
+    if a.summarize_counters:
+        summarize_counters(a.summarize_counters)
         return
     if a.gpus != 1:
         print(f"bench.py measures one GPU: this layer's hot path runs on a single MI355X and has no multi-GPU "
               f"mode (asked for --gpus {a.gpus}).", file=sys.stderr)
         sys.exit(2)
+    # the one-core oracle runs in a child process, started before this
+    # process touches the GPU
+    one_core = None
+    if not a.no_cpu_baseline and a.workload == "train":
+        log("[bench] oracle on one core (tiny workload)")
+        one_core = oracle_one_core()
 
     import torch
     if a.copy_probe:
@@ -397,100 +716,54 @@ def main():
         bench_ep_shard(a)
         return
     from mixture_experts_layer_free_amd import _lib
-    from mixture_experts_layer_free_amd.layer import CallTimer, MoELayer, Shape
-    from workloads import CONFIGS, make_inputs
+    from workloads import CONFIGS
 
     _lib.lib()
     cfg = CONFIGS[a.workload]
     train = cfg.train
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
-    log(f"[bench] generating inputs for {cfg.name}")
-    inp = make_inputs(cfg)
-    d = lambda k: _dev(inp.get(k), device)
-    shape = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, torch.bfloat16, cfg.score, cfg.shared, cfg.f_shared,
-                  cfg.bias_update, cfg.gamma, train, fuse_permute=not a.no_fuse_permute)
-    layer = MoELayer(shape, d("w_router"), d("w_gate_up"), d("w_down"), d("bias"), d("logit_offset"),
-                     d("w_gate_up_shared"), d("w_down_shared"), device=device)
-    x = d("x")
-    dy = d("dy") if train else None
-
-    def step(timer=None):
-        layer.forward(x, timer=timer)
-        if train:
-            layer.backward(x, dy, timer=timer)
-
-    log(f"[bench] warmup {a.warmup}")
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    # timed region 1: eager launches with HIP events around every library call
-    timer = CallTimer()
-    log(f"[bench] timing {a.steps} eager steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(a.steps):
-        step(timer)
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t0) / a.steps * 1e3
-    calls = {n: round(timer.mean_ms(n), 4) for n in timer.pairs}
-    log(f"[bench] eager {eager_ms:.3f} ms/step, per call ms: {calls}")
-    # timed region 2: the same step captured once in a HIP graph and replayed
-    if a.no_graph:
-        ms = eager_ms
-    else:
-        graph = layer.capture(x, dy)
-        for _ in range(a.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        log(f"[bench] timing {a.steps} graph replays")
-        t0 = time.perf_counter()
-        for _ in range(a.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) / a.steps * 1e3
-        log(f"[bench] graph {ms:.3f} ms/step")
-    value = cfg.T / (ms * 1e-3)
-
-    # per-call rooflines: algorithmic work per call / the call's event time
-    traffic = measured_traffic(cfg.name)
-    rooflines = {}
-    gather = not a.no_fuse_permute                 # the expert GEMMs read x through token_of
-    fused = gather                                 # and then no X_perm is written
-    for call, (flops, nbytes, peak_flops) in algorithmic(cfg, fused, gather).items():
-        if call not in calls:
-            continue
-        t = calls[call] * 1e-3
-        tr = traffic.get(call) if traffic else None
-        if flops and flops / nbytes >= peak_flops / PEAK_HBM_GBS * 1e3:   # at or above the ridge: compute-bound
-            ach, peak, unit = flops / t / 1e12, peak_flops, "TFLOP/s"
-            bound, dt = "mfma", ("fp32" if peak_flops < PEAK_BF16_TFLOPS else "bf16")
-        else:
-            ach, peak, unit, bound, dt = nbytes / t / 1e9, PEAK_HBM_GBS, "GB/s", "hbm", None
-        rooflines[call] = {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit,
-                           "frac": round(ach / peak, 4), "call_ms": calls[call], "peak_dtype": dt,
-                           "flops": flops, "bytes": nbytes, "traffic": (tr["read"] + tr["write"]) if tr else None}
-    dom = max((c for c in rooflines), key=lambda c: calls[c])
-    roof = dict(rooflines[dom])
-    roof["kernel"] = f"moe_{dom} (library call, all of its kernels)"
-
-    res = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
-           "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": describe(cfg, train) + (", permute fused into the expert GEMMs"
-                                                          if fused else ""),
-                      "global_batch": cfg.T, "seq_len": None,
-                      "parallelism": "none (1 GPU)"},
-           "eager_ms_per_step": round(eager_ms, 4), "step_mode": "eager" if a.no_graph else "hip_graph_replay",
-           "calls_ms": calls, "expert_tflops": round(expert_flops(cfg, train) / (ms * 1e-3) / 1e12, 1),
-           "roofline": roof, "rooflines": rooflines}
+    fuse = not a.no_fuse_permute
+    cpu_tokens = None if a.no_cpu_baseline else (a.cpu_tokens or CPU_TOKENS[cfg.name])
+    head = measure(cfg, a, device, fuse, cpu_tokens, graph=not a.no_graph)
+    lib_gemms = library_gemms(cfg, a.steps, device) if (a.library_gemms and train) else None
+    fwd_lines = {}
     if train and not a.no_fwd:
-        res["fwd"] = fwd_line(_lib, a, device)
-    if not a.no_cpu_baseline:
-        # about 10-30 s of oracle work on the host's cores
-        tokens = a.cpu_tokens or {"train": 16384, "fine": 8192, "coarse": 4096, "dsv3": 1024}[cfg.name]
-        log(f"[bench] cpu oracle on {tokens} tokens")
-        res["cpu_baseline"] = cpu_baseline(cfg, inp, train, tokens)
+        for name in [n for n in a.fwd_lines.split(",") if n]:
+            c = CONFIGS[name]
+            r = measure(c, a, device, True, None if a.no_cpu_baseline else CPU_TOKENS[name], graph=not a.no_graph)
+            r["workload"] = describe(c, False) + ", permute fused into the expert GEMM"
+            fwd_lines[name] = r
+    # the dominant kernel: the longest backward stage that is one GEMM kernel
+    # (training), else the longest library call
+    if train and head.get("kernel_rooflines"):
+        kr = {k: v for k, v in head["kernel_rooflines"].items() if "kernel" in v}
+        dom = max(kr, key=lambda k: kr[k]["ms"])
+        roof = dict(kr[dom])
+        roof["kernel"] = f"{roof['kernel']} (moe_backward stage {dom}, one launch per step)"
+    else:
+        dom = max(head["rooflines"], key=lambda c: head["rooflines"][c]["ms"])
+        roof = dict(head["rooflines"][dom])
+        roof["kernel"] = f"moe_{dom} (library call, all of its kernels)"
+    res = {"metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+           "warmup": a.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": describe(cfg, train) + (", permute fused into the expert GEMMs" if fuse else ""),
+                      "global_batch": cfg.T, "seq_len": None, "parallelism": "none (1 GPU)"},
+           "step_mode": ("eager" if a.no_graph else "hip_graph_replay") + ", ms_per_step = median of the steps",
+           "roofline": roof}
+    for k in ("ms_per_step_mean", "ms_per_step_wall", "eager_ms_per_step", "calls_ms", "backward_stages_ms",
+              "expert_tflops", "rooflines", "kernel_rooflines", "routing"):
+        if k in head:
+            res[k] = head[k]
+    if fwd_lines:
+        res["fwd_lines"] = fwd_lines
+    if lib_gemms:
+        res["library_gemms"] = lib_gemms
+    if "cpu_baseline" in head:
+        res["cpu_baseline"] = head["cpu_baseline"]
+        if one_core:
+            res["cpu_baseline"]["one_core_tiny"] = one_core
     print(json.dumps(res), flush=True)
 
 

@@ -347,12 +347,13 @@ moe_status moe_aux_loss(const float* logits, const int32_t* counts, int64_t T, i
  * forward above.  The selection bias and the logit offset get no gradient
  * (lesson, Key terms: the loss-free bias adds no gradient signal), and the
  * discrete top-k choice is held fixed.
- *   combine:  dg[t,j] = <dy[t], y_perm[row_of[t,j]]>,
- *             dY_perm[row_of[t,j]] = bf16(gate[t,j] * dy[t])
+ *   combine:  dg[t,j] = <dy[t], y_perm[row_of[t,j]]>, computed as
+ *             <dy[t] W_down[e], H[row]> (the same sum, y_perm = H W_down^T,
+ *             so y_perm is not read), dY_perm[row_of[t,j]] = bf16(gate[t,j] * dy[t])
  *   gates:    softmax: dl_j = g_j (dg_j - D), D = sum_i g_i dg_i;
  *             normalised scores: dl_j = (dg_j - D) / S * s'(l_j), S = sum s
  *   router:   dW_r = dL^T x, dx_r = dL W_r (dL = dl at the chosen experts)
- *   experts:  dH = dY_perm W_down; dG = bf16(dH U silu'(G));
+ *   experts:  dH = gate * (dy W_down) (fp32); dG = bf16(dH U silu'(G));
  *             dU = bf16(dH silu(G)) from the saved bf16 G, U;
  *             dW_down = dY_perm^T H; dW_gate = dG^T X; dW_up = dU^T X;
  *             dX_perm = dG W_gate + dU W_up
@@ -383,7 +384,8 @@ typedef struct moe_bwd_args {
                                   for row r (no X_perm buffer needed) */
   const void* gu_saved;        /* [T*k, 2f] bf16 */
   const void* h;               /* [T*k, f] bf16 */
-  const float* y_perm;         /* [T*k, d] f32 */
+  const float* y_perm;         /* not read, may be NULL (kept for the struct
+                                  layout): dg is formed from dy W_down and H */
   const void* w_gate_up;       /* [E, 2f, d] bf16 */
   const void* w_down;          /* [E, d, f] bf16 */
   /* outputs (f32) */
@@ -427,9 +429,10 @@ typedef struct moe_bwd_args {
 
 /* Stages of moe_backward, in stream order (for moe_bwd_args.stage_events). */
 enum moe_bwd_stage {
-  MOE_BWD_COMBINE = 0,      /* combine backward and gate backward (dg, dl) */
-  MOE_BWD_ROUTER = 1,       /* router weight gradient */
-  MOE_BWD_DGRAD_DOWN = 2,   /* tile schedule; dH = dY_perm W_down, SwiGLU backward -> dG|dU */
+  MOE_BWD_COMBINE = 0,      /* combine backward: dY_perm = bf16(g dy) per expert row */
+  MOE_BWD_DGRAD_DOWN = 1,   /* tile schedule; dH' = dy W_down, dg partials <dH', H>,
+                               dH = g dH', SwiGLU backward -> dG|dU */
+  MOE_BWD_ROUTER = 2,       /* gate backward (dg, dl) and the router weight gradient */
   MOE_BWD_WGRAD_DOWN = 3,   /* dW_down = dY_perm^T H */
   MOE_BWD_WGRAD_UP = 4,     /* dW_gate_up = [dG|dU]^T X */
   MOE_BWD_DGRAD_UP = 5,     /* dX_perm = [dG|dU] W_gate_up */

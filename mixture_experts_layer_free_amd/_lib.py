@@ -22,7 +22,7 @@ SCORE = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "uniform": 3}
 (MOE_CALL_ROUTE, MOE_CALL_PERMUTE, MOE_CALL_GROUPED_FFN, MOE_CALL_BACKWARD, MOE_CALL_AUX_LOSS,
  MOE_CALL_BACKWARD_SHARED) = range(6)
 # stages of moe_backward (enum moe_bwd_stage), in stream order
-BWD_STAGES = ("combine", "router", "dgrad_down", "wgrad_down", "wgrad_up", "dgrad_up", "shared", "unpermute")
+BWD_STAGES = ("combine", "dgrad_down", "router", "wgrad_down", "wgrad_up", "dgrad_up", "shared", "unpermute")
 MAX_EXPERTS, MAX_TOPK = 1024, 16
 PERMUTE_NOALLOC_SCRATCH = 4 << 20   # bytes of moe_permute_noalloc's static device scratch
 

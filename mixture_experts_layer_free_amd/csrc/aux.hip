@@ -252,8 +252,7 @@ __global__ __launch_bounds__(256) void unpermute_bwd_dense_kernel(const f32x4* _
     f32x4 acc = extra ? __builtin_nontemporal_load(extra + t * nv + v) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      const f32x4 l = __builtin_nontemporal_load(xr[j] + v);
-      if (live[j]) acc += l;
+      if (live[j]) acc += __builtin_nontemporal_load(xr[j] + v);
     }
     for (int e = 0; e < E; ++e) {
       const float w = dlr[e];

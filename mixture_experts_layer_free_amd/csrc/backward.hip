@@ -5,19 +5,25 @@
 // step 1).  The selection bias and the logit offset get no gradient (Key
 // terms: the loss-free bias adds no gradient signal) and the top-k choice is
 // held fixed.  Kernels, in stream order:
-//   1. combine_bwd   one wave per expert row: dg = <dy, y_perm[row]>,
-//                    dY_perm = bf16(g*dy); then one wave per token for the
-//                    gate backward (dl on the chosen experts)
-//   2. router wgrad  dW_r[e] = sum over e's rows of dl * x_perm, read from x
-//                    through token_of (row-chunk partials, then an ordered
-//                    reduction: deterministic)
-//   3. dgrad down    dH = dY_perm W_down, epilogue SwiGLU backward -> dG|dU
+//   1. combine_bwd   one wave per expert row r (token t, slot j):
+//                    dY_perm[r] = bf16(g*dy[t]), and the row's gate g
+//   2. dgrad down    dH' = dy[t] W_down (dy rows read through token_of);
+//                    epilogue: gate-gradient partials dg += <dH', H> over 32
+//                    columns (dg = <dy, y_perm row> = <dy W_down, H>, so the
+//                    fp32 expert output is never read back), then
+//                    dH = g dH' and the SwiGLU backward -> dG|dU
+//   3. gate_bwd      one wave per token: dg from the partials, dl on the
+//                    chosen experts; router weight gradient dW_r[e] = sum over
+//                    e's rows of dl * x rows (row-chunk partials, then an
+//                    ordered reduction: deterministic)
 //   4. wgrad down    dW_down[e] = dY_perm^T H over e's rows
 //   5. wgrad up      dW_gate_up[e] = [dG|dU]^T X_perm over e's rows (with
 //                    no X_perm given, its rows are read from x through
 //                    token_of inside the GEMM's slab loads)
 //   6. dgrad up      dX_perm = [dG|dU] W_gate_up (fp32)
-//   7. unpermute_bwd one wave per token: dx = sum_j dX_perm[row] + sum_j dl*W_r[e]
+//   7. shared expert (optional) the same products over all tokens
+//   8. unpermute_bwd one wave per token: dx = sum_j dX_perm[row_of[t,j]]
+//                    + sum_j dl*W_r[e] (+ the shared expert's input gradient)
 // With an expert capacity (moe_permute_capacity), a dropped assignment has
 // no expert output: it gets dg = 0 and no dY_perm / dX_perm row, but its
 // logit still has a gradient through the gate normalisation, and the router
@@ -39,18 +45,17 @@ __device__ __forceinline__ float score_of(float l, int fn) {
   return l;
 }
 
-// Combine backward in the permuted domain, one wave per expert row r (of
-// token t, slot j): dY_perm[r] = bf16(g[t,j] * dy[t]) and
-// dgp[r] = <dy[t], y_perm[r]>.  Rows are streamed in order (y_perm read and
-// dY_perm written sequentially); only dy rows are gathered, and those are
-// re-read k times from cache.
-__global__ __launch_bounds__(256) void combine_bwd_rows_kernel(const bf16_t* __restrict__ dy, const float* __restrict__ y,
+// Combine backward in the permuted domain, one wave per kept expert row r
+// (of token t, slot j): dY_perm[r] = bf16(g[t,j] * dy[t]) and gperm[r] = g[t,j].
+// dY_perm is written in row order; dy rows are gathered and re-read k times
+// from cache.
+__global__ __launch_bounds__(256) void combine_bwd_rows_kernel(const bf16_t* __restrict__ dy,
                                                                const int32_t* __restrict__ row_of,
                                                                const int32_t* __restrict__ token_of,
                                                                const float* __restrict__ gate,
                                                                const int32_t* __restrict__ kept_rows, int64_t A, int k,
                                                                int64_t d, bf16_t* __restrict__ dy_perm,
-                                                               float* __restrict__ dgp) {
+                                                               float* __restrict__ gperm) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= A || r >= *kept_rows) return;   // rows past the kept ones have no expert output
@@ -60,37 +65,25 @@ __global__ __launch_bounds__(256) void combine_bwd_rows_kernel(const bf16_t* __r
   const float g = gate[t * k + j];
   const int64_t nv = d / 8;   // 8 values per 16-byte bf16 vector
   const u32x4* dyv = reinterpret_cast<const u32x4*>(dy + t * d);
-  const f32x4* yr = reinterpret_cast<const f32x4*>(y + r * d);
   u32x4* out = reinterpret_cast<u32x4*>(dy_perm + r * d);
-  float part = 0.f;
   for (int64_t v = lane; v < nv; v += MOE_WAVE) {
     const u32x4 raw = dyv[v];
-    const f32x4 y0 = __builtin_nontemporal_load(yr + 2 * v);
-    const f32x4 y1 = __builtin_nontemporal_load(yr + 2 * v + 1);
-    float a[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      a[2 * q] = bf16_to_f32(raw[q] & 0xFFFFu);
-      a[2 * q + 1] = bf16_to_f32(raw[q] >> 16);
-    }
-    part = fmaf(a[0], y0[0], part); part = fmaf(a[1], y0[1], part);
-    part = fmaf(a[2], y0[2], part); part = fmaf(a[3], y0[3], part);
-    part = fmaf(a[4], y1[0], part); part = fmaf(a[5], y1[1], part);
-    part = fmaf(a[6], y1[2], part); part = fmaf(a[7], y1[3], part);
     u32x4 o;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(g * a[2 * q], g * a[2 * q + 1]);
-    out[v] = o;
+    for (int q = 0; q < 4; ++q)
+      o[q] = pack_bf16x2(g * bf16_to_f32(raw[q] & 0xFFFFu), g * bf16_to_f32(raw[q] >> 16));
+    __builtin_nontemporal_store(o, out + v);
   }
-  part = wave_sum(part);
-  if (lane == 0) dgp[r] = part;
+  if (lane == 0) gperm[r] = g;
 }
 
 // Gate backward, one wave per token (lanes 0..k-1 hold the chosen experts):
-// dl on the chosen experts from dg = dgp[row_of[t,j]].  dg and dl are
+// dg = the sum of the row's np32 partials from the dgrad-down epilogue, then
+// dl on the chosen experts.  dg and dl are
 // written for every slot.  An expert id outside [0, E) is invalid input (its
 // token's results are unspecified); such a slot is never used as an index.
-__global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__ dgp, const int32_t* __restrict__ row_of,
+__global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__ dg_part, int np32,
+                                                       const int32_t* __restrict__ row_of,
                                                        const float* __restrict__ gate, const int32_t* __restrict__ idx,
                                                        const float* __restrict__ logits, int T, int k, int E, int fn,
                                                        float* __restrict__ dg_out, float* __restrict__ dl_out,
@@ -106,7 +99,11 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
   const int myr = slot ? row_of[t * k + lane] : 0;
   const float myg = act ? gate[t * k + lane] : 0.f;
   const int mye = act ? e_in : 0;
-  const float dg = act && myr >= 0 ? dgp[myr] : 0.f;   // a dropped slot adds nothing to the output
+  float dg = 0.f;   // a dropped slot adds nothing to the output
+  if (act && myr >= 0) {
+    const float* pr = dg_part + (int64_t)myr * np32;   // the row's partials, in column order
+    for (int b = 0; b < np32; ++b) dg += pr[b];
+  }
   const int prow = myr >= 0 ? myr : (myr == INT32_MIN ? -1 : ~myr);   // its x_perm row, kept or dropped
   const float D = wave_sum(act ? myg * dg : 0.f);
   float dl;
@@ -251,7 +248,8 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* _
 }
 
 // dx[t] = extra[t] + sum_j dx_perm[row_of[t,j]] + sum_j dl[t,j] * w_router[idx[t,j]]
-// (extra: the shared expert's input gradient, or null)
+// (extra: the shared expert's input gradient, or null; a slot without a row,
+// row_of < 0, is never read)
 // (a dropped slot, row_of < 0, has no dx_perm row: its load goes to row 0 and
 // is replaced by zero)
 template <int K, bool ROUTER>
@@ -284,8 +282,7 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restr
     f32x4 xs[K], ws[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      const f32x4 l = __builtin_nontemporal_load(xr[j] + v);
-      xs[j] = live[j] ? l : f32x4{0.f, 0.f, 0.f, 0.f};
+      xs[j] = live[j] ? __builtin_nontemporal_load(xr[j] + v) : f32x4{0.f, 0.f, 0.f, 0.f};
       if (ROUTER) ws[j] = wr[j][v];
     }
     f32x4 acc = extra ? __builtin_nontemporal_load(extra + t * nv + v) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -312,8 +309,24 @@ __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
 }
 
 struct BwdLayout {
-  size_t dy_perm, dgu, dx_perm, dg, dl, dl_perm, dgp, mt_prefix, rc_prefix, seg_beg, seg_end, rpart, aux, total;
+  size_t dy_perm, dgu, dx_perm, dg, dl, dl_perm, gperm, dg_part, mt_prefix, rc_prefix, seg_beg, seg_end, rpart, aux,
+      kg_sched, kg_partial, total;
 };
+
+// Tile choices and chunk plans of the two weight-gradient GEMMs (M x N
+// outputs over `rows` reduction rows in G groups).
+inline bool wgrad_down_large(int64_t d, int64_t f) { return d >= moe_gemm::BM_LARGE && f >= moe_gemm::BN_LARGE; }
+inline bool wgrad_up_large(int64_t d, int64_t f) { return 2 * f >= moe_gemm::BM_LARGE && d >= moe_gemm::BN_LARGE; }
+inline size_t kg_sched_need(int64_t rows, int G, int64_t d, int64_t f) {
+  using namespace moe_gemm;
+  return std::max(kg_sched_bytes(kg_plan(d, f, rows, G, wgrad_down_large(d, f)), G),
+                  kg_sched_bytes(kg_plan(2 * f, d, rows, G, wgrad_up_large(d, f)), G));
+}
+inline size_t kg_partial_need(int64_t rows, int G, int64_t d, int64_t f) {
+  using namespace moe_gemm;
+  return std::max(kg_partial_bytes(kg_plan(d, f, rows, G, wgrad_down_large(d, f))),
+                  kg_partial_bytes(kg_plan(2 * f, d, rows, G, wgrad_up_large(d, f))));
+}
 
 BwdLayout layout(int64_t T, int k, int E, int64_t d, int64_t f) {
   const int64_t A = T * k;
@@ -326,13 +339,16 @@ BwdLayout layout(int64_t T, int k, int E, int64_t d, int64_t f) {
   L.dg = take((size_t)T * k * 4);
   L.dl = take((size_t)T * k * 4);
   L.dl_perm = take((size_t)A * 4);
-  L.dgp = take((size_t)A * 4);
+  L.gperm = take((size_t)A * 4);
+  L.dg_part = take((size_t)A * (size_t)(f / 32) * 4);
   L.mt_prefix = take((size_t)(E + 1) * 4);
   L.rc_prefix = take((size_t)(2 * E + 1) * 4);
   L.seg_beg = take((size_t)2 * E * 4);
   L.seg_end = take((size_t)2 * E * 4);
   L.rpart = take((size_t)(ceil_div(A, RCH) + 2 * E) * d * 4);
   L.aux = take(moe_aux_bwd_workspace(T, E, d));
+  L.kg_sched = take(kg_sched_need(A, E, d, f));
+  L.kg_partial = take(kg_partial_need(A, E, d, f));
   L.total = o;
   return L;
 }
@@ -340,7 +356,7 @@ BwdLayout layout(int64_t T, int k, int E, int64_t d, int64_t f) {
 // Workspace of the shared expert's backward: dG|dU [T, 2fs] bf16, its input
 // gradient [T, d] f32, and its one-group offsets and tile prefix.
 struct SharedLayout {
-  size_t dgu, dx, offs, mt_prefix, total;
+  size_t dgu, dx, offs, mt_prefix, kg_sched, kg_partial, total;
 };
 
 SharedLayout shared_layout(int64_t T, int64_t d, int64_t fs) {
@@ -351,6 +367,8 @@ SharedLayout shared_layout(int64_t T, int64_t d, int64_t fs) {
   L.dx = take((size_t)T * d * 4);
   L.offs = take(2 * 4);
   L.mt_prefix = take(2 * 4);
+  L.kg_sched = take(kg_sched_need(T, 1, d, fs));
+  L.kg_partial = take(kg_partial_need(T, 1, d, fs));
   L.total = o;
   return L;
 }
@@ -384,7 +402,7 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   if (a->score_fn < MOE_SOFTMAX_CHOSEN || a->score_fn > MOE_UNIFORM_GATES) return MOE_EINVAL;
   const bool router = a->score_fn != MOE_UNIFORM_GATES;
   if (!a->dy || !a->x || !a->topk_idx || !a->topk_gate || !a->row_of || !a->token_of || !a->offsets ||
-      !a->gu_saved || !a->h || !a->y_perm || !a->w_gate_up || !a->w_down || !a->dx || !a->dw_gate_up || !a->dw_down)
+      !a->gu_saved || !a->h || !a->w_gate_up || !a->w_down || !a->dx || !a->dw_gate_up || !a->dw_down)
     return MOE_EINVAL;
   if (router && (!a->w_router || !a->logits || !a->dw_router)) return MOE_EINVAL;
   const bool aux = aux_alpha != 0.0f;
@@ -428,7 +446,10 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   float* dg = a->dgate ? a->dgate : reinterpret_cast<float*>(ws + Lo.dg);
   float* dl = a->dlogit ? a->dlogit : reinterpret_cast<float*>(ws + Lo.dl);
   float* dl_perm = reinterpret_cast<float*>(ws + Lo.dl_perm);
-  float* dgp = reinterpret_cast<float*>(ws + Lo.dgp);
+  float* gperm = reinterpret_cast<float*>(ws + Lo.gperm);
+  float* dg_part = reinterpret_cast<float*>(ws + Lo.dg_part);
+  int32_t* kg_sched = reinterpret_cast<int32_t*>(ws + Lo.kg_sched);
+  float* kg_partial = reinterpret_cast<float*>(ws + Lo.kg_partial);
   int32_t* mt_prefix = reinterpret_cast<int32_t*>(ws + Lo.mt_prefix);
   int32_t* rc_prefix = reinterpret_cast<int32_t*>(ws + Lo.rc_prefix);
   int32_t* seg_beg = reinterpret_cast<int32_t*>(ws + Lo.seg_beg);
@@ -438,16 +459,41 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   const bf16_t* wgu = static_cast<const bf16_t*>(a->w_gate_up);
   const bf16_t* wd = static_cast<const bf16_t*>(a->w_down);
 
-  // 1. combine backward (permuted domain) + gate backward
-  combine_bwd_rows_kernel<<<(unsigned)ceil_div(A, 4), 256, 0, s>>>(static_cast<const bf16_t*>(a->dy), a->y_perm,
-                                                                     a->row_of, a->token_of, a->topk_gate,
-                                                                     a->offsets + E, A, k, d, dy_perm, dgp);
-  MOE_LAUNCH_CHECK();
-  gate_bwd_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(dgp, a->row_of, a->topk_gate, a->topk_idx, a->logits, (int)T,
-                                                           k, E, a->score_fn, dg, dl, dl_perm);
+  using namespace moe_gemm;
+  const bool large = use_large_tile(f);
+  const int np32 = (int)(f / 32);
+  // 1. combine backward (permuted domain): dY_perm and each row's gate
+  combine_bwd_rows_kernel<<<(unsigned)ceil_div(A, 4), 256, 0, s>>>(static_cast<const bf16_t*>(a->dy), a->row_of,
+                                                                     a->token_of, a->topk_gate, a->offsets + E, A, k,
+                                                                     d, dy_perm, gperm);
   MOE_LAUNCH_CHECK();
   MOE_MARK(MOE_BWD_COMBINE);
-  // 2. router weight gradient (with the aux loss: dense, together with dx below)
+  // 2. dH' = dy W_down over each expert's rows (dy rows gathered through
+  //    token_of); epilogue: dg partials against H, dH = g dH', SwiGLU
+  //    backward -> dG|dU
+  moe_status st = moe_tile_schedule_launch(a->offsets, E, large ? BM_LARGE : BM, mt_prefix, s);
+  if (st != MOE_OK) return st;
+  {
+    Args g{};
+    g.A = static_cast<const bf16_t*>(a->dy); g.lda = d;
+    g.a_rows = a->token_of; g.a_rows_total = T;
+    g.B = wd; g.ldb = f; g.b_group = d * f;
+    g.K = d; g.N = f;
+    g.offsets = a->offsets; g.mt_prefix = mt_prefix; g.G = E;
+    g.gu_in = static_cast<const bf16_t*>(a->gu_saved);
+    g.gu_out = dgu;
+    g.row_scale = gperm;
+    g.h_in = static_cast<const bf16_t*>(a->h);
+    g.dg_part = dg_part;
+    st = launch_gemm<true, false, false, EPI_SWIGLU_BWD>(g, large, A, s);
+    if (st != MOE_OK) return st;
+  }
+  MOE_MARK(MOE_BWD_DGRAD_DOWN);
+  // 3. gate backward (dg, dl), then the router weight gradient (with the aux
+  //    loss: dense, together with dx below)
+  gate_bwd_kernel<<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(dg_part, np32, a->row_of, a->topk_gate, a->topk_idx,
+                                                           a->logits, (int)T, k, E, a->score_fn, dg, dl, dl_perm);
+  MOE_LAUNCH_CHECK();
   if (aux) {
   } else if (router) {
     router_seg_schedule_kernel<<<1, 1024, 0, s>>>(a->offsets, counts, E, seg_beg, seg_end, rc_prefix);
@@ -464,23 +510,6 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
     MOE_LAUNCH_CHECK();
   }
   MOE_MARK(MOE_BWD_ROUTER);
-  // expert GEMMs
-  using namespace moe_gemm;
-  const bool large = use_large_tile(f);
-  moe_status st = moe_tile_schedule_launch(a->offsets, E, large ? BM_LARGE : BM, mt_prefix, s);
-  if (st != MOE_OK) return st;
-  {  // 3. dH = dY_perm W_down -> dG|dU
-    Args g{};
-    g.A = dy_perm; g.lda = d;
-    g.B = wd; g.ldb = f; g.b_group = d * f;
-    g.K = d; g.N = f;
-    g.offsets = a->offsets; g.mt_prefix = mt_prefix; g.G = E;
-    g.gu_in = static_cast<const bf16_t*>(a->gu_saved);
-    g.gu_out = dgu;
-    st = launch_gemm<true, false, false, EPI_SWIGLU_BWD>(g, large, A, s);
-    if (st != MOE_OK) return st;
-  }
-  MOE_MARK(MOE_BWD_DGRAD_DOWN);
   {  // 4. dW_down[e] = dY_perm^T H
     Args g{};
     g.A = dy_perm; g.lda = d;
@@ -488,7 +517,8 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
     g.M = d; g.N = f;
     g.offsets = a->offsets; g.G = E;
     g.out = a->dw_down; g.ldo = f; g.out_group = d * f;
-    st = launch_gemm<false, false, true, EPI_F32>(g, d >= BM_LARGE && f >= BN_LARGE, 0, s);
+    g.kg_sched = kg_sched; g.kg_partial = kg_partial;
+    st = launch_gemm<false, false, true, EPI_F32>(g, wgrad_down_large(d, f), A, s);
     if (st != MOE_OK) return st;
   }
   MOE_MARK(MOE_BWD_WGRAD_DOWN);
@@ -499,15 +529,16 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
     g.M = 2 * f; g.N = d;
     g.offsets = a->offsets; g.G = E;
     g.out = a->dw_gate_up; g.ldo = d; g.out_group = 2 * f * d;
-    const bool large = 2 * f >= BM_LARGE && d >= BN_LARGE;
+    g.kg_sched = kg_sched; g.kg_partial = kg_partial;
+    const bool large = wgrad_up_large(d, f);
     if (x_perm) {
       g.B = x_perm;
-      st = launch_gemm<false, false, true, EPI_F32>(g, large, 0, s);
+      st = launch_gemm<false, false, true, EPI_F32>(g, large, A, s);
     } else {
       g.B = static_cast<const bf16_t*>(a->x);
       g.b_gather = a->token_of;
       g.b_gather_rows = T;
-      st = launch_gemm<false, false, true, EPI_F32, true>(g, large, 0, s);
+      st = launch_gemm<false, false, true, EPI_F32, true>(g, large, A, s);
     }
     if (st != MOE_OK) return st;
   }
@@ -531,6 +562,8 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
     bf16_t* dgu_sh = reinterpret_cast<bf16_t*>(wss + Ls.dgu);
     int32_t* offs_sh = reinterpret_cast<int32_t*>(wss + Ls.offs);
     int32_t* mt_sh = reinterpret_cast<int32_t*>(wss + Ls.mt_prefix);
+    int32_t* kg_sched_sh = reinterpret_cast<int32_t*>(wss + Ls.kg_sched);
+    float* kg_partial_sh = reinterpret_cast<float*>(wss + Ls.kg_partial);
     const bf16_t* dyb = static_cast<const bf16_t*>(a->dy);
     const bf16_t* xb = static_cast<const bf16_t*>(a->x);
     const bool large_sh = use_large_tile(fs);
@@ -556,7 +589,8 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
       g.M = d; g.N = fs;
       g.offsets = offs_sh; g.G = 1;
       g.out = a->dw_down_shared; g.ldo = fs; g.out_group = 0;
-      st = launch_gemm<false, false, true, EPI_F32>(g, d >= BM_LARGE && fs >= BN_LARGE, 0, s);
+      g.kg_sched = kg_sched_sh; g.kg_partial = kg_partial_sh;
+      st = launch_gemm<false, false, true, EPI_F32>(g, wgrad_down_large(d, fs), T, s);
       if (st != MOE_OK) return st;
     }
     {  // dW_gate_up_sh = [dG|dU]^T x
@@ -566,7 +600,8 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
       g.M = 2 * fs; g.N = d;
       g.offsets = offs_sh; g.G = 1;
       g.out = a->dw_gate_up_shared; g.ldo = d; g.out_group = 0;
-      st = launch_gemm<false, false, true, EPI_F32>(g, 2 * fs >= BM_LARGE && d >= BN_LARGE, 0, s);
+      g.kg_sched = kg_sched_sh; g.kg_partial = kg_partial_sh;
+      st = launch_gemm<false, false, true, EPI_F32>(g, wgrad_up_large(d, fs), T, s);
       if (st != MOE_OK) return st;
     }
     {  // dx_sh = [dG|dU] W_gate_up_sh (f32; added to dx by the unpermute below)

@@ -45,6 +45,148 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(const int32_t* __re
 }
 
 // ---------------------------------------------------------------------------
+// K-grouped chunk schedule (see moe_gemm::KgPlan in gemm.h).  One workgroup
+// of 1024 threads, one group per thread (G <= 1024).
+
+__device__ __forceinline__ int block_excl_scan_1024(int v, int32_t* s_w, int& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(inc, o, MOE_WAVE);
+    if (lane >= o) inc += u;
+  }
+  if (lane == 63) s_w[wave] = inc;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) base += s_w[w];
+    total += s_w[w];
+  }
+  __syncthreads();
+  return base + inc - v;
+}
+
+__global__ __launch_bounds__(1024) void kg_schedule_kernel(const int32_t* __restrict__ offsets, int G, int C, int tpg,
+                                                           int gmax, int32_t* __restrict__ ks) {
+  __shared__ int32_t s_w[16];
+  __shared__ int32_t s_rrows[1024];      // remainder rows (or -1: none), per group
+  __shared__ int64_t s_rcost[1024];      // remainder chunk cost by rank, then its prefix sums
+  const int e = threadIdx.x;
+  const int64_t full_cost = (int64_t)C + moe_gemm::KG_OVERHEAD_ROWS;
+  const int n = e < G ? offsets[e + 1] - offsets[e] : 0;
+  const int q = n / C, r = n - q * C;
+  const bool has_rem = e < G && (r > 0 || n == 0);   // an empty group keeps one (empty) chunk: its output is zeros
+  const int nc = e < G ? q + (has_rem ? 1 : 0) : 0;
+  const bool split = nc > 1;
+  int Qtot, nslot, ns, nrem;
+  const int fbase = block_excl_scan_1024(q, s_w, Qtot);
+  const int sbase = block_excl_scan_1024(split ? nc : 0, s_w, nslot);
+  const int sidx = block_excl_scan_1024(split ? 1 : 0, s_w, ns);
+  (void)block_excl_scan_1024(has_rem ? 1 : 0, s_w, nrem);
+  s_rrows[e] = has_rem ? r : -1;
+  __syncthreads();
+  // rank of this group's remainder chunk: more rows first, then the lower group
+  int rank = 0;
+  if (has_rem)
+    for (int o = 0; o < G; ++o) {
+      const int ro = s_rrows[o];
+      rank += ro > r || (ro == r && o < e);
+    }
+  int32_t* g_e = ks + moe_gemm::KG_HDR;
+  int32_t* g_kb = g_e + gmax;
+  int32_t* g_ke = g_kb + gmax;
+  int32_t* g_out = g_ke + gmax;
+  int32_t* s_e = g_out + gmax;
+  int32_t* s_s0 = s_e + G;
+  int32_t* s_nc = s_s0 + G;
+  const int off = e < G ? offsets[e] : 0;
+  for (int c = 0; c < q; ++c) {
+    const int g = fbase + c;
+    g_e[g] = e;
+    g_kb[g] = off + c * C;
+    g_ke[g] = off + (c + 1) * C;
+    g_out[g] = split ? sbase + c : -1;
+  }
+  if (has_rem) {
+    const int g = Qtot + rank;
+    g_e[g] = e;
+    g_kb[g] = off + q * C;
+    g_ke[g] = off + n;
+    g_out[g] = split ? sbase + q : -1;
+    s_rcost[rank] = (int64_t)((r + 63) / 64 * 64) + moe_gemm::KG_OVERHEAD_ROWS;
+  }
+  if (split) {
+    s_e[sidx] = e;
+    s_s0[sidx] = sbase;
+    s_nc[sidx] = nc;
+  }
+  __syncthreads();
+  // inclusive prefix of the remainder costs, in rank order (serial: at most G values)
+  if (e == 0) {
+    int64_t acc = 0;
+    for (int i = 0; i < nrem; ++i) {
+      acc += s_rcost[i];
+      s_rcost[i] = acc;
+    }
+  }
+  __syncthreads();
+  const int ng = Qtot + nrem;
+  // cost of the chunks before chunk g (each of its tpg tiles costs the chunk's cost)
+  auto before = [&](int g) -> int64_t {
+    if (g <= Qtot) return (int64_t)g * full_cost;
+    return (int64_t)Qtot * full_cost + s_rcost[g - Qtot - 1];
+  };
+  if (e < 9) {
+    int64_t item;
+    if (e == 0) {
+      item = 0;
+    } else if (e == 8) {
+      item = (int64_t)ng * tpg;
+    } else {
+      const int64_t target = before(ng) * e / 8;   // in chunk-cost units (per tile)
+      int lo = 0, hi = ng;                          // last chunk starting at or before target
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (before(mid) <= target) lo = mid; else hi = mid;
+      }
+      const int64_t cst = before(lo + 1) - before(lo);
+      const int64_t t = cst > 0 ? ((target - before(lo)) * tpg + cst - 1) / cst : 0;
+      item = (int64_t)lo * tpg + (t < tpg ? t : tpg);
+    }
+    ks[e] = (int32_t)item;
+    if (e < 8) ks[9 + e] = (int32_t)item;
+  }
+  if (e == 0) {
+    ks[17] = ns;
+    ks[18] = ng;
+    ks[19] = gmax;
+  }
+}
+
+// out[e] = sum over the chunks c of split group e of partial[slot0 + c], in
+// chunk order; grid-stride over (split group, 4-float vector).
+__global__ __launch_bounds__(256) void kg_reduce_kernel(const int32_t* __restrict__ ks, int G,
+                                                        const f32x4* __restrict__ partial, int64_t mn4,
+                                                        f32x4* __restrict__ out, int64_t out_group4) {
+  const int ns = ks[17], gmax = ks[19];
+  const int32_t* s_e = ks + moe_gemm::KG_HDR + 4 * gmax;
+  const int32_t* s_s0 = s_e + G;
+  const int32_t* s_nc = s_s0 + G;
+  const int64_t total = (int64_t)ns * mn4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int sgi = (int)(i / mn4);
+    const int64_t v = i - (int64_t)sgi * mn4;
+    const int64_t s0 = s_s0[sgi];
+    const int nc = s_nc[sgi];
+    f32x4 acc = __builtin_nontemporal_load(partial + s0 * mn4 + v);
+    for (int c = 1; c < nc; ++c) acc += __builtin_nontemporal_load(partial + (s0 + c) * mn4 + v);
+    __builtin_nontemporal_store(acc, out + (int64_t)s_e[sgi] * out_group4 + v);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path: one thread per output element, serial fp32 FMA along the
 // reduction (used for fp32 layers, which are small).
 
@@ -114,6 +256,26 @@ int grid_for(int64_t tiles_upper, int per_cu) {
   const int max_wg = (per_cu * moe_num_cus()) & ~7;
   const int64_t t = (tiles_upper + 7) & ~int64_t(7);
   return (int)std::max<int64_t>(8, std::min<int64_t>(max_wg, t));
+}
+}  // namespace moe_gemm
+
+namespace moe_gemm {
+moe_status kg_schedule_launch(const int32_t* offsets, int G, const KgPlan& k, int32_t* sched, hipStream_t s) {
+  kg_schedule_kernel<<<1, 1024, 0, s>>>(offsets, G, (int)k.chunk, (int)k.tpg, (int)k.gmax, sched);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+moe_status kg_reduce_launch(const int32_t* sched, const KgPlan& k, int G, const float* partial, float* out,
+                            int64_t out_group, hipStream_t s) {
+  // enough workgroups for the largest possible sum; most exit at once when
+  // no group was split
+  const int64_t work = std::min<int64_t>(k.smax / 2, G) * (k.mn / 4);
+  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(2048, ceil_div(work, 256)));
+  kg_reduce_kernel<<<grid, 256, 0, s>>>(sched, G, reinterpret_cast<const f32x4*>(partial), k.mn / 4,
+                                         reinterpret_cast<f32x4*>(out), out_group / 4);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
 }
 }  // namespace moe_gemm
 

@@ -44,6 +44,7 @@
 // round, so neighbouring tiles (sharing a weight or activation panel) meet in
 // one XCD's L2.
 #pragma once
+#include <algorithm>
 #include <atomic>
 
 #include "moe_common.h"
@@ -89,7 +90,50 @@ struct Args {
   // row b_gather[r] of B, which has b_gather_rows rows
   const int32_t* b_gather;
   int64_t b_gather_rows;
+  // SwiGLU-bwd only: the accumulator row r is scaled by row_scale[r] before
+  // the SwiGLU backward (or by 1 when null); with h_in set, the epilogue also
+  // writes dg_part[r * (N / 32) + c / 32] = sum over the 32 columns c.. of
+  // acc[r][c] * h_in[r][c] (the unscaled accumulator against the saved H)
+  const float* row_scale;
+  const bf16_t* h_in;
+  float* dg_part;
+  // K-grouped only: the chunk schedule (kg_schedule_kernel) and the partial
+  // outputs of experts split into several row chunks (see launch_cfg)
+  int32_t* kg_sched;
+  float* kg_partial;
 };
+
+// K-grouped (weight-gradient) schedule.  Each group's reduction rows are cut
+// into chunks of at most C rows; an item is one output tile of one chunk.
+// A group of more than one chunk writes one partial output per chunk, and
+// kg_reduce_kernel adds them in chunk order (deterministic).  Chunks go in
+// order of decreasing cost; the item list is cut into 8 ranges of equal
+// cost, one per XCD, and an XCD's workgroups take the range's items in order
+// from an atomic counter (which only spreads the work: each item is computed
+// once, so results do not depend on the order).
+// Schedule block (int32): [0..8] item range starts per XCD (9 = end),
+// [9..16] the XCDs' next items, [17] split groups, [18] chunks, [19] gmax
+// (the chunk arrays' length), then chunk expert / first row / end row /
+// output slot (gmax each), then split group / first slot / chunk count (G each).
+constexpr int KG_HDR = 32;
+constexpr int KG_OVERHEAD_ROWS = 448;   // a tile's prologue and epilogue, in rows of K
+struct KgPlan {
+  int64_t tpg, chunk, gmax, smax, mn;
+};
+inline KgPlan kg_plan(int64_t M, int64_t N, int64_t rows, int G, bool large) {
+  const int64_t tm = large ? BM_LARGE : BM, tn = large ? BN_LARGE : BN;
+  KgPlan k{};
+  k.tpg = ceil_div(M, tm) * ceil_div(N, tn);
+  // a chunk's tile costs at most half a workgroup's share on a 256-workgroup grid
+  const int64_t c = ceil_div(std::max<int64_t>(rows, 1) * k.tpg, 512);
+  k.chunk = std::max<int64_t>(512, ceil_div(c, 64) * 64);
+  k.gmax = G + ceil_div(rows, k.chunk);
+  k.smax = 2 * ceil_div(rows, k.chunk);
+  k.mn = M * N;
+  return k;
+}
+inline size_t kg_sched_bytes(const KgPlan& k, int G) { return (size_t)(KG_HDR + 4 * k.gmax + 3 * (int64_t)G) * 4; }
+inline size_t kg_partial_bytes(const KgPlan& k) { return (size_t)(k.smax * k.mn) * 4; }
 
 // p[i] for a wave-uniform i, loaded through the scalar cache (constant
 // address space): p must not change while the kernel runs.
@@ -172,7 +216,7 @@ __device__ __forceinline__ void interleave() {
 // epilogue as described at the top of this file.
 template <int TM, int TN, int WN, bool AK, bool BKC, bool KG, int EPI, bool GB>
 __device__ __forceinline__ void gemm_tile(const Args& p, char* smem, int e, int nb, int64_t row0, int64_t row_end,
-                                          int64_t kbeg, int64_t kend) {
+                                          int64_t kbeg, int64_t kend, float* kg_out = nullptr) {
   constexpr int WTM = TM / (4 / WN), WTN = TN / WN, FM = WTM / 32, FN = WTN / 32;
   constexpr int SA = TM * BK * 2, SB = TN * BK * 2, STAGE = SA + SB;   // bytes
   constexpr int LA = SA / 4096, LB = SB / 4096;                         // 1 KB loads per wave per slab
@@ -191,7 +235,7 @@ __device__ __forceinline__ void gemm_tile(const Args& p, char* smem, int e, int 
   int64_t a_bytes, b_bytes;
   uint32_t a_voff[LA], b_voff[LB];
   uint32_t a_step, b_step;   // bytes per slab
-  if (AK && !KG && EPI == EPI_SWIGLU && p.a_rows) {   // only the up-projection gathers
+  if (AK && !KG && (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD) && p.a_rows) {   // row-grouped A gathered through a_rows
     // gathered rows: the buffer spans all of A (under 2^31 bytes), a row past
     // the group's end or an index outside [0, a_rows_total) gets an offset
     // past the buffer (its loads read zeros); a valid index's offset fits 32 bits
@@ -300,10 +344,17 @@ __device__ __forceinline__ void gemm_tile(const Args& p, char* smem, int e, int 
   auto gb_rows = [&](int slab) -> i32x8 {
     const int64_t r0 = gb_row0(slab);
     i32x8 t;
+    if (r0 + 8 <= kend) {
+      // all eight rows inside the group (every slab but a group's last):
+      // consecutive addresses, which the compiler merges into one wide load
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t r = r0 + i;
-      t[i] = scalar_load_i32(p.b_gather, r < kend ? r : kbeg);   // kbeg < kend: a row of the group
+      for (int i = 0; i < 8; ++i) t[i] = scalar_load_i32(p.b_gather, r0 + i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t r = r0 + i;
+        t[i] = scalar_load_i32(p.b_gather, r < kend ? r : kbeg);   // kbeg < kend: a row of the group
+      }
     }
     return t;
   };
@@ -536,44 +587,54 @@ do {                                                                            
             const f32x4 v = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c4);
             const int64_t col = col0 + c4;
             if (row < row_end && col < p.N) {
-              float* C = static_cast<float*>(p.out) + (KG ? (int64_t)e * p.out_group : 0);
+              float* C = KG ? kg_out : static_cast<float*>(p.out);   // K-grouped: this chunk's output
               __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(C + row * p.ldo + col));
             }
           }
         }
       }
     } else {  // EPI_SWIGLU_BWD: dH block -> dG, dU from the saved G, U
-      // The saved G|U come from HBM: 16-byte loads (8 columns) issued PF
-      // blocks ahead, into the registers the fragments used in the loop, so
-      // PF blocks of loads are in flight while earlier blocks compute.
+      // The saved G|U (and H, for the gate-gradient partials) come from HBM:
+      // 16-byte loads (8 columns) issued PF blocks ahead, into the registers
+      // the fragments used in the loop, so PF blocks of loads are in flight
+      // while earlier blocks compute.
       constexpr int NBLK = FM * FN, PF = NBLK < 4 ? NBLK : 4;
-      u32x4 gq[PF][2], uq[PF][2];
-      auto load_gu = [&](int b, u32x4 (&gb)[2], u32x4 (&ub)[2]) {
+      const bool dgp = p.h_in != nullptr;
+      const int64_t np32 = p.N / 32;   // gate-gradient partials per row
+      u32x4 gq[PF][2], uq[PF][2], hq[PF][2];
+      float sq[PF][2];
+      auto load_gu = [&](int b, u32x4 (&gb)[2], u32x4 (&ub)[2], u32x4 (&hb)[2], float (&sb)[2]) {
         const int mi = b / FN, ni = b % FN;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int idx = lane + 64 * j, rr = idx >> 2, c8 = (idx & 3) * 8;
           const int64_t row = row0 + wm * WTM + mi * 32 + rr;
           const int64_t col = (int64_t)nb * TN + wn * WTN + ni * 32 + c8;
-          gb[j] = ub[j] = u32x4{0u, 0u, 0u, 0u};
+          gb[j] = ub[j] = hb[j] = u32x4{0u, 0u, 0u, 0u};
+          sb[j] = 1.0f;
           if (row < row_end && col < p.N) {
             gb[j] = *reinterpret_cast<const u32x4*>(p.gu_in + row * 2 * p.N + col);
             ub[j] = *reinterpret_cast<const u32x4*>(p.gu_in + row * 2 * p.N + p.N + col);
+            if (dgp) hb[j] = *reinterpret_cast<const u32x4*>(p.h_in + row * p.N + col);
+            if (p.row_scale) sb[j] = p.row_scale[row];
           }
         }
       };
 #pragma unroll
-      for (int b = 0; b < PF; ++b) load_gu(b, gq[b], uq[b]);
+      for (int b = 0; b < PF; ++b) load_gu(b, gq[b], uq[b], hq[b], sq[b]);
 #pragma unroll
       for (int b = 0; b < NBLK; ++b) {
         const int mi = b / FN, ni = b % FN;
-        u32x4 gc[2], uc[2];
+        u32x4 gc[2], uc[2], hc[2];
+        float sc[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           gc[j] = gq[b % PF][j];
           uc[j] = uq[b % PF][j];
+          hc[j] = hq[b % PF][j];
+          sc[j] = sq[b % PF][j];
         }
-        if (b + PF < NBLK) load_gu(b + PF, gq[b % PF], uq[b % PF]);
+        if (b + PF < NBLK) load_gu(b + PF, gq[b % PF], uq[b % PF], hq[b % PF], sq[b % PF]);
         stage(stg0, acc[mi][ni]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -582,8 +643,26 @@ do {                                                                            
           const int64_t col = (int64_t)nb * TN + wn * WTN + ni * 32 + c8;
           const f32x4 v0 = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c8);
           const f32x4 v1 = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c8 + 4);
-          if (row < row_end && col < p.N) {
-            const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          const bool live = row < row_end && col < p.N;
+          if (dgp) {
+            // gate-gradient partial of this row's 32 columns: the four lanes
+            // holding them (consecutive lanes) add their 8 products in a fixed order
+            float part = 0.f;
+            if (live) {
+              const float vv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                part = fmaf(vv[2 * q], bf16_to_f32(hc[j][q] & 0xFFFFu), part);
+                part = fmaf(vv[2 * q + 1], bf16_to_f32(hc[j][q] >> 16), part);
+              }
+            }
+            part += __shfl_xor(part, 1, MOE_WAVE);
+            part += __shfl_xor(part, 2, MOE_WAVE);
+            if (live && (lane & 3) == 0) p.dg_part[row * np32 + (col >> 5)] = part;
+          }
+          if (live) {
+            const float s = sc[j];
+            const float v[8] = {s * v0[0], s * v0[1], s * v0[2], s * v0[3], s * v1[0], s * v1[1], s * v1[2], s * v1[3]};
             u32x4 o1, o2;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -627,19 +706,37 @@ void gemm_kernel(Args p) {
   const int total = KG ? p.G * p.MT * NB : s_pref[p.G] * NB;
   const int per = gridDim.x >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
 
+  if constexpr (KG) {
+    // items from this XCD's range of the chunk schedule, in order
+    const int32_t* ks = p.kg_sched;
+    const int end = ks[xcd + 1], tpg = p.MT * NB, gmax = ks[19];
+    const int32_t* g_e = ks + KG_HDR;
+    const int32_t* g_kb = g_e + gmax;
+    const int32_t* g_ke = g_kb + gmax;
+    const int32_t* g_out = g_ke + gmax;
+    int32_t* s_item = s_pref;
+    (void)total, (void)per, (void)slot;
+    for (;;) {
+      if (tid == 0) *s_item = atomicAdd(p.kg_sched + 9 + xcd, 1);
+      __syncthreads();
+      const int L = *s_item;
+      if (L >= end) break;
+      const int g = L / tpg;
+      int mt, nb;
+      band_order(L - g * tpg, p.MT, NB, mt, nb);
+      const int e = g_e[g], oslot = g_out[g];
+      float* outp = oslot < 0 ? static_cast<float*>(p.out) + (int64_t)e * p.out_group
+                              : p.kg_partial + (int64_t)oslot * p.M * p.N;
+      gemm_tile<TM, TN, 2, AK, BKC, KG, EPI, GB>(p, smem, e, nb, (int64_t)mt * TM, p.M, g_kb[g], g_ke[g], outp);
+    }
+    return;
+  }
   for (int base = 0;; base += gridDim.x) {
     const int L = base + xcd * per + slot;
     if (L >= total) break;
     int e, mt, nb;
     int64_t row0, row_end, kbeg, kend;
-    if (KG) {
-      e = L / (p.MT * NB);
-      band_order(L - e * p.MT * NB, p.MT, NB, mt, nb);
-      row0 = (int64_t)mt * TM;
-      row_end = p.M;
-      kbeg = p.offsets[e];
-      kend = p.offsets[e + 1];
-    } else {
+    {
       int lo = 0, hi = p.G;
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -669,6 +766,12 @@ void gemm_kernel(Args p) {
 // Persistent grid: at most `per_cu` workgroups per CU, a multiple of 8.
 int grid_for(int64_t tiles_upper, int per_cu);
 
+// The K-grouped chunk schedule (into a.kg_sched) and, after the GEMM, the
+// ordered sum of the split groups' partial outputs (ffn.hip).
+moe_status kg_schedule_launch(const int32_t* offsets, int G, const KgPlan& k, int32_t* sched, hipStream_t s);
+moe_status kg_reduce_launch(const int32_t* sched, const KgPlan& k, int G, const float* partial, float* out,
+                            int64_t out_group, hipStream_t s);
+
 // Raises a kernel's dynamic-LDS limit on the current device.
 moe_status lds_attr(const void* fn, int bytes);
 
@@ -690,13 +793,21 @@ moe_status lds_attr_once(std::atomic<int> (&done)[kMaxAttrDevices], K* fn, int b
 // (row-grouped only) bounds the row tiles: sum over groups of
 // ceil(n_g/TM) <= ceil(rows/TM) + G.  a.mt_prefix must have been built with
 // bm = TM.
+// K-grouped launches (rows = the reduction rows of all groups) run the chunk
+// schedule first and the partial-output sum after; a.kg_sched and
+// a.kg_partial must hold kg_sched_bytes / kg_partial_bytes of
+// kg_plan(a.M, a.N, rows, a.G, TM == BM_LARGE).
 template <int TM, int TN, bool AK, bool BKC, bool KG, int EPI, bool GB = false>
 moe_status launch_cfg(Args a, int64_t rows, hipStream_t s) {
   a.NB = EPI == EPI_SWIGLU ? (int)(a.N / (TN / 2)) : (int)ceil_div(a.N, TN);
   int64_t tiles;
+  KgPlan kp{};
   if (KG) {
     a.MT = (int)ceil_div(a.M, TM);
-    tiles = (int64_t)a.G * a.MT * a.NB;
+    kp = kg_plan(a.M, a.N, rows, a.G, TM == BM_LARGE);
+    tiles = kp.gmax * a.MT * a.NB;
+    const moe_status st = kg_schedule_launch(a.offsets, a.G, kp, a.kg_sched, s);
+    if (st != MOE_OK) return st;
   } else {
     tiles = (ceil_div(rows, TM) + a.G) * a.NB;
   }
@@ -706,6 +817,7 @@ moe_status launch_cfg(Args a, int64_t rows, hipStream_t s) {
   if (attr != MOE_OK) return attr;
   gemm_kernel<TM, TN, AK, BKC, KG, EPI, GB><<<grid_for(tiles, TM * TN > 128 * 128 ? 1 : 2), 256, lds, s>>>(a);
   MOE_LAUNCH_CHECK();
+  if (KG) return kg_reduce_launch(a.kg_sched, kp, a.G, a.kg_partial, static_cast<float*>(a.out), a.out_group, s);
   return MOE_OK;
 }
 

@@ -7,8 +7,9 @@ Where the pages leave a step open, the reading taken is stated at the function.
 Everything is computed in float64.  For layers whose storage type is bf16 the
 oracle rounds to bf16 exactly where such a layer stores a bf16 tensor
 (``bf16_points=True``): the saved gate/up pre-activations G and U, the SwiGLU
-output H, the gate-scaled output gradient dY_perm and the SwiGLU input
-gradients dG, dU.  Expert outputs, the combined output and every gradient that
+output H, the gate-scaled output gradient dY_perm (the input of W_down's
+weight gradient; the data gradient scales dY W_down by the gate instead) and
+the SwiGLU input gradients dG, dU.  Expert outputs, the combined output and every gradient that
 leaves the layer stay in high precision.
 """
 from __future__ import annotations
@@ -211,21 +212,22 @@ def _silu(z):
 def expert_ffn(xr, w_gate_up, w_down, bf16_points: bool) -> dict:
     """SwiGLU expert on rows xr [n, d]: G = xr Wg^T, U = xr Wu^T,
     H = silu(G) * U (computed from the unrounded G and U), Y = H Wd^T.
-    Returns G, U (saved form: bf16-rounded when bf16_points), H, Y."""
+    Returns G, U (saved form: bf16-rounded when bf16_points), H, Y, and
+    H_raw (H before its bf16 rounding)."""
     xr = _f64(xr)
     wgu = _f64(w_gate_up)
     wd = _f64(w_down)
     f = wd.shape[1]
     G = xr @ wgu[:f].T
     U = xr @ wgu[f:].T
-    H = _silu(G) * U
+    H_raw = _silu(G) * U
     if bf16_points:
-        H = bf16_round(H)
+        H = bf16_round(H_raw)
         Gs, Us = bf16_round(G), bf16_round(U)
     else:
-        Gs, Us = G, U
+        H, Gs, Us = H_raw, G, U
     Y = H @ wd.T
-    return {"G": Gs, "U": Us, "H": H, "Y": Y}
+    return {"G": Gs, "U": Us, "H": H, "Y": Y, "H_raw": H_raw}
 
 
 def grouped_ffn(x_perm, offsets, w_gate_up, w_down, bf16_points: bool) -> dict:
@@ -235,7 +237,7 @@ def grouped_ffn(x_perm, offsets, w_gate_up, w_down, bf16_points: bool) -> dict:
     A = x_perm.shape[0]
     f = np.asarray(w_down).shape[2]
     d = np.asarray(w_down).shape[1]
-    out = {"G": np.zeros((A, f)), "U": np.zeros((A, f)), "H": np.zeros((A, f)),
+    out = {"G": np.zeros((A, f)), "U": np.zeros((A, f)), "H": np.zeros((A, f)), "H_raw": np.zeros((A, f)),
            "Y": np.zeros((A, d))}
     for e in range(G_):
         a, b = int(offsets[e]), int(offsets[e + 1])
@@ -325,7 +327,7 @@ def forward(x, w_router, w_gate_up, w_down, k: int, score_fn: str, bf16_points: 
     out = combine(ex["Y"], row_of, r["gates"], shared_y)
     res = dict(r)
     res.update(counts=counts, offsets=offsets, row_of=row_of, token_of=token_of,
-               x_perm=x_perm, G=ex["G"], U=ex["U"], H=ex["H"], y_perm=ex["Y"],
+               x_perm=x_perm, G=ex["G"], U=ex["U"], H=ex["H"], H_raw=ex["H_raw"], y_perm=ex["Y"],
                shared=sh, shared_y=shared_y, out=out)
     return res
 
@@ -400,17 +402,20 @@ def router_backward(dl, idx, x, w_router):
     return dL.T @ x, dL @ w
 
 
-def expert_backward_rows(dy_rows, xr, G, U, H, w_gate_up, w_down, bf16_points: bool) -> dict:
+def expert_backward_rows(dy_rows, xr, G, U, H, w_gate_up, w_down, bf16_points: bool, dy_wgrad=None) -> dict:
     """Backward of one SwiGLU expert over rows xr, given d loss / d Y rows.
 
     dH = dY Wd; dG = dH * U * silu'(G); dU = dH * silu(G) (G, U in their saved
     form); dWd = dY^T H; dWg = dG^T xr; dWu = dU^T xr; dX = dG Wg + dU Wu.
-    silu'(z) = sigma(z) (1 + z (1 - sigma(z)))."""
+    silu'(z) = sigma(z) (1 + z (1 - sigma(z))).
+    dy_wgrad: the form of dY that the weight gradient dWd uses when it differs
+    from the one the data gradient uses (a bf16-stored copy); default dy_rows."""
     xr = _f64(xr)
     wgu = _f64(w_gate_up)
     wd = _f64(w_down)
     f = wd.shape[1]
     dy = np.asarray(dy_rows, np.float64)
+    dyw = dy if dy_wgrad is None else np.asarray(dy_wgrad, np.float64)
     dH = dy @ wd
     sg = 1.0 / (1.0 + np.exp(-G))
     dG = dH * U * sg * (1.0 + G * (1.0 - sg))
@@ -419,7 +424,7 @@ def expert_backward_rows(dy_rows, xr, G, U, H, w_gate_up, w_down, bf16_points: b
         dG, dU = bf16_round(dG), bf16_round(dU)
     dX = dG @ wgu[:f] + dU @ wgu[f:]
     dWgu = np.concatenate([dG.T @ xr, dU.T @ xr], axis=0)
-    dWd = dy.T @ H
+    dWd = dyw.T @ H
     return {"dH": dH, "dG": dG, "dU": dU, "dX": dX, "dW_gate_up": dWgu, "dW_down": dWd}
 
 
@@ -450,8 +455,9 @@ def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
         keep = row_of[:, j] >= 0          # a dropped slot has no expert output: dg = 0
         dg[keep, j] = np.sum(dy[keep] * y[row_of[keep, j]], axis=1)
         dy_perm[row_of[keep, j]] = gates[keep, j:j + 1] * dy[keep]
-    if bf16_points:
-        dy_perm = bf16_round(dy_perm)
+    # bf16 layers store g*dY in bf16 for the weight gradient of W_down only;
+    # the data gradient scales dY W_down by g in high precision
+    dy_perm_w = bf16_round(dy_perm) if bf16_points else dy_perm
     if score_fn == "uniform":           # constant gates: no logit and no router gradient
         dl = np.zeros((T, k))
         dW_r, dx = np.zeros((E, d)), np.zeros((T, d))
@@ -479,7 +485,7 @@ def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
         if a == b:
             continue
         r = expert_backward_rows(dy_perm[a:b], fwd["x_perm"][a:b], fwd["G"][a:b], fwd["U"][a:b],
-                                 fwd["H"][a:b], w_gate_up[e], w_down[e], bf16_points)
+                                 fwd["H"][a:b], w_gate_up[e], w_down[e], bf16_points, dy_wgrad=dy_perm_w[a:b])
         dW_gu[e], dW_d[e] = r["dW_gate_up"], r["dW_down"]
         dX_perm[a:b] = r["dX"]
         dGU[a:b, :f], dGU[a:b, f:] = r["dG"], r["dU"]
@@ -487,7 +493,7 @@ def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
         keep = row_of[:, j] >= 0
         dx[keep] += dX_perm[row_of[keep, j]]
     out = {"dx": dx, "dw_router": dW_r, "dw_gate_up": dW_gu, "dw_down": dW_d,
-           "dg": dg, "dl": dl, "dy_perm": dy_perm, "dx_perm": dX_perm, "dgu": dGU}
+           "dg": dg, "dl": dl, "dy_perm": dy_perm_w, "dx_perm": dX_perm, "dgu": dGU}
     if aux_alpha and score_fn != "uniform":
         out["dl_dense"] = dL
     if w_gate_up_shared is not None:

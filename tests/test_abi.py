@@ -193,6 +193,7 @@ def test_backward_validation(L):
     assert bwd(d=96) == L.MOE_ENOTSUP
     assert bwd(x_perm=None, d=96) == L.MOE_ENOTSUP                # x_perm may be NULL (x is read through token_of)
     assert bwd(x_perm=None, x=None) == L.MOE_EINVAL               # x may not
+    assert bwd(y_perm=None, workspace_bytes=0) == L.MOE_EWORKSPACE   # y_perm is not read
     assert bwd(f=100) == L.MOE_ENOTSUP
     assert bwd(E=2048, k=8) == L.MOE_ENOTSUP
     assert bwd(T=1 << 20, d=1024, workspace_bytes=1 << 50) == L.MOE_ENOTSUP   # X_perm past 2 GiB

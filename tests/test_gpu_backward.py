@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import as_f64, check_close, dev, host, say
+from gpu_helpers import as_f64, check_close, close_errors, dev, dg_flip_allowance, host, say
 from workloads import CONFIGS, make_inputs, scaled
 
 pytestmark = pytest.mark.gpu
@@ -194,46 +194,54 @@ def test_backward_empty_and_skewed_experts(f):
     check_close(host(layer.dw_router), g["dw_router"], "bf16", "dW_router")
 
 
-def test_backward_full_training_shape():
-    cfg = CONFIGS["train"]
+@pytest.mark.parametrize("name", ["train", "train_skew"])
+def test_backward_full_training_shape(name):
+    """The training workload at full size (16384 tokens, 64 experts top-8;
+    train_skew adds the Zipf logit offset, about 6x max/mean load, so the
+    weight gradients of the hottest experts are split into row chunks):
+    every output of the step against the oracle's forward and chain rule over
+    all tokens -- dg, dl and dx of every token, dW_r, and dW_down and
+    dW_gate_up of all 64 experts over all of their rows.  Stage-isolated
+    (S14): the oracle routes with the GPU's expert choice (index parity at
+    this size is checked by the routing tests) and computes everything else,
+    gates included, itself."""
+    cfg = CONFIGS[name]
     say(f"[backward full train T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} f={cfg.f}]")
     inp = make_inputs(cfg)
     layer = _run(cfg, inp)
-    k = cfg.k
     idx = host(layer.idx).astype(np.int64)
-    gates = host(layer.gate)
-    offsets = host(layer.offsets)
-    token_of = host(layer.token_of)
-    row_of = host(layer.row_of)
-    x64 = as_f64(inp["x"])
-    dy64 = as_f64(inp["dy"])
-    rng = np.random.default_rng(0)
-    # --- sampled tokens: dg, dl, dx
-    toks = np.sort(rng.choice(cfg.T, 24, replace=False))
-    fw = oracle.forward(inp["x"][toks], inp["w_router"], inp["w_gate_up"], inp["w_down"], k, cfg.score, True,
-                        idx=idx[toks])
-    gb = oracle.backward(fw, inp["dy"][toks], inp["x"][toks], inp["w_router"], inp["w_gate_up"], inp["w_down"],
-                         cfg.score, True)
-    check_close(host(layer.dgate)[toks], gb["dg"], "bf16", "dg (sampled tokens)")
-    check_close(host(layer.dlogit)[toks], gb["dl"], "bf16", "dl (sampled tokens)")
-    check_close(host(layer.dx)[toks], gb["dx"], "bf16", "dx (sampled tokens)")
-    # --- router weight gradient: the oracle's router backward fed the GPU's dl
-    dwr, _ = oracle.router_backward(host(layer.dlogit).astype(np.float64), idx, inp["x"], inp["w_router"])
-    check_close(host(layer.dw_router), dwr, "bf16", "dW_router (GPU dl)")
-    # --- expert weight gradients of sampled experts, over all of their rows
-    counts = np.diff(offsets)
-    for e in sorted({int(counts.argmin()), int(counts.argmax()), int(rng.integers(0, cfg.E))}):
-        a, b = int(offsets[e]), int(offsets[e + 1])
-        rows = np.arange(a, b)
-        tk = token_of[rows]
-        slot = np.array([np.nonzero(row_of[t] == r)[0][0] for t, r in zip(tk, rows)])
-        ex = oracle.expert_ffn(x64[tk], inp["w_gate_up"][e], inp["w_down"][e], True)
-        dyp = oracle.bf16_round(gates[tk, slot][:, None].astype(np.float64) * dy64[tk])
-        r = oracle.expert_backward_rows(dyp, x64[tk], ex["G"], ex["U"], ex["H"], inp["w_gate_up"][e],
-                                        inp["w_down"][e], True)
-        say(f"  expert {e}: {b - a} rows")
-        check_close(host(layer.dw_down[e]), r["dW_down"], "bf16", f"dW_down[{e}]")
-        check_close(host(layer.dw_gate_up[e]), r["dW_gate_up"], "bf16", f"dW_gate_up[{e}]")
+    say("  oracle forward + backward over every token")
+    fw = oracle.forward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], cfg.k, cfg.score, True,
+                        sel_bias=inp["bias"], logit_offset=inp["logit_offset"], idx=idx)
+    assert np.array_equal(host(layer.offsets), fw["offsets"]) and np.array_equal(host(layer.row_of), fw["row_of"])
+    g = oracle.backward(fw, inp["dy"], inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], cfg.score, True)
+    dwd, dwgu = host(layer.dw_down), host(layer.dw_gate_up)
+    pairs = [("out", host(layer.out), fw["out"]), ("dg", host(layer.dgate), g["dg"]),
+             ("dl", host(layer.dlogit), g["dl"]), ("dx", host(layer.dx), g["dx"]),
+             ("dW_router", host(layer.dw_router), g["dw_router"]), ("dW_down", dwd, g["dw_down"]),
+             ("dW_gate_up", dwgu, g["dw_gate_up"])]
+    counts = np.diff(fw["offsets"])
+    pairs += [(f"dW_down[{e}] ({counts[e]} rows)", dwd[e], g["dw_down"][e]) for e in range(cfg.E)]
+    pairs += [(f"dW_gate_up[{e}]", dwgu[e], g["dw_gate_up"][e]) for e in range(cfg.E)]
+    # dg sums d products of H, a bf16 quantised code: its bound adds the
+    # effect of the H values that sit on a rounding midpoint (gpu_helpers)
+    allow = dg_flip_allowance(fw, inp["dy"], inp["w_down"], fw["token_of"])
+    bad = []
+    for name, got, ref in pairs:   # every tensor reported before any assertion
+        mx, rel, at = close_errors(got, ref)
+        g64, r64 = as_f64(got), as_f64(ref)
+        bound = 2e-2 + (allow if name == "dg" else 0.0)
+        ok = bool(np.all(np.abs(g64 - r64) <= bound)) and rel <= 1e-2
+        extra = ""
+        if name == "dg":
+            used = np.abs(g64 - r64) > 2e-2
+            extra = (f"; {int(used.sum())} above 2e-2, all within 2e-2 + their rounding-flip allowance "
+                     f"(largest allowance {float(allow.max()):.3e})" if ok else "")
+        say(f"  {name}: max-abs {mx:.3e} rel-L2 {rel:.3e} at {at} (got {g64[at]:.6g}, ref {r64[at]:.6g})"
+            f"{extra}{'' if ok else '  FAILED'}")
+        if not ok:
+            bad.append(name)
+    assert not bad, bad
 
 
 @pytest.mark.parametrize("score", oracle.SCORE_FNS)
@@ -334,3 +342,70 @@ def test_backward_stage_events():
     assert sum(ms) <= total + 1e-3 and sum(ms) >= 0.5 * total, (sum(ms), total)
     for n, v in ref.items():
         assert np.array_equal(host(getattr(layer, n)), v), n
+
+
+
+def _kg_chunk(rows, M, N):
+    """Rows per chunk of a weight-gradient GEMM's schedule (the rule of
+    moe_gemm::kg_plan: a chunk's tile costs at most half of one workgroup's
+    share on 256 workgroups, at least 512 rows, a multiple of 64)."""
+    large = M >= 256 and N >= 256
+    t = 256 if large else 128
+    tpg = -(-M // t) * -(-N // t)
+    c = -(-rows * tpg // 512)
+    return max(512, -(-c // 64) * 64)
+
+
+@pytest.mark.parametrize("score", ["sigmoid", "softmax"])
+@pytest.mark.parametrize("T,d,E,k,f,hot", [(1500, 256, 8, 2, 128, 0.7), (3000, 256, 6, 1, 128, 0.95),
+                                           (1200, 384, 16, 3, 192, 0.5)])
+def test_backward_split_weight_gradients(score, T, d, E, k, f, hot):
+    """Weight gradients of experts split into several row chunks (partial
+    outputs added in chunk order afterwards): a routing replay sends a
+    fraction `hot` of the tokens' first slot to expert 1, so that expert's
+    rows exceed the chunk size of both weight-gradient GEMMs, next to an
+    empty expert and small ones; every gradient against the oracle."""
+    say(f"[backward split weight gradients {score} T={T} d={d} E={E} k={k} f={f} hot={hot}]")
+    cfg = scaled(CONFIGS["train"], T=T, d=d, E=E, k=k, f=f, score=score, bias="uniform")
+    inp = make_inputs(cfg)
+    rng = np.random.default_rng(11)
+    ridx = np.stack([rng.permutation(np.arange(2, E))[:k] for _ in range(T)]).astype(np.int64)   # expert 0 empty
+    ridx[rng.random(T) < hot, 0] = 1
+    n1 = int((ridx == 1).sum())
+    A = T * k
+    for M, N in ((d, f), (2 * f, d)):
+        assert n1 > _kg_chunk(A, M, N), (n1, M, N)     # expert 1 is split in both GEMMs
+    layer = _layer(cfg, inp)
+    x = dev(inp["x"])
+    layer.forward(x, replay_idx=dev(ridx.astype(np.int32)))
+    layer.backward(x, dev(inp["dy"]))
+    torch.cuda.synchronize()
+    fwd = oracle.forward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], k, score, True,
+                         logit_offset=inp["logit_offset"], idx=ridx)
+    g = oracle.backward(fwd, inp["dy"], inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], score, True)
+    say(f"  expert 1 holds {n1} of {A} rows; expert 0 none")
+    dwd, dwgu = host(layer.dw_down), host(layer.dw_gate_up)
+    assert np.all(dwd[0] == 0) and np.all(dwgu[0] == 0)
+    check_close(dwd[1], g["dw_down"][1], "bf16", "dW_down[1] (split)")
+    check_close(dwgu[1], g["dw_gate_up"][1], "bf16", "dW_gate_up[1] (split)")
+    check_close(dwd, g["dw_down"], "bf16", "dW_down")
+    check_close(dwgu, g["dw_gate_up"], "bf16", "dW_gate_up")
+    check_close(host(layer.dx), g["dx"], "bf16", "dx")
+    check_close(host(layer.dw_router), g["dw_router"], "bf16", "dW_router")
+
+
+def test_backward_deterministic_under_skew():
+    """The weight-gradient schedule hands tiles out dynamically: two runs of
+    the same skewed step give bit-identical gradients."""
+    cfg = scaled(CONFIGS["train_skew"], T=4000, d=256, E=16, k=4, f=128)
+    inp = make_inputs(cfg)
+    layer = _layer(cfg, inp)
+    x, dy = dev(inp["x"]), dev(inp["dy"])
+    outs = []
+    for _ in range(2):
+        layer.forward(x)
+        layer.backward(x, dy)
+        torch.cuda.synchronize()
+        outs.append([host(getattr(layer, n)).copy() for n in ("dx", "dw_router", "dw_gate_up", "dw_down")])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)

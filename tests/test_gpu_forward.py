@@ -183,8 +183,9 @@ def test_route_fewer_experts_at_serving(score):
                                          (513, 17, 3, "sigmoid")])
 def test_aux_loss(T, E, k, score):
     """Auxiliary load-balancing loss and the mean router probabilities against
-    the oracle fed the GPU's own logits and counts (fixed-order reductions:
-    also bit-reproducible run to run)."""
+    the oracle's own fp64 logits; the counts are the GPU's integer counts,
+    which equal the oracle's wherever no token is a near-tie (fixed-order
+    reductions: also bit-reproducible run to run)."""
     say(f"[aux loss T={T} E={E} k={k} {score}]")
     cfg = scaled(CONFIGS["fine"], T=T, d=64, E=E, k=k, f=64, score=score, bias="uniform")
     inp = make_inputs(cfg, experts=False)
@@ -195,7 +196,10 @@ def test_aux_loss(T, E, k, score):
     loss = L.moe_aux_loss(logits, counts, k, score, 0.01, p_mean_out=p_mean)
     loss2 = L.moe_aux_loss(logits, counts, k, score, 0.01)
     torch.cuda.synchronize()
-    lg = host(logits).astype(np.float64)
+    ref = oracle.route(inp["x"], inp["w_router"], k, score, inp["bias"], inp["logit_offset"])
+    lg = ref["logits"]
+    if np.all(ref["margin"] >= 1e-6):
+        assert np.array_equal(host(counts), oracle.permute(ref["idx"], E)[0])
     want = oracle.aux_loss(lg, host(counts), k, score, 0.01)
     assert abs(float(host(loss)[0]) - want) <= 1e-5 * abs(want), (float(host(loss)[0]), want)
     check_close(host(p_mean), oracle.aux_probs(lg, score).mean(axis=0), "f32", "P")
@@ -412,6 +416,37 @@ def test_ffn_gather_out_of_range_token_reads_zero():
         assert np.count_nonzero(yh[4]) > 0
 
 
+@pytest.mark.parametrize("name", ["coarse", "fine", "dsv3"])
+def test_ffn_full_size_every_expert(name):
+    """The grouped FFN at full size in the layer's configuration (x gathered
+    through token_of): the first and the last row of every expert against
+    the oracle's expert FFN, so every expert's weights are checked."""
+    cfg = CONFIGS[name]
+    say(f"[ffn full size {name}: every expert's first and last row]")
+    inp = make_inputs(cfg)
+    x = dev(inp["x"])
+    idx, _, _ = L.moe_route(x, dev(inp["w_router"]), cfg.k, cfg.score, dev(inp["logit_offset"]), dev(inp["bias"]))
+    _, offsets, _, token_of, _ = L.moe_permute(idx, x, cfg.E, copy=False)
+    wgu, wd = dev(inp["w_gate_up"]), dev(inp["w_down"])
+    _, h, y = L.moe_grouped_ffn_gather(x, token_of, offsets, wgu, wd)
+    torch.cuda.synchronize()
+    off, tok = host(offsets).astype(np.int64), host(token_of)
+    del wgu, wd, h
+    rows, exps = [], []
+    for e in range(cfg.E):
+        ends = sorted({int(off[e]), int(off[e + 1] - 1)}) if off[e + 1] > off[e] else []
+        rows += ends
+        exps += [e] * len(ends)
+    rows, exps = np.array(rows), np.array(exps)
+    say(f"  {len(set(exps.tolist()))} experts with rows, {len(rows)} rows compared")
+    yh = host(y)[rows]
+    ref = np.empty_like(yh, dtype=np.float64)
+    for e in np.unique(exps):
+        sel = exps == e
+        ref[sel] = oracle.expert_ffn(inp["x"][tok[rows[sel]]], inp["w_gate_up"][e], inp["w_down"][e], True)["Y"]
+    check_close(yh, ref, "bf16", "Y (first and last row of every expert)")
+
+
 def test_ffn_ep8_shard():
     """One expert-parallel rank's share of the 256-expert shape: a 32768-token
     global batch routed and permuted on the GPU, the rank's 32 experts (about
@@ -547,11 +582,12 @@ def test_forward_bf16_small(score):
     _forward_check(cfg, make_inputs(cfg))
 
 
-@pytest.mark.parametrize("name,n_sample", [("coarse", 48), ("fine", 48), ("dsv3", 16)])
+@pytest.mark.parametrize("name,n_sample", [("coarse", 512), ("fine", 1024), ("dsv3", 256)])
 def test_forward_full_size(name, n_sample):
-    """Full-size layer forward, sampled tokens against the oracle (the 256+1
-    expert shape holds 22.6 GB of expert weights; its oracle converts one
-    expert at a time, so fewer tokens are sampled there)."""
+    """Full-size layer forward, sampled tokens against the oracle (the whole
+    layer: routing, every chosen expert and, for the 256+1 expert shape, the
+    shared expert; that shape holds 22.6 GB of expert weights, which its
+    oracle converts one expert at a time)."""
     cfg = CONFIGS[name]
     say(f"[forward full {name}]")
     inp = make_inputs(cfg)

@@ -22,6 +22,8 @@ MoE layer is measured on:
               weights N(0, 0.006), bias U(-0.05, 0.05), seed 3.
 * ``train``  the fine-grained shape at T=16384 with sqrt(softplus) scores,
               forward plus backward with dY N(0, 1) in bf16, seed 4.
+              ``train_skew`` adds the Zipf logit offset of ``fine`` (skewed
+              expert load in training).
 
 One expert-parallel rank's share (``ep_shard``): ``dsv3_ep8`` is rank 0 of 8
 ranks on the ``dsv3`` shape.  The global batch is 8 x 4096 tokens drawn like
@@ -92,6 +94,9 @@ CONFIGS = {
                        train=True),
 }
 CONFIGS["tiny_dense"] = replace(CONFIGS["tiny"], name="tiny_dense", E=1, k=1)
+# the training shape under the fine workload's skewed load: the same Zipf
+# logit offset (0.5 * ln(rank^-1.2) for a random rank of each expert)
+CONFIGS["train_skew"] = replace(CONFIGS["train"], name="train_skew", zipf_s=1.2)
 
 
 def scaled(cfg: MoEConfig, **changes) -> MoEConfig:
