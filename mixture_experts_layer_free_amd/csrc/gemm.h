@@ -109,8 +109,9 @@ struct Args {
 // kg_reduce_kernel adds them in chunk order (deterministic).  Chunks go in
 // order of decreasing cost; the item list is cut into 8 ranges of equal
 // cost, one per XCD, and an XCD's workgroups take the range's items in order
-// from an atomic counter (which only spreads the work: each item is computed
-// once, so results do not depend on the order).
+// from an atomic counter, then help drain the other XCDs' ranges (which
+// only spreads the work: each item is computed once, so results do not
+// depend on the order).
 // Schedule block (int32): [0..8] item range starts per XCD (9 = end),
 // [9..16] the XCDs' next items, [17] split groups, [18] chunks, [19] gmax
 // (the chunk arrays' length), then chunk expert / first row / end row /
@@ -707,20 +708,35 @@ void gemm_kernel(Args p) {
   const int per = gridDim.x >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
 
   if constexpr (KG) {
-    // items from this XCD's range of the chunk schedule, in order
+    // items from this XCD's range of the chunk schedule, in order; once it is
+    // drained, from the next XCDs' ranges (each range's tail holds its
+    // cheapest items), so no workgroup idles while any item is left
     const int32_t* ks = p.kg_sched;
-    const int end = ks[xcd + 1], tpg = p.MT * NB, gmax = ks[19];
+    const int tpg = p.MT * NB, gmax = ks[19];
     const int32_t* g_e = ks + KG_HDR;
     const int32_t* g_kb = g_e + gmax;
     const int32_t* g_ke = g_kb + gmax;
     const int32_t* g_out = g_ke + gmax;
     int32_t* s_item = s_pref;
     (void)total, (void)per, (void)slot;
+    int src = xcd, hops = 0;   // thread 0's current range and the ranges it has left behind
     for (;;) {
-      if (tid == 0) *s_item = atomicAdd(p.kg_sched + 9 + xcd, 1);
+      if (tid == 0) {
+        int L = -1;
+        while (hops < 8) {
+          const int t = atomicAdd(p.kg_sched + 9 + src, 1);
+          if (t < ks[src + 1]) {
+            L = t;
+            break;
+          }
+          src = (src + 1) & 7;
+          ++hops;
+        }
+        *s_item = L;
+      }
       __syncthreads();
       const int L = *s_item;
-      if (L >= end) break;
+      if (L < 0) break;
       const int g = L / tpg;
       int mt, nb;
       band_order(L - g * tpg, p.MT, NB, mt, nb);
