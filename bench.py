@@ -15,8 +15,9 @@ replays timed between two device synchronisations.  ``roofline`` covers the
 dominant kernel (the longest backward stage, one GEMM launch, timed with the
 HIP events moe_backward records on its stream after each stage);
 ``rooflines`` covers every library call and ``kernel_rooflines`` every
-backward stage.  ``fwd_lines`` repeats the measurement for the forward-only
-workloads (8 experts top-2, 64 experts top-8, 256 + 1 shared top-8).
+backward stage.  ``train_lines`` repeats the training measurement under a
+skewed expert load, ``fwd_lines`` for the forward-only workloads (8 experts
+top-2, 64 experts top-8, 256 + 1 shared top-8).
 ``cpu_baseline`` times the CPU oracle on a bounded sample of each workload.
 Progress goes to stderr.
 """
@@ -260,10 +261,10 @@ def algorithmic(cfg, fused=False, gather=None):
         out["shared_ffn"] = (6.0 * T * d * fs, T * d * xb + 3 * d * fs * xb + 2 * T * fs * xb + T * d * 4,
                              PEAK_BF16_TFLOPS)
     if cfg.train:
-        # inputs dY, Y, x (or X_perm), G|U, H, weights; outputs dx, dW; dY_perm, dG|U, dX_perm written and
-        # read once
-        nbytes = (T * d * 2 + A * d * 4 + rows_in + A * 2 * f * 2 + A * f * 2 + 3 * E * d * f * 2
-                  + T * d * 4 + 3 * E * d * f * 4 + 2 * (A * d * 2 + A * 2 * f * 2 + A * d * 4))
+        # inputs dY, x (or X_perm), G|U, H, weights; outputs dx, dW; dY_perm, dG|U and dX_perm (bf16)
+        # written and read once (the backward does not read Y)
+        nbytes = (T * d * 2 + rows_in + A * 2 * f * 2 + A * f * 2 + 3 * E * d * f * 2
+                  + T * d * 4 + 3 * E * d * f * 4 + 2 * (A * d * 2 + A * 2 * f * 2 + A * d * 2))
         out["backward"] = (12.0 * A * d * f + 4.0 * A * d, nbytes, PEAK_BF16_TFLOPS)
     return out
 
@@ -388,14 +389,19 @@ def stage_algorithmic(cfg):
     T, d, E, k, f, A = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.T * cfg.k
     fs = cfg.f_shared * cfg.shared
     return {
-        "combine": (0, A * d * 4 + T * d * 2 + A * d * 2 + T * k * 12, None),
-        "router": (2.0 * A * d, T * d * 2 + A * 4 + E * d * 4, None),
-        "dgrad_down": (2.0 * A * d * f, A * d * 2 + E * d * f * 2 + 2 * A * 2 * f * 2, PEAK_BF16_TFLOPS),
+        # dy rows in, dY_perm = bf16(g dy) and each row's gate out
+        "combine": (0, T * d * 2 + A * d * 2 + A * 4 + T * k * 12, None),
+        # gate backward (dg partials in) and the router weight gradient
+        "router": (2.0 * A * d, A * (f // 32) * 4 + T * d * 2 + A * 4 + E * d * 4 + T * k * 12, None),
+        # dy rows and W_down in; G|U and H in for the epilogue; dG|dU and the dg partials out
+        "dgrad_down": (2.0 * A * d * f, T * d * 2 + E * d * f * 2 + A * 2 * f * 2 + A * f * 2 + A * 2 * f * 2
+                       + A * (f // 32) * 4, PEAK_BF16_TFLOPS),
         "wgrad_down": (2.0 * A * d * f, A * d * 2 + A * f * 2 + E * d * f * 4, PEAK_BF16_TFLOPS),
         "wgrad_up": (4.0 * A * d * f, A * 2 * f * 2 + T * d * 2 + E * 2 * f * d * 4, PEAK_BF16_TFLOPS),
-        "dgrad_up": (4.0 * A * d * f, A * 2 * f * 2 + E * 2 * f * d * 2 + A * d * 4, PEAK_BF16_TFLOPS),
+        "dgrad_up": (4.0 * A * d * f, A * 2 * f * 2 + E * 2 * f * d * 2 + A * d * 2, PEAK_BF16_TFLOPS),
         "shared": (12.0 * T * d * fs, 0, PEAK_BF16_TFLOPS),
-        "unpermute": (0, A * d * 4 + T * d * 4 + E * d * 4 + T * k * 12, None),
+        # bf16 dX_perm rows and W_r rows in, dx (fp32) out
+        "unpermute": (0, A * d * 2 + T * d * 4 + E * d * 4 + T * k * 12, None),
     }
 
 
@@ -406,7 +412,6 @@ STAGE_KERNEL = {
     "wgrad_down": "gemm_kernel<256, 256, false, false, true, 1, false>",
     "wgrad_up": "gemm_kernel<256, 256, false, false, true, 1, true>",
     "dgrad_up": "gemm_kernel<256, 256, true, false, false, 1, false>",
-    "combine": "combine_bwd_rows_kernel",
     "unpermute": "unpermute_bwd_kernel<8, true>",
 }
 
@@ -708,8 +713,22 @@ def main():
         ev[1].record()
         torch.cuda.synchronize()
         ms = ev[0].elapsed_time(ev[1]) / a.steps
-        print(json.dumps({"copy_bytes_per_launch": 2 * n, "ms": round(ms, 4),
-                          "gb_per_s": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+        res = {"copy_bytes_per_launch": 2 * n, "ms": round(ms, 4), "gb_per_s": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+        # reference read-only and write-only streams of the same 2 GiB (torch's own kernels)
+        f32 = src.view(torch.float32)
+        acc = torch.empty((), dtype=torch.float32, device="cuda:0")
+        for name, fn in (("read", lambda: torch.sum(f32, out=acc)), ("write", lambda: dst.fill_(3))):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            ev[0].record()
+            for _ in range(a.steps):
+                fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            t = ev[0].elapsed_time(ev[1]) / a.steps
+            res[f"{name}_gb_per_s"] = round(n / (t * 1e-3) / 1e9, 1)
+        print(json.dumps(res), flush=True)
         return
     from workloads import EP_SHARDS
     if a.workload in EP_SHARDS:
@@ -727,6 +746,12 @@ def main():
     cpu_tokens = None if a.no_cpu_baseline else (a.cpu_tokens or CPU_TOKENS[cfg.name])
     head = measure(cfg, a, device, fuse, cpu_tokens, graph=not a.no_graph)
     lib_gemms = library_gemms(cfg, a.steps, device) if (a.library_gemms and train) else None
+    train_lines = {}
+    if train and not a.no_fwd and cfg.name == "train":
+        c = CONFIGS["train_skew"]
+        r = measure(c, a, device, fuse, None, graph=not a.no_graph)
+        r["workload"] = describe(c, True) + " with the Zipf logit offset of the 64-expert forward (skewed load)"
+        train_lines["train_skew"] = r
     fwd_lines = {}
     if train and not a.no_fwd:
         for name in [n for n in a.fwd_lines.split(",") if n]:
@@ -756,6 +781,8 @@ def main():
               "expert_tflops", "rooflines", "kernel_rooflines", "routing"):
         if k in head:
             res[k] = head[k]
+    if train_lines:
+        res["train_lines"] = train_lines
     if fwd_lines:
         res["fwd_lines"] = fwd_lines
     if lib_gemms:

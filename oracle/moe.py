@@ -8,8 +8,9 @@ Everything is computed in float64.  For layers whose storage type is bf16 the
 oracle rounds to bf16 exactly where such a layer stores a bf16 tensor
 (``bf16_points=True``): the saved gate/up pre-activations G and U, the SwiGLU
 output H, the gate-scaled output gradient dY_perm (the input of W_down's
-weight gradient; the data gradient scales dY W_down by the gate instead) and
-the SwiGLU input gradients dG, dU.  Expert outputs, the combined output and every gradient that
+weight gradient; the data gradient scales dY W_down by the gate instead),
+the SwiGLU input gradients dG, dU, and each expert row's input gradient
+dX_perm (its k rows per token are summed in high precision).  Expert outputs, the combined output and every gradient that
 leaves the layer stay in high precision.
 """
 from __future__ import annotations
@@ -418,14 +419,17 @@ def expert_backward_rows(dy_rows, xr, G, U, H, w_gate_up, w_down, bf16_points: b
     dyw = dy if dy_wgrad is None else np.asarray(dy_wgrad, np.float64)
     dH = dy @ wd
     sg = 1.0 / (1.0 + np.exp(-G))
-    dG = dH * U * sg * (1.0 + G * (1.0 - sg))
-    dU = dH * (G * sg)
+    dG_raw = dH * U * sg * (1.0 + G * (1.0 - sg))
+    dU_raw = dH * (G * sg)
     if bf16_points:
-        dG, dU = bf16_round(dG), bf16_round(dU)
+        dG, dU = bf16_round(dG_raw), bf16_round(dU_raw)
+    else:
+        dG, dU = dG_raw, dU_raw
     dX = dG @ wgu[:f] + dU @ wgu[f:]
     dWgu = np.concatenate([dG.T @ xr, dU.T @ xr], axis=0)
     dWd = dyw.T @ H
-    return {"dH": dH, "dG": dG, "dU": dU, "dX": dX, "dW_gate_up": dWgu, "dW_down": dWd}
+    return {"dH": dH, "dG": dG, "dU": dU, "dX": dX, "dW_gate_up": dWgu, "dW_down": dWd,
+            "dGU_raw": np.concatenate([dG_raw, dU_raw], axis=1)}
 
 
 def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
@@ -479,6 +483,7 @@ def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
     dW_d = np.zeros((E, d, f))
     dX_perm = np.zeros((A, d))
     dGU = np.zeros((A, 2 * f))
+    dGU_raw = np.zeros((A, 2 * f))
     offs = fwd["offsets"]
     for e in range(E):
         a, b = int(offs[e]), int(offs[e + 1])
@@ -489,11 +494,17 @@ def backward(fwd: dict, dy, x, w_router, w_gate_up, w_down, score_fn: str,
         dW_gu[e], dW_d[e] = r["dW_gate_up"], r["dW_down"]
         dX_perm[a:b] = r["dX"]
         dGU[a:b, :f], dGU[a:b, f:] = r["dG"], r["dU"]
+        dGU_raw[a:b] = r["dGU_raw"]
+    # bf16 layers store each expert row's input gradient in bf16 and sum the
+    # k rows of a token in high precision
+    dX_rows = bf16_round(dX_perm) if bf16_points else dX_perm
     for j in range(k):
         keep = row_of[:, j] >= 0
-        dx[keep] += dX_perm[row_of[keep, j]]
+        dx[keep] += dX_rows[row_of[keep, j]]
+    # *_raw: the values before their bf16 rounding (bf16 layers)
     out = {"dx": dx, "dw_router": dW_r, "dw_gate_up": dW_gu, "dw_down": dW_d,
-           "dg": dg, "dl": dl, "dy_perm": dy_perm_w, "dx_perm": dX_perm, "dgu": dGU}
+           "dg": dg, "dl": dl, "dy_perm": dy_perm_w, "dy_perm_raw": dy_perm, "dx_perm": dX_perm, "dgu": dGU,
+           "dgu_raw": dGU_raw}
     if aux_alpha and score_fn != "uniform":
         out["dl_dense"] = dL
     if w_gate_up_shared is not None:

@@ -13,7 +13,9 @@ Comparison rules:
   are correct.  rounding_ambiguous flags such values (within 2^-16 relative,
   several times the GPU's fp32 error), and a quantity summed over them gets
   the exact effect of flipping every flagged one as extra allowance
-  (dg_flip_allowance); this is the rounding analogue of the near-tie rule;
+  (dg_flip_allowance for the gate gradient over H, wgrad_flip_allowance for
+  the expert weight gradients over dY_perm, H and dG|dU); this is the
+  rounding analogue of the near-tie rule;
 * gates and logits (fp32 in every layer): max-abs <= 1e-4.
 """
 from __future__ import annotations
@@ -76,6 +78,35 @@ def rounding_ambiguous(v, rel=2.0 ** -16):
     ulp = np.ldexp(1.0, e - 8)
     dist = np.abs(scaled - np.floor(scaled) - 0.5) * ulp
     return (dist <= rel * v) & (v > 0), ulp
+
+
+def _flips(raw):
+    """Per element: the change a flip of its bf16 rounding would make (ulp
+    where the value is rounding-ambiguous, else 0)."""
+    amb, ulp = rounding_ambiguous(raw)
+    return np.where(amb, ulp, 0.0)
+
+
+def wgrad_flip_allowance(fw, g, x):
+    """Per weight-gradient element, the largest change that flipping every
+    rounding-ambiguous bf16 input of its sum could cause.  dW_down[e] =
+    dY_perm^T H over e's rows, with both factors bf16-rounded from fp32 (GPU)
+    or fp64 (oracle) values: |flips(dY_perm)|^T |H| + |dY_perm|^T |flips(H)|.
+    dW_gate_up[e] = [dG|dU]^T x, x exact: |flips(dG|dU)|^T |x|.  From the
+    oracle's unrounded values."""
+    offs = fw["offsets"]
+    x64 = np.abs(as_f64(x))
+    tok = fw["token_of"]
+    ad = np.zeros(g["dw_down"].shape)
+    au = np.zeros(g["dw_gate_up"].shape)
+    for e in range(len(offs) - 1):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if b == a:
+            continue
+        dyp, h = g["dy_perm"][a:b], fw["H"][a:b]
+        ad[e] = _flips(g["dy_perm_raw"][a:b]).T @ np.abs(h) + np.abs(dyp).T @ _flips(fw["H_raw"][a:b])
+        au[e] = _flips(g["dgu_raw"][a:b]).T @ x64[tok[a:b]]
+    return ad, au
 
 
 def dg_flip_allowance(fw, dy, w_down, token_of):

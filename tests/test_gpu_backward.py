@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import as_f64, check_close, close_errors, dev, dg_flip_allowance, host, say
+from gpu_helpers import (as_f64, check_close, close_errors, dev, dg_flip_allowance, host, say,
+                         wgrad_flip_allowance)
 from workloads import CONFIGS, make_inputs, scaled
 
 pytestmark = pytest.mark.gpu
@@ -216,27 +217,34 @@ def test_backward_full_training_shape(name):
     assert np.array_equal(host(layer.offsets), fw["offsets"]) and np.array_equal(host(layer.row_of), fw["row_of"])
     g = oracle.backward(fw, inp["dy"], inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], cfg.score, True)
     dwd, dwgu = host(layer.dw_down), host(layer.dw_gate_up)
+    counts = np.diff(fw["offsets"])
     pairs = [("out", host(layer.out), fw["out"]), ("dg", host(layer.dgate), g["dg"]),
              ("dl", host(layer.dlogit), g["dl"]), ("dx", host(layer.dx), g["dx"]),
              ("dW_router", host(layer.dw_router), g["dw_router"]), ("dW_down", dwd, g["dw_down"]),
              ("dW_gate_up", dwgu, g["dw_gate_up"])]
-    counts = np.diff(fw["offsets"])
     pairs += [(f"dW_down[{e}] ({counts[e]} rows)", dwd[e], g["dw_down"][e]) for e in range(cfg.E)]
     pairs += [(f"dW_gate_up[{e}]", dwgu[e], g["dw_gate_up"][e]) for e in range(cfg.E)]
-    # dg sums d products of H, a bf16 quantised code: its bound adds the
-    # effect of the H values that sit on a rounding midpoint (gpu_helpers)
-    allow = dg_flip_allowance(fw, inp["dy"], inp["w_down"], fw["token_of"])
+    # dg sums d products of H, a bf16 quantised code, and the weight
+    # gradients sum products of bf16-rounded dY_perm, H and dG|dU: their
+    # bounds add the effect of the values that sit on a rounding midpoint
+    # (gpu_helpers); everything else is held to the plain bar
+    say("  rounding-flip allowances")
+    allow = {"dg": dg_flip_allowance(fw, inp["dy"], inp["w_down"], fw["token_of"])}
+    allow["dW_down"], allow["dW_gate_up"] = wgrad_flip_allowance(fw, g, inp["x"])
+    for e in range(cfg.E):
+        allow[f"dW_down[{e}] ({counts[e]} rows)"] = allow["dW_down"][e]
+        allow[f"dW_gate_up[{e}]"] = allow["dW_gate_up"][e]
     bad = []
     for name, got, ref in pairs:   # every tensor reported before any assertion
         mx, rel, at = close_errors(got, ref)
         g64, r64 = as_f64(got), as_f64(ref)
-        bound = 2e-2 + (allow if name == "dg" else 0.0)
-        ok = bool(np.all(np.abs(g64 - r64) <= bound)) and rel <= 1e-2
+        al = allow.get(name, 0.0)
+        ok = bool(np.all(np.abs(g64 - r64) <= 2e-2 + al)) and rel <= 1e-2
         extra = ""
-        if name == "dg":
+        if name in allow:
             used = np.abs(g64 - r64) > 2e-2
             extra = (f"; {int(used.sum())} above 2e-2, all within 2e-2 + their rounding-flip allowance "
-                     f"(largest allowance {float(allow.max()):.3e})" if ok else "")
+                     f"(largest allowance {float(np.max(al)):.3e})" if ok and used.any() else "")
         say(f"  {name}: max-abs {mx:.3e} rel-L2 {rel:.3e} at {at} (got {g64[at]:.6g}, ref {r64[at]:.6g})"
             f"{extra}{'' if ok else '  FAILED'}")
         if not ok:
