@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256) void router_dense_wgrad_reduce_kernel(const fl
 // dx[t] = sum_j dx_perm[row_of[t,j]] + sum_e dl_dense[t,e] * w_router[e]
 // (dropped slots, row_of < 0, have no dx_perm row).
 template <int K>
-__global__ __launch_bounds__(256) void unpermute_bwd_dense_kernel(const f32x4* __restrict__ dx_perm,
+__global__ __launch_bounds__(256) void unpermute_bwd_dense_kernel(const u32x2* __restrict__ dx_perm,
                                                                   const int32_t* __restrict__ row_of,
                                                                   const float* __restrict__ dl_dense,
                                                                   const f32x4* __restrict__ w_router,
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(256) void unpermute_bwd_dense_kernel(const f32x4* _
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int myr = lane < K ? row_of[t * K + lane] : 0;
-  const f32x4* xr[K];
+  const u32x2* xr[K];
   bool live[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
@@ -252,7 +252,11 @@ __global__ __launch_bounds__(256) void unpermute_bwd_dense_kernel(const f32x4* _
     f32x4 acc = extra ? __builtin_nontemporal_load(extra + t * nv + v) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      if (live[j]) acc += __builtin_nontemporal_load(xr[j] + v);
+      if (live[j]) {
+        const u32x2 b = xr[j][v];   // four bf16 of the row, summed in fp32
+        acc += f32x4{bf16_to_f32(b[0] & 0xFFFFu), bf16_to_f32(b[0] >> 16), bf16_to_f32(b[1] & 0xFFFFu),
+                     bf16_to_f32(b[1] >> 16)};
+      }
     }
     for (int e = 0; e < E; ++e) {
       const float w = dlr[e];
@@ -275,7 +279,7 @@ size_t moe_aux_bwd_workspace(int64_t T, int E, int64_t d) {
 }
 
 moe_status moe_aux_backward_launch(const float* logits, const int32_t* counts, const int32_t* idx, const float* dl,
-                                   const bf16_t* x, const float* w_router, const f32x4* dx_perm,
+                                   const bf16_t* x, const float* w_router, const u32x4* dx_perm,
                                    const f32x4* extra, const int32_t* row_of, int64_t T, int E, int k, int64_t d,
                                    int fn, float alpha, float* dw_router, float* dx, void* ws, hipStream_t s) {
   float* dl_dense = static_cast<float*>(ws);
@@ -292,7 +296,8 @@ moe_status moe_aux_backward_launch(const float* logits, const int32_t* counts, c
   MOE_LAUNCH_CHECK();
 #define MOE_UBWD_DENSE(K)                                                                                  \
   unpermute_bwd_dense_kernel<K><<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(                                  \
-      dx_perm, row_of, dl_dense, reinterpret_cast<const f32x4*>(w_router), extra, (int)T, E, d / 4,        \
+      reinterpret_cast<const u32x2*>(dx_perm), row_of, dl_dense, reinterpret_cast<const f32x4*>(w_router),  \
+      extra, (int)T, E, d / 4,                                                                              \
       reinterpret_cast<f32x4*>(dx))
   MOE_DISPATCH_K(k, MOE_UBWD_DENSE);
 #undef MOE_UBWD_DENSE

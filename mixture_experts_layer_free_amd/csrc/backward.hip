@@ -20,7 +20,8 @@
 //   5. wgrad up      dW_gate_up[e] = [dG|dU]^T X_perm over e's rows (with
 //                    no X_perm given, its rows are read from x through
 //                    token_of inside the GEMM's slab loads)
-//   6. dgrad up      dX_perm = [dG|dU] W_gate_up (fp32)
+//   6. dgrad up      dX_perm = [dG|dU] W_gate_up (stored in bf16, like the
+//                    other per-row activation gradients; summed in fp32 below)
 //   7. shared expert (optional) the same products over all tokens
 //   8. unpermute_bwd one wave per token: dx = sum_j dX_perm[row_of[t,j]]
 //                    + sum_j dl*W_r[e] (+ the shared expert's input gradient)
@@ -248,17 +249,16 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* _
 }
 
 // dx[t] = extra[t] + sum_j dx_perm[row_of[t,j]] + sum_j dl[t,j] * w_router[idx[t,j]]
-// (extra: the shared expert's input gradient, or null; a slot without a row,
-// row_of < 0, is never read)
-// (a dropped slot, row_of < 0, has no dx_perm row: its load goes to row 0 and
-// is replaced by zero)
+// (dx_perm: bf16 rows, summed in fp32; extra: the shared expert's input
+// gradient in fp32, or null; a slot without a row, row_of < 0, is never
+// read).  Eight columns (16 bytes of dx_perm) per lane and step.
 template <int K, bool ROUTER>
-__global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restrict__ dx_perm,
+__global__ __launch_bounds__(256) void unpermute_bwd_kernel(const u32x4* __restrict__ dx_perm,
                                                             const int32_t* __restrict__ row_of,
                                                             const int32_t* __restrict__ idx, const float* __restrict__ dl,
                                                             const f32x4* __restrict__ w_router,
                                                             const f32x4* __restrict__ extra, int T, int E,
-                                                            int64_t nv, f32x4* __restrict__ dx) {
+                                                            int64_t nv8, f32x4* __restrict__ dx) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restr
   const int e_in = lane < K ? idx[t * K + lane] : 0;
   const int mye = e_in >= 0 && e_in < E ? e_in : 0;   // an invalid id is never used as an index
   const float myl = lane < K ? dl[t * K + lane] : 0.f;
-  const f32x4* xr[K];
+  const u32x4* xr[K];
   const f32x4* wr[K];
   float w[K];
   bool live[K];
@@ -274,28 +274,34 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const f32x4* __restr
   for (int j = 0; j < K; ++j) {
     const int r = __shfl(myr, j, MOE_WAVE);
     live[j] = r >= 0;
-    xr[j] = dx_perm + (int64_t)(live[j] ? r : 0) * nv;
-    wr[j] = ROUTER ? w_router + (int64_t)__shfl(mye, j, MOE_WAVE) * nv : nullptr;
+    xr[j] = dx_perm + (int64_t)(live[j] ? r : 0) * nv8;
+    wr[j] = ROUTER ? w_router + (int64_t)__shfl(mye, j, MOE_WAVE) * 2 * nv8 : nullptr;
     w[j] = __shfl(myl, j, MOE_WAVE);
   }
-  for (int64_t v = lane; v < nv; v += MOE_WAVE) {
-    f32x4 xs[K], ws[K];
+  for (int64_t v = lane; v < nv8; v += MOE_WAVE) {
+    u32x4 xs[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) xs[j] = live[j] ? __builtin_nontemporal_load(xr[j] + v) : u32x4{0u, 0u, 0u, 0u};
+    f32x4 a0 = extra ? __builtin_nontemporal_load(extra + t * 2 * nv8 + 2 * v) : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 a1 = extra ? __builtin_nontemporal_load(extra + t * 2 * nv8 + 2 * v + 1) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      xs[j] = live[j] ? __builtin_nontemporal_load(xr[j] + v) : f32x4{0.f, 0.f, 0.f, 0.f};
-      if (ROUTER) ws[j] = wr[j][v];
+      a0 += f32x4{bf16_to_f32(xs[j][0] & 0xFFFFu), bf16_to_f32(xs[j][0] >> 16), bf16_to_f32(xs[j][1] & 0xFFFFu),
+                  bf16_to_f32(xs[j][1] >> 16)};
+      a1 += f32x4{bf16_to_f32(xs[j][2] & 0xFFFFu), bf16_to_f32(xs[j][2] >> 16), bf16_to_f32(xs[j][3] & 0xFFFFu),
+                  bf16_to_f32(xs[j][3] >> 16)};
     }
-    f32x4 acc = extra ? __builtin_nontemporal_load(extra + t * nv + v) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < K; ++j) acc += xs[j];
 #pragma unroll
     for (int j = 0; j < K && ROUTER; ++j) {
-      acc[0] = fmaf(w[j], ws[j][0], acc[0]);
-      acc[1] = fmaf(w[j], ws[j][1], acc[1]);
-      acc[2] = fmaf(w[j], ws[j][2], acc[2]);
-      acc[3] = fmaf(w[j], ws[j][3], acc[3]);
+      const f32x4 w0 = wr[j][2 * v], w1 = wr[j][2 * v + 1];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a0[q] = fmaf(w[j], w0[q], a0[q]);
+        a1[q] = fmaf(w[j], w1[q], a1[q]);
+      }
     }
-    dx[t * nv + v] = acc;
+    dx[t * 2 * nv8 + 2 * v] = a0;
+    dx[t * 2 * nv8 + 2 * v + 1] = a1;
   }
 }
 
@@ -335,7 +341,7 @@ BwdLayout layout(int64_t T, int k, int E, int64_t d, int64_t f) {
   auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
   L.dy_perm = take((size_t)A * d * 2);
   L.dgu = take((size_t)A * 2 * f * 2);
-  L.dx_perm = take((size_t)A * d * 4);
+  L.dx_perm = take((size_t)A * d * 2);
   L.dg = take((size_t)T * k * 4);
   L.dl = take((size_t)T * k * 4);
   L.dl_perm = take((size_t)A * 4);
@@ -442,7 +448,7 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   char* ws = static_cast<char*>(a->workspace);
   bf16_t* dy_perm = reinterpret_cast<bf16_t*>(ws + Lo.dy_perm);
   bf16_t* dgu = reinterpret_cast<bf16_t*>(ws + Lo.dgu);
-  float* dx_perm = reinterpret_cast<float*>(ws + Lo.dx_perm);
+  bf16_t* dx_perm = reinterpret_cast<bf16_t*>(ws + Lo.dx_perm);
   float* dg = a->dgate ? a->dgate : reinterpret_cast<float*>(ws + Lo.dg);
   float* dl = a->dlogit ? a->dlogit : reinterpret_cast<float*>(ws + Lo.dl);
   float* dl_perm = reinterpret_cast<float*>(ws + Lo.dl_perm);
@@ -550,7 +556,7 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
     g.K = 2 * f; g.N = d;
     g.offsets = a->offsets; g.mt_prefix = mt_prefix; g.G = E;
     g.out = dx_perm; g.ldo = d;
-    st = launch_gemm<true, false, false, EPI_F32>(g, large, A, s);
+    st = launch_gemm<true, false, false, EPI_BF16>(g, large, A, s);
     if (st != MOE_OK) return st;
   }
   MOE_MARK(MOE_BWD_DGRAD_UP);
@@ -619,7 +625,7 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   // 7. unpermute + router input gradient (+ the shared expert's)
   if (aux) {
     st = moe_aux_backward_launch(a->logits, counts, a->topk_idx, dl, static_cast<const bf16_t*>(a->x), a->w_router,
-                                 reinterpret_cast<const f32x4*>(dx_perm), reinterpret_cast<const f32x4*>(dx_sh),
+                                 reinterpret_cast<const u32x4*>(dx_perm), reinterpret_cast<const f32x4*>(dx_sh),
                                  a->row_of, T, E, k, d, a->score_fn, aux_alpha, a->dw_router, a->dx, ws + Lo.aux, s);
     if (st != MOE_OK) return st;
   } else {
@@ -627,13 +633,13 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   do {                                                                                                          \
     if (router)                                                                                                 \
       unpermute_bwd_kernel<K, true><<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(                                   \
-          reinterpret_cast<const f32x4*>(dx_perm), a->row_of, a->topk_idx, dl,                                  \
-          reinterpret_cast<const f32x4*>(a->w_router), reinterpret_cast<const f32x4*>(dx_sh), (int)T, E, d / 4, \
+          reinterpret_cast<const u32x4*>(dx_perm), a->row_of, a->topk_idx, dl,                                  \
+          reinterpret_cast<const f32x4*>(a->w_router), reinterpret_cast<const f32x4*>(dx_sh), (int)T, E, d / 8, \
           reinterpret_cast<f32x4*>(a->dx));                                                                     \
     else                                                                                                        \
       unpermute_bwd_kernel<K, false><<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(                                  \
-          reinterpret_cast<const f32x4*>(dx_perm), a->row_of, a->topk_idx, dl, nullptr,                        \
-          reinterpret_cast<const f32x4*>(dx_sh), (int)T, E, d / 4, reinterpret_cast<f32x4*>(a->dx));            \
+          reinterpret_cast<const u32x4*>(dx_perm), a->row_of, a->topk_idx, dl, nullptr,                        \
+          reinterpret_cast<const f32x4*>(dx_sh), (int)T, E, d / 8, reinterpret_cast<f32x4*>(a->dx));            \
   } while (0)
     MOE_DISPATCH_K(k, MOE_UBWD);
 #undef MOE_UBWD

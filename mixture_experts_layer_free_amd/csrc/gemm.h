@@ -60,6 +60,7 @@ enum Epi {
   EPI_SWIGLU = 0,      // H = silu(G)*U from paired gate/up columns; optional bf16 G|U save
   EPI_F32 = 1,         // plain fp32 store
   EPI_SWIGLU_BWD = 2,  // dG = dH*U*silu'(G), dU = dH*silu(G) from saved G|U, bf16 out
+  EPI_BF16 = 3,        // plain bf16 store (round to nearest even), row-grouped only
 };
 
 struct Args {
@@ -590,6 +591,31 @@ do {                                                                            
             if (row < row_end && col < p.N) {
               float* C = KG ? kg_out : static_cast<float*>(p.out);   // K-grouped: this chunk's output
               __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(C + row * p.ldo + col));
+            }
+          }
+        }
+      }
+    } else if (EPI == EPI_BF16) {
+      static_assert(EPI != EPI_BF16 || !KG, "bf16 store: row-grouped GEMMs only");
+      bf16_t* C = static_cast<bf16_t*>(p.out);
+#pragma unroll
+      for (int ni = 0; ni < FN; ++ni) {
+        const int64_t col0 = (int64_t)nb * TN + wn * WTN + ni * 32;
+        if (col0 >= p.N) continue;
+#pragma unroll
+        for (int mi = 0; mi < FM; ++mi) {
+          stage(stg0, acc[mi][ni]);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {   // 8 columns (16 bytes of bf16) per lane
+            const int idx = lane + 64 * j, rr = idx >> 2, c8 = (idx & 3) * 8;
+            const int64_t row = row0 + wm * WTM + mi * 32 + rr;
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c8);
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c8 + 4);
+            const int64_t col = col0 + c8;
+            if (row < row_end && col < p.N) {
+              const u32x4 o = {pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v1[0], v1[1]),
+                               pack_bf16x2(v1[2], v1[3])};
+              __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(C + row * p.ldo + col));
             }
           }
         }
