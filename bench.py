@@ -102,8 +102,8 @@ CALL_OF = [
     ("combine_bwd", "backward"), ("gate_bwd", "backward"), ("router_wgrad", "backward"), ("unpermute_bwd", "backward"),
     ("router_seg_schedule", "backward"), ("aux_dl_dense", "backward"), ("router_dense_wgrad", "backward"),
     ("fill_zero", "backward"), ("aux_prob", "aux_loss"), ("aux_loss_final", "aux_loss"),
-    ("replay_gate", "route"), ("hash_route", "route"),
-    ("gemm_kernel", "backward"),
+    ("replay_gate", "route"), ("hash_route", "route"), ("kg_schedule", "backward"), ("kg_reduce", "backward"),
+    ("shared_offsets", "backward"), ("gemm_kernel", "backward"),
 ]
 
 
@@ -207,33 +207,54 @@ def measured_traffic(workload):
 
 
 def summarize_counters(files):
-    """Per-kernel table of rocprofv3 --pmc runs (one counter_collection.csv
-    per pass, each run of the same program): every counter summed over a
-    kernel's dispatches, divided by the dispatch count.  Derived columns:
-    MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SQ_BUSY_CU_CYCLES), clock from
-    GRBM_GUI_ACTIVE over the kernel's average duration (when the run also
-    traced kernels), LDS bank conflicts per LDS instruction."""
+    """Per-kernel table of rocprofv3 --pmc runs of one program (one
+    counter_collection.csv per pass; a kernel_trace.csv of a pass gives the
+    durations): each counter averaged over the kernel's dispatches, then
+      MFMA busy  = MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs));
+      clock      = GRBM_GUI_ACTIVE / 8 XCDs / average duration;
+      TA busy    = TA_BUSY_avr / (GRBM_GUI_ACTIVE / 8);
+      waiting    = SQ_WAIT_ANY / SQ_WAVE_CYCLES (wave cycles spent at a wait);
+      L2 hit     = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum);
+    and LdsUtil, LdsBankConflict, VALUBusy as rocprofv3 derives them."""
     import csv
-    per = {}
-    dur = {}
+    vals, dur = {}, {}
     for f in files:
+        if f.endswith("kernel_trace.csv"):
+            for r in csv.DictReader(open(f)):
+                k = short_name(r["Kernel_Name"])
+                dur.setdefault(k, []).append((float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-9)
+            continue
         for r in csv.DictReader(open(f)):
             k = short_name(r["Kernel_Name"])
-            d = per.setdefault(k, {})
-            key = r["Counter_Name"]
-            d.setdefault(key, {})
-            d[key][r["Dispatch_Id"]] = d[key].get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
-            if "Start_Timestamp" in r and r.get("End_Timestamp"):
-                dur.setdefault(k, {})[r["Dispatch_Id"]] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
-    cols = sorted({c for d in per.values() for c in d})
-    print("| kernel | " + " | ".join(cols) + " |")
-    print("|---|" + "---:|" * len(cols))
-    for k, d in sorted(per.items(), key=lambda kv: -sum(len(v) for v in kv[1].values())):
-        vals = []
-        for c in cols:
-            v = d.get(c)
-            vals.append(f"{sum(v.values()) / len(v):.4g}" if v else "")
-        print(f"| `{k}` | " + " | ".join(vals) + " |")
+            d = vals.setdefault(k, {}).setdefault(r["Counter_Name"], {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+
+    def avg(k, c):
+        d = vals.get(k, {}).get(c)
+        return sum(d.values()) / len(d) if d else None
+
+    rows = []
+    for k in vals:
+        gui = avg(k, "GRBM_GUI_ACTIVE")
+        t = sum(dur[k]) / len(dur[k]) if dur.get(k) else None
+        cyc = gui / 8 if gui else None
+        hit, miss = avg(k, "TCC_HIT_sum"), avg(k, "TCC_MISS_sum")
+        wait, wcyc = avg(k, "SQ_WAIT_ANY"), avg(k, "SQ_WAVE_CYCLES")
+        ta = avg(k, "TA_BUSY_avr")
+        rows.append((k, len(next(iter(vals[k].values()))), t, avg(k, "MfmaUtil"), cyc / t / 1e9 if cyc and t else None,
+                     100 * ta / cyc if ta is not None and cyc else None, avg(k, "LdsUtil"), avg(k, "LdsBankConflict"),
+                     avg(k, "VALUBusy"), 100 * hit / (hit + miss) if hit is not None and miss else None,
+                     100 * wait / wcyc if wait is not None and wcyc else None))
+    fmt = lambda v, f: "" if v is None else format(v, f)
+    print("| kernel | dispatches | avg us | MFMA busy % | clock GHz | TA busy % | LdsUtil % | LdsBankConflict | "
+          "VALUBusy % | L2 hit % | waiting % |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|")
+    for r in sorted(rows, key=lambda r: -(r[2] or 0)):
+        if r[2] is not None and r[2] < 50e-6:
+            continue
+        print(f"| `{r[0][:72]}` | {r[1]} | {fmt(r[2] and r[2] * 1e6, '.1f')} | {fmt(r[3], '.1f')} | {fmt(r[4], '.2f')} | "
+              f"{fmt(r[5], '.0f')} | {fmt(r[6], '.1f')} | {fmt(r[7], '.3f')} | {fmt(r[8], '.1f')} | {fmt(r[9], '.1f')} | "
+              f"{fmt(r[10], '.0f')} |")
 
 
 def algorithmic(cfg, fused=False, gather=None):
@@ -694,7 +715,7 @@ def main():
     # the one-core oracle runs in a child process, started before this
     # process touches the GPU
     one_core = None
-    if not a.no_cpu_baseline and a.workload == "train":
+    if not a.no_cpu_baseline and a.workload == "train" and not a.copy_probe:
         log("[bench] oracle on one core (tiny workload)")
         one_core = oracle_one_core()
 
@@ -716,8 +737,7 @@ def main():
         res = {"copy_bytes_per_launch": 2 * n, "ms": round(ms, 4), "gb_per_s": round(2 * n / (ms * 1e-3) / 1e9, 1)}
         # reference read-only and write-only streams of the same 2 GiB (torch's own kernels)
         f32 = src.view(torch.float32)
-        acc = torch.empty((), dtype=torch.float32, device="cuda:0")
-        for name, fn in (("read", lambda: torch.sum(f32, out=acc)), ("write", lambda: dst.fill_(3))):
+        for name, fn in (("read", lambda: f32.sum()), ("write", lambda: dst.fill_(3))):
             for _ in range(3):
                 fn()
             torch.cuda.synchronize()
