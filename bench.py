@@ -450,12 +450,15 @@ def roofline_entry(flops, nbytes, peak_flops, ms, traffic=None):
             "peak_dtype": None, "traffic": traffic}
 
 
-def build_layer(cfg, inp, device, fuse=True):
+def build_layer(cfg, inp, device, fuse=True, packed=False):
+    """packed: a forward-only layer packs its expert weights once, at
+    construction (outside any timed region), as a serving layer would."""
     import torch
     from mixture_experts_layer_free_amd.layer import MoELayer, Shape
     d = lambda k: _dev(inp.get(k), device)
     shape = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, torch.bfloat16, cfg.score, cfg.shared, cfg.f_shared,
-                  cfg.bias_update, cfg.gamma, cfg.train, fuse_permute=fuse)
+                  cfg.bias_update, cfg.gamma, cfg.train, fuse_permute=fuse,
+                  packed_weights=packed and not cfg.train and cfg.f % 128 == 0)
     layer = MoELayer(shape, d("w_router"), d("w_gate_up"), d("w_down"), d("bias"), d("logit_offset"),
                      d("w_gate_up_shared"), d("w_down_shared"), device=device)
     return layer, d("x"), (d("dy") if cfg.train else None)
@@ -476,7 +479,7 @@ def measure(cfg, a, device, fuse=True, cpu_tokens=None, graph=True):
     log(f"[bench] {cfg.name}: generating inputs")
     from workloads import make_inputs
     inp = make_inputs(cfg)
-    layer, x, dy = build_layer(cfg, inp, device, fuse)
+    layer, x, dy = build_layer(cfg, inp, device, fuse, packed=not a.given_weights)
 
     def step(timer=None, stage_events=None):
         layer.forward(x, timer=timer)
@@ -634,7 +637,12 @@ def bench_ep_shard(a):
     del wgu_np, wd_np
     h = torch.empty((rows, cfg.f), dtype=torch.bfloat16, device=device)
     y = torch.empty((rows, cfg.d), dtype=torch.float32, device=device)
-    run = lambda: _lib.moe_grouped_ffn(xs, g_off, wgu, wd, h=h, y=y)
+    if not a.given_weights:
+        pgu, pd = _lib.moe_pack_expert_weights(wgu, wd)
+        del wgu, wd
+        run = lambda: _lib.moe_grouped_ffn_packed(xs, None, g_off, pgu, pd, cfg.f, h=h, y=y)
+    else:
+        run = lambda: _lib.moe_grouped_ffn(xs, g_off, wgu, wd, h=h, y=y)
     for _ in range(a.warmup):
         run()
     torch.cuda.synchronize()
@@ -661,7 +669,8 @@ def bench_ep_shard(a):
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": f"{a.workload}: rank 0 of 8 on the 256-expert top-8 shape (d_model={d}, "
                                   f"expert_ffn={f}): experts {e0}..{e1 - 1} of a {cfg.T}-token global batch, "
-                                  f"{rows} rows; grouped FFN only, no all-to-all",
+                                  f"{rows} rows; grouped FFN only, no all-to-all"
+                                  + ("" if a.given_weights else "; expert weights packed in tile order once"),
                       "global_batch": cfg.T, "seq_len": None, "parallelism": "ep8 (one rank's share on 1 GPU)"},
            "expert_tflops": round(ach, 1), "roofline": roof}
     print(json.dumps(res), flush=True)
@@ -683,6 +692,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--no-fwd", action="store_true", help="skip the forward-only lines")
+    ap.add_argument("--given-weights", action="store_true",
+                    help="forward-only layers use the expert weights as given (default: packed in tile order "
+                         "once, at construction, as a serving layer would)")
     ap.add_argument("--library-gemms", action="store_true",
                     help="also time hipBLASLt GEMMs with the M, N, K of the training step's six expert GEMMs")
     ap.add_argument("--no-fuse-permute", action="store_true",
@@ -777,7 +789,8 @@ def main():
         for name in [n for n in a.fwd_lines.split(",") if n]:
             c = CONFIGS[name]
             r = measure(c, a, device, True, None if a.no_cpu_baseline else CPU_TOKENS[name], graph=not a.no_graph)
-            r["workload"] = describe(c, False) + ", permute fused into the expert GEMM"
+            r["workload"] = describe(c, False) + ", permute fused into the expert GEMM" + (
+                "" if a.given_weights else ", expert weights packed in tile order once at construction")
             fwd_lines[name] = r
     # the dominant kernel: the longest backward stage that is one GEMM kernel
     # (training), else the longest library call
@@ -793,7 +806,8 @@ def main():
     res = {"metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
            "warmup": a.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": describe(cfg, train) + (", permute fused into the expert GEMMs" if fuse else ""),
+           "config": {"workload": describe(cfg, train) + (", permute fused into the expert GEMMs" if fuse else "")
+                      + ("" if train or a.given_weights else ", expert weights packed in tile order once at construction"),
                       "global_batch": cfg.T, "seq_len": None, "parallelism": "none (1 GPU)"},
            "step_mode": ("eager" if a.no_graph else "hip_graph_replay") + ", ms_per_step = median of the steps",
            "roofline": roof}

@@ -291,6 +291,43 @@ moe_status moe_grouped_ffn_gather(const void* x, int64_t T, const int32_t* token
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Expert weights packed in the order the bf16 GEMM tiles stream them.
+ * The expert GEMM's slab loads fetch, per 32-deep step, 64 bytes from each
+ * of 256 weight rows; at the 256-expert shape the expert weights are read
+ * from HBM about once per forward, and that strided pattern streams at
+ * about two thirds of what the same bytes read in order do.  A serving
+ * caller whose weights do not change between calls packs them once
+ * (moe_pack_expert_weights) and runs moe_grouped_ffn_packed, which reads
+ * each slab as one contiguous 16 KB block and gives bit for bit the
+ * results of moe_grouped_ffn / moe_grouped_ffn_gather on the unpacked
+ * weights.  The Lesson's Concept section defines the expert FFN computed;
+ * the packing is a storage order only.
+ *
+ * moe_packed_weight_bytes: bytes of the packed copy of w_gate_up (which =
+ * 0: G*2f*d*2) or of w_down (which = 1: G*ceil(d/256)*256*f*2, rows past d
+ * zero); 0 for other arguments.
+ *
+ * moe_pack_expert_weights: w_gate_up [G, 2f, d] and w_down [G, d, f], bf16,
+ * as moe_grouped_ffn takes them, into packed_gate_up / packed_down (device
+ * buffers of moe_packed_weight_bytes, caller-owned; the layout is private
+ * to this library).  ENOTSUP unless d is a multiple of 64 and f of 128 (the
+ * 256 x 256 tile), G <= MOE_MAX_EXPERTS.
+ *
+ * moe_grouped_ffn_packed: moe_grouped_ffn_gather (token_of set: GEMM row r
+ * reads row token_of[r] of x, which has T rows) or moe_grouped_ffn
+ * (token_of NULL: x holds the `rows` rows; T is ignored) on packed weights,
+ * bf16 only.  Other arguments, outputs and errors as those calls; ENOTSUP
+ * when f is not a multiple of 128.
+ */
+size_t moe_packed_weight_bytes(int which, int64_t G, int64_t d, int64_t f);
+moe_status moe_pack_expert_weights(const void* w_gate_up, const void* w_down, int64_t G, int64_t d, int64_t f,
+                                   void* packed_gate_up, void* packed_down, void* stream);
+moe_status moe_grouped_ffn_packed(const void* x, int64_t T, const int32_t* token_of, int64_t rows, int64_t d,
+                                  const int32_t* offsets, int G, int64_t f, const void* packed_gate_up,
+                                  const void* packed_down, void* gu_saved, void* h, float* y,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * moe_combine — gate-weighted sum of each token's expert outputs.
  * Lesson, Concept: the layer adds, over the chosen experts, gate times the
  * expert's output; shared experts add their output unweighted.  The residual

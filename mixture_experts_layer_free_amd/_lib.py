@@ -57,6 +57,9 @@ _SIGS = {
     "moe_grouped_ffn": [_vp, _i64, _i64, _int, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_grouped_ffn_gather": [_vp, _i64, _vp, _i64, _i64, _int, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                _vp],
+    "moe_packed_weight_bytes": [_int, _i64, _i64, _i64],
+    "moe_pack_expert_weights": [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp],
+    "moe_grouped_ffn_packed": [_vp, _i64, _vp, _i64, _i64, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_combine": [_vp, _vp, _vp, _vp, _i64, _int, _i64, _vp, _int, _vp],
     "moe_bias_update": [_vp, _vp, _int, _i64, _int, ctypes.c_float, _vp],
     "moe_aux_loss": [_vp, _vp, _i64, _int, _int, _int, ctypes.c_float, _vp, _vp, _vp, _sz, _vp],
@@ -81,6 +84,7 @@ def lib():
             fn.argtypes = args
             fn.restype = _int
         L.moe_workspace_size.restype = _sz
+        L.moe_packed_weight_bytes.restype = _sz
         L.moe_status_str.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -323,6 +327,52 @@ def moe_grouped_ffn_gather(x, token_of, offsets, w_gate_up, w_down, gu_saved=Non
     ws, n = _workspace(MOE_CALL_GROUPED_FFN, rows, 1, G, d, f, dev, workspace)
     _check("moe_grouped_ffn_gather", lib().moe_grouped_ffn_gather(
         _p(x), T, _p(token_of), rows, d, _dtype_code(x), _p(offsets), G, f, _p(w_gate_up), _p(w_down),
+        _p(gu_saved), _p(h), _p(y), _p(ws), n, _stream(stream)))
+    return gu_saved, h, y
+
+
+def packed_weight_bytes(which: int, G: int, d: int, f: int) -> int:
+    return int(lib().moe_packed_weight_bytes(which, G, d, f))
+
+
+def moe_pack_expert_weights(w_gate_up, w_down, packed_gate_up=None, packed_down=None, stream=None):
+    """Tile-order copies of the expert weights for moe_grouped_ffn_packed
+    (uint8 device tensors of moe_packed_weight_bytes; the layout is the
+    library's own)."""
+    G, f2, d = w_gate_up.shape
+    f = f2 // 2
+    _req(w_gate_up, "w_gate_up", torch.bfloat16)
+    _req(w_down, "w_down", torch.bfloat16, (G, d, f))
+    dev = w_gate_up.device
+    packed_gate_up = _out(packed_gate_up, "packed_gate_up", torch.uint8, (packed_weight_bytes(0, G, d, f),), dev)
+    packed_down = _out(packed_down, "packed_down", torch.uint8, (packed_weight_bytes(1, G, d, f),), dev)
+    _check("moe_pack_expert_weights", lib().moe_pack_expert_weights(_p(w_gate_up), _p(w_down), G, d, f,
+                                                                    _p(packed_gate_up), _p(packed_down),
+                                                                    _stream(stream)))
+    return packed_gate_up, packed_down
+
+
+def moe_grouped_ffn_packed(x, token_of, offsets, packed_gate_up, packed_down, f, gu_saved=None, h=None, y=None,
+                           save_gu=False, workspace=None, stream=None):
+    """moe_grouped_ffn_gather (token_of given) or moe_grouped_ffn (token_of
+    None: x holds the permuted rows) on weights from moe_pack_expert_weights."""
+    T, d = x.shape
+    rows = token_of.shape[0] if token_of is not None else T
+    G = offsets.shape[0] - 1
+    _req(x, "x", torch.bfloat16)
+    if token_of is not None:
+        _req(token_of, "token_of", torch.int32, (rows,))
+    _req(offsets, "offsets", torch.int32)
+    _req(packed_gate_up, "packed_gate_up", torch.uint8, (packed_weight_bytes(0, G, d, f),))
+    _req(packed_down, "packed_down", torch.uint8, (packed_weight_bytes(1, G, d, f),))
+    dev = x.device
+    if save_gu or gu_saved is not None:
+        gu_saved = _out(gu_saved, "gu_saved", x.dtype, (rows, 2 * f), dev)
+    h = _out(h, "h", x.dtype, (rows, f), dev)
+    y = _out(y, "y", torch.float32, (rows, d), dev)
+    ws, n = _workspace(MOE_CALL_GROUPED_FFN, rows, 1, G, d, f, dev, workspace)
+    _check("moe_grouped_ffn_packed", lib().moe_grouped_ffn_packed(
+        _p(x), T, _p(token_of), rows, d, _p(offsets), G, f, _p(packed_gate_up), _p(packed_down),
         _p(gu_saved), _p(h), _p(y), _p(ws), n, _stream(stream)))
     return gu_saved, h, y
 

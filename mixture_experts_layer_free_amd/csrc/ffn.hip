@@ -243,6 +243,31 @@ __global__ __launch_bounds__(256) void ffn_down_f32_kernel(const float* __restri
   Y[row * d + n] = a;
 }
 
+// Expert weights in the order the 256 x 256 bf16 GEMM tile streams them
+// (Args::b_packed): block (g, nb, s) holds, for r < 256, row rowmap(nb, r)
+// of group g's [rows, K] weight, columns 32 s .. 32 s + 31 (64 bytes at
+// r * 64 in the block); a row at or past `rows` is zero.  swiglu (the
+// up-projection): column block nb holds gate rows nb*128 .. +127 and up
+// rows f + nb*128 .. +127 in 32-row blocks alternating gate, up -- the
+// order the SwiGLU tile pairs them in.  One 16-byte chunk per thread and
+// step, written in order.
+__global__ __launch_bounds__(256) void pack_b_kernel(const u32x4* __restrict__ src, int64_t G, int64_t rows,
+                                                     int64_t K, int NB, int swiglu, int64_t f, u32x4* __restrict__ dst) {
+  const int64_t nslab = K / 32;
+  const int64_t total = G * NB * nslab * 1024;   // 16-byte chunks: 256 rows x 4 per block
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int c = (int)(i & 3), r = (int)((i >> 2) & 255);
+    int64_t b = i >> 10;
+    const int64_t sl = b % nslab;
+    b /= nslab;
+    const int nb = (int)(b % NB);
+    const int64_t g = b / NB;
+    const int64_t n = swiglu ? ((r >> 5) & 1 ? f : 0) + (int64_t)nb * 128 + (r >> 6) * 32 + (r & 31)
+                             : (int64_t)nb * 256 + r;
+    dst[i] = n < rows ? src[((g * rows + n) * K + sl * 32) / 8 + c] : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
 }  // namespace
 
 size_t moe_ffn_workspace(int G) { return align256((size_t)(G + 1) * sizeof(int32_t)); }
@@ -288,11 +313,14 @@ moe_status moe_tile_schedule_launch(const int32_t* offsets, int G, int bm, int32
 // Tile schedule plus the two bf16 expert GEMMs of a grouped SwiGLU FFN.
 // row_token (or null): GEMM row r of the up-projection reads row
 // row_token[r] of x_rows, which then has x_total rows.
+// packed: wgu and wd are the tile-order copies of moe_pack_expert_weights
+// (the 256 x 256 tile only).
 moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, const int32_t* row_token, int64_t x_total,
                                const int32_t* offsets, int32_t* mt_prefix, int G, int64_t f, const bf16_t* wgu,
-                               const bf16_t* wd, bf16_t* gu, bf16_t* h, float* y, hipStream_t s) {
+                               const bf16_t* wd, bf16_t* gu, bf16_t* h, float* y, hipStream_t s, bool packed) {
   using namespace moe_gemm;
   const bool large = use_large_tile(f);
+  if (packed && !large) return MOE_ENOTSUP;
   moe_status st = moe_tile_schedule_launch(offsets, G, large ? BM_LARGE : BM, mt_prefix, s);
   if (st != MOE_OK) return st;
   Args a{};
@@ -312,6 +340,7 @@ moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, co
   a.gu_out = gu;
   a.a_rows = row_token;
   a.a_rows_total = x_total;
+  a.b_packed = packed;
   st = launch_gemm<true, true, false, EPI_SWIGLU>(a, large, rows, s);
   if (st != MOE_OK) return st;
   Args b{};
@@ -328,6 +357,7 @@ moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, co
   b.G = G;
   b.out = y;
   b.ldo = d;
+  b.b_packed = packed;
   return launch_gemm<true, true, false, EPI_F32>(b, large, rows, s);
 }
 
@@ -336,7 +366,7 @@ namespace {
 moe_status grouped_ffn_impl(const void* x, int64_t x_total, const int32_t* row_token, int64_t rows, int64_t d,
                             int dtype, const int32_t* offsets, int G, int64_t f, const void* w_gate_up,
                             const void* w_down, void* gu_saved, void* h, float* y, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            size_t workspace_bytes, void* stream, bool packed = false) {
   if (!x || !offsets || !w_gate_up || !w_down || !h || !y) return MOE_EINVAL;
   if (rows < 1 || d < 1 || f < 1 || G < 1 || x_total < 1) return MOE_EINVAL;
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EINVAL;
@@ -351,8 +381,9 @@ moe_status grouped_ffn_impl(const void* x, int64_t x_total, const int32_t* row_t
     int32_t* mt_prefix = static_cast<int32_t*>(workspace);
     return moe_ffn_bf16_launch(static_cast<const bf16_t*>(x), rows, d, row_token, x_total, offsets, mt_prefix, G, f,
                                static_cast<const bf16_t*>(w_gate_up), static_cast<const bf16_t*>(w_down),
-                               static_cast<bf16_t*>(gu_saved), static_cast<bf16_t*>(h), y, s);
+                               static_cast<bf16_t*>(gu_saved), static_cast<bf16_t*>(h), y, s, packed);
   }
+  if (packed) return MOE_ENOTSUP;   // packed weights: bf16 only
   if (d % 4 != 0) return MOE_ENOTSUP;
   ffn_up_f32_kernel<<<(unsigned)ceil_div(rows * f, 256), 256, 0, s>>>(
       static_cast<const float*>(x), rows, d, row_token, x_total, offsets, G, f, static_cast<const float*>(w_gate_up),
@@ -380,4 +411,38 @@ extern "C" moe_status moe_grouped_ffn_gather(const void* x, int64_t T, const int
   if (!token_of) return MOE_EINVAL;
   return grouped_ffn_impl(x, T, token_of, rows, d, dtype, offsets, G, f, w_gate_up, w_down, gu_saved, h, y, workspace,
                           workspace_bytes, stream);
+}
+
+extern "C" size_t moe_packed_weight_bytes(int which, int64_t G, int64_t d, int64_t f) {
+  if (G < 1 || d < 1 || f < 1) return 0;
+  if (which == 0) return (size_t)G * 2 * f * d * 2;                 // f/128 column blocks, d/32 slabs of 16 KB
+  if (which == 1) return (size_t)G * ceil_div(d, 256) * 256 * f * 2;   // ceil(d/256) column blocks, f/32 slabs
+  return 0;
+}
+
+extern "C" moe_status moe_pack_expert_weights(const void* w_gate_up, const void* w_down, int64_t G, int64_t d,
+                                              int64_t f, void* packed_gate_up, void* packed_down, void* stream) {
+  if (!w_gate_up || !w_down || !packed_gate_up || !packed_down) return MOE_EINVAL;
+  if (G < 1 || d < 1 || f < 1) return MOE_EINVAL;
+  if (G > MOE_MAX_EXPERTS || d % 64 != 0 || f % 128 != 0) return MOE_ENOTSUP;
+  hipStream_t s = moe_stream(stream);
+  const int nb_gu = (int)(f / 128), nb_d = (int)ceil_div(d, 256);
+  auto grid = [](int64_t chunks) { return (unsigned)std::min<int64_t>(65536, std::max<int64_t>(1, ceil_div(chunks, 256))); };
+  pack_b_kernel<<<grid(G * nb_gu * (d / 32) * 1024), 256, 0, s>>>(static_cast<const u32x4*>(w_gate_up), G, 2 * f, d,
+                                                                 nb_gu, 1, f, static_cast<u32x4*>(packed_gate_up));
+  MOE_LAUNCH_CHECK();
+  pack_b_kernel<<<grid(G * nb_d * (f / 32) * 1024), 256, 0, s>>>(static_cast<const u32x4*>(w_down), G, d, f, nb_d, 0,
+                                                                f, static_cast<u32x4*>(packed_down));
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_grouped_ffn_packed(const void* x, int64_t T, const int32_t* token_of, int64_t rows,
+                                             int64_t d, const int32_t* offsets, int G, int64_t f,
+                                             const void* packed_gate_up, const void* packed_down, void* gu_saved,
+                                             void* h, float* y, void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  if (f % 128 != 0) return MOE_ENOTSUP;
+  return grouped_ffn_impl(x, token_of ? T : rows, token_of, rows, d, MOE_BF16, offsets, G, f, packed_gate_up,
+                          packed_down, gu_saved, h, y, workspace, workspace_bytes, stream, true);
 }

@@ -102,6 +102,11 @@ struct Args {
   // outputs of experts split into several row chunks (see launch_cfg)
   int32_t* kg_sched;
   float* kg_partial;
+  // Row-grouped with a K-contiguous B on the 256 x 256 tile only: B is held
+  // in tile order (pack_b_kernel): the TN x BK slab s of group g's column
+  // block nb is one contiguous block at B + ((g * NB + nb) * (K / BK) + s) *
+  // TN * BK, its row r at r * BK -- each slab is one contiguous read
+  int b_packed;
 };
 
 // K-grouped (weight-gradient) schedule.  Each group's reduction rows are cut
@@ -275,7 +280,18 @@ __device__ __forceinline__ void gemm_tile(const Args& p, char* smem, int e, int 
       a_voff[q] = (uint32_t)((int64_t)k * p.lda * 2 + (row0 + c * 8) * 2);
     }
   }
-  if (BKC) {
+  if (BKC && p.b_packed) {
+    const int64_t nslab = p.K / BK;
+    b_base = p.B + ((int64_t)e * p.NB + nb) * nslab * (TN * BK);
+    b_bytes = nslab * (TN * BK * 2);
+    b_step = TN * BK * 2;
+#pragma unroll
+    for (int q = 0; q < LB; ++q) {
+      const int r = (wave * LB + q) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ swz_kc(r);
+      b_voff[q] = (uint32_t)(r * (BK * 2) + c * 16);
+    }
+  } else if (BKC) {
     b_base = p.B + (int64_t)e * p.b_group;
     b_bytes = p.b_rows * p.ldb * 2;
     b_step = BK * 2;

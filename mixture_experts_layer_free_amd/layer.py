@@ -36,6 +36,7 @@ class Shape:
     salt: int = 0                    # hash router: per-layer salt
     aux_alpha: float = 0.0           # weight of the auxiliary load-balancing loss (0: off)
     fuse_permute: bool = True        # the up-projection and W_gate_up's weight gradient gather x rows: no X_perm copy
+    packed_weights: bool = False     # forward-only: expert weights packed once in tile order (moe_pack_expert_weights)
 
 
 def expert_capacity(factor: float, T: int, k: int, E: int) -> int:
@@ -113,6 +114,16 @@ class MoELayer:
         # read x through token_of (the permute fused into the expert GEMMs):
         # then no X_perm is written
         self.gather = s.fuse_permute
+        # a serving layer whose weights do not change packs them once: each
+        # GEMM slab is then one contiguous read (the backward reads the
+        # weights unpacked, so a training layer keeps them as given)
+        self.packed = self.packed_sh = None
+        if s.packed_weights:
+            if s.train:
+                raise ValueError("packed expert weights are for forward-only layers")
+            self.packed = L.moe_pack_expert_weights(w_gate_up, w_down)
+            if s.shared and s.f_shared % 128 == 0:
+                self.packed_sh = L.moe_pack_expert_weights(w_gate_up_shared, w_down_shared)
         self.x_perm = None if self.gather else z(A, d, dtype=dt)
         self.gu = z(A, 2 * f, dtype=dt) if s.train else None
         self.h = z(A, f, dtype=dt)
@@ -174,7 +185,11 @@ class MoELayer:
                                        self.token_of, self.x_perm, workspace=self.ws_perm, stream=stream,
                                        copy=self.x_perm is not None)
         with _span(timer, "grouped_ffn", stream):
-            if self.gather:
+            if self.packed is not None:
+                L.moe_grouped_ffn_packed(x if self.gather else self.x_perm, self.token_of if self.gather else None,
+                                         self.offsets, *self.packed, s.f, self.gu, self.h, self.y_perm,
+                                         workspace=self.ws_ffn, stream=stream)
+            elif self.gather:
                 L.moe_grouped_ffn_gather(x, self.token_of, self.offsets, self.w_gate_up, self.w_down, self.gu,
                                          self.h, self.y_perm, workspace=self.ws_ffn, stream=stream)
             else:
@@ -183,8 +198,12 @@ class MoELayer:
         shared_y = None
         if s.shared:
             with _span(timer, "shared_ffn", stream):
-                L.moe_grouped_ffn(x, self.sh_offsets, self.w_gate_up_shared, self.w_down_shared, self.sh_gu,
-                                  self.sh_h, self.sh_y, workspace=self.ws_sh, stream=stream)
+                if self.packed_sh is not None:
+                    L.moe_grouped_ffn_packed(x, None, self.sh_offsets, *self.packed_sh, s.f_shared, self.sh_gu,
+                                             self.sh_h, self.sh_y, workspace=self.ws_sh, stream=stream)
+                else:
+                    L.moe_grouped_ffn(x, self.sh_offsets, self.w_gate_up_shared, self.w_down_shared, self.sh_gu,
+                                      self.sh_h, self.sh_y, workspace=self.ws_sh, stream=stream)
             shared_y = self.sh_y
         with _span(timer, "combine", stream):
             L.moe_combine(self.y_perm, self.row_of, self.gate, shared_y, self.out, stream=stream)

@@ -108,6 +108,32 @@ def test_permute_without_copy_needs_no_x(L):
     assert lib.moe_permute(P, 1000, 8, 64, None, 1, 64, P, P, P, P, P, P, need, None) == L.MOE_EINVAL
 
 
+def test_packed_weight_calls(L):
+    """The packed-weight entry points: sizes of the packed copies, and the
+    argument checks of packing and of the packed grouped FFN."""
+    lib = L.lib()
+    assert L.packed_weight_bytes(0, 3, 192, 256) == 3 * 512 * 192 * 2       # gate/up: the same bytes
+    assert L.packed_weight_bytes(1, 3, 192, 256) == 3 * 256 * 256 * 2       # down: rows padded to 256
+    assert L.packed_weight_bytes(1, 2, 512, 128) == 2 * 512 * 128 * 2
+    assert L.packed_weight_bytes(2, 3, 192, 256) == 0 and L.packed_weight_bytes(0, 0, 192, 256) == 0
+    pack = lambda **kw: lib.moe_pack_expert_weights(kw.get("gu", P), P, kw.get("G", 4), kw.get("d", 256),
+                                                    kw.get("f", 256), kw.get("pgu", P), P, None)
+    assert pack(gu=None) == L.MOE_EINVAL
+    assert pack(pgu=None) == L.MOE_EINVAL
+    assert pack(G=0) == L.MOE_EINVAL
+    assert pack(d=96) == L.MOE_ENOTSUP
+    assert pack(f=192) == L.MOE_ENOTSUP          # the 256 x 256 tile needs f % 128 == 0
+    assert pack(G=2000) == L.MOE_ENOTSUP
+    need = L.workspace_size(L.MOE_CALL_GROUPED_FFN, 1000, 1, 64, 256, 256)
+    ffn = lambda **kw: lib.moe_grouped_ffn_packed(kw.get("x", P), 1000, kw.get("tok", P), 1000, kw.get("d", 256), P,
+                                                  64, kw.get("f", 256), P, P, None, P, P, kw.get("ws", P),
+                                                  kw.get("wsb", need), None)
+    assert ffn(f=192) == L.MOE_ENOTSUP
+    assert ffn(x=None) == L.MOE_EINVAL
+    assert ffn(d=96) == L.MOE_ENOTSUP
+    assert ffn(wsb=0) == L.MOE_EWORKSPACE
+
+
 def test_combine_and_bias_validation(L):
     lib = L.lib()
     assert lib.moe_combine(None, P, P, None, 10, 2, 64, P, 0, None) == L.MOE_EINVAL

@@ -473,6 +473,82 @@ def test_ffn_ep8_shard():
     _ffn_case(cfg, g_off, xs_np, wgu, wd, rows_to_check=check, save_gu=False)
 
 
+@pytest.mark.parametrize("case", ["256 experts of ~100 rows, gathered", "8 ragged experts, d = 512, f = 384",
+                                  "empty and skewed experts, d = 192", "one expert, permuted rows"])
+def test_ffn_packed_weights_bit_identical(case):
+    """moe_grouped_ffn_packed on the tile-order copies of
+    moe_pack_expert_weights gives bit for bit what the unpacked call gives
+    (half tiles, ragged and empty experts, down-projection rows padded past
+    d, gathered and already-permuted rows), and matches the oracle's expert
+    FFN on sampled rows."""
+    from workloads import f32_to_bf16_bits
+    say(f"[ffn packed weights: {case}]")
+    rng = np.random.default_rng(len(case))
+    if case.startswith("256"):
+        E, d, f, T = 256, 256, 256, 3000
+        counts = rng.integers(60, 160, E)
+    elif case.startswith("8"):
+        E, d, f, T = 8, 512, 384, 900
+        counts = np.array([300, 1, 0, 777, 256, 255, 129, 40])
+    elif case.startswith("empty"):
+        E, d, f, T = 16, 192, 128, 1200
+        counts = np.zeros(E, np.int64)
+        counts[[1, 5, 6]] = [1000, 3, 700]
+    else:
+        E, d, f, T = 1, 128, 256, 640
+        counts = np.array([640])
+    rows = int(counts.sum())
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    bits = lambda *shape, sd: f32_to_bf16_bits((rng.standard_normal(shape) * sd).astype(np.float32))
+    x = bits(T, d, sd=1.0)
+    wgu, wd = bits(E, 2 * f, d, sd=0.05), bits(E, d, f, sd=0.05)
+    gathered = case != "one expert, permuted rows"
+    tok = rng.integers(0, T, rows).astype(np.int32) if gathered else None
+    xd, offd, wgud, wdd = dev(x), dev(offsets), dev(wgu), dev(wd)
+    if gathered:
+        g0, h0, y0 = L.moe_grouped_ffn_gather(xd, dev(tok), offd, wgud, wdd, save_gu=True)
+    else:
+        g0, h0, y0 = L.moe_grouped_ffn(xd, offd, wgud, wdd, save_gu=True)
+    pgu, pd = L.moe_pack_expert_weights(wgud, wdd)
+    g1, h1, y1 = L.moe_grouped_ffn_packed(xd, dev(tok) if gathered else None, offd, pgu, pd, f, save_gu=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(h0, h1) and torch.equal(g0, g1)
+    sample = np.unique(np.concatenate([offsets[:-1][counts > 0], offsets[1:][counts > 0] - 1,
+                                       rng.integers(0, rows, 32)]))
+    grp = np.searchsorted(offsets, sample, side="right") - 1
+    ref = np.zeros((len(sample), d))
+    xin = x[tok] if gathered else x
+    for e in np.unique(grp):
+        sel = grp == e
+        ref[sel] = oracle.expert_ffn(xin[sample[sel]], wgu[e], wd[e], True)["Y"]
+    check_close(host(y1)[sample], ref, "bf16", f"Y ({len(sample)} rows)")
+
+
+def test_forward_packed_weights():
+    """A forward-only layer with packed expert weights (routed and shared)
+    gives the same output, bit for bit, as with the weights as given, and
+    the oracle's."""
+    say("[forward packed weights]")
+    from mixture_experts_layer_free_amd.layer import MoELayer, Shape
+    cfg = scaled(CONFIGS["dsv3"], T=700, d=256, E=24, k=3, f=128, f_shared=256, bias_update=False)
+    inp = make_inputs(cfg)
+    outs = []
+    for packed in (False, True):
+        sh = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, torch.bfloat16, cfg.score, cfg.shared, cfg.f_shared,
+                   packed_weights=packed)
+        layer = MoELayer(sh, dev(inp["w_router"]), dev(inp["w_gate_up"]), dev(inp["w_down"]), dev(inp["bias"]),
+                         dev(inp["logit_offset"]), dev(inp["w_gate_up_shared"]), dev(inp["w_down_shared"]))
+        assert (layer.packed is not None) == packed and (layer.packed_sh is not None) == packed
+        outs.append(host(layer.forward(dev(inp["x"]))).copy())
+    torch.cuda.synchronize()
+    assert np.array_equal(outs[0], outs[1])
+    ref = oracle.forward(inp["x"], inp["w_router"], inp["w_gate_up"], inp["w_down"], cfg.k, cfg.score, True,
+                         sel_bias=inp["bias"], logit_offset=inp["logit_offset"],
+                         w_gate_up_shared=inp["w_gate_up_shared"], w_down_shared=inp["w_down_shared"])
+    keep = ref["margin"] >= 1e-6
+    check_close(outs[1][keep], ref["out"][keep], "bf16", "out (packed weights)")
+
+
 # ---------------------------------------------------------------------------- combine / bias
 
 @pytest.mark.parametrize("k,shared,bf16", [(2, False, False), (8, True, False), (16, False, True), (1, True, True)])
