@@ -94,9 +94,13 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const u32x4* __restric
 
 // Gate backward, one wave per token (lanes 0..k-1 hold the chosen experts):
 // dg = the sum of the row's np32 partials from the dgrad-down epilogue, then
-// dl on the chosen experts.  dg and dl are
-// written for every slot.  An expert id outside [0, E) is invalid input (its
-// token's results are unspecified); such a slot is never used as an index.
+// dl on the chosen experts.  The k rows' partials are read by the whole
+// wave at once: slot j's row goes to the L lanes j*L .. j*L+L-1 (L the
+// largest power of two with k*L <= 64), lane j*L+i sums partials i, i+L,
+// i+2L, ..., and the L lane sums are added by a butterfly (a fixed order).
+// dg and dl are written for every slot.  An expert id outside [0, E) is
+// invalid input (its token's results are unspecified); such a slot is never
+// used as an index.
 __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__ dg_part, int np32,
                                                        const int32_t* __restrict__ row_of,
                                                        const float* __restrict__ gate, const int32_t* __restrict__ idx,
@@ -114,11 +118,19 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
   const int myr = slot ? row_of[t * k + lane] : 0;
   const float myg = act ? gate[t * k + lane] : 0.f;
   const int mye = act ? e_in : 0;
-  float dg = 0.f;   // a dropped slot adds nothing to the output
-  if (act && myr >= 0) {
-    const float* pr = dg_part + (int64_t)myr * np32;   // the row's partials, in column order
-    for (int b = 0; b < np32; ++b) dg += pr[b];
+  // a dropped slot (no row) adds nothing to the output: dg = 0
+  int L = 64;
+  while (L * k > 64) L >>= 1;
+  const int js = lane / L, sub = lane - js * L;
+  const int rj = __shfl(act ? myr : -1, js < k ? js : 0, MOE_WAVE);   // slot js's row, or -1
+  float part = 0.f;
+  if (js < k && rj >= 0) {
+    const float* pr = dg_part + (int64_t)rj * np32;
+    for (int b = sub; b < np32; b += L) part += pr[b];
   }
+  for (int m = 1; m < L; m <<= 1) part += __shfl_xor(part, m, MOE_WAVE);
+  float dg = __shfl(part, (lane < k ? lane : 0) * L, MOE_WAVE);
+  if (!(act && myr >= 0)) dg = 0.f;
   const int prow = myr >= 0 ? myr : (myr == INT32_MIN ? -1 : ~myr);   // its x_perm row, kept or dropped
   const float D = wave_sum(act ? myg * dg : 0.f);
   float dl;
