@@ -331,6 +331,80 @@ __global__ __launch_bounds__(256) void unpermute_bwd_kernel(const u32x4* __restr
   }
 }
 
+// The same sum with the router weights staged in LDS, for E <= UPL_EMAX: a
+// workgroup owns a UPL_CW-column slice of dx for UPL_TB tokens and first
+// copies that slice of all E router rows into LDS, so each router row is
+// read from L2 once per workgroup instead of once per token that chose it
+// (16384 tokens, top-8, d = 2048: 134 MB instead of 1 GB).  Each wave
+// takes two tokens at a time, 32 lanes each, 8 columns (16 bytes of
+// dx_perm) per lane; UPL_NT / 64 waves share the slice.  Sums as
+// unpermute_bwd_kernel: the K rows in slot order in fp32, then the K
+// router terms in slot order.
+constexpr int UPL_CW = 256, UPL_TB = 128, UPL_EMAX = 64, UPL_NT = 512;
+template <int K>
+__global__ __launch_bounds__(UPL_NT) __attribute__((amdgpu_waves_per_eu(4))) void unpermute_bwd_lds_kernel(const u32x4* __restrict__ dx_perm,
+                                                                const int32_t* __restrict__ row_of,
+                                                                const int32_t* __restrict__ idx,
+                                                                const float* __restrict__ dl,
+                                                                const f32x4* __restrict__ w_router,
+                                                                const f32x4* __restrict__ extra, int T, int E,
+                                                                int64_t d, f32x4* __restrict__ dx) {
+  __shared__ f32x4 s_w[UPL_EMAX * UPL_CW / 4];
+  const int64_t c0 = (int64_t)blockIdx.x * UPL_CW;   // this workgroup's columns c0 .. c0 + UPL_CW - 1
+  const int64_t nv4 = d / 4;
+  for (int i = threadIdx.x; i < E * UPL_CW / 4; i += UPL_NT) {
+    const int e = i / (UPL_CW / 4), v = i % (UPL_CW / 4);
+    s_w[i] = w_router[(int64_t)e * nv4 + c0 / 4 + v];
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, hl = lane & 31;   // token of the pair, lane within it
+  const int64_t nv8 = d / 8, col8 = c0 / 8 + hl;   // this lane's 8 columns, as a 16-byte vector index
+  const int64_t tbeg = (int64_t)blockIdx.y * UPL_TB;
+  for (int64_t tp = tbeg + 2 * wave; tp < tbeg + UPL_TB && tp < T; tp += 2 * (UPL_NT / 64)) {
+    const int64_t t = tp + half;
+    const bool tok = t < T;
+    const int64_t tt = tok ? t : tp;
+    const int myr = hl < K ? row_of[tt * K + hl] : 0;
+    const int e_in = hl < K ? idx[tt * K + hl] : 0;
+    const int mye = e_in >= 0 && e_in < E ? e_in : 0;   // an invalid id is never used as an index
+    const float myl = hl < K ? dl[tt * K + hl] : 0.f;
+    u32x4 xs[K];
+    bool live[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int r = __shfl(myr, half * 32 + j, MOE_WAVE);
+      live[j] = r >= 0;
+      const u32x4 l = __builtin_nontemporal_load(dx_perm + (int64_t)(live[j] ? r : 0) * nv8 + col8);
+      xs[j] = live[j] ? l : u32x4{0u, 0u, 0u, 0u};
+    }
+    f32x4 a0 = extra ? __builtin_nontemporal_load(extra + tt * 2 * nv8 + 2 * col8) : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 a1 = extra ? __builtin_nontemporal_load(extra + tt * 2 * nv8 + 2 * col8 + 1) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      a0 += f32x4{bf16_to_f32(xs[j][0] & 0xFFFFu), bf16_to_f32(xs[j][0] >> 16), bf16_to_f32(xs[j][1] & 0xFFFFu),
+                  bf16_to_f32(xs[j][1] >> 16)};
+      a1 += f32x4{bf16_to_f32(xs[j][2] & 0xFFFFu), bf16_to_f32(xs[j][2] >> 16), bf16_to_f32(xs[j][3] & 0xFFFFu),
+                  bf16_to_f32(xs[j][3] >> 16)};
+    }
+#pragma unroll 1
+    for (int j = 0; j < K; ++j) {   // one router row at a time: its LDS reads are not hoisted into registers
+      const float w = __shfl(myl, half * 32 + j, MOE_WAVE);
+      const int e = __shfl(mye, half * 32 + j, MOE_WAVE);
+      const f32x4 w0 = s_w[e * (UPL_CW / 4) + 2 * hl], w1 = s_w[e * (UPL_CW / 4) + 2 * hl + 1];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a0[q] = fmaf(w, w0[q], a0[q]);
+        a1[q] = fmaf(w, w1[q], a1[q]);
+      }
+    }
+    if (tok) {
+      dx[t * 2 * nv8 + 2 * col8] = a0;
+      dx[t * 2 * nv8 + 2 * col8 + 1] = a1;
+    }
+  }
+}
+
 // offsets {0, T} of the shared expert's one row group
 __global__ void shared_offsets_kernel(int32_t* __restrict__ o, int32_t T) {
   if (threadIdx.x < 2) o[threadIdx.x] = threadIdx.x ? T : 0;
@@ -660,7 +734,12 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
   } else {
 #define MOE_UBWD(K)                                                                                             \
   do {                                                                                                          \
-    if (router)                                                                                                 \
+    if (router && E <= UPL_EMAX && d % UPL_CW == 0)                                                             \
+      unpermute_bwd_lds_kernel<K><<<dim3((unsigned)(d / UPL_CW), (unsigned)ceil_div(T, UPL_TB)), UPL_NT, 0, s>>>( \
+          reinterpret_cast<const u32x4*>(dx_perm), a->row_of, a->topk_idx, dl,                                  \
+          reinterpret_cast<const f32x4*>(a->w_router), reinterpret_cast<const f32x4*>(dx_sh), (int)T, E, d,     \
+          reinterpret_cast<f32x4*>(a->dx));                                                                     \
+    else if (router)                                                                                            \
       unpermute_bwd_kernel<K, true><<<(unsigned)ceil_div(T, 4), 256, 0, s>>>(                                   \
           reinterpret_cast<const u32x4*>(dx_perm), a->row_of, a->topk_idx, dl,                                  \
           reinterpret_cast<const f32x4*>(a->w_router), reinterpret_cast<const f32x4*>(dx_sh), (int)T, E, d / 8, \
