@@ -433,7 +433,7 @@ STAGE_KERNEL = {
     "wgrad_down": "gemm_kernel<256, 256, false, false, true, 1, false>",
     "wgrad_up": "gemm_kernel<256, 256, false, false, true, 1, true>",
     "dgrad_up": "gemm_kernel<256, 256, true, false, false, 3, false>",
-    "unpermute": "unpermute_bwd_kernel<8, true>",
+    "unpermute": "unpermute_bwd_lds_kernel<8>",
 }
 
 
