@@ -189,8 +189,11 @@ __device__ __forceinline__ bf16x8 join8(s16x4 lo, s16x4 hi) {
 // round hands each XCD a run of consecutive tiles, so its concurrent tiles
 // form a compact (rows x BAND) block: every operand slab an XCD pulls into its
 // L2 feeds several workgroups (row panels are shared by BAND tiles, column
-// panels by all the block's row tiles).
-constexpr int BAND = 8;
+// panels by all the block's row tiles).  The forward expert GEMMs use bands
+// of 4 (an XCD's 32 tiles: 8 row tiles x 4 column blocks; 64-expert
+// training shape, both forward GEMMs: 1.733 -> 1.688 ms against bands of 8),
+// the others bands of 8.
+template <int BAND>
 __device__ __forceinline__ void band_order(int t, int mts, int nbs, int& mt, int& nb) {
   const int band = t / (mts * BAND);
   const int r = t - band * mts * BAND;
@@ -785,7 +788,7 @@ void gemm_kernel(Args p) {
       // its B panels (for W_gate_up's gradient, gathered x rows, the costlier
       // operand to fetch) and re-read A's instead (W_gate_up's gradient on
       // 16384 tokens, top-8: 1.36 -> 1.32 ms)
-      band_order(L - g * tpg, NB, p.MT, nb, mt);
+      band_order<8>(L - g * tpg, NB, p.MT, nb, mt);
       const int e = g_e[g], oslot = g_out[g];
       float* outp = oslot < 0 ? static_cast<float*>(p.out) + (int64_t)e * p.out_group
                               : p.kg_partial + (int64_t)oslot * p.M * p.N;
@@ -805,7 +808,7 @@ void gemm_kernel(Args p) {
         if (s_pref[mid] * NB <= L) lo = mid; else hi = mid;
       }
       e = lo;
-      band_order(L - s_pref[e] * NB, s_pref[e + 1] - s_pref[e], NB, mt, nb);
+      band_order<BKC ? 4 : 8>(L - s_pref[e] * NB, s_pref[e + 1] - s_pref[e], NB, mt, nb);
       row0 = p.offsets[e] + (int64_t)mt * TM;
       row_end = p.offsets[e + 1];
       kbeg = 0;
