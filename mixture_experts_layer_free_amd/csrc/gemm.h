@@ -142,18 +142,6 @@ inline KgPlan kg_plan(int64_t M, int64_t N, int64_t rows, int G, bool large) {
 inline size_t kg_sched_bytes(const KgPlan& k, int G) { return (size_t)(KG_HDR + 4 * k.gmax + 3 * (int64_t)G) * 4; }
 inline size_t kg_partial_bytes(const KgPlan& k) { return (size_t)(k.smax * k.mn) * 4; }
 
-// p[i] for a wave-uniform i, loaded through the scalar cache (constant
-// address space): p must not change while the kernel runs.
-__device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p, int64_t i) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  typedef const __attribute__((address_space(4))) int32_t* cptr;
-  return reinterpret_cast<cptr>(reinterpret_cast<uintptr_t>(p))[i];
-#else
-  (void)p, (void)i;   // the host pass never runs device code
-  return 0;
-#endif
-}
-
 typedef __attribute__((address_space(3))) void lds_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -349,50 +337,41 @@ __device__ __forceinline__ void gemm_tile(const Args& p, char* smem, int e, int 
   const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(uni(b_base), uni(b_bytes));
 
   // Gathered B (GB): a wave's loads of one slab cover its rows 8*wave ..
-  // 8*wave+7 (BK/4 rows, since each wave moves a quarter of the slab).  Their
-  // row indices are read with scalar loads one slab ahead (gb_rows); a row
-  // past the group's end gets -1.  gb_voffs turns them into the per-lane
-  // byte offsets of a slab's loads; a row outside B (or -1) gets an offset
-  // past the buffer, so its load reads zeros.
+  // 8*wave+7 (BK/4 rows, since each wave moves a quarter of the slab); lane
+  // l of load q takes row q*RPL + l/(TN/8) of them.  Each lane reads the LB
+  // row indices it needs with vector loads one slab ahead (gb_rows), over a
+  // buffer holding the group's rows only; a row past the group's end gets
+  // -1.  gb_voffs turns them into the per-lane byte offsets of a slab's
+  // loads; a row outside B (or -1) gets an offset past the buffer, so its
+  // load reads zeros.  (Scalar loads of the indices would bring the scalar
+  // memory counter into the loop; those loads complete out of order with
+  // the LDS reads, so every wait for a fragment read would then have to
+  // wait for the scalar load just issued as well.)
   static_assert(!GB || (KG && !BKC && LB * 64 / (TN / 8) == 8), "gathered B: K-grouped, K-strided, 8 rows per wave");
-  const int wv = (int)uni((uint32_t)wave);
-  // (held as a vector value, not an array: a lane-dependent choice between
-  // two elements of an array becomes an indexed load from scratch memory)
-  typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
-  // The loaded values are first used a step later (gb_voffs), so the wait
-  // for the scalar loads never holds up a step's LDS reads.
-  auto gb_row0 = [&](int slab) -> int64_t { return uni(kbeg + (int64_t)uni((uint32_t)slab) * BK + 8 * wv); };
-  auto gb_rows = [&](int slab) -> i32x8 {
-    const int64_t r0 = gb_row0(slab);
-    i32x8 t;
-    if (r0 + 8 <= kend) {
-      // all eight rows inside the group (every slab but a group's last):
-      // consecutive addresses, which the compiler merges into one wide load
-#pragma unroll
-      for (int i = 0; i < 8; ++i) t[i] = scalar_load_i32(p.b_gather, r0 + i);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t r = r0 + i;
-        t[i] = scalar_load_i32(p.b_gather, r < kend ? r : kbeg);   // kbeg < kend: a row of the group
-      }
-    }
-    return t;
-  };
-  // each load of a wave covers RPL consecutive rows of its 8 (64 lanes of
-  // 16 bytes, TN / 8 lanes per row): lane l of load q takes row q*RPL + l/(TN/8)
   constexpr int RPL = 64 / (TN / 8);
   static_assert(!GB || RPL == 2 || RPL == 4, "gathered B: 2 or 4 rows per load");
-  const bool gb_b0 = (lane / (TN / 8)) & 1, gb_b1 = (lane / (TN / 8)) & 2;
-  const uint32_t gb_rb = (uint32_t)(p.ldb * 2), gb_nrows = (uint32_t)p.b_gather_rows;
-  auto gb_voffs = [&](int slab, i32x8 t, uint32_t (&vo)[LB]) {
-    const int64_t r0 = gb_row0(slab);
+  typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+  const int wv = (int)uni((uint32_t)wave);
+  const uint32_t gb_lrow = (uint32_t)(lane / (TN / 8));   // this lane's row within a load's RPL rows
+  const uint32_t gb_nrel = (uint32_t)(kend - kbeg);        // the group's rows (under 2^31)
+  const __amdgpu_buffer_rsrc_t rs_g =
+      make_rsrc(uni((const void*)(GB ? p.b_gather + kbeg : p.offsets)), uni(GB ? (kend - kbeg) * 4 : (int64_t)0));
+  // row of the group (from kbeg) that this lane's load q of a slab takes
+  auto gb_rel = [&](int slab, int q) -> uint32_t {
+    return uni((uint32_t)slab) * BK + 8 * wv + q * RPL + gb_lrow;
+  };
+  auto gb_rows = [&](int slab) -> i32x4 {
+    i32x4 t = {0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) t[i] = r0 + i < kend ? t[i] : -1;   // rows past the group's end
+    for (int q = 0; q < LB; ++q)
+      t[q] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rs_g, gb_rel(slab, q) * 4u, 0, 0);
+    return t;
+  };
+  const uint32_t gb_rb = (uint32_t)(p.ldb * 2), gb_nrows = (uint32_t)p.b_gather_rows;
+  auto gb_voffs = [&](int slab, i32x4 t, uint32_t (&vo)[LB]) {
 #pragma unroll
     for (int q = 0; q < LB; ++q) {
-      int32_t row = gb_b0 ? t[q * RPL + 1] : t[q * RPL];
-      if constexpr (RPL == 4) row = gb_b1 ? (gb_b0 ? t[q * RPL + 3] : t[q * RPL + 2]) : row;
+      const int32_t row = gb_rel(slab, q) < gb_nrel ? t[q] : -1;   // rows past the group's end
       // B has under 2^31 bytes, so a row inside it gives a 32-bit offset;
       // -1 and any row outside B go past the buffer
       vo[q] = (uint32_t)row < gb_nrows ? (uint32_t)row * gb_rb + b_voff[q] : 0x80000000u;
@@ -505,9 +484,10 @@ do {                                                                            
   // reads zeros past the group's rows).  On the last step the reads fetch a
   // stage whose contents are never used.
   // With a gathered B, the step first turns the row indices read one step
-  // earlier (tc) into load offsets, in a scheduling region of its own (its
-  // wait for the scalar loads then covers those loads only), and starts the
-  // scalar loads of the next slab's rows (tn).
+  // earlier (tc) into load offsets and starts the loads of the next slab's
+  // row indices (tn), in a scheduling region of its own ahead of the slab
+  // loads: the index loads are then older than the slab loads that the next
+  // step's wait leaves in flight.
 #define MOE_STEP(it_, ca, cb, na, nb_, tc, tn)                                                    \
 do {                                                                                          \
   const int it = (it_);                                                                       \
@@ -516,8 +496,8 @@ do {                                                                            
   uint32_t gvo[LB];                                                                           \
   if constexpr (GB) {                                                                         \
     gb_voffs(it + STAGES - 1, tc, gvo);                                                       \
-    __builtin_amdgcn_sched_barrier(0);                                                        \
     tn = gb_rows(it + STAGES);                                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
   }                                                                                           \
   if constexpr (AK && BKC) read_frags(smem + ((it + 1) % STAGES) * STAGE, na, nb_);           \
   else read_frags_r(smem + ((it + 1) % STAGES) * STAGE, na, nb_);                             \
@@ -530,10 +510,10 @@ do {                                                                            
   // Stores of the previous tile's epilogue may still be in flight: they are
   // older than this tile's loads, so the load waits below cover them too.
   if (nk > 0) {
-    i32x8 tk0 = {}, tk1 = {};   // gathered B: row indices of the slab the next step loads, and of the one after
+    i32x4 tk0 = {}, tk1 = {};   // gathered B: row indices of the slab the next step loads, and of the one after
     if constexpr (GB) {
       static_assert(STAGES == 4, "gathered-B prologue");
-      const i32x8 t0 = gb_rows(0), t1 = gb_rows(1), t2 = gb_rows(2);
+      const i32x4 t0 = gb_rows(0), t1 = gb_rows(1), t2 = gb_rows(2);
       uint32_t v0[LB], v1[LB], v2[LB];
       gb_voffs(0, t0, v0);
       gb_voffs(1, t1, v1);
