@@ -483,11 +483,12 @@ do {                                                                            
   // GEMM is a multiple of 64; a K-grouped tile rounds up and its extra slab
   // reads zeros past the group's rows).  On the last step the reads fetch a
   // stage whose contents are never used.
-  // With a gathered B, the step first turns the row indices read one step
-  // earlier (tc) into load offsets and starts the loads of the next slab's
+  // With a gathered B, the step first starts the loads of the next slab's
   // row indices (tn), in a scheduling region of its own ahead of the slab
-  // loads: the index loads are then older than the slab loads that the next
-  // step's wait leaves in flight.
+  // loads (so they are older than the slab loads that the next step's wait
+  // leaves in flight), then turns the indices read one step earlier (tc)
+  // into load offsets inside the MFMA region, where that chain of vector
+  // instructions runs in the shadow of the MFMAs instead of before them.
 #define MOE_STEP(it_, ca, cb, na, nb_, tc, tn)                                                    \
 do {                                                                                          \
   const int it = (it_);                                                                       \
@@ -495,9 +496,9 @@ do {                                                                            
   block_barrier();                                                                            \
   uint32_t gvo[LB];                                                                           \
   if constexpr (GB) {                                                                         \
-    gb_voffs(it + STAGES - 1, tc, gvo);                                                       \
     tn = gb_rows(it + STAGES);                                                                \
     __builtin_amdgcn_sched_barrier(0);                                                        \
+    gb_voffs(it + STAGES - 1, tc, gvo);                                                       \
   }                                                                                           \
   if constexpr (AK && BKC) read_frags(smem + ((it + 1) % STAGES) * STAGE, na, nb_);           \
   else read_frags_r(smem + ((it + 1) % STAGES) * STAGE, na, nb_);                             \
