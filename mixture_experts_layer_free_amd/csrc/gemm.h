@@ -641,26 +641,33 @@ do {                                                                            
       // 16-byte loads (8 columns) issued PF blocks ahead, into the registers
       // the fragments used in the loop, so PF blocks of loads are in flight
       // while earlier blocks compute.
-      constexpr int NBLK = FM * FN, PF = NBLK < 4 ? NBLK : 4;
+      constexpr int NBLK = FM * FN, PF = NBLK < 2 ? NBLK : 2;
       const bool dgp = p.h_in != nullptr;
       const int64_t np32 = p.N / 32;   // gate-gradient partials per row
       u32x4 gq[PF][2], uq[PF][2], hq[PF][2];
       float sq[PF][2];
+      // Every lane loads, from a clamped address when its row or column is
+      // past the end (the value is then never used: the arithmetic and the
+      // stores below keep to live lanes).  Loads under a per-lane branch,
+      // into registers zeroed first, made the compiler wait for every load
+      // in flight before each block, which emptied the prefetch.
+      const bool scaled = p.row_scale != nullptr;
+      const bf16_t* hsrc = dgp ? p.h_in : p.gu_in;                           // any readable rows when absent
+      const float* ssrc = scaled ? p.row_scale : reinterpret_cast<const float*>(p.gu_in);
       auto load_gu = [&](int b, u32x4 (&gb)[2], u32x4 (&ub)[2], u32x4 (&hb)[2], float (&sb)[2]) {
         const int mi = b / FN, ni = b % FN;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int idx = lane + 64 * j, rr = idx >> 2, c8 = (idx & 3) * 8;
-          const int64_t row = row0 + wm * WTM + mi * 32 + rr;
-          const int64_t col = (int64_t)nb * TN + wn * WTN + ni * 32 + c8;
-          gb[j] = ub[j] = hb[j] = u32x4{0u, 0u, 0u, 0u};
-          sb[j] = 1.0f;
-          if (row < row_end && col < p.N) {
-            gb[j] = *reinterpret_cast<const u32x4*>(p.gu_in + row * 2 * p.N + col);
-            ub[j] = *reinterpret_cast<const u32x4*>(p.gu_in + row * 2 * p.N + p.N + col);
-            if (dgp) hb[j] = *reinterpret_cast<const u32x4*>(p.h_in + row * p.N + col);
-            if (p.row_scale) sb[j] = p.row_scale[row];
-          }
+          int64_t row = row0 + wm * WTM + mi * 32 + rr;
+          int64_t col = (int64_t)nb * TN + wn * WTN + ni * 32 + c8;
+          row = row < row_end ? row : row_end - 1;
+          col = col < p.N ? col : p.N - 8;
+          gb[j] = *reinterpret_cast<const u32x4*>(p.gu_in + row * 2 * p.N + col);
+          ub[j] = *reinterpret_cast<const u32x4*>(p.gu_in + row * 2 * p.N + p.N + col);
+          hb[j] = *reinterpret_cast<const u32x4*>(hsrc + (dgp ? row * p.N + col : 0));
+          const float sv = ssrc[scaled ? row : 0];
+          sb[j] = scaled ? sv : 1.0f;
         }
       };
 #pragma unroll
