@@ -566,25 +566,27 @@ do {                                                                            
           stage(stg0, acc[mi][2 * pi]);
           stage(stg1, acc[mi][2 * pi + 1]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int idx = lane + 64 * j, rr = idx >> 3, c4 = (idx & 7) * 4;
+          for (int j = 0; j < 2; ++j) {   // 8 columns (16 bytes of bf16) per lane
+            const int idx = lane + 64 * j, rr = idx >> 2, c8 = (idx & 3) * 8;
             const int64_t row = row0 + wm * WTM + mi * 32 + rr;
-            const f32x4 g = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c4);
-            const f32x4 u = *reinterpret_cast<const f32x4*>(stg1 + rr * SLD + c4);
+            const f32x4 g0 = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c8);
+            const f32x4 g1 = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c8 + 4);
+            const f32x4 u0 = *reinterpret_cast<const f32x4*>(stg1 + rr * SLD + c8);
+            const f32x4 u1 = *reinterpret_cast<const f32x4*>(stg1 + rr * SLD + c8 + 4);
             if (row < row_end) {
-              const int64_t col = col0 + c4;
-              uint2 h;
-              h.x = pack_bf16x2(silu_f32(g[0]) * u[0], silu_f32(g[1]) * u[1]);
-              h.y = pack_bf16x2(silu_f32(g[2]) * u[2], silu_f32(g[3]) * u[3]);
-              __builtin_nontemporal_store(u32x2{h.x, h.y}, reinterpret_cast<u32x2*>(H + row * p.ldo + col));
+              const int64_t col = col0 + c8;
+              const u32x4 h = {pack_bf16x2(silu_f32(g0[0]) * u0[0], silu_f32(g0[1]) * u0[1]),
+                               pack_bf16x2(silu_f32(g0[2]) * u0[2], silu_f32(g0[3]) * u0[3]),
+                               pack_bf16x2(silu_f32(g1[0]) * u1[0], silu_f32(g1[1]) * u1[1]),
+                               pack_bf16x2(silu_f32(g1[2]) * u1[2], silu_f32(g1[3]) * u1[3])};
+              __builtin_nontemporal_store(h, reinterpret_cast<u32x4*>(H + row * p.ldo + col));
               if (p.gu_out) {
-                uint2 gg, uu;
-                gg.x = pack_bf16x2(g[0], g[1]);
-                gg.y = pack_bf16x2(g[2], g[3]);
-                uu.x = pack_bf16x2(u[0], u[1]);
-                uu.y = pack_bf16x2(u[2], u[3]);
-                __builtin_nontemporal_store(u32x2{gg.x, gg.y}, reinterpret_cast<u32x2*>(p.gu_out + row * 2 * p.N + col));
-                __builtin_nontemporal_store(u32x2{uu.x, uu.y}, reinterpret_cast<u32x2*>(p.gu_out + row * 2 * p.N + p.N + col));
+                const u32x4 gg = {pack_bf16x2(g0[0], g0[1]), pack_bf16x2(g0[2], g0[3]), pack_bf16x2(g1[0], g1[1]),
+                                  pack_bf16x2(g1[2], g1[3])};
+                const u32x4 uu = {pack_bf16x2(u0[0], u0[1]), pack_bf16x2(u0[2], u0[3]), pack_bf16x2(u1[0], u1[1]),
+                                  pack_bf16x2(u1[2], u1[3])};
+                __builtin_nontemporal_store(gg, reinterpret_cast<u32x4*>(p.gu_out + row * 2 * p.N + col));
+                __builtin_nontemporal_store(uu, reinterpret_cast<u32x4*>(p.gu_out + row * 2 * p.N + p.N + col));
               }
             }
           }
