@@ -12,10 +12,11 @@ seeded input already resident in HBM:
 
 Prints one JSON line.  ``value`` is tokens/s of the median step of graph
 replays timed between two device synchronisations.  ``roofline`` covers the
-dominant kernel (the longest backward stage, one GEMM launch, timed with the
-HIP events moe_backward records on its stream after each stage);
-``rooflines`` covers every library call and ``kernel_rooflines`` every
-backward stage.  ``train_lines`` repeats the training measurement under a
+dominant kernel: the longest stage that is one GEMM launch, among the two
+GEMMs of the routed grouped FFN call and the backward's stages, timed with
+the HIP events the library records on its stream after each of them
+(moe_ffn_stage_events, moe_bwd_args.stage_events).  ``rooflines`` covers
+every library call and ``kernel_rooflines`` every such stage.  ``train_lines`` repeats the training measurement under a
 skewed expert load, ``fwd_lines`` for the forward-only workloads (8 experts
 top-2, 64 experts top-8, 256 + 1 shared top-8).
 ``cpu_baseline`` times the CPU oracle on a bounded sample of each workload.
@@ -405,11 +406,17 @@ def time_replays(graph, steps, warmup):
 
 
 def stage_algorithmic(cfg):
-    """Per backward stage (moe_bwd_stage): (flops, bytes, peak TFLOP/s or
-    None for a memory-bound stage) -- each tensor read or written once."""
+    """Per stage of the routed grouped FFN call (moe_ffn_stage) and of the
+    backward (moe_bwd_stage): (flops, bytes, peak TFLOP/s or None for a
+    memory-bound stage) -- each tensor read or written once."""
     T, d, E, k, f, A = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.T * cfg.k
     fs = cfg.f_shared * cfg.shared
     return {
+        # x rows and W_gate_up in; H out, and G|U out in training
+        "ffn_up": (4.0 * A * d * f, T * d * 2 + E * 2 * f * d * 2 + A * f * 2 + (A * 2 * f * 2 if cfg.train else 0),
+                   PEAK_BF16_TFLOPS),
+        # H and W_down in, Y_perm (fp32) out
+        "ffn_down": (2.0 * A * d * f, A * f * 2 + E * d * f * 2 + A * d * 4, PEAK_BF16_TFLOPS),
         # dy rows in, dY_perm = bf16(g dy) and each row's gate out
         "combine": (0, T * d * 2 + A * d * 2 + A * 4 + T * k * 12, None),
         # gate backward (dg partials in) and the router weight gradient
@@ -426,9 +433,11 @@ def stage_algorithmic(cfg):
     }
 
 
-# kernel of each backward stage that dominates it (for the per-kernel roofline
-# and its PMC traffic record)
+# kernel of each stage that dominates it (for the per-kernel roofline and its
+# PMC traffic record)
 STAGE_KERNEL = {
+    "ffn_up": "gemm_kernel<256, 256, true, true, false, 0, false>",
+    "ffn_down": "gemm_kernel<256, 256, true, true, false, 1, false>",
     "dgrad_down": "gemm_kernel<256, 256, true, false, false, 2, false>",
     "wgrad_down": "gemm_kernel<256, 256, false, false, true, 1, false>",
     "wgrad_up": "gemm_kernel<256, 256, false, false, true, 1, true>",
@@ -497,31 +506,35 @@ def measure(cfg, a, device, fuse=True, cpu_tokens=None, graph=True):
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    # eager timed region: events around every library call and every backward stage
+    # eager timed region: events around every library call, after each GEMM
+    # of the routed grouped FFN call, and after every backward stage
     timer = CallTimer()
-    nst = len(_lib.BWD_STAGES)
+    nst, nfs = len(_lib.BWD_STAGES), len(_lib.FFN_STAGES)
     stage_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(a.steps)]
-    for evs in stage_ev:
+    ffn_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nfs + 1)] for _ in range(a.steps)]
+    for evs in stage_ev + ffn_ev:
         for e in evs:
             e.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(a.steps):
+        layer.forward(x, timer=timer, ffn_events=ffn_ev[i])
         if train:
-            layer.forward(x, timer=timer)
             stage_ev[i][0].record()
             layer.backward(x, dy, timer=timer, stage_events=stage_ev[i][1:])
-        else:
-            step(timer)
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) / a.steps * 1e3
     calls = {n: round(statistics.median(ea.elapsed_time(eb) for ea, eb in timer.pairs[n]), 4) for n in timer.pairs}
+    fstages = {"ffn_" + name: round(statistics.median(ffn_ev[i][si].elapsed_time(ffn_ev[i][si + 1])
+                                                      for i in range(a.steps)), 4)
+               for si, name in enumerate(_lib.FFN_STAGES)}
     stages = {}
     if train:
         for si, name in enumerate(_lib.BWD_STAGES):
             stages[name] = round(statistics.median(stage_ev[i][si].elapsed_time(stage_ev[i][si + 1])
                                                    for i in range(a.steps)), 4)
-    log(f"[bench] {cfg.name}: eager {eager_ms:.3f} ms/step; calls {calls}; backward stages {stages}")
+    log(f"[bench] {cfg.name}: eager {eager_ms:.3f} ms/step; calls {calls}; grouped FFN stages {fstages}; "
+        f"backward stages {stages}")
     if graph:
         g = layer.capture(x, dy)
         log(f"[bench] {cfg.name}: timing {a.steps} graph replays")
@@ -539,11 +552,12 @@ def measure(cfg, a, device, fuse=True, cpu_tokens=None, graph=True):
             rooflines[call] = roofline_entry(flops, nbytes, peak_flops, calls[call],
                                              (tr["read"] + tr["write"]) if tr else None)
     kernels = {}
+    timed = {**fstages, **stages}
     for name, (flops, nbytes, peak_flops) in stage_algorithmic(cfg).items():
-        if name in stages and (flops or nbytes):
+        if name in timed and (flops or nbytes):
             kn = STAGE_KERNEL.get(name)
             tr = ktraffic.get(kn) if kn else None
-            kernels[name] = roofline_entry(flops, nbytes, peak_flops, stages[name],
+            kernels[name] = roofline_entry(flops, nbytes, peak_flops, timed[name],
                                            (tr["read"] + tr["write"]) if tr else None)
             if kn:
                 kernels[name]["kernel"] = kn
@@ -551,9 +565,10 @@ def measure(cfg, a, device, fuse=True, cpu_tokens=None, graph=True):
            "tokens_per_s": round(cfg.T / (med * 1e-3), 1), "eager_ms_per_step": round(eager_ms, 4),
            "calls_ms": calls, "rooflines": rooflines,
            "expert_tflops": round(expert_flops(cfg, train) / (med * 1e-3) / 1e12, 1)}
+    res["grouped_ffn_stages_ms"] = fstages
+    res["kernel_rooflines"] = kernels
     if train:
         res["backward_stages_ms"] = stages
-        res["kernel_rooflines"] = kernels
     res["routing"] = routing_stats(cfg, inp, idx0, counts0)
     log(f"[bench] {cfg.name}: routing {res['routing']}")
     del layer, x, dy
@@ -792,13 +807,14 @@ def main():
             r["workload"] = describe(c, False) + ", permute fused into the expert GEMM" + (
                 "" if a.given_weights else ", expert weights packed in tile order once at construction")
             fwd_lines[name] = r
-    # the dominant kernel: the longest backward stage that is one GEMM kernel
-    # (training), else the longest library call
-    if train and head.get("kernel_rooflines"):
-        kr = {k: v for k, v in head["kernel_rooflines"].items() if "kernel" in v}
+    # the dominant kernel: the longest stage that is one GEMM kernel (the
+    # routed grouped FFN's two, the backward's), else the longest library call
+    kr = {k: v for k, v in head.get("kernel_rooflines", {}).items() if "kernel" in v}
+    if kr:
         dom = max(kr, key=lambda k: kr[k]["ms"])
         roof = dict(kr[dom])
-        roof["kernel"] = f"{roof['kernel']} (moe_backward stage {dom}, one launch per step)"
+        where = f"grouped FFN stage {dom[4:]}" if dom.startswith("ffn_") else f"moe_backward stage {dom}"
+        roof["kernel"] = f"{roof['kernel']} ({where}, one launch per step)"
     else:
         dom = max(head["rooflines"], key=lambda c: head["rooflines"][c]["ms"])
         roof = dict(head["rooflines"][dom])
@@ -811,7 +827,8 @@ def main():
                       "global_batch": cfg.T, "seq_len": None, "parallelism": "none (1 GPU)"},
            "step_mode": ("eager" if a.no_graph else "hip_graph_replay") + ", ms_per_step = median of the steps",
            "roofline": roof}
-    for k in ("ms_per_step_mean", "ms_per_step_wall", "eager_ms_per_step", "calls_ms", "backward_stages_ms",
+    for k in ("ms_per_step_mean", "ms_per_step_wall", "eager_ms_per_step", "calls_ms", "grouped_ffn_stages_ms",
+              "backward_stages_ms",
               "expert_tflops", "rooflines", "kernel_rooflines", "routing"):
         if k in head:
             res[k] = head[k]

@@ -328,6 +328,29 @@ moe_status moe_grouped_ffn_packed(const void* x, int64_t T, const int32_t* token
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_ffn_stage_events — per-GEMM timing of one grouped FFN call.  The next
+ * moe_grouped_ffn, moe_grouped_ffn_gather or moe_grouped_ffn_packed call
+ * made from the calling host thread records events[MOE_FFN_STAGE_UP] on
+ * its stream after the up-projection (with its tile schedule) and
+ * events[MOE_FFN_STAGE_DOWN] after the down-projection, so a caller that
+ * records one event before the call can time both GEMMs with
+ * hipEventElapsedTime (the two expert GEMMs of the Lesson's Concept section
+ * and its Cost profile).  The setting is taken by that one call, whatever
+ * it returns, and then cleared.
+ *   events   NULL (no timing), or a HOST array of MOE_FFN_STAGES hipEvent_t
+ *            (as void*, NULL entries skipped) owned by the caller; the array
+ *            must stay valid until the call that takes it returns.
+ * Returns MOE_OK.  A failed event record makes the grouped FFN call return
+ * MOE_EHIP after its kernels are enqueued.
+ */
+enum moe_ffn_stage {
+  MOE_FFN_STAGE_UP = 0,     /* tile schedule; x W_gate_up with the SwiGLU epilogue */
+  MOE_FFN_STAGE_DOWN = 1,   /* H W_down */
+  MOE_FFN_STAGES = 2
+};
+moe_status moe_ffn_stage_events(void* const* events);
+
+/*
  * moe_combine — gate-weighted sum of each token's expert outputs.
  * Lesson, Concept: the layer adds, over the chosen experts, gate times the
  * expert's output; shared experts add their output unweighted.  The residual

@@ -23,6 +23,7 @@ SCORE = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2, "uniform": 3}
  MOE_CALL_BACKWARD_SHARED) = range(6)
 # stages of moe_backward (enum moe_bwd_stage), in stream order
 BWD_STAGES = ("combine", "dgrad_down", "router", "wgrad_down", "wgrad_up", "dgrad_up", "shared", "unpermute")
+FFN_STAGES = ("up", "down")
 MAX_EXPERTS, MAX_TOPK = 1024, 16
 PERMUTE_NOALLOC_SCRATCH = 4 << 20   # bytes of moe_permute_noalloc's static device scratch
 
@@ -60,6 +61,7 @@ _SIGS = {
     "moe_packed_weight_bytes": [_int, _i64, _i64, _i64],
     "moe_pack_expert_weights": [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp],
     "moe_grouped_ffn_packed": [_vp, _i64, _vp, _i64, _i64, _vp, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_ffn_stage_events": [ctypes.POINTER(_vp)],
     "moe_combine": [_vp, _vp, _vp, _vp, _i64, _int, _i64, _vp, _int, _vp],
     "moe_bias_update": [_vp, _vp, _int, _i64, _int, ctypes.c_float, _vp],
     "moe_aux_loss": [_vp, _vp, _i64, _int, _int, _int, ctypes.c_float, _vp, _vp, _vp, _sz, _vp],
@@ -375,6 +377,24 @@ def moe_grouped_ffn_packed(x, token_of, offsets, packed_gate_up, packed_down, f,
         _p(x), T, _p(token_of), rows, d, _p(offsets), G, f, _p(packed_gate_up), _p(packed_down),
         _p(gu_saved), _p(h), _p(y), _p(ws), n, _stream(stream)))
     return gu_saved, h, y
+
+
+_ffn_events_keep = None   # the host array handed to the library, alive until the next setting
+
+
+def moe_ffn_stage_events(events):
+    """events: None, or len(FFN_STAGES) torch.cuda.Event objects, each
+    recorded once before (so that it exists).  The next grouped FFN call on
+    this thread records event s on its stream after stage s."""
+    global _ffn_events_keep
+    if events is None:
+        _ffn_events_keep = None
+        _check("moe_ffn_stage_events", lib().moe_ffn_stage_events(None))
+        return
+    if len(events) != len(FFN_STAGES):
+        raise ValueError(f"moe_ffn_stage_events needs {len(FFN_STAGES)} events")
+    _ffn_events_keep = (_vp * len(FFN_STAGES))(*[ev.cuda_event for ev in events])
+    _check("moe_ffn_stage_events", lib().moe_ffn_stage_events(ctypes.cast(_ffn_events_keep, ctypes.POINTER(_vp))))
 
 
 def moe_combine(y_perm, row_of, topk_gate, shared_y=None, out=None, out_dtype=torch.float32, stream=None):

@@ -315,9 +315,31 @@ moe_status moe_tile_schedule_launch(const int32_t* offsets, int G, int bm, int32
 // row_token[r] of x_rows, which then has x_total rows.
 // packed: wgu and wd are the tile-order copies of moe_pack_expert_weights
 // (the 256 x 256 tile only).
+namespace {
+
+// Events for the next grouped FFN call of this host thread (moe_ffn_stage_events).
+thread_local void* const* t_ffn_events = nullptr;
+
+// Records stage event i of a grouped FFN call (when the caller asked for it).
+moe_status ffn_mark(void* const* events, int i, hipStream_t s) {
+  if (events && events[i] && hipEventRecord(static_cast<hipEvent_t>(events[i]), s) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_EHIP;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" moe_status moe_ffn_stage_events(void* const* events) {
+  t_ffn_events = events;
+  return MOE_OK;
+}
+
 moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, const int32_t* row_token, int64_t x_total,
                                const int32_t* offsets, int32_t* mt_prefix, int G, int64_t f, const bf16_t* wgu,
-                               const bf16_t* wd, bf16_t* gu, bf16_t* h, float* y, hipStream_t s, bool packed) {
+                               const bf16_t* wd, bf16_t* gu, bf16_t* h, float* y, hipStream_t s, bool packed,
+                               void* const* events) {
   using namespace moe_gemm;
   const bool large = use_large_tile(f);
   if (packed && !large) return MOE_ENOTSUP;
@@ -342,6 +364,7 @@ moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, co
   a.a_rows_total = x_total;
   a.b_packed = packed;
   st = launch_gemm<true, true, false, EPI_SWIGLU>(a, large, rows, s);
+  if (st == MOE_OK) st = ffn_mark(events, MOE_FFN_STAGE_UP, s);
   if (st != MOE_OK) return st;
   Args b{};
   b.A = h;
@@ -358,7 +381,9 @@ moe_status moe_ffn_bf16_launch(const bf16_t* x_rows, int64_t rows, int64_t d, co
   b.out = y;
   b.ldo = d;
   b.b_packed = packed;
-  return launch_gemm<true, true, false, EPI_F32>(b, large, rows, s);
+  st = launch_gemm<true, true, false, EPI_F32>(b, large, rows, s);
+  if (st != MOE_OK) return st;
+  return ffn_mark(events, MOE_FFN_STAGE_DOWN, s);
 }
 
 namespace {
@@ -367,6 +392,8 @@ moe_status grouped_ffn_impl(const void* x, int64_t x_total, const int32_t* row_t
                             int dtype, const int32_t* offsets, int G, int64_t f, const void* w_gate_up,
                             const void* w_down, void* gu_saved, void* h, float* y, void* workspace,
                             size_t workspace_bytes, void* stream, bool packed = false) {
+  void* const* events = t_ffn_events;   // one call's worth: taken here whatever the call returns
+  t_ffn_events = nullptr;
   if (!x || !offsets || !w_gate_up || !w_down || !h || !y) return MOE_EINVAL;
   if (rows < 1 || d < 1 || f < 1 || G < 1 || x_total < 1) return MOE_EINVAL;
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EINVAL;
@@ -381,7 +408,7 @@ moe_status grouped_ffn_impl(const void* x, int64_t x_total, const int32_t* row_t
     int32_t* mt_prefix = static_cast<int32_t*>(workspace);
     return moe_ffn_bf16_launch(static_cast<const bf16_t*>(x), rows, d, row_token, x_total, offsets, mt_prefix, G, f,
                                static_cast<const bf16_t*>(w_gate_up), static_cast<const bf16_t*>(w_down),
-                               static_cast<bf16_t*>(gu_saved), static_cast<bf16_t*>(h), y, s, packed);
+                               static_cast<bf16_t*>(gu_saved), static_cast<bf16_t*>(h), y, s, packed, events);
   }
   if (packed) return MOE_ENOTSUP;   // packed weights: bf16 only
   if (d % 4 != 0) return MOE_ENOTSUP;
@@ -389,10 +416,12 @@ moe_status grouped_ffn_impl(const void* x, int64_t x_total, const int32_t* row_t
       static_cast<const float*>(x), rows, d, row_token, x_total, offsets, G, f, static_cast<const float*>(w_gate_up),
       static_cast<float*>(gu_saved), static_cast<float*>(h));
   MOE_LAUNCH_CHECK();
+  moe_status st = ffn_mark(events, MOE_FFN_STAGE_UP, s);
+  if (st != MOE_OK) return st;
   ffn_down_f32_kernel<<<(unsigned)ceil_div(rows * d, 256), 256, 0, s>>>(static_cast<const float*>(h), rows, d, offsets, G,
                                                                         f, static_cast<const float*>(w_down), y);
   MOE_LAUNCH_CHECK();
-  return MOE_OK;
+  return ffn_mark(events, MOE_FFN_STAGE_DOWN, s);
 }
 
 }  // namespace

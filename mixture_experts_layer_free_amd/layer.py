@@ -160,9 +160,12 @@ class MoELayer:
             self.aux_p = z(E)
             self.ws_aux = z(max(1, L.workspace_size(L.MOE_CALL_AUX_LOSS, T, k, E, d, f)), dtype=torch.uint8)
 
-    def forward(self, x, stream=None, timer=None, token_ids=None, replay_idx=None):
+    def forward(self, x, stream=None, timer=None, token_ids=None, replay_idx=None, ffn_events=None):
         """One forward.  ``replay_idx`` [T, k] int32 forces the expert choice
-        (routing replay); the hash router needs ``token_ids`` [T] int32."""
+        (routing replay); the hash router needs ``token_ids`` [T] int32.
+        ``ffn_events``: None, or 1 + len(_lib.FFN_STAGES) torch.cuda.Event
+        objects: the first is recorded before the routed experts' grouped FFN
+        call, the others by the library after its up- and down-projection."""
         s = self.s
         with _span(timer, "route", stream):
             if s.router == "hash":
@@ -184,6 +187,9 @@ class MoELayer:
                 L.moe_permute_capacity(self.idx, x, s.E, s.capacity, self.counts, self.offsets, self.row_of,
                                        self.token_of, self.x_perm, workspace=self.ws_perm, stream=stream,
                                        copy=self.x_perm is not None)
+        if ffn_events is not None:
+            ffn_events[0].record(stream)
+            L.moe_ffn_stage_events(ffn_events[1:])
         with _span(timer, "grouped_ffn", stream):
             if self.packed is not None:
                 L.moe_grouped_ffn_packed(x if self.gather else self.x_perm, self.token_of if self.gather else None,

@@ -89,6 +89,13 @@ int main() {
                                                         P, nullptr, P, p<float>(), P, 0, nullptr), MOE_EWORKSPACE);
   if (moe_packed_weight_bytes(1, 3, 192, 256) != size_t(3) * 256 * 256 * 2 || moe_packed_weight_bytes(7, 3, 192, 256))
     std::printf("FAIL packed weight bytes\n"), ++failures;
+  {
+    void* ev[MOE_FFN_STAGES] = {P, P};   // taken by the next grouped FFN call, which fails its checks first
+    expect("ffn stage events", moe_ffn_stage_events(ev), MOE_OK);
+    expect("ffn h=NULL after events", moe_grouped_ffn(P, 1000, 256, MOE_BF16, p<int32_t>(), 64, 128, P, P, nullptr,
+                                                      nullptr, p<float>(), P, fw, nullptr), MOE_EINVAL);
+    expect("ffn stage events cleared", moe_ffn_stage_events(nullptr), MOE_OK);
+  }
 
   // combine, bias update, aux loss
   expect("combine y=NULL", moe_combine(nullptr, p<int32_t>(), p<float>(), nullptr, 10, 2, 64, P, MOE_F32, nullptr),

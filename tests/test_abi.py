@@ -101,6 +101,18 @@ def test_grouped_ffn_gather_validation(L):
     assert lib.moe_grouped_ffn_gather(*a(T=1 << 23, d=128)) == L.MOE_ENOTSUP   # x past one buffer resource
 
 
+def test_ffn_stage_events_setting(L):
+    """The timing hook takes a host array (or NULL) and returns OK; a grouped
+    FFN call that fails its checks takes the setting and records nothing."""
+    lib = L.lib()
+    lib.moe_ffn_stage_events.restype = ctypes.c_int
+    arr = (ctypes.c_void_p * 2)(None, None)
+    assert lib.moe_ffn_stage_events(ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))) == L.MOE_OK
+    need = L.workspace_size(L.MOE_CALL_GROUPED_FFN, 1000, 1, 64, 256, 128)
+    assert lib.moe_grouped_ffn(P, 1000, 256, 1, P, 64, 128, P, P, None, None, P, P, need, None) == L.MOE_EINVAL
+    assert lib.moe_ffn_stage_events(None) == L.MOE_OK
+
+
 def test_permute_without_copy_needs_no_x(L):
     lib = L.lib()
     need = L.workspace_size(L.MOE_CALL_PERMUTE, 1000, 8, 64)

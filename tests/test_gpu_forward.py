@@ -549,6 +549,36 @@ def test_forward_packed_weights():
     check_close(outs[1][keep], ref["out"][keep], "bf16", "out (packed weights)")
 
 
+@pytest.mark.parametrize("packed,fp32", [(False, False), (True, False), (False, True)])
+def test_forward_ffn_stage_events(packed, fp32):
+    """The grouped FFN timing hook: the routed call records both events (the
+    output unchanged, bit for bit), and only that call (the shared expert's
+    call after it and a later forward leave them as they were)."""
+    say(f"[forward ffn stage events packed={packed} fp32={fp32}]")
+    from mixture_experts_layer_free_amd.layer import MoELayer, Shape
+    cfg = scaled(CONFIGS["dsv3"], T=700, d=256, E=24, k=3, f=128, f_shared=256, bias_update=False)
+    inp = make_inputs(cfg)
+    dt = torch.float32 if fp32 else torch.bfloat16
+    sh = Shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, dt, cfg.score, cfg.shared, cfg.f_shared, packed_weights=packed)
+    cast = (lambda a: dev(a).float()) if fp32 else dev
+    layer = MoELayer(sh, dev(inp["w_router"]), cast(inp["w_gate_up"]), cast(inp["w_down"]), dev(inp["bias"]),
+                     dev(inp["logit_offset"]), cast(inp["w_gate_up_shared"]), cast(inp["w_down_shared"]))
+    x = cast(inp["x"])
+    plain = host(layer.forward(x)).copy()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(1 + len(L.FFN_STAGES))]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    timed = host(layer.forward(x, ffn_events=evs)).copy()
+    torch.cuda.synchronize()
+    assert np.array_equal(plain, timed)
+    t_up, t_down = evs[0].elapsed_time(evs[1]), evs[1].elapsed_time(evs[2])
+    assert t_up > 0 and t_down > 0, (t_up, t_down)
+    layer.forward(x)
+    torch.cuda.synchronize()
+    assert (evs[0].elapsed_time(evs[1]), evs[1].elapsed_time(evs[2])) == (t_up, t_down)
+
+
 # ---------------------------------------------------------------------------- combine / bias
 
 @pytest.mark.parametrize("k,shared,bf16", [(2, False, False), (8, True, False), (16, False, True), (1, True, True)])
