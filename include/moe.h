@@ -341,7 +341,7 @@ moe_status moe_grouped_ffn_packed(const void* x, int64_t T, const int32_t* token
  *            (as void*, NULL entries skipped) owned by the caller; the array
  *            must stay valid until the call that takes it returns.
  * Returns MOE_OK.  A failed event record makes the grouped FFN call return
- * MOE_EHIP after its kernels are enqueued.
+ * MOE_EHIP at that point (what it enqueued before stays enqueued).
  */
 enum moe_ffn_stage {
   MOE_FFN_STAGE_UP = 0,     /* tile schedule; x W_gate_up with the SwiGLU epilogue */
