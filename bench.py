@@ -446,6 +446,23 @@ STAGE_KERNEL = {
 }
 
 
+def dominant_roofline(line):
+    """The roofline entry of a measured line's dominant kernel: the longest
+    stage that is one GEMM kernel (the routed grouped FFN's two, the
+    backward's), else the longest library call."""
+    kr = {k: v for k, v in line.get("kernel_rooflines", {}).items() if "kernel" in v}
+    if kr:
+        dom = max(kr, key=lambda k: kr[k]["ms"])
+        roof = dict(kr[dom])
+        where = f"grouped FFN stage {dom[4:]}" if dom.startswith("ffn_") else f"moe_backward stage {dom}"
+        roof["kernel"] = f"{roof['kernel']} ({where}, one launch per step)"
+        return roof
+    dom = max(line["rooflines"], key=lambda c: line["rooflines"][c]["ms"])
+    roof = dict(line["rooflines"][dom])
+    roof["kernel"] = f"moe_{dom} (library call, all of its kernels)"
+    return roof
+
+
 def roofline_entry(flops, nbytes, peak_flops, ms, traffic=None):
     t = ms * 1e-3
     if flops and peak_flops and (not nbytes or flops / nbytes >= peak_flops / PEAK_HBM_GBS * 1e3):
@@ -807,18 +824,7 @@ def main():
             r["workload"] = describe(c, False) + ", permute fused into the expert GEMM" + (
                 "" if a.given_weights else ", expert weights packed in tile order once at construction")
             fwd_lines[name] = r
-    # the dominant kernel: the longest stage that is one GEMM kernel (the
-    # routed grouped FFN's two, the backward's), else the longest library call
-    kr = {k: v for k, v in head.get("kernel_rooflines", {}).items() if "kernel" in v}
-    if kr:
-        dom = max(kr, key=lambda k: kr[k]["ms"])
-        roof = dict(kr[dom])
-        where = f"grouped FFN stage {dom[4:]}" if dom.startswith("ffn_") else f"moe_backward stage {dom}"
-        roof["kernel"] = f"{roof['kernel']} ({where}, one launch per step)"
-    else:
-        dom = max(head["rooflines"], key=lambda c: head["rooflines"][c]["ms"])
-        roof = dict(head["rooflines"][dom])
-        roof["kernel"] = f"moe_{dom} (library call, all of its kernels)"
+    roof = dominant_roofline(head)
     res = {"metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
            "warmup": a.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
