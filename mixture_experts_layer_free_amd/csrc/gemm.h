@@ -212,7 +212,7 @@ __device__ __forceinline__ void interleave() {
 // One output tile: TM x TN, the four waves WM x WN (WM = 4 / WN), each
 // (TM / WM) x (TN / WN) of 32x32 MFMA blocks; operand slabs, main loop and
 // epilogue as described at the top of this file.
-template <int TM, int TN, int WN, bool AK, bool BKC, bool KG, int EPI, bool GB>
+template <int TM, int TN, int WN, bool AK, bool BKC, bool KG, int EPI, bool GB, int SPLIT = 1>
 __device__ __forceinline__ void gemm_tile(const Args& p, char* smem, int e, int nb, int64_t row0, int64_t row_end,
                                           int64_t kbeg, int64_t kend, float* kg_out = nullptr) {
   constexpr int WTM = TM / (4 / WN), WTN = TN / WN, FM = WTM / 32, FN = WTN / 32;
@@ -272,10 +272,14 @@ __device__ __forceinline__ void gemm_tile(const Args& p, char* smem, int e, int 
     }
   }
   if (BKC && p.b_packed) {
+    // packed blocks are TN * SPLIT wide; a column part (SPLIT > 1) reads rows
+    // (nb % SPLIT) * TN .. of its block's slabs
+    constexpr int TNP = TN * SPLIT;
     const int64_t nslab = p.K / BK;
-    b_base = p.B + ((int64_t)e * p.NB + nb) * nslab * (TN * BK);
-    b_bytes = nslab * (TN * BK * 2);
-    b_step = TN * BK * 2;
+    const int64_t part_off = (int64_t)(nb % SPLIT) * TN * BK;
+    b_base = p.B + ((int64_t)e * p.NB + nb / SPLIT) * nslab * (TNP * BK) + part_off;
+    b_bytes = nslab * (TNP * BK * 2) - part_off * 2;
+    b_step = TNP * BK * 2;
 #pragma unroll
     for (int q = 0; q < LB; ++q) {
       const int r = (wave * LB + q) * 16 + (lane >> 2);
@@ -802,24 +806,54 @@ void gemm_kernel(Args p) {
     }
     return;
   }
-  for (int base = 0;; base += gridDim.x) {
-    const int L = base + xcd * per + slot;
-    if (L >= total) break;
-    int e, mt, nb;
-    int64_t row0, row_end, kbeg, kend;
-    {
-      int lo = 0, hi = p.G;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_pref[mid] * NB <= L) lo = mid; else hi = mid;
-      }
-      e = lo;
-      band_order<BKC ? 4 : 8>(L - s_pref[e] * NB, s_pref[e + 1] - s_pref[e], NB, mt, nb);
-      row0 = p.offsets[e] + (int64_t)mt * TM;
-      row_end = p.offsets[e + 1];
-      kbeg = 0;
-      kend = p.K;
+  // Tile L of the row-grouped list: its group, row tile and column block.
+  auto tile_at = [&](int L, int& e, int& mt, int& nb) {
+    int lo = 0, hi = p.G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pref[mid] * NB <= L) lo = mid; else hi = mid;
     }
+    e = lo;
+    band_order<BKC ? 4 : 8>(L - s_pref[e] * NB, s_pref[e + 1] - s_pref[e], NB, mt, nb);
+  };
+  const int grid = gridDim.x, pos = xcd * per + slot;
+  int end = total;
+  // The last round, when under half full, runs its tiles cut into `split`
+  // column parts (256 x 128, or 256 x 64 with a K-contiguous B) on the
+  // workgroups that would otherwise idle through it.  A column part makes
+  // each of its outputs by the same MFMA sequence along K as the whole tile,
+  // so the results are the same bits.  The parts run first, outside the
+  // persistent loop: inside it, the compiler keeps their set-up values live
+  // across every tile, which costs registers the whole-tile path needs.
+  // An XCD's positions are contiguous, so a tile's parts share its L2.
+  if constexpr (TM == 256 && TN == 256 && AK && !KG) {
+    const int full_end = total - total % grid, rem = total - full_end;
+    constexpr int smax = BKC ? 4 : 2;   // a K-strided slab's swizzle needs rows of 128 columns
+    int split = 1;
+    while (rem > 0 && split < smax && rem * split * 2 <= grid) split *= 2;
+    split = (int)uni((uint32_t)split);
+    if (split > 1) {
+      end = full_end;
+      if (pos < rem * split) {
+        int e, mt, nb;
+        tile_at(full_end + pos / split, e, mt, nb);
+        const int part = pos % split;
+        const int64_t row0 = p.offsets[e] + (int64_t)mt * TM, row_end = p.offsets[e + 1];
+        if (BKC && split == 4)
+          gemm_tile<TM, TN / smax, smax == 4 ? 1 : 2, AK, BKC, KG, EPI, GB, smax>(p, smem, e, nb * smax + part,
+                                                                                row0, row_end, 0, p.K);
+        else
+          gemm_tile<TM, TN / 2, 2, AK, BKC, KG, EPI, GB, 2>(p, smem, e, nb * 2 + part, row0, row_end, 0, p.K);
+      }
+    }
+  }
+  for (int base = 0;; base += grid) {
+    const int L = base + pos;
+    if (L >= end) break;
+    int e, mt, nb;
+    tile_at(L, e, mt, nb);
+    const int64_t row0 = p.offsets[e] + (int64_t)mt * TM, row_end = p.offsets[e + 1];
+    const int64_t kbeg = 0, kend = p.K;
     // A 256-row tile whose group ends within its first 128 rows (a small
     // expert, or a group's ragged last tile) runs as 128 x 256 with the waves
     // side by side: half the MFMA work on each wave's path and half the A

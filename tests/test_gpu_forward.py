@@ -524,6 +524,68 @@ def test_ffn_packed_weights_bit_identical(case):
     check_close(host(y1)[sample], ref, "bf16", f"Y ({len(sample)} rows)")
 
 
+
+def _last_round_split(counts, NB, rows, smax):
+    """Column parts per tile of a row-grouped 256 x 256 GEMM's last round, as
+    the kernel decides it: the persistent grid (one workgroup per CU at
+    most, a multiple of 8, sized by the upper bound on tiles) and the tiles
+    left for its last round, cut in 2 or 4 while they fill at most the grid."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    total = int(sum(-(-int(n) // 256) for n in counts)) * NB
+    upper = (-(-rows // 256) + len(counts)) * NB
+    grid = max(8, min(cus & ~7, (upper + 7) & ~7))
+    rem, s = total % grid, 1
+    while rem > 0 and s < smax and rem * s * 2 <= grid:
+        s *= 2
+    return s
+
+
+@pytest.mark.parametrize("mode", ["rows given", "gathered", "packed weights"])
+def test_ffn_last_round_column_parts_bit_identical(mode):
+    """Tiles of a GEMM's under-filled last round run as 2 or 4 column parts;
+    each part computes its outputs exactly as the whole tile does.  Two
+    calls on the same experts 0 and 1: in the first they make up the whole
+    (last) round and both expert GEMMs cut their tiles in four; in the
+    second a large expert 2 fills the grid past half, nothing is cut, and
+    expert 0's ragged tile runs as a 128-row half tile.  Rows of experts 0
+    and 1 must come out bit for bit the same, and match the oracle."""
+    from workloads import f32_to_bf16_bits
+    say(f"[ffn last-round column parts: {mode}]")
+    rng = np.random.default_rng(11)
+    E, d, f = 8, 256, 256
+    bits = lambda *shape, sd: f32_to_bf16_bits((rng.standard_normal(shape) * sd).astype(np.float32))
+    wgu, wd = bits(E, 2 * f, d, sd=0.05), bits(E, d, f, sd=0.05)
+    runs = []
+    for extra in (0, 4096):
+        counts = np.array([300, 200, extra, 0, 0, 0, 0, 0])
+        rows = int(counts.sum())
+        split_up = _last_round_split(counts, f // 128, rows, 4)
+        split_down = _last_round_split(counts, -(-d // 256), rows, 4)
+        assert (split_up, split_down) == ((4, 4) if extra == 0 else (1, 1)), (split_up, split_down)
+        runs.append(counts)
+    x = bits(4596, d, sd=1.0)
+    tok = rng.permutation(4596).astype(np.int32)
+    xd, wgud, wdd = dev(x), dev(wgu), dev(wd)
+    packed = L.moe_pack_expert_weights(wgud, wdd) if mode == "packed weights" else None
+    outs = []
+    for counts in runs:
+        rows = int(counts.sum())
+        offd = dev(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32))
+        if mode == "rows given":
+            outs.append(L.moe_grouped_ffn(dev(x[:rows]), offd, wgud, wdd, save_gu=True))
+        elif mode == "gathered":
+            outs.append(L.moe_grouped_ffn_gather(xd, dev(tok[:rows]), offd, wgud, wdd, save_gu=True))
+        else:
+            outs.append(L.moe_grouped_ffn_packed(xd, dev(tok[:rows]), offd, packed[0], packed[1], f, save_gu=True))
+    torch.cuda.synchronize()
+    for a, b, what in zip(outs[0], outs[1], ("G|U", "H", "Y")):
+        assert torch.equal(a[:500], b[:500]), what
+    xin = x[:500] if mode == "rows given" else x[tok[:500]]
+    for e, (r0, r1) in enumerate([(0, 300), (300, 500)]):
+        o = oracle.expert_ffn(xin[r0:r1], wgu[e], wd[e], True)
+        check_close(host(outs[0][2])[r0:r1], o["Y"], "bf16", f"Y expert {e}")
+        check_close(host(outs[0][1])[r0:r1], o["H"], "bf16", f"H expert {e}")
+
 def test_forward_packed_weights():
     """A forward-only layer with packed expert weights (routed and shared)
     gives the same output, bit for bit, as with the weights as given, and
