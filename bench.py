@@ -323,15 +323,26 @@ while time.perf_counter() - t0 < 3.0:
                    sel_bias=inp["bias"])
     n += 1
 dt = time.perf_counter() - t0
-print(json.dumps({"value": round(n * cfg.T / dt, 1), "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
-                  "calls": n}))
+res = {"value": round(n * cfg.T / dt, 1), "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)), "calls": n}
+from oracle import pure
+L = lambda a: np.asarray(a, np.float64).tolist()
+args = [L(inp[key]) for key in ("x", "w_router", "w_gate_up", "w_down")]
+bias = L(inp["bias"])
+n, t0 = 0, time.perf_counter()
+while time.perf_counter() - t0 < 3.0:
+    pure.forward(*args, cfg.k, cfg.score, False, sel_bias=bias)
+    n += 1
+dt = time.perf_counter() - t0
+res["pure_python"] = {"value": round(n * cfg.T / dt, 1), "unit": "tokens/s", "cores": 1, "calls": n}
+print(json.dumps(res))
 """
 
 
 def oracle_one_core():
     """The oracle's forward on the tiny fp32 workload (T=64, 8 experts top-2)
-    on one host core with single-threaded BLAS, in a child process started
-    before this process touches the GPU."""
+    on one host core with single-threaded BLAS, and the same forward in plain
+    Python loops (oracle/pure.py), in a child process started before this
+    process touches the GPU."""
     import subprocess
     env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
     try:
@@ -340,6 +351,8 @@ def oracle_one_core():
         out = json.loads(r.stdout.strip().splitlines()[-1])
         out.update(kind="oracle", sample="tiny workload (T=64 d=32 E=8 top-2 fp32) forward, repeated for 3 s, "
                                          "one core, BLAS single-threaded")
+        out["pure_python"].update(kind="oracle (oracle/pure.py)",
+                                  sample="the same forward in plain Python loops, repeated for 3 s, one core")
         return out
     except Exception as e:  # pragma: no cover
         return {"error": str(e)[:200]}

@@ -19,10 +19,13 @@ Sources (titles of the pages the method is taken from):
 
 Parity pins: every public function here is checked by ``tests/test_oracle_*``
 against closed forms, library routines, brute force, finite differences or
-numbers the pages print.  PARITY UNPINNED: ``aux_loss`` / ``aux_grad_logits``
-(the auxiliary load-balancing loss): the pages name the loss but give no
-formula; the Switch/GShard form is taken, and only its internal consistency
-(closed forms, finite differences, autograd) is checked.
+numbers the pages print; ``oracle.pure`` codes the forward a second time in
+plain Python loops, and the two are checked against each other.
+
+PARITY UNPINNED: ``aux_loss`` / ``aux_grad_logits`` (the auxiliary
+load-balancing loss): the pages name the loss but give no formula; the
+Switch/GShard form is taken, and only its internal consistency (closed
+forms, finite differences, autograd) is checked.
 """
 from .moe import (  # noqa: F401
     SCORE_FNS,
