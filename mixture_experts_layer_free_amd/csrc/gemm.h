@@ -560,7 +560,49 @@ do {                                                                            
 #pragma unroll
       for (int r = 0; r < 16; ++r) stg[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * SLD + (lane & 31)] = v[r];
     };
-    if (EPI == EPI_SWIGLU) {
+    if constexpr (EPI == EPI_SWIGLU && FN % 4 == 0) {
+      // Two (gate, up) pairs at a time: their 64 H columns (and 64 of G and
+      // of U) make whole 128-byte rows, 8 rows per store.  Four staged blocks
+      // per wave (the ring is idle).
+      bf16_t* H = static_cast<bf16_t*>(p.out);
+      float* sg = reinterpret_cast<float*>(smem) + wave * (4 * 32 * SLD);
+#pragma unroll
+      for (int pi = 0; pi < FN / 2; pi += 2) {
+        const int64_t col0 = (int64_t)nb * (TN / 2) + (wn * (WTN / 64) + pi) * 32;
+#pragma unroll
+        for (int mi = 0; mi < FM; ++mi) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) stage(sg + q * 32 * SLD, acc[mi][2 * pi + q]);   // gate, up, gate, up
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {   // 8 columns (16 bytes of bf16) per lane
+            const int idx = lane + 64 * j, rr = idx >> 3, c8 = (idx & 7) * 8;
+            const int64_t row = row0 + wm * WTM + mi * 32 + rr;
+            const float* gs = sg + (2 * (c8 >> 5)) * 32 * SLD + rr * SLD + (c8 & 31);
+            const float* us = gs + 32 * SLD;
+            const f32x4 g0 = *reinterpret_cast<const f32x4*>(gs);
+            const f32x4 g1 = *reinterpret_cast<const f32x4*>(gs + 4);
+            const f32x4 u0 = *reinterpret_cast<const f32x4*>(us);
+            const f32x4 u1 = *reinterpret_cast<const f32x4*>(us + 4);
+            if (row < row_end) {
+              const int64_t col = col0 + c8;
+              const u32x4 h = {pack_bf16x2(silu_f32(g0[0]) * u0[0], silu_f32(g0[1]) * u0[1]),
+                               pack_bf16x2(silu_f32(g0[2]) * u0[2], silu_f32(g0[3]) * u0[3]),
+                               pack_bf16x2(silu_f32(g1[0]) * u1[0], silu_f32(g1[1]) * u1[1]),
+                               pack_bf16x2(silu_f32(g1[2]) * u1[2], silu_f32(g1[3]) * u1[3])};
+              __builtin_nontemporal_store(h, reinterpret_cast<u32x4*>(H + row * p.ldo + col));
+              if (p.gu_out) {
+                const u32x4 gg = {pack_bf16x2(g0[0], g0[1]), pack_bf16x2(g0[2], g0[3]), pack_bf16x2(g1[0], g1[1]),
+                                  pack_bf16x2(g1[2], g1[3])};
+                const u32x4 uu = {pack_bf16x2(u0[0], u0[1]), pack_bf16x2(u0[2], u0[3]), pack_bf16x2(u1[0], u1[1]),
+                                  pack_bf16x2(u1[2], u1[3])};
+                __builtin_nontemporal_store(gg, reinterpret_cast<u32x4*>(p.gu_out + row * 2 * p.N + col));
+                __builtin_nontemporal_store(uu, reinterpret_cast<u32x4*>(p.gu_out + row * 2 * p.N + p.N + col));
+              }
+            }
+          }
+        }
+      }
+    } else if (EPI == EPI_SWIGLU) {
       bf16_t* H = static_cast<bf16_t*>(p.out);
 #pragma unroll
       for (int pi = 0; pi < FN / 2; ++pi) {   // wave column blocks come in (gate, up) pairs
@@ -618,21 +660,26 @@ do {                                                                            
         }
       }
     } else if (EPI == EPI_BF16) {
+      // two neighbouring 32-column blocks at a time, so each store covers
+      // whole 128-byte rows (8 rows of 64 columns per store)
       static_assert(EPI != EPI_BF16 || !KG, "bf16 store: row-grouped GEMMs only");
+      static_assert(FN % 2 == 0, "column blocks in pairs");
       bf16_t* C = static_cast<bf16_t*>(p.out);
 #pragma unroll
-      for (int ni = 0; ni < FN; ++ni) {
+      for (int ni = 0; ni < FN; ni += 2) {
         const int64_t col0 = (int64_t)nb * TN + wn * WTN + ni * 32;
         if (col0 >= p.N) continue;
 #pragma unroll
         for (int mi = 0; mi < FM; ++mi) {
           stage(stg0, acc[mi][ni]);
+          stage(stg1, acc[mi][ni + 1]);
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {   // 8 columns (16 bytes of bf16) per lane
-            const int idx = lane + 64 * j, rr = idx >> 2, c8 = (idx & 3) * 8;
+          for (int j = 0; j < 4; ++j) {   // 8 columns (16 bytes of bf16) per lane
+            const int idx = lane + 64 * j, rr = idx >> 3, c8 = (idx & 7) * 8;
             const int64_t row = row0 + wm * WTM + mi * 32 + rr;
-            const f32x4 v0 = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c8);
-            const f32x4 v1 = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c8 + 4);
+            const float* src = (c8 < 32 ? stg0 : stg1 - 32) + rr * SLD + c8;
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
             const int64_t col = col0 + c8;
             if (row < row_end && col < p.N) {
               const u32x4 o = {pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v1[0], v1[1]),
@@ -643,15 +690,20 @@ do {                                                                            
         }
       }
     } else {  // EPI_SWIGLU_BWD: dH block -> dG, dU from the saved G, U
-      // The saved G|U (and H, for the gate-gradient partials) come from HBM:
-      // 16-byte loads (8 columns) issued PF blocks ahead, into the registers
-      // the fragments used in the loop, so PF blocks of loads are in flight
-      // while earlier blocks compute.
-      constexpr int NBLK = FM * FN, PF = NBLK < 2 ? NBLK : 2;
+      // Two neighbouring 32-column blocks at a time (a pair), so every load
+      // and store covers whole 128-byte rows: each instruction moves 8 rows
+      // of 64 columns (a unit; a pair is 4 units).  The saved G|U (and H,
+      // for the gate-gradient partials) come from HBM by 16-byte loads (8
+      // columns per lane) into a ring of 4 units in the registers the
+      // fragments used in the loop: unit j of pair b is reloaded with unit j
+      // of pair b + 1 as soon as it is consumed, so a pair's worth of loads
+      // stays in flight.
+      static_assert(FN % 2 == 0, "column blocks in pairs");
+      constexpr int NPAIR = FM * FN / 2;
       const bool dgp = p.h_in != nullptr;
       const int64_t np32 = p.N / 32;   // gate-gradient partials per row
-      u32x4 gq[PF][2], uq[PF][2], hq[PF][2];
-      float sq[PF][2];
+      u32x4 gq[4], uq[4], hq[4];
+      float sq[4];
       // Every lane loads, from a clamped address when its row or column is
       // past the end (the value is then never used: the arithmetic and the
       // stores below keep to live lanes).  Loads under a per-lane branch,
@@ -660,45 +712,37 @@ do {                                                                            
       const bool scaled = p.row_scale != nullptr;
       const bf16_t* hsrc = dgp ? p.h_in : p.gu_in;                           // any readable rows when absent
       const float* ssrc = scaled ? p.row_scale : reinterpret_cast<const float*>(p.gu_in);
-      auto load_gu = [&](int b, u32x4 (&gb)[2], u32x4 (&ub)[2], u32x4 (&hb)[2], float (&sb)[2]) {
-        const int mi = b / FN, ni = b % FN;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int idx = lane + 64 * j, rr = idx >> 2, c8 = (idx & 3) * 8;
-          int64_t row = row0 + wm * WTM + mi * 32 + rr;
-          int64_t col = (int64_t)nb * TN + wn * WTN + ni * 32 + c8;
-          row = row < row_end ? row : row_end - 1;
-          col = col < p.N ? col : p.N - 8;
-          gb[j] = *reinterpret_cast<const u32x4*>(p.gu_in + row * 2 * p.N + col);
-          ub[j] = *reinterpret_cast<const u32x4*>(p.gu_in + row * 2 * p.N + p.N + col);
-          hb[j] = *reinterpret_cast<const u32x4*>(hsrc + (dgp ? row * p.N + col : 0));
-          const float sv = ssrc[scaled ? row : 0];
-          sb[j] = scaled ? sv : 1.0f;
-        }
+      auto load_unit = [&](int b, int j, u32x4& gb, u32x4& ub, u32x4& hb, float& sb) {
+        const int mi = b / (FN / 2), ni = 2 * (b % (FN / 2));
+        const int idx = lane + 64 * j, rr = idx >> 3, c8 = (idx & 7) * 8;
+        int64_t row = row0 + wm * WTM + mi * 32 + rr;
+        int64_t col = (int64_t)nb * TN + wn * WTN + ni * 32 + c8;
+        row = row < row_end ? row : row_end - 1;
+        col = col < p.N ? col : p.N - 8;
+        gb = *reinterpret_cast<const u32x4*>(p.gu_in + row * 2 * p.N + col);
+        ub = *reinterpret_cast<const u32x4*>(p.gu_in + row * 2 * p.N + p.N + col);
+        hb = *reinterpret_cast<const u32x4*>(hsrc + (dgp ? row * p.N + col : 0));
+        const float sv = ssrc[scaled ? row : 0];
+        sb = scaled ? sv : 1.0f;
       };
 #pragma unroll
-      for (int b = 0; b < PF; ++b) load_gu(b, gq[b], uq[b], hq[b], sq[b]);
+      for (int j = 0; j < 4; ++j) load_unit(0, j, gq[j], uq[j], hq[j], sq[j]);
 #pragma unroll
-      for (int b = 0; b < NBLK; ++b) {
-        const int mi = b / FN, ni = b % FN;
-        u32x4 gc[2], uc[2], hc[2];
-        float sc[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          gc[j] = gq[b % PF][j];
-          uc[j] = uq[b % PF][j];
-          hc[j] = hq[b % PF][j];
-          sc[j] = sq[b % PF][j];
-        }
-        if (b + PF < NBLK) load_gu(b + PF, gq[b % PF], uq[b % PF], hq[b % PF], sq[b % PF]);
+      for (int b = 0; b < NPAIR; ++b) {
+        const int mi = b / (FN / 2), ni = 2 * (b % (FN / 2));
         stage(stg0, acc[mi][ni]);
+        stage(stg1, acc[mi][ni + 1]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int idx = lane + 64 * j, rr = idx >> 2, c8 = (idx & 3) * 8;
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 gcj = gq[j], ucj = uq[j], hcj = hq[j];
+          const float scj = sq[j];
+          if (b + 1 < NPAIR) load_unit(b + 1, j, gq[j], uq[j], hq[j], sq[j]);
+          const int idx = lane + 64 * j, rr = idx >> 3, c8 = (idx & 7) * 8;
           const int64_t row = row0 + wm * WTM + mi * 32 + rr;
           const int64_t col = (int64_t)nb * TN + wn * WTN + ni * 32 + c8;
-          const f32x4 v0 = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c8);
-          const f32x4 v1 = *reinterpret_cast<const f32x4*>(stg0 + rr * SLD + c8 + 4);
+          const float* src = (c8 < 32 ? stg0 : stg1 - 32) + rr * SLD + c8;
+          const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
+          const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
           const bool live = row < row_end && col < p.N;
           if (dgp) {
             // gate-gradient partial of this row's 32 columns: the four lanes
@@ -708,8 +752,8 @@ do {                                                                            
               const float vv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                part = fmaf(vv[2 * q], bf16_to_f32(hc[j][q] & 0xFFFFu), part);
-                part = fmaf(vv[2 * q + 1], bf16_to_f32(hc[j][q] >> 16), part);
+                part = fmaf(vv[2 * q], bf16_to_f32(hcj[q] & 0xFFFFu), part);
+                part = fmaf(vv[2 * q + 1], bf16_to_f32(hcj[q] >> 16), part);
               }
             }
             part += __shfl_xor(part, 1, MOE_WAVE);
@@ -717,7 +761,7 @@ do {                                                                            
             if (live && (lane & 3) == 0) p.dg_part[row * np32 + (col >> 5)] = part;
           }
           if (live) {
-            const float s = sc[j];
+            const float s = scj;
             const float v[8] = {s * v0[0], s * v0[1], s * v0[2], s * v0[3], s * v1[0], s * v1[1], s * v1[2], s * v1[3]};
             u32x4 o1, o2;
 #pragma unroll
@@ -725,7 +769,7 @@ do {                                                                            
               float dg[2], du[2];
 #pragma unroll
               for (int h = 0; h < 2; ++h) {
-                const uint32_t gw = gc[j][q], uw = uc[j][q];
+                const uint32_t gw = gcj[q], uw = ucj[q];
                 const float g = bf16_to_f32(h ? gw >> 16 : gw & 0xFFFFu);
                 const float u = bf16_to_f32(h ? uw >> 16 : uw & 0xFFFFu);
                 const float sg = sigmoid_fast(g);
