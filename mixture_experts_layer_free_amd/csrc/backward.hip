@@ -274,6 +274,183 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* _
   dw[(int64_t)e * d + c] = s;
 }
 
+// The router weight gradient on the bf16 MFMA (E <= 64, d a multiple of
+// 256): dW_r = dL^T x, with dL [T, E] the slots' dl placed at their experts
+// (a slot counts when its expert id is valid and it has a row, kept or
+// dropped, as in dl_perm).  Each fp32 dl is split exactly into three bf16
+// parts (split3x2: 8 + 8 + 8 bits of its significand) and x is bf16, so
+// every product is exact in fp32 and three MFMAs per 16-deep step add them
+// in fp32.  x is read once (T * d * 2 bytes) instead of k gathered copies.
+// Workgroup: all 64 expert rows x 256 columns over a chunk of RW_TCH
+// tokens, 4 waves of 64 x 64, two workgroups per CU; per 32-token slab the
+// three dL planes ([64 experts][32 tokens], K-contiguous) are built in LDS
+// and x's slab ([32 tokens][256 columns], K-strided) is copied in,
+// double-buffered, its loads two slabs ahead.
+// part[chunk][e][c]; router_wgrad_chunks_reduce_kernel adds the chunks in
+// order (deterministic).
+constexpr int RW_TCH = 256, RW_EMAX = 64;
+constexpr int RW_PLANE = RW_EMAX * 32 * 2;          // bytes of one dL plane
+constexpr int RW_BUF = 3 * RW_PLANE + 32 * 256 * 2; // dL planes + x slab
+__global__ __launch_bounds__(256) void router_wgrad_mfma_kernel(const bf16_t* __restrict__ x,
+                                                                const int32_t* __restrict__ idx,
+                                                                const int32_t* __restrict__ row_of,
+                                                                const float* __restrict__ dl, int T, int k, int E,
+                                                                int64_t d, float* __restrict__ part) {
+  using namespace moe_gemm;
+  __shared__ __attribute__((aligned(16))) char smem[2 * RW_BUF];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * 256;
+  const int t0 = blockIdx.y * RW_TCH, t1 = min(T, t0 + RW_TCH);
+  const int nslab = (t1 - t0 + 31) / 32;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x16{};
+  // x slab: 32 rows x 256 columns = 1024 16-byte chunks, 4 per thread; chunk
+  // q of thread tid is row (tid + 256 q) / 32, column chunk (tid + 256 q) % 32
+  auto load_x = [&](int slab, u32x4 (&v)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = tid + 256 * q, r = i >> 5, cc = i & 31;
+      const int t = t0 + slab * 32 + r;
+      v[q] = t < t1 ? *reinterpret_cast<const u32x4*>(x + (int64_t)t * d + c0 + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_x = [&](char* buf, const u32x4 (&v)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = tid + 256 * q, r = i >> 5, cc = i & 31;
+      *reinterpret_cast<u32x4*>(buf + 3 * RW_PLANE + r * 512 + ((cc ^ swz_ks(r)) << 4)) = v[q];
+    }
+  };
+  // A slab's 32 k slots, at most two per thread (k <= 16): expert id, row
+  // and dl, loaded two slabs ahead like x
+  struct Slots {
+    int e[2], row[2];
+    float v[2];
+  };
+  auto load_slots = [&](int slab, Slots& sl) {
+    const int tb = t0 + slab * 32;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + 256 * u, t = tb + i / k;
+      const bool in = i < 32 * k && t < t1;
+      const int64_t q = in ? (int64_t)t * k + i % k : 0;
+      sl.e[u] = in ? idx[q] : -1;
+      sl.row[u] = row_of[q];
+      sl.v[u] = dl[q];
+    }
+  };
+  // dL planes of a slab (zeroed before): one bf16 part per slot and plane
+  // at (expert, token) -- the k experts of a token are distinct
+  auto build_dl = [&](char* buf, const Slots& sl) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + 256 * u, e = sl.e[u];
+      if (e < 0 || e >= E || sl.row[u] == INT32_MIN) continue;
+      uint32_t h, m, l;
+      split3x2(sl.v[u], 0.f, h, m, l);
+      const int r = i / k, off = e * 64 + (((r >> 3) ^ swz_kc(e)) << 4) + (r & 7) * 2;
+      *reinterpret_cast<uint16_t*>(buf + off) = (uint16_t)h;
+      *reinterpret_cast<uint16_t*>(buf + RW_PLANE + off) = (uint16_t)m;
+      *reinterpret_cast<uint16_t*>(buf + 2 * RW_PLANE + off) = (uint16_t)l;
+    }
+  };
+  auto zero_dl = [&](char* buf) {
+    for (int i = tid; i < 3 * RW_PLANE / 16; i += 256) reinterpret_cast<u32x4*>(buf)[i] = u32x4{0u, 0u, 0u, 0u};
+  };
+  u32x4 xv[2][4];
+  Slots sv[2];
+  load_x(0, xv[0]);
+  load_slots(0, sv[0]);
+  load_x(1, xv[1]);
+  load_slots(1, sv[1]);
+  for (int sl = 0; sl < nslab; ++sl) {
+    char* buf = smem + (sl & 1) * RW_BUF;
+    zero_dl(buf);
+    if (sl & 1) store_x(buf, xv[1]);   // register sets by parity, so both stay in registers
+    else store_x(buf, xv[0]);
+    __syncthreads();
+    if (sl & 1) build_dl(buf, sv[1]);
+    else build_dl(buf, sv[0]);
+    if (sl + 2 < nslab) {
+      if (sl & 1) {
+        load_x(sl + 2, xv[1]);
+        load_slots(sl + 2, sv[1]);
+      } else {
+        load_x(sl + 2, xv[0]);
+        load_slots(sl + 2, sv[0]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kk = 16 * h;
+      bf16x8 fa[3][2], fb[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const int row = mi * 32 + (lane & 31), cch = (kk >> 3) + (lane >> 5);
+        const int off = row * 64 + ((cch ^ swz_kc(row)) << 4);
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl) fa[pl][mi] = *reinterpret_cast<const bf16x8*>(buf + pl * RW_PLANE + off);
+      }
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int col0 = wave * 64 + ni * 32;
+        s16x4 p2[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int g = lane >> 4, a = lane & 15;
+          const int kr = kk + 8 * (g >> 1) + 4 * tt + (a >> 2);
+          const int m = col0 + 16 * (g & 1) + 4 * (a & 3);
+          const int off = 3 * RW_PLANE + kr * 512 + (((m >> 3) ^ swz_ks(kr)) << 4) + ((m & 7) << 1);
+          p2[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + off));
+        }
+        fb[ni] = join8(p2[0], p2[1]);
+      }
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[pl][mi], fb[ni], acc[mi][ni], 0, 0, 0);
+    }
+  }
+  // MFMA layout: register r of a lane is row 8(r/4) + 4(lane/32) + r%4 of
+  // its 32 x 32 block, column lane % 32
+  float* pb = part + (int64_t)blockIdx.y * E * d;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int e = mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (e < E) pb[(int64_t)e * d + c0 + wave * 64 + ni * 32 + (lane & 31)] = acc[mi][ni][r];
+      }
+}
+
+// dW_r[e][c] = sum over the token chunks, in order, of part[chunk][e][c];
+// eight chunks' loads in flight at a time, added in chunk order
+__global__ __launch_bounds__(256) void router_wgrad_chunks_reduce_kernel(const float* __restrict__ part, int nchunk,
+                                                                         int E, int64_t d, float* __restrict__ dw) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x, n = (int64_t)E * d;
+  if (i >= n) return;
+  float s = 0.f;
+  int c = 0;
+  for (; c + 8 <= nchunk; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(c + u) * n + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; c < nchunk; ++c) s += part[(int64_t)c * n + i];
+  dw[i] = s;
+}
+
 // dx[t] = extra[t] + sum_j dx_perm[row_of[t,j]] + sum_j dl[t,j] * w_router[idx[t,j]]
 // (dx_perm: bf16 rows, summed in fp32; extra: the shared expert's input
 // gradient in fp32, or null; a slot without a row, row_of < 0, is never
@@ -414,6 +591,8 @@ __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
 
+inline bool router_mfma(int E, int64_t d) { return E <= RW_EMAX && d % 256 == 0; }
+
 struct BwdLayout {
   size_t dy_perm, dgu, dx_perm, dg, dl, dl_perm, gperm, dg_part, mt_prefix, rc_prefix, seg_beg, seg_end, rpart, aux,
       kg_sched, kg_partial, total;
@@ -451,7 +630,8 @@ BwdLayout layout(int64_t T, int k, int E, int64_t d, int64_t f) {
   L.rc_prefix = take((size_t)(2 * E + 1) * 4);
   L.seg_beg = take((size_t)2 * E * 4);
   L.seg_end = take((size_t)2 * E * 4);
-  L.rpart = take((size_t)(ceil_div(A, RCH) + 2 * E) * d * 4);
+  L.rpart = take(std::max((size_t)(ceil_div(A, RCH) + 2 * E) * d * 4,
+                           router_mfma(E, d) ? (size_t)ceil_div(T, RW_TCH) * E * d * 4 : 0));
   L.aux = take(moe_aux_bwd_workspace(T, E, d));
   L.kg_sched = take(kg_sched_need(A, E, d, f));
   L.kg_partial = take(kg_partial_need(A, E, d, f));
@@ -604,6 +784,14 @@ extern "C" moe_status moe_backward(const moe_bwd_args* a, void* stream) {
                                                            a->logits, (int)T, k, E, a->score_fn, dg, dl, dl_perm);
   MOE_LAUNCH_CHECK();
   if (aux) {
+  } else if (router && router_mfma(E, d)) {
+    const int nchunk = (int)ceil_div(T, RW_TCH);
+    router_wgrad_mfma_kernel<<<dim3((unsigned)(d / 256), (unsigned)nchunk), 256, 0, s>>>(
+        static_cast<const bf16_t*>(a->x), a->topk_idx, a->row_of, dl, (int)T, k, E, d, rpart);
+    MOE_LAUNCH_CHECK();
+    router_wgrad_chunks_reduce_kernel<<<(unsigned)ceil_div((int64_t)E * d, 256), 256, 0, s>>>(rpart, nchunk, E, d,
+                                                                                           a->dw_router);
+    MOE_LAUNCH_CHECK();
   } else if (router) {
     router_seg_schedule_kernel<<<1, 1024, 0, s>>>(a->offsets, counts, E, seg_beg, seg_end, rc_prefix);
     MOE_LAUNCH_CHECK();

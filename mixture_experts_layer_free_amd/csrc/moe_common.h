@@ -38,6 +38,24 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
 }
 __device__ __forceinline__ float silu_f32(float z) { return z * sigmoid_fast(z); }
 
+// Splits two fp32 values a, b exactly into three bf16 parts each, v = hi +
+// mid + lo, packed in pairs (a in the low half): hi = the top 16 bits
+// (truncation, so v - hi is exact), mid = the top 16 bits of r1 = v - hi, lo
+// = the top 16 bits of r2 = r1 - mid, which has at most 8 significant bits
+// left and so is exact (8 + 8 + 8 bits hold the 24-bit fp32 significand, in
+// the normal range).  Each pair is one byte permutation of the two words.
+// Against a bf16 factor, each part's product is exact in fp32.
+__device__ __forceinline__ void split3x2(float a, float b, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  constexpr uint32_t TOP = 0x07060302u;   // bytes 2, 3 of the second operand, then of the first
+  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+  hi = __builtin_amdgcn_perm(ub, ua, TOP);
+  const float ra = a - __uint_as_float(ua & 0xFFFF0000u), rb = b - __uint_as_float(ub & 0xFFFF0000u);
+  const uint32_t va = __float_as_uint(ra), vb = __float_as_uint(rb);
+  mid = __builtin_amdgcn_perm(vb, va, TOP);
+  const float sa = ra - __uint_as_float(va & 0xFFFF0000u), sb = rb - __uint_as_float(vb & 0xFFFF0000u);
+  lo = __builtin_amdgcn_perm(__float_as_uint(sb), __float_as_uint(sa), TOP);
+}
+
 // Raw buffer resource over [base, base + bytes), bytes >= 0: loads at
 // offsets past the end read zeros (offsets of 2^31 and up are always past it).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {

@@ -160,21 +160,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
 // (16-byte x loads, 32-byte w loads, 32-bit offsets within the tile's rows, so
 // d < 2^24); the next four 16-deep steps load while the current four
 // multiply.  The RKS partial tiles are added in range order through LDS.
-// Splits two fp32 weights a, b into their bf16 parts, packed in pairs (a in
-// the low half): hi = the top 16 bits (truncation, so w - hi is exact), mid
-// = the top 16 bits of r1 = w - hi, lo = the top 16 bits of r2 = r1 - mid,
-// which has at most 8 significant bits left and so is exact.  Each pair is
-// one byte permutation of the two words.
-__device__ __forceinline__ void split3x2(float a, float b, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-  constexpr uint32_t TOP = 0x07060302u;   // bytes 2, 3 of the second operand, then of the first
-  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
-  hi = __builtin_amdgcn_perm(ub, ua, TOP);
-  const float ra = a - __uint_as_float(ua & 0xFFFF0000u), rb = b - __uint_as_float(ub & 0xFFFF0000u);
-  const uint32_t va = __float_as_uint(ra), vb = __float_as_uint(rb);
-  mid = __builtin_amdgcn_perm(vb, va, TOP);
-  const float sa = ra - __uint_as_float(va & 0xFFFF0000u), sb = rb - __uint_as_float(vb & 0xFFFF0000u);
-  lo = __builtin_amdgcn_perm(__float_as_uint(sb), __float_as_uint(sa), TOP);
-}
+// (split3x2, in moe_common.h, splits each weight into its three bf16 parts.)
 
 constexpr int RB_STEPS = 4;   // 16-deep steps in flight
 
