@@ -324,8 +324,8 @@ __global__ __launch_bounds__(256) void router_wgrad_mfma_kernel(const bf16_t* __
       *reinterpret_cast<u32x4*>(buf + 3 * RW_PLANE + r * 512 + ((cc ^ swz_ks(r)) << 4)) = v[q];
     }
   };
-  // A slab's 32 k slots, at most two per thread (k <= 16): expert id, row
-  // and dl, loaded two slabs ahead like x
+  // A slab's 32 * k slots (32 tokens), at most two per thread (k <= 16):
+  // expert id, row and dl, loaded two slabs ahead like x
   struct Slots {
     int e[2], row[2];
     float v[2];
