@@ -863,18 +863,20 @@ void gemm_kernel(Args p) {
   const int grid = gridDim.x, pos = xcd * per + slot;
   int end = total;
   // The last round, when under half full, runs its tiles cut into `split`
-  // column parts (256 x 128, or 256 x 64 with a K-contiguous B) on the
-  // workgroups that would otherwise idle through it.  A column part makes
+  // parts (two column halves of 256 x 128, or four quarters of 128 x 128)
+  // on the workgroups that would otherwise idle through it.  A part makes
   // each of its outputs by the same MFMA sequence along K as the whole tile,
-  // so the results are the same bits.  The parts run first, outside the
-  // persistent loop: inside it, the compiler keeps their set-up values live
-  // across every tile, which costs registers the whole-tile path needs.
-  // An XCD's positions are contiguous, so a tile's parts share its L2.
+  // so the results are the same bits.  A quarter moves half the operand
+  // bytes per slab of a 256 x 64 column part for the same MFMA work; a
+  // quarter below the group's last row has nothing to do and is skipped.
+  // The parts run first, outside the persistent loop: inside it, the
+  // compiler keeps their set-up values live across every tile, which costs
+  // registers the whole-tile path needs.  An XCD's positions are
+  // contiguous, so a tile's parts share its L2.
   if constexpr (TM == 256 && TN == 256 && AK && !KG) {
     const int full_end = total - total % grid, rem = total - full_end;
-    constexpr int smax = BKC ? 4 : 2;   // a K-strided slab's swizzle needs rows of 128 columns
     int split = 1;
-    while (rem > 0 && split < smax && rem * split * 2 <= grid) split *= 2;
+    while (rem > 0 && split < 4 && rem * split * 2 <= grid) split *= 2;
     split = (int)uni((uint32_t)split);
     if (split > 1) {
       end = full_end;
@@ -883,11 +885,14 @@ void gemm_kernel(Args p) {
         tile_at(full_end + pos / split, e, mt, nb);
         const int part = pos % split;
         const int64_t row0 = p.offsets[e] + (int64_t)mt * TM, row_end = p.offsets[e + 1];
-        if (BKC && split == 4)
-          gemm_tile<TM, TN / smax, smax == 4 ? 1 : 2, AK, BKC, KG, EPI, GB, smax>(p, smem, e, nb * smax + part,
-                                                                                row0, row_end, 0, p.K);
-        else
+        if (split == 4) {
+          const int64_t r0 = row0 + (int64_t)(part >> 1) * (TM / 2);
+          if (uni(r0) < uni(row_end))
+            gemm_tile<TM / 2, TN / 2, 2, AK, BKC, KG, EPI, GB, 2>(p, smem, e, nb * 2 + (part & 1), r0, row_end, 0,
+                                                                 p.K);
+        } else {
           gemm_tile<TM, TN / 2, 2, AK, BKC, KG, EPI, GB, 2>(p, smem, e, nb * 2 + part, row0, row_end, 0, p.K);
+        }
       }
     }
   }
